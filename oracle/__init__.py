@@ -1,0 +1,156 @@
+"""fp64 CPU oracle of the selective-SSM scan -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never calls it, and it
+shares no code with the library; both sides only share the seeded input
+generator in ``workloads``.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision); this module
+only converts numpy arrays to contiguous float64 (exact for fp32 and bf16
+values) and calls it through ctypes.  ``oracle.c`` names the pages each
+function follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+class OracleLib:
+    """ctypes binding of one compiled copy of ``oracle.c``."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        lib.oracle_scan_fwd.restype = ctypes.c_int
+        lib.oracle_scan_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp,
+                                        _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+        lib.oracle_state_update.restype = ctypes.c_int
+        lib.oracle_state_update.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int,
+                                            _dp, _i64, _i64, _i64]
+        lib.oracle_affine_compose.restype = None
+        lib.oracle_affine_compose.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64]
+        lib.oracle_step_size.restype = None
+        lib.oracle_step_size.argtypes = [_dp, _dp, ctypes.c_int, _dp, _i64, _i64]
+        lib.oracle_abi_version.restype = ctypes.c_int
+        self.path = path
+        self.lib = lib
+
+    def scan_fwd(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
+                 chunk: int = 0, nthreads: int | None = None, return_state: bool = True):
+        """Sequential fp64 scan from a zero state.
+
+        x, delta, z: [batch, L, d_inner]; B, C: [batch, L, d_state]; A: [d_inner, d_state];
+        D, delta_bias: [d_inner].  Returns (out [batch, L, d_inner], last_state
+        [batch, d_inner, d_state] or None), float64.  ``chunk > 0`` runs the chunked
+        form: per-chunk affine pairs composed in time order, then each chunk re-run."""
+        x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
+        D, z, delta_bias = map(_f64, (D, z, delta_bias))
+        if x.ndim != 3:
+            raise ValueError("x must be [batch, L, d_inner]")
+        batch, L, Dn = x.shape
+        N = A.shape[1]
+        if delta.shape != x.shape or (z is not None and z.shape != x.shape):
+            raise ValueError("delta and z must match x")
+        if A.shape != (Dn, N) or B.shape != (batch, L, N) or C.shape != (batch, L, N):
+            raise ValueError("bad A/B/C shape")
+        if (D is not None and D.shape != (Dn,)) or (delta_bias is not None and delta_bias.shape != (Dn,)):
+            raise ValueError("bad D/delta_bias shape")
+        out = np.empty((batch, L, Dn), dtype=np.float64)
+        last = np.empty((batch, Dn, N), dtype=np.float64) if return_state else None
+        rc = self.lib.oracle_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(delta_bias), int(bool(softplus)), _ptr(out), _ptr(last),
+                                      batch, L, Dn, N, int(chunk), int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle_scan_fwd rejected its arguments")
+        return out, last
+
+    def state_update(self, state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True):
+        """One decode step.  state: [batch, d_inner, d_state]; x, delta, z: [batch, d_inner];
+        B, C: [batch, d_state].  Returns (out [batch, d_inner], new_state) as float64; the
+        ``state`` argument itself is not modified."""
+        st = np.array(state, dtype=np.float64, order="C", copy=True)
+        x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
+        D, z, delta_bias = map(_f64, (D, z, delta_bias))
+        batch, Dn = x.shape
+        N = A.shape[1]
+        if st.shape != (batch, Dn, N) or B.shape != (batch, N) or C.shape != (batch, N):
+            raise ValueError("bad state/B/C shape")
+        out = np.empty((batch, Dn), dtype=np.float64)
+        rc = self.lib.oracle_state_update(_ptr(st), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                          _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                                          _ptr(out), batch, Dn, N)
+        if rc != 0:
+            raise ValueError("oracle_state_update rejected its arguments")
+        return out, st
+
+    def affine_compose(self, later, earlier):
+        """(a2, b2) o (a1, b1) = (a2*a1, a2*b1 + b2): ``earlier`` acts first, then ``later``."""
+        a2, b2 = (np.atleast_1d(_f64(v)) for v in later)
+        a1, b1 = (np.atleast_1d(_f64(v)) for v in earlier)
+        n = a2.size
+        a = np.empty(n)
+        b = np.empty(n)
+        self.lib.oracle_affine_compose(_ptr(a2), _ptr(b2), _ptr(a1), _ptr(b1), _ptr(a), _ptr(b), n)
+        return a, b
+
+    def step_size(self, delta, delta_bias=None, softplus=True):
+        """dt = softplus(delta + bias), or delta + bias; delta: [rows, d_inner]."""
+        d = _f64(np.atleast_2d(delta))
+        bias = _f64(delta_bias)
+        out = np.empty_like(d)
+        self.lib.oracle_step_size(_ptr(d), _ptr(bias), int(bool(softplus)), _ptr(out), d.shape[0], d.shape[1])
+        return out
+
+
+_default: OracleLib | None = None
+
+
+def load() -> OracleLib:
+    """The oracle built from ``oracle.c`` (compiled first if missing or stale)."""
+    global _default
+    if _default is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        _default = OracleLib(path)
+    return _default
+
+
+def scan_fwd(*args, **kw):
+    return load().scan_fwd(*args, **kw)
+
+
+def state_update(*args, **kw):
+    return load().state_update(*args, **kw)
+
+
+def affine_compose(*args, **kw):
+    return load().affine_compose(*args, **kw)
+
+
+def step_size(*args, **kw):
+    return load().step_size(*args, **kw)

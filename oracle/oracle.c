@@ -1,0 +1,246 @@
+/*
+ * oracle.c -- plain, sequential fp64 CPU reference of the selective-SSM scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library calls this code; only the
+ * test suite, the smoke check and the CPU-baseline leg of the benchmark load it.
+ * It shares no source with the GPU library.
+ *
+ * What it computes (every input is upcast exactly to double by the caller):
+ *
+ *   for every batch row b and channel d, independently:
+ *     h[0..N) = 0                                   (zero initial state)
+ *     for t = 0 .. L-1:
+ *       u   = delta[b,t,d] + bias[d]                (bias optional, 0 if absent)
+ *       dt  = softplus(u) if softplus_on else u     (softplus(u) = log(1 + e^u))
+ *       for n: h[n] = exp(dt * A[d,n]) * h[n] + (dt * B[b,t,n]) * x[b,t,d]
+ *       y   = sum_n C[b,t,n] * h[n]
+ *       y  += D[d] * x[b,t,d]                       (optional skip)
+ *       y  *= z * sigmoid(z), z = z[b,t,d]          (optional SiLU gate)
+ *       out[b,t,d] = y
+ *     last_state[b,d,:] = h                         (optional)
+ *
+ * Sources (the pages this follows):
+ *  - "Mamba и State Space Models" (nareshka.ru), section "Ключевая инновация:
+ *    input-dependent parameters": the selective recurrence
+ *    h_t = exp(Delta_t A) h_{t-1} + Delta_t B_t x_t, y_t = C_t h_t; section
+ *    "Selective Scan (core algorithm)": softplus on the step, dA = exp(dt*A),
+ *    dB = dt*B, h starts at zero, y is read after the update at step t;
+ *    section "Реализация MambaBlock": the output is gated by SiLU of the
+ *    residual branch.
+ *  - "State Space Models: Mamba и альтернатива Transformer" (johe.ru), the
+ *    MambaBlock "_scan" code: the D skip y_t = C_t h_t + D x_t, added before
+ *    the gate that the block applies afterwards.
+ *  - "Модуль 8. Альтернативы Transformer" (vladkulikov.com), section 6:
+ *    softplus(u) = log(1 + e^u) keeps the step positive.
+ *  - Same page, section 7: an affine step h -> a h + b is the pair (a, b) and
+ *    two steps compose as (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2), the later
+ *    step written first; the chunked mode below joins chunks with it.
+ *  - Same page, sections 7 and 14: the decode step is the same recurrence for
+ *    one token, continuing from the stored ssm_state [batch, d_inner, d_state].
+ *
+ * Threads split independent (b, d) rows only; the order of the arithmetic
+ * within a row is exactly the loop above.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_ABI 1
+
+int oracle_abi_version(void) { return ORACLE_ABI; }
+
+/* softplus(u) = log(1 + e^u), written as max(u, 0) + log1p(exp(-|u|)) so that
+ * neither branch overflows; the two forms are equal for every real u. */
+static double softplus(double u) { return fmax(u, 0.0) + log1p(exp(-fabs(u))); }
+
+/* SiLU(z) = z * sigmoid(z) = z / (1 + e^{-z}). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* The step size dt for one (b, t, d). */
+static double step_size(double delta, const double* bias, int64_t d, int softplus_on) {
+  double u = delta + (bias ? bias[d] : 0.0);
+  return softplus_on ? softplus(u) : u;
+}
+
+/* One recurrence step of one channel: updates h[0..N) in place and returns y. */
+static double scan_step(double* h, double x, double dt, const double* A_d, const double* B_t,
+                        const double* C_t, const double* D, int64_t d, const double* zp, int64_t N) {
+  for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A_d[n]) * h[n] + (dt * B_t[n]) * x;
+  double y = 0.0;
+  for (int64_t n = 0; n < N; ++n) y += C_t[n] * h[n];
+  if (D) y += D[d] * x;
+  if (zp) y *= silu(*zp);
+  return y;
+}
+
+typedef struct {
+  const double *x, *delta, *A, *B, *C, *D, *z, *bias;
+  int softplus_on;
+  double *out, *last_state;
+  int64_t batch, L, Dn, N, chunk;
+  int64_t row_begin, row_end; /* rows are r = b * Dn + d */
+} job_t;
+
+static void scan_rows(const job_t* j) {
+  double* h = (double*)calloc((size_t)j->N, sizeof(double));
+  for (int64_t r = j->row_begin; r < j->row_end; ++r) {
+    int64_t b = r / j->Dn, d = r % j->Dn;
+    for (int64_t n = 0; n < j->N; ++n) h[n] = 0.0;
+    for (int64_t t = 0; t < j->L; ++t) {
+      int64_t e = (b * j->L + t) * j->Dn + d;          /* [batch, L, d_inner] */
+      const double* Bt = j->B + (b * j->L + t) * j->N; /* [batch, L, d_state] */
+      const double* Ct = j->C + (b * j->L + t) * j->N;
+      double dt = step_size(j->delta[e], j->bias, d, j->softplus_on);
+      double y = scan_step(h, j->x[e], dt, j->A + d * j->N, Bt, Ct, j->D, d, j->z ? j->z + e : NULL, j->N);
+      j->out[e] = y;
+    }
+    if (j->last_state)
+      for (int64_t n = 0; n < j->N; ++n) j->last_state[(b * j->Dn + d) * j->N + n] = h[n];
+  }
+  free(h);
+}
+
+/* Chunked form: each chunk of `chunk` steps is first reduced to its affine
+ * pair per state coordinate, (P, e) with P = product of the chunk's exp(dt*A)
+ * and e = the chunk's end state started from zero.  The pairs are composed in
+ * time order, (a2,b2) o (a1,b1) = (a2*a1, a2*b1 + b2), which gives each chunk's
+ * incoming state; each chunk is then re-run from that state to produce y. */
+static void scan_rows_chunked(const job_t* j) {
+  const int64_t N = j->N, L = j->L, Tc = j->chunk;
+  const int64_t nch = (L + Tc - 1) / Tc;
+  double* P = (double*)malloc((size_t)(nch * N) * sizeof(double));
+  double* E = (double*)malloc((size_t)(nch * N) * sizeof(double));
+  double* h = (double*)malloc((size_t)N * sizeof(double));
+  double* acc_a = (double*)malloc((size_t)N * sizeof(double));
+  double* acc_b = (double*)malloc((size_t)N * sizeof(double));
+  for (int64_t r = j->row_begin; r < j->row_end; ++r) {
+    int64_t b = r / j->Dn, d = r % j->Dn;
+    const double* A_d = j->A + d * N;
+    /* pass 1: per-chunk affine pairs */
+    for (int64_t k = 0; k < nch; ++k) {
+      double* Pk = P + k * N;
+      double* Ek = E + k * N;
+      for (int64_t n = 0; n < N; ++n) { Pk[n] = 1.0; Ek[n] = 0.0; }
+      int64_t t1 = (k + 1) * Tc < L ? (k + 1) * Tc : L;
+      for (int64_t t = k * Tc; t < t1; ++t) {
+        int64_t e = (b * L + t) * j->Dn + d;
+        const double* Bt = j->B + (b * L + t) * N;
+        double dt = step_size(j->delta[e], j->bias, d, j->softplus_on);
+        for (int64_t n = 0; n < N; ++n) {
+          double a = exp(dt * A_d[n]);
+          Pk[n] = a * Pk[n];
+          Ek[n] = a * Ek[n] + (dt * Bt[n]) * j->x[e];
+        }
+      }
+    }
+    /* pass 2: compose the pairs in time order; chunk k starts from acc applied to h = 0 */
+    for (int64_t n = 0; n < N; ++n) { acc_a[n] = 1.0; acc_b[n] = 0.0; }
+    for (int64_t k = 0; k < nch; ++k) {
+      for (int64_t n = 0; n < N; ++n) h[n] = acc_b[n]; /* acc(0) = acc_a*0 + acc_b */
+      int64_t t1 = (k + 1) * Tc < L ? (k + 1) * Tc : L;
+      for (int64_t t = k * Tc; t < t1; ++t) {
+        int64_t e = (b * L + t) * j->Dn + d;
+        const double* Bt = j->B + (b * L + t) * N;
+        const double* Ct = j->C + (b * L + t) * N;
+        double dt = step_size(j->delta[e], j->bias, d, j->softplus_on);
+        j->out[e] = scan_step(h, j->x[e], dt, A_d, Bt, Ct, j->D, d, j->z ? j->z + e : NULL, N);
+      }
+      for (int64_t n = 0; n < N; ++n) { /* acc = (P_k, E_k) o acc */
+        double a2 = P[k * N + n], b2 = E[k * N + n];
+        acc_b[n] = a2 * acc_b[n] + b2;
+        acc_a[n] = a2 * acc_a[n];
+      }
+    }
+    if (j->last_state)
+      for (int64_t n = 0; n < N; ++n) j->last_state[(b * j->Dn + d) * N + n] = acc_b[n];
+  }
+  free(P); free(E); free(h); free(acc_a); free(acc_b);
+}
+
+static void* run_job(void* p) {
+  const job_t* j = (const job_t*)p;
+  if (j->chunk > 0) scan_rows_chunked(j);
+  else scan_rows(j);
+  return NULL;
+}
+
+static int run_threads(job_t base, int nthreads) {
+  int64_t rows = base.batch * base.Dn;
+  if (rows <= 0) return 0;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > rows) nthreads = (int)rows;
+  if (nthreads == 1) { base.row_begin = 0; base.row_end = rows; run_job(&base); return 0; }
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  job_t* jobs = (job_t*)malloc(sizeof(job_t) * (size_t)nthreads);
+  int started = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = base;
+    jobs[i].row_begin = rows * i / nthreads;
+    jobs[i].row_end = rows * (i + 1) / nthreads;
+  }
+  for (int i = 0; i < nthreads; ++i) {
+    if (pthread_create(&th[i], NULL, run_job, &jobs[i]) != 0) break;
+    ++started;
+  }
+  for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+  /* rows a failed thread creation left undone are run here */
+  for (int i = started; i < nthreads; ++i) run_job(&jobs[i]);
+  free(th); free(jobs);
+  return 0;
+}
+
+/* Full forward scan.  Shapes: x, delta, z, out [batch, L, Dn]; B, C [batch, L, N];
+ * A [Dn, N]; D, bias [Dn]; last_state [batch, Dn, N].  D, z, bias, last_state may be
+ * NULL.  chunk > 0 selects the chunked form with chunks of that many steps.
+ * Returns 0, or -1 on bad arguments. */
+int oracle_scan_fwd(const double* x, const double* delta, const double* A, const double* B,
+                    const double* C, const double* D, const double* z, const double* bias,
+                    int softplus_on, double* out, double* last_state, int64_t batch, int64_t L,
+                    int64_t Dn, int64_t N, int64_t chunk, int nthreads) {
+  if (!x || !delta || !A || !B || !C || !out) return -1;
+  if (batch < 0 || L < 0 || Dn < 0 || N <= 0 || chunk < 0) return -1;
+  if (L == 0) {
+    if (last_state) memset(last_state, 0, sizeof(double) * (size_t)(batch * Dn * N));
+    return 0;
+  }
+  job_t j = {x, delta, A, B, C, D, z, bias, softplus_on, out, last_state, batch, L, Dn, N, chunk, 0, 0};
+  return run_threads(j, nthreads);
+}
+
+/* One decode step: state [batch, Dn, N] is read and overwritten; x, delta, z, out
+ * [batch, Dn]; B, C [batch, N].  Same arithmetic as one step of the scan. */
+int oracle_state_update(double* state, const double* x, const double* delta, const double* A,
+                        const double* B, const double* C, const double* D, const double* z,
+                        const double* bias, int softplus_on, double* out, int64_t batch,
+                        int64_t Dn, int64_t N) {
+  if (!state || !x || !delta || !A || !B || !C || !out) return -1;
+  if (batch < 0 || Dn < 0 || N <= 0) return -1;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t d = 0; d < Dn; ++d) {
+      int64_t e = b * Dn + d;
+      double dt = step_size(delta[e], bias, d, softplus_on);
+      out[e] = scan_step(state + e * N, x[e], dt, A + d * N, B + b * N, C + b * N, D, d,
+                         z ? z + e : NULL, N);
+    }
+  return 0;
+}
+
+/* The affine-pair operator on arrays: (a, b) = (a2, b2) o (a1, b1), later step first. */
+void oracle_affine_compose(const double* a2, const double* b2, const double* a1, const double* b1,
+                           double* a, double* b, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    double na = a2[i] * a1[i];
+    double nb = a2[i] * b1[i] + b2[i];
+    a[i] = na;
+    b[i] = nb;
+  }
+}
+
+/* The step size on its own (softplus branch pinned against a library routine). */
+void oracle_step_size(const double* delta, const double* bias, int softplus_on, double* out,
+                      int64_t rows, int64_t Dn) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t d = 0; d < Dn; ++d) out[r * Dn + d] = step_size(delta[r * Dn + d], bias, d, softplus_on);
+}

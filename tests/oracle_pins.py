@@ -1,0 +1,334 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes a bound oracle (``oracle.OracleLib``) and raises
+AssertionError when the oracle disagrees with an independent statement of the
+result: a brute-force formula computed here with numpy (never the oracle's
+recurrence), a closed form, a special case, an invariant, or a value printed
+on the pages.  ``test_oracle_pins.py`` runs them against the real oracle and
+``test_oracle_mutants.py`` runs them against copies of the oracle with planted
+mistakes, each of which must fail at least one pin.
+
+Sources of the statements:
+  * "State Space Models: Mamba и альтернатива Transformer" (johe.ru), S4
+    section, step 3 "Convolution form": a time-invariant SSM is a causal
+    convolution y = K * u with K = [C B, C A B, C A^2 B, ...] (the discrete
+    B-bar is meant), and the "Параллельная форма" passage: the state is a
+    sum over inputs of products of the transitions between them.
+  * "Модуль 8. Альтернативы Transformer" (vladkulikov.com), section 7: the
+    coefficient of input j in output i >= j is C_i^T B_j times the product of
+    the transitions r = j+1..i (semi-separable matrix); the affine-pair
+    operator and its worked example (tests/golden/affine_pair.txt); section
+    3 "Фильтр": with stable diagonal dynamics each coordinate decays on its
+    own; section 4: a NaN spreads to all later steps.
+  * "Mamba и State Space Models" (nareshka.ru), "Ключевая инновация": the
+    selective recurrence and the readout after the update.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _softplus(u):
+    return np.logaddexp(0.0, u)  # log(e^0 + e^u) = log(1 + e^u), numpy's routine
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    scale = max(1e-300, float(np.max(np.abs(b))))
+    err = float(np.max(np.abs(a - b))) / scale
+    assert err <= rtol, f"{what}: relative error {err:.3e} > {rtol:.1e}"
+
+
+def _rand_case(rng, batch, L, Dn, N, dmin=-4.0, dmax=0.5):
+    return dict(
+        x=rng.standard_normal((batch, L, Dn)),
+        delta=rng.uniform(dmin, dmax, (batch, L, Dn)),
+        z=rng.standard_normal((batch, L, Dn)),
+        B=rng.standard_normal((batch, L, N)),
+        C=rng.standard_normal((batch, L, N)),
+        A=-np.exp(rng.uniform(-1.0, 1.5, (Dn, N))),
+        D=rng.standard_normal(Dn),
+        delta_bias=rng.uniform(-1.0, 1.0, Dn),
+    )
+
+
+# --------------------------------------------------------------------------- pins
+
+
+def pin_affine_worked_example(orc):
+    """The pages' worked example of the affine-pair operator, exact in integers."""
+    rows = np.loadtxt(os.path.join(GOLDEN, "affine_pair.txt"), comments="#", ndmin=2)
+    for la, lb, ea, eb, ca, cb in rows:
+        a, b = orc.affine_compose((la, lb), (ea, eb))
+        assert (a[0], b[0]) == (ca, cb), f"({la},{lb}) o ({ea},{eb}) gave ({a[0]},{b[0]}), expected ({ca},{cb})"
+
+
+def pin_step_size(orc):
+    """softplus(delta + bias) against numpy's logaddexp(0, u); the identity branch exactly."""
+    rng = np.random.default_rng(5)
+    delta = np.concatenate([np.linspace(-60, 60, 241), rng.uniform(-10, 10, 259)]).reshape(5, 100)
+    bias = rng.uniform(-2, 2, 100)
+    got = orc.step_size(delta, bias, softplus=True)
+    want = _softplus(delta + bias)
+    rel = np.max(np.abs(got - want) / np.abs(want))
+    assert rel < 4e-16 * 8, f"softplus relative error {rel:.2e}"
+    mid = delta[np.abs(delta + bias) < 30]
+    midb = np.broadcast_to(bias, delta.shape)[np.abs(delta + bias) < 30]
+    textbook = np.array([math.log1p(math.exp(u)) for u in (mid + midb)])
+    got_mid = got[np.abs(delta + bias) < 30]
+    assert np.max(np.abs(got_mid - textbook) / textbook) < 1e-15, "softplus vs log1p(exp(u))"
+    got0 = orc.step_size(delta, bias, softplus=False)
+    assert np.array_equal(got0, delta + bias), "softplus=0 must give delta + bias exactly"
+    # large arguments: softplus(u) -> u, tiny: softplus(u) -> e^u
+    big = orc.step_size(np.array([[700.0]]), None, softplus=True)[0, 0]
+    assert big == 700.0
+    tiny = orc.step_size(np.array([[-700.0]]), None, softplus=True)[0, 0]
+    assert abs(tiny - math.exp(-700.0)) <= 1e-15 * math.exp(-700.0)
+
+
+def pin_lti_convolution(orc):
+    """Time-invariant Delta, B, C: the scan equals the causal convolution y = K * x
+    (+ D x, then the gate) with K_k = sum_n C_n exp(k dt A_n) dt B_n, brute force."""
+    rng = np.random.default_rng(11)
+    batch, L, Dn, N = 2, 40, 3, 4
+    A = -np.exp(rng.uniform(-1.0, 1.5, (Dn, N)))
+    Bc = rng.standard_normal((batch, N))
+    Cc = rng.standard_normal((batch, N))
+    dconst = rng.uniform(-3.0, 0.0, (batch, Dn))
+    bias = rng.uniform(-1.0, 1.0, Dn)
+    dt = _softplus(dconst + bias)                       # [batch, Dn]
+    x = rng.standard_normal((batch, L, Dn))
+    z = rng.standard_normal((batch, L, Dn))
+    D = rng.standard_normal(Dn)
+    delta = np.repeat(dconst[:, None, :], L, axis=1)
+    B = np.repeat(Bc[:, None, :], L, axis=1)
+    C = np.repeat(Cc[:, None, :], L, axis=1)
+    out, last = orc.scan_fwd(x, delta, A, B, C, D, z, bias, softplus=True)
+    k = np.arange(L, dtype=np.float64)
+    # decay[b, d, k, n] = exp(k * dt[b,d] * A[d,n])
+    decay = np.exp(k[None, None, :, None] * dt[:, :, None, None] * A[None, :, None, :])
+    K = np.einsum("bn,bdkn->bdk", Cc, decay * (dt[:, :, None, None] * Bc[:, None, None, :]))
+    y = np.zeros((batch, L, Dn))
+    for t in range(L):
+        for j in range(t + 1):
+            y[:, t, :] += K[:, :, t - j] * x[:, j, :]
+    y = (y + D * x) * _silu(z)
+    _close(out, y, 1e-12, "LTI convolution")
+    # final state: h[n] = sum_j exp((L-1-j) dt A_n) dt B_n x_j
+    hs = np.zeros((batch, Dn, N))
+    for j in range(L):
+        hs += decay[:, :, L - 1 - j, :] * dt[:, :, None] * Bc[:, None, :] * x[:, j, :, None]
+    _close(last, hs, 1e-12, "LTI final state")
+
+
+def pin_semiseparable(orc):
+    """Time-varying (selective) case: y_i = sum_{j<=i} sum_n C_i[n] exp(A_n * sum_{r=j+1..i} dt_r)
+    dt_j B_j[n] x_j + D x_i, gated; brute force over (i, j) with the step sums taken directly."""
+    for softplus in (True, False):
+        rng = np.random.default_rng(21 + softplus)
+        batch, L, Dn, N = 2, 24, 3, 3
+        c = _rand_case(rng, batch, L, Dn, N, dmin=-4.0 if softplus else 0.01, dmax=0.5)
+        if not softplus:
+            c["delta_bias"] = rng.uniform(0.0, 0.2, Dn)
+        out, last = orc.scan_fwd(softplus=softplus, **c)
+        u = c["delta"] + c["delta_bias"]
+        dt = _softplus(u) if softplus else u               # [batch, L, Dn]
+        A, B, C, x = c["A"], c["B"], c["C"], c["x"]
+        y = np.zeros((batch, L, Dn))
+        hL = np.zeros((batch, Dn, N))
+        for i in range(L):
+            for j in range(i + 1):
+                seg = dt[:, j + 1:i + 1, :].sum(axis=1)    # [batch, Dn]
+                w = np.exp(seg[:, :, None] * A[None, :, :]) * (dt[:, j, :, None] * B[:, j, None, :])
+                y[:, i, :] += np.einsum("bn,bdn->bd", C[:, i, :], w) * x[:, j, :]
+                if i == L - 1:
+                    hL += w * x[:, j, :, None]
+        y = (y + c["D"] * x) * _silu(c["z"])
+        _close(out, y, 1e-11, f"semi-separable form (softplus={softplus})")
+        _close(last, hL, 1e-11, f"semi-separable final state (softplus={softplus})")
+
+
+def pin_delta_zero(orc):
+    """Delta = 0 with softplus off: the transition is the identity and the input term vanishes,
+    so h stays 0 and y = D x exactly (times the gate); a tiny Delta moves y by O(Delta)."""
+    rng = np.random.default_rng(31)
+    batch, L, Dn, N = 2, 16, 5, 4
+    c = _rand_case(rng, batch, L, Dn, N)
+    c["delta"] = np.zeros_like(c["delta"])
+    out, last = orc.scan_fwd(c["x"], c["delta"], c["A"], c["B"], c["C"], c["D"], None, None, softplus=False)
+    assert np.array_equal(out, c["D"] * c["x"]), "Delta=0 must give y = D x exactly"
+    assert np.array_equal(last, np.zeros_like(last)), "Delta=0 must leave the state at zero"
+    out, _ = orc.scan_fwd(c["x"], c["delta"], c["A"], c["B"], c["C"], c["D"], c["z"], None, softplus=False)
+    _close(out, c["D"] * c["x"] * _silu(c["z"]), 1e-15, "Delta=0 with the gate")
+    eps = 1e-8
+    out, _ = orc.scan_fwd(c["x"], c["delta"] + eps, c["A"], c["B"], c["C"], c["D"], None, None, softplus=False)
+    dev = np.max(np.abs(out - c["D"] * c["x"]))
+    bound = eps * L * N * np.max(np.abs(c["B"])) * np.max(np.abs(c["C"])) * np.max(np.abs(c["x"]))
+    assert 0 < dev <= bound, f"Delta=1e-8 deviation {dev:.3e} outside (0, {bound:.3e}]"
+
+
+def pin_impulse_closed_form(orc):
+    """N = 1, constant dt, B = C = 1, x = unit impulse at t = 0, no D, no gate:
+    y_t = dt * exp(t * dt * A).  With dt = 0.1 and A = -1, y_5 = 0.1 * e^{-0.5}."""
+    L = 12
+    x = np.zeros((1, L, 1))
+    x[0, 0, 0] = 1.0
+    out, last = orc.scan_fwd(x, np.full((1, L, 1), 0.1), np.array([[-1.0]]), np.ones((1, L, 1)),
+                             np.ones((1, L, 1)), None, None, None, softplus=False)
+    want = 0.1 * np.exp(-0.1 * np.arange(L))
+    _close(out[0, :, 0], want, 1e-14, "impulse response")
+    assert abs(out[0, 5, 0] - 0.1 * math.exp(-0.5)) <= 1e-15 * 0.1
+    assert abs(last[0, 0, 0] - 0.1 * math.exp(-0.1 * (L - 1))) <= 1e-15 * 0.1
+
+
+def pin_chunked_composition(orc):
+    """The chunked form (affine pairs composed in time order) equals the sequential scan
+    for every chunk length, including ones that do not divide L."""
+    rng = np.random.default_rng(41)
+    batch, L, Dn, N = 2, 29, 3, 4
+    c = _rand_case(rng, batch, L, Dn, N)
+    ref, ref_last = orc.scan_fwd(**c)
+    for tc in (1, 2, 3, 7, L // 4, L - 1, L, L + 5):
+        out, last = orc.scan_fwd(chunk=tc, **c)
+        _close(out, ref, 1e-12, f"chunked output (chunk={tc})")
+        _close(last, ref_last, 1e-12, f"chunked final state (chunk={tc})")
+
+
+def pin_decode_equals_scan(orc):
+    """L decode steps from a zero state reproduce one scan bitwise, and
+    prefill(L1) followed by L2 decode steps equals scan(L1 + L2) bitwise."""
+    rng = np.random.default_rng(51)
+    batch, L, Dn, N = 3, 17, 4, 5
+    c = _rand_case(rng, batch, L, Dn, N)
+    ref, ref_last = orc.scan_fwd(**c)
+    state = np.zeros((batch, Dn, N))
+    for t in range(L):
+        y, state = orc.state_update(state, c["x"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t],
+                                    c["D"], c["z"][:, t], c["delta_bias"])
+        assert np.array_equal(y, ref[:, t]), f"decode step {t} differs from the scan"
+    assert np.array_equal(state, ref_last), "decode final state differs from the scan"
+    L1 = 9
+    pre = {k: (v[:, :L1] if k in ("x", "delta", "z", "B", "C") else v) for k, v in c.items()}
+    out1, st = orc.scan_fwd(**pre)
+    assert np.array_equal(out1, ref[:, :L1])
+    for t in range(L1, L):
+        y, st = orc.state_update(st, c["x"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t],
+                                 c["D"], c["z"][:, t], c["delta_bias"])
+        assert np.array_equal(y, ref[:, t]), f"continued decode step {t} differs"
+    assert np.array_equal(st, ref_last)
+
+
+def pin_invariants(orc):
+    """Linearity in x, causality, channel permutation, B*s with C/s, batch independence."""
+    rng = np.random.default_rng(61)
+    batch, L, Dn, N = 2, 20, 6, 4
+    c = _rand_case(rng, batch, L, Dn, N)
+    y, _ = orc.scan_fwd(**c)
+    # linearity in x (Delta, B, C, z fixed)
+    x2 = rng.standard_normal(c["x"].shape)
+    y2, _ = orc.scan_fwd(**{**c, "x": x2})
+    y12, _ = orc.scan_fwd(**{**c, "x": 2.0 * c["x"] - 3.0 * x2})
+    _close(y12, 2.0 * y - 3.0 * y2, 1e-13, "linearity in x")
+    # causality: changing x at t0 leaves every earlier output bitwise unchanged, changes later ones
+    t0 = 11
+    xp = c["x"].copy()
+    xp[:, t0, :] += 1.0
+    yp, _ = orc.scan_fwd(**{**c, "x": xp})
+    assert np.array_equal(yp[:, :t0], y[:, :t0]), "output before t0 depends on x[t0]"
+    assert np.all(yp[:, t0] != y[:, t0]), "output at t0 does not depend on x[t0]"
+    # permutation of channels
+    perm = rng.permutation(Dn)
+    cp = dict(c)
+    for k in ("x", "delta", "z"):
+        cp[k] = c[k][:, :, perm]
+    cp["A"], cp["D"], cp["delta_bias"] = c["A"][perm], c["D"][perm], c["delta_bias"][perm]
+    yq, _ = orc.scan_fwd(**cp)
+    assert np.array_equal(yq, y[:, :, perm]), "channel permutation"
+    # B scaled by s and C by 1/s (powers of two: exact)
+    ys, _ = orc.scan_fwd(**{**c, "B": c["B"] * 8.0, "C": c["C"] / 8.0})
+    assert np.array_equal(ys, y), "B*s, C/s must leave y unchanged"
+    # batch rows are independent
+    for b in range(batch):
+        cb = {k: (v[b:b + 1] if k in ("x", "delta", "z", "B", "C") else v) for k, v in c.items()}
+        yb, _ = orc.scan_fwd(**cb)
+        assert np.array_equal(yb[0], y[b]), f"batch row {b} depends on other rows"
+
+
+def pin_decay(orc):
+    """Stable diagonal dynamics (A < 0, dt > 0) with no input: every state coordinate's
+    magnitude is non-increasing, step by step, and strictly decreases when nonzero."""
+    rng = np.random.default_rng(71)
+    batch, Dn, N = 2, 3, 4
+    A = -np.exp(rng.uniform(-1.0, 1.5, (Dn, N)))
+    state = rng.standard_normal((batch, Dn, N))
+    zeros = np.zeros((batch, Dn))
+    for t in range(10):
+        delta = rng.uniform(-3, 1, (batch, Dn))
+        y, nxt = orc.state_update(state, zeros, delta, A, rng.standard_normal((batch, N)),
+                                  rng.standard_normal((batch, N)), None, None, None)
+        assert np.all(np.abs(nxt) < np.abs(state)), f"step {t}: a coordinate did not decay"
+        state = nxt
+
+
+def pin_nan_propagation(orc):
+    """A NaN is never dropped: in x[b,t0,d0] it reaches y[b, t>=t0, d0] and the final state of
+    (b, d0) only; in B[b,t0,:] every channel of row b from t0 on; in C[b,t0,:] only step t0 of row b."""
+    rng = np.random.default_rng(81)
+    batch, L, Dn, N = 2, 12, 3, 4
+    c = _rand_case(rng, batch, L, Dn, N)
+    t0, b0, d0 = 5, 1, 2
+    cx = {**c, "x": c["x"].copy()}
+    cx["x"][b0, t0, d0] = np.nan
+    y, last = orc.scan_fwd(**cx)
+    mask = np.zeros(y.shape, bool)
+    mask[b0, t0:, d0] = True
+    assert np.all(np.isnan(y[mask])) and np.all(np.isfinite(y[~mask])), "NaN in x: wrong spread"
+    lm = np.zeros(last.shape, bool)
+    lm[b0, d0, :] = True
+    assert np.all(np.isnan(last[lm])) and np.all(np.isfinite(last[~lm])), "NaN in x: wrong final state"
+    cb = {**c, "B": c["B"].copy()}
+    cb["B"][b0, t0, 1] = np.nan
+    y, _ = orc.scan_fwd(**cb)
+    mask = np.zeros(y.shape, bool)
+    mask[b0, t0:, :] = True
+    assert np.all(np.isnan(y[mask])) and np.all(np.isfinite(y[~mask])), "NaN in B: wrong spread"
+    cc = {**c, "C": c["C"].copy()}
+    cc["C"][b0, t0, 1] = np.nan
+    y, _ = orc.scan_fwd(**cc)
+    mask = np.zeros(y.shape, bool)
+    mask[b0, t0, :] = True
+    assert np.all(np.isnan(y[mask])) and np.all(np.isfinite(y[~mask])), "NaN in C: wrong spread"
+
+
+def pin_optional_inputs(orc):
+    """Each optional input switches exactly its own term: no D means no skip (y = C h),
+    no gate means no SiLU factor, no bias means dt = softplus(delta)."""
+    rng = np.random.default_rng(91)
+    batch, L, Dn, N = 1, 10, 3, 4
+    c = _rand_case(rng, batch, L, Dn, N)
+    full, _ = orc.scan_fwd(**c)
+    noD, _ = orc.scan_fwd(**{**c, "D": None})
+    _close((noD / _silu(c["z"]) + c["D"] * c["x"]) * _silu(c["z"]), full, 1e-13, "D skip term")
+    nogate, _ = orc.scan_fwd(**{**c, "z": None})
+    _close(nogate * _silu(c["z"]), full, 1e-13, "SiLU gate factor")
+    nobias, _ = orc.scan_fwd(**{**c, "delta_bias": None, "delta": c["delta"] + c["delta_bias"]})
+    _close(nobias, full, 1e-13, "bias folded into delta")
+
+
+ALL_PINS = [
+    pin_affine_worked_example, pin_step_size, pin_lti_convolution, pin_semiseparable, pin_delta_zero,
+    pin_impulse_closed_form, pin_chunked_composition, pin_decode_equals_scan, pin_invariants,
+    pin_decay, pin_nan_propagation, pin_optional_inputs,
+]

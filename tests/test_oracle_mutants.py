@@ -1,0 +1,73 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Each mutant is a copy of oracle/oracle.c with one plausible mistake (a dropped
+term, a wrong sign or index, a transposed operand, a wrong composition order),
+compiled with gcc into a temporary directory.  If every pin still passed for
+some mutant, the pins would not be pinning that part of the oracle.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+import oracle_pins
+
+MUTANTS = {
+    "drop_D_skip": ("if (D) y += D[d] * x;", ""),
+    "exp_sign": ("h[n] = exp(dt * A_d[n]) * h[n]", "h[n] = exp(-dt * A_d[n]) * h[n]"),
+    "drop_dt_in_input": ("(dt * B_t[n]) * x", "(B_t[n]) * x"),
+    "A_same_for_all_n": ("h[n] = exp(dt * A_d[n])", "h[n] = exp(dt * A_d[0])"),
+    "readout_uses_B": ("y += C_t[n] * h[n]", "y += B_t[n] * h[n]"),
+    "B_state_index": ("(dt * B_t[n]) * x", "(dt * B_t[N - 1 - n]) * x"),
+    "gate_sigmoid": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    "softplus_drop_max": ("return fmax(u, 0.0) + log1p(exp(-fabs(u)));", "return log1p(exp(-fabs(u)));"),
+    "softplus_sign": ("log1p(exp(-fabs(u)))", "log1p(exp(fabs(u)))"),
+    "bias_ignored": ("double u = delta + (bias ? bias[d] : 0.0);", "double u = delta;"),
+    "readout_before_update": (
+        "  for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A_d[n]) * h[n] + (dt * B_t[n]) * x;\n"
+        "  double y = 0.0;\n  for (int64_t n = 0; n < N; ++n) y += C_t[n] * h[n];\n",
+        "  double y = 0.0;\n  for (int64_t n = 0; n < N; ++n) y += C_t[n] * h[n];\n"
+        "  for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A_d[n]) * h[n] + (dt * B_t[n]) * x;\n"),
+    "B_previous_step": ("const double* Bt = j->B + (b * j->L + t) * j->N;",
+                        "const double* Bt = j->B + (b * j->L + (t > 0 ? t - 1 : 0)) * j->N;"),
+    "x_batch_index": ("int64_t e = (b * j->L + t) * j->Dn + d;          /* [batch, L, d_inner] */",
+                      "int64_t e = (t) * j->Dn + d + 0 * b;"),
+    "A_transposed": ("j->A + d * j->N, Bt", "j->A + d, Bt"),
+    "compose_order": ("acc_b[n] = a2 * acc_b[n] + b2;", "acc_b[n] = acc_a[n] * b2 + acc_b[n];"),
+    "compose_example": ("double nb = a2[i] * b1[i] + b2[i];", "double nb = a1[i] * b2[i] + b1[i];"),
+    "decode_B_row": ("A + d * N, B + b * N, C + b * N", "A + d * N, B, C + b * N"),
+    "last_state_index": ("j->last_state[(b * j->Dn + d) * j->N + n] = h[n];",
+                         "j->last_state[(d * j->N + n) * 0 + (b * j->Dn + d) * j->N + (j->N - 1 - n)] = h[n];"),
+    "gate_before_skip": ("  if (D) y += D[d] * x;\n  if (zp) y *= silu(*zp);",
+                         "  if (zp) y *= silu(*zp);\n  if (D) y += D[d] * x;"),
+}
+
+
+def _run_pins(orc):
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as e:  # an assertion, a shape error or NaN: the pin caught it
+            failed.append((pin.__name__, type(e).__name__))
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = tmp_path / f"oracle_{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = obuild.build(src=str(path), lib=str(tmp_path / f"liboracle_{name}.so"))
+    failed = _run_pins(oracle.OracleLib(lib))
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    path = tmp_path / "oracle_copy.c"
+    path.write_text(open(obuild.SRC).read())
+    lib = obuild.build(src=str(path), lib=str(tmp_path / "liboracle_copy.so"))
+    assert _run_pins(oracle.OracleLib(lib)) == []
