@@ -1,0 +1,266 @@
+"""Benchmark of libssmscan on one MI355X.
+
+Default: the Mamba-2.8B-like layer scan (batch 8, d_inner 5120, d_state 16,
+seqlen 2048; bf16 x/delta/z/B/C, fp32 state, softplus(delta + bias) fused,
+D skip and SiLU(z) gate on, fp32 out).  One step = one ssm_scan_fwd call over
+the whole batch with inputs resident in HBM.  Prints ONE JSON line:
+
+  value       GB/s of algorithmic traffic (x, delta, z, B, C read once + out
+              written once) over the K timed steps;
+  roofline    the scan kernel against its binding ceiling (the fp32 VALU rate),
+              with its HBM fraction beside it;
+  cpu_baseline the fp64 oracle on the host cores over the same workload;
+  decode      512 consecutive ssm_state_update steps at batch 256, d_inner 8192:
+              tokens/s (the second half of the metric).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--out-dtype f32|bf16] [--no-cpu-baseline] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, AMD spec
+# fp32 vector VALU without packed-FP32 instructions (the build disables them):
+# 256 CUs x 4 SIMD x 16 lanes x 2 flop (FMA) x 2.4 GHz
+VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+FLOPS_PER_STATE_UPDATE = 7       # mul (dt*A), exp, mul (dt*x*B), FMA (update, 2), FMA (readout, 2)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2p8b",
+                    choices=["mamba2p8b", "mamba130m", "long_dna", "tiny_fp32", "decode"])
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--plan", default=None, help="states_per_wave,chunk_len (tuning only)")
+    return ap.parse_args()
+
+
+def scan_case(name, out_dtype, plan_arg):
+    import torch
+
+    import sequence_scan_amd as ssm
+    import workloads
+
+    cfg = workloads.SCAN_CONFIGS[name]
+    t0 = time.time()
+    inp = workloads.scan_inputs(cfg, seed=0)
+    log(f"generated {name} inputs in {time.time() - t0:.1f}s")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = {}
+    for k, v in inp.items():
+        if k == "dtype":
+            continue
+        t = torch.from_numpy(v)
+        if k in ("x", "delta", "z", "B", "C"):
+            t = t.to(tdt)
+        dev[k] = t.cuda()
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = torch.empty((cfg.batch, cfg.seqlen, cfg.d_inner), dtype=odt, device="cuda")
+    last = torch.empty((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32, device="cuda")
+    plan = None
+    if plan_arg:
+        ns, cl = plan_arg.split(",")
+        plan = {"states_per_wave": int(ns), "chunk_len": int(cl)}
+
+    def run():
+        ssm.ssm_scan_fwd(dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                         dev["delta_bias"], softplus=True, out=out, last_state=last, plan=plan)
+
+    nbytes = workloads.scan_algorithmic_bytes(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, out_dtype)
+    return cfg, inp, run, nbytes, plan
+
+
+def time_steps(run, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def per_launch_ms(run, reps, flush_bytes=0):
+    """Average duration of one call, events around each call on the launch stream;
+    with flush_bytes > 0 a buffer that size is overwritten before each call
+    (outside the events) so the call starts with a cold last-level cache."""
+    import torch
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda") if flush_bytes else None
+    times = []
+    for _ in range(reps):
+        if buf is not None:
+            buf.fill_(1.0)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        run()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    times.sort()
+    return sum(times) / len(times), times[len(times) // 2], times[0]
+
+
+def cpu_baseline(cfg, inp):
+    import oracle
+    nthreads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                    softplus=True, nthreads=nthreads, return_state=False)
+    return time.perf_counter() - t0, nthreads
+
+
+def decode_case(steps):
+    import torch
+
+    import sequence_scan_amd as ssm
+    import workloads
+
+    cfg = workloads.DECODE_CONFIG
+    t0 = time.time()
+    inp = workloads.decode_inputs(cfg, seed=0, steps=steps)
+    log(f"generated decode inputs ({steps} steps) in {time.time() - t0:.1f}s")
+    dev = {}
+    for k, v in inp.items():
+        if k == "dtype":
+            continue
+        t = torch.from_numpy(v).cuda()
+        if k in ("x", "delta", "z", "B", "C"):
+            t = t.to(torch.bfloat16)  # exact: the values are bf16-representable
+        dev[k] = t
+    del inp
+    state = torch.zeros((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32, device="cuda")
+    out = torch.empty((steps, cfg.batch, cfg.d_inner), dtype=torch.float32, device="cuda")
+
+    def run_all():
+        for s in range(steps):
+            ssm.ssm_state_update(state, dev["x"][s], dev["delta"][s], dev["A"], dev["B"][s], dev["C"][s], dev["D"],
+                                 dev["z"][s], dev["delta_bias"], softplus=True, out=out[s])
+
+    run_all()  # warm-up pass (state then continues; the timing does not depend on values)
+    torch.cuda.synchronize()
+    state.zero_()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run_all()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    per_step_bytes = workloads.decode_algorithmic_bytes(cfg.batch, cfg.d_inner, cfg.d_state, "bf16", "f32")
+    step_ms = ms / steps
+    return {
+        "workload": f"decode batch {cfg.batch}, d_inner {cfg.d_inner}, d_state 16, {steps} steps, bf16 in, fp32 state/out",
+        "tokens_per_s": cfg.batch * steps / (ms / 1e3),
+        "us_per_step": step_ms * 1e3,
+        "GBps_incl_state": per_step_bytes / (step_ms / 1e3) / 1e9,
+        "hbm_frac_incl_state": per_step_bytes / (step_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(rows shard over GPUs with no communication; run one process per GPU).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    import sequence_scan_amd as ssm
+    ssm.library()
+
+    if args.workload == "decode":
+        d = decode_case(args.decode_steps)
+        print(json.dumps({"metric": "decode tokens/sec at batch 256", "value": round(d["tokens_per_s"], 1),
+                          "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "decode": d}), flush=True)
+        return
+
+    cfg, inp, run, nbytes, plan = scan_case(args.workload, args.out_dtype, args.plan)
+    plan_used = plan or ssm.ssm_scan_plan(cfg.batch, cfg.seqlen, cfg.d_inner)
+    log(f"plan {plan_used}; algorithmic bytes {nbytes}")
+    ms, wall = time_steps(run, args.steps, args.warmup)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"{args.steps} steps: {ms * 1e3:.1f} us/step (events), wall {wall * 1e3:.1f} ms, {gbs:.1f} GB/s")
+
+    # dominant kernel: with one time chunk the whole step is one launch of the scan kernel
+    k_avg, k_med, k_min = per_launch_ms(run, max(10, args.steps))
+    c_avg, c_med, c_min = per_launch_ms(run, 10, flush_bytes=1 << 30)
+    states = cfg.batch * cfg.seqlen * cfg.d_inner * cfg.d_state
+    tflops = states * FLOPS_PER_STATE_UPDATE / (k_avg / 1e3) / 1e12
+    k_gbs = nbytes / (k_avg / 1e3) / 1e9
+    single_launch = plan_used.get("n_chunks", 1) in (1, None)
+    roofline = {
+        "bound": "alu",
+        "achieved": round(tflops, 2),
+        "peak": round(VALU_PEAK_TFLOPS, 2),
+        "unit": "TFLOP/s",
+        "frac": round(tflops / VALU_PEAK_TFLOPS, 4),
+        "traffic": None,
+        "kernel": "scan_chunk_kernel (pass B)" if single_launch else "ssm_scan_fwd (all passes)",
+        "flops_per_state_update": FLOPS_PER_STATE_UPDATE,
+        "state_updates_per_launch": states,
+        "avg_launch_us": round(k_avg * 1e3, 2),
+        "hbm": {"achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes},
+        "cold_llc_us": {"avg": round(c_avg * 1e3, 2), "median": round(c_med * 1e3, 2), "min": round(c_min * 1e3, 2)},
+    }
+    line = {
+        "metric": "selective-scan GB/s and % HBM peak (prefill); decode tokens/sec at batch 256",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and distributions of the workload table)",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "batch": cfg.batch, "seqlen": cfg.seqlen,
+                   "d_inner": cfg.d_inner, "d_state": cfg.d_state, "in_dtype": cfg.dtype,
+                   "out_dtype": args.out_dtype, "plan": plan_used},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host cores")
+        secs, cores = cpu_baseline(cfg, inp)
+        line["cpu_baseline"] = {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": cores,
+                                "kind": "oracle", "seconds": round(secs, 2),
+                                "sample": f"the full {cfg.name} workload (every row and step), fp64"}
+    del inp
+    if not args.no_decode and args.workload == "mamba2p8b":
+        line["decode"] = decode_case(args.decode_steps)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

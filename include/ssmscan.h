@@ -1,0 +1,154 @@
+/*
+ * ssmscan.h -- C ABI of libssmscan, the selective-SSM (Mamba-1) scan on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (pages: "Mamba и State Space Models", nareshka.ru, sections
+ * "Ключевая инновация: input-dependent parameters" and "Selective Scan (core
+ * algorithm)"; "State Space Models: Mamba и альтернатива Transformer",
+ * johe.ru, MambaBlock "_scan" code for the D skip; "Модуль 8. Альтернативы
+ * Transformer", vladkulikov.com, section 6 for softplus and sections 7 and 14
+ * for the recurrent decode step and the shape of ssm_state):
+ *
+ *   for every batch row b and channel d, from a zero state h = 0:
+ *     dt  = softplus(delta[b,t,d] + bias[d])     (or delta + bias if softplus == 0)
+ *     h[n] = exp(dt * A[d,n]) * h[n] + dt * B[b,t,n] * x[b,t,d]     n < d_state
+ *     y   = sum_n C[b,t,n] * h[n] + D[d] * x[b,t,d]
+ *     out[b,t,d] = y * z[b,t,d] * sigmoid(z[b,t,d])                  (SiLU gate)
+ *   softplus(u) = log(1 + e^u).  y is read after the update of step t.
+ *
+ * Layouts (all row-major, last index fastest, no strides):
+ *   x, delta, z, out : [batch, seqlen, d_inner]
+ *   B, C             : [batch, seqlen, d_state]  (one B_t, C_t per batch row
+ *                                                 and step, shared by every channel)
+ *   A                : [d_inner, d_state] fp32   (the caller passes A itself,
+ *                                                 e.g. A = -exp(A_log))
+ *   D, delta_bias    : [d_inner] fp32
+ *   last_state, state: [batch, d_inner, d_state] fp32
+ *
+ * Precision: x, delta, z, B and C are all fp32 or all bf16 (in_dtype); the
+ * state and every intermediate are fp32; out is fp32 or bf16 (out_dtype,
+ * rounded to nearest even).
+ *
+ * Ownership: every pointer is a device pointer owned by the caller.  The
+ * library keeps no device memory between calls.  A scan over more than one
+ * time chunk takes a temporary workspace with hipMallocAsync on `stream` and
+ * releases it with hipFreeAsync on the same stream.
+ *
+ * Errors: every argument is checked on the host before anything is enqueued.
+ * A non-OK status means nothing was enqueued and no output was written;
+ * ssm_last_error() then holds a message for the calling thread.  Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL is the null stream): faults
+ * during execution surface at the caller's next synchronisation.  Results
+ * are bitwise reproducible for identical inputs and plan (no atomics).
+ */
+#ifndef SSMSCAN_H
+#define SSMSCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL_ARG = 1,    /* a required pointer is NULL                                   */
+  SSM_ERR_BAD_SHAPE = 2,   /* a size is negative or the element count overflows int64      */
+  SSM_ERR_UNSUPPORTED = 3, /* dtype, d_state, alignment, aliasing or plan not supported    */
+  SSM_ERR_HIP = 4          /* the HIP runtime refused an allocation or a launch            */
+} ssm_status;
+
+/*
+ * Forward scan (prefill / training forward) from a zero state.
+ *
+ * Required: x, delta, A, B, C, out (a required pointer may be NULL only when
+ * its tensor has no elements, as PyTorch gives empty tensors).  Optional (NULL
+ * turns the term off):
+ *   D           -- no skip term;
+ *   z           -- no gate (out = y);
+ *   delta_bias  -- bias 0;
+ *   last_state  -- final state h after step seqlen-1 is not stored.
+ * softplus: nonzero applies softplus to delta + bias; zero uses delta + bias as
+ *   the step size as given (the caller guarantees it is a meaningful step).
+ * Sizes: batch, seqlen, d_inner >= 0 (a zero size is a valid empty call;
+ *   with seqlen == 0 a non-NULL last_state is set to zero); d_state == 16.
+ * Alignment: every pointer 16-byte aligned.
+ * Aliasing: out and last_state must not overlap any input or each other.
+ */
+ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* delta_bias,
+                        int softplus, void* out, float* last_state, int64_t batch, int64_t seqlen,
+                        int64_t d_inner, int64_t d_state, ssm_dtype in_dtype, ssm_dtype out_dtype,
+                        void* stream);
+
+/*
+ * Single-token decode: one step of the same recurrence for every (b, d),
+ * continuing from `state`, which is read and overwritten in place.
+ *   state          : [batch, d_inner, d_state] fp32, in/out
+ *   x, delta, z, out: [batch, d_inner]; B, C: [batch, d_state]
+ * Optional arguments, sizes, alignment and errors as for ssm_scan_fwd; out
+ * must not overlap state or any input.  Running seqlen steps from a zero
+ * state gives the same outputs and final state as one ssm_scan_fwd call.
+ */
+ssm_status ssm_state_update(float* state, const void* x, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D, const void* z,
+                            const float* delta_bias, int softplus, void* out, int64_t batch,
+                            int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
+                            ssm_dtype out_dtype, void* stream);
+
+/*
+ * Execution plan of a scan: how many of the d_state states one wavefront
+ * carries per channel (states_per_wave in {1, 2, 4, 8, 16}; a workgroup
+ * holds d_state / states_per_wave wavefronts on the same 64 channels), and the
+ * time-chunk length (chunk_len >= 1; the sequence is cut into
+ * ceil(seqlen / chunk_len) chunks scanned in parallel and joined by the
+ * affine-pair carry pass).  ssm_scan_plan reports the plan ssm_scan_fwd picks;
+ * ssm_scan_fwd_plan runs with a given plan (tests and tuning).  Any valid plan
+ * computes the same function; only rounding order and speed differ.
+ */
+typedef struct {
+  int32_t states_per_wave;
+  int32_t reserved0;
+  int64_t chunk_len;
+  int64_t n_chunks;      /* output of ssm_scan_plan; ignored on input */
+  int64_t reserved[4];
+} ssm_plan;
+
+ssm_status ssm_scan_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                         ssm_plan* plan);
+
+ssm_status ssm_scan_fwd_plan(const void* x, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z,
+                             const float* delta_bias, int softplus, void* out, float* last_state,
+                             int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                             ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream,
+                             const ssm_plan* plan);
+
+/*
+ * The affine-pair operator on its own, for checking the carry pass's combine
+ * (page "Модуль 8. Альтернативы Transformer", section 7: the step h -> a h + b
+ * is the pair (a, b), and (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2), the later
+ * step first).  Given n pairs (a[k], b[k]) in time order (device arrays, fp32),
+ * writes the exclusive prefix: out_b[k] = state after pairs 0..k-1 applied to
+ * h = 0 (out_b[0] = 0) and out_a[k] = product of a[0..k-1] (out_a[0] = 1).
+ * Runs the same wavefront scan the carry pass uses.  n >= 0.
+ */
+ssm_status ssm_affine_exclusive_scan(const float* a, const float* b, float* out_a, float* out_b,
+                                     int64_t n, void* stream);
+
+/* Static string for a status code. */
+const char* ssm_status_string(ssm_status s);
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* ssm_last_error(void);
+/* SSM_ABI_VERSION of the loaded library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSMSCAN_H */

@@ -1,0 +1,193 @@
+"""Python binding of libssmscan (the selective-SSM scan on MI355X).
+
+Argument marshalling only: tensors are passed to the C ABI as device
+pointers, sizes and the current HIP stream; every step of the computation
+runs in the library's gfx950 kernels.  PyTorch provides device memory and
+streams.  There is no fallback: if ``libssmscan.so`` is missing or cannot be
+loaded, every call raises.
+
+Functions carry the C names: ``ssm_scan_fwd``, ``ssm_state_update``,
+``ssm_scan_fwd_plan``, ``ssm_scan_plan``, ``ssm_affine_exclusive_scan``,
+``ssm_status_string``, ``ssm_last_error``, ``ssm_abi_version``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ssmscan.h")
+
+SSM_F32 = 0
+SSM_BF16 = 1
+SSM_OK, SSM_ERR_NULL_ARG, SSM_ERR_BAD_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP = range(5)
+STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_BAD_SHAPE", 3: "SSM_ERR_UNSUPPORTED",
+                4: "SSM_ERR_HIP"}
+D_STATE = 16
+
+
+class SSMError(RuntimeError):
+    """A non-OK status from libssmscan; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class ssm_plan(ctypes.Structure):
+    _fields_ = [("states_per_wave", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
+                ("reserved", ctypes.c_int64 * 4)]
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libssmscan.so is not built ({LIB_PATH}); run sequence_scan_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    scan_args = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
+                 _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
+    lib.ssm_scan_fwd.argtypes = scan_args
+    lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd_plan.argtypes = scan_args + [ctypes.POINTER(ssm_plan)]
+    lib.ssm_scan_fwd_plan.restype = ctypes.c_int
+    lib.ssm_state_update.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                                     _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
+    lib.ssm_state_update.restype = ctypes.c_int
+    lib.ssm_scan_plan.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(ssm_plan)]
+    lib.ssm_scan_plan.restype = ctypes.c_int
+    lib.ssm_affine_exclusive_scan.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp]
+    lib.ssm_affine_exclusive_scan.restype = ctypes.c_int
+    lib.ssm_status_string.argtypes = [ctypes.c_int]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_last_error.argtypes = []
+    lib.ssm_last_error.restype = ctypes.c_char_p
+    lib.ssm_abi_version.argtypes = []
+    lib.ssm_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def _check(status: int):
+    if status != SSM_OK:
+        raise SSMError(status, _load().ssm_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def ssm_status_string(status: int) -> str:
+    return _load().ssm_status_string(int(status)).decode()
+
+
+def ssm_last_error() -> str:
+    return _load().ssm_last_error().decode()
+
+
+def ssm_abi_version() -> int:
+    return int(_load().ssm_abi_version())
+
+
+def ssm_scan_plan(batch: int, seqlen: int, d_inner: int, d_state: int = D_STATE) -> dict:
+    """The plan ``ssm_scan_fwd`` picks for these sizes."""
+    p = ssm_plan()
+    _check(_load().ssm_scan_plan(batch, seqlen, d_inner, d_state, ctypes.byref(p)))
+    return {"states_per_wave": p.states_per_wave, "chunk_len": p.chunk_len, "n_chunks": p.n_chunks}
+
+
+def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                 out=None, last_state=None, out_dtype=None, stream=None, plan: Optional[dict] = None):
+    """Forward selective scan from a zero state (see include/ssmscan.h).
+
+    x, delta, z: [batch, seqlen, d_inner]; B, C: [batch, seqlen, d_state] (all float32 or
+    all bfloat16); A: [d_inner, d_state], D, delta_bias: [d_inner] (float32).  ``out``
+    (allocated if None, dtype ``out_dtype`` or x's) and ``last_state`` (float32
+    [batch, d_inner, d_state], optional) are written on the current stream.  ``plan`` =
+    {"states_per_wave": .., "chunk_len": ..} forces an execution plan.  Returns out.
+    """
+    import torch
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, d_inner]")
+    batch, seqlen, d_inner = x.shape
+    d_state = A.shape[-1] if A.dim() == 2 else -1
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    lib = _load()
+    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(softplus)), _ptr(out), _ptr(last_state), batch, seqlen, d_inner, d_state,
+            _dtype_code(x), _dtype_code(out), _stream(stream))
+    if plan is None:
+        _check(lib.ssm_scan_fwd(*args))
+    else:
+        p = ssm_plan()
+        p.states_per_wave = int(plan["states_per_wave"])
+        p.chunk_len = int(plan["chunk_len"])
+        _check(lib.ssm_scan_fwd_plan(*args, ctypes.byref(p)))
+    return out
+
+
+def ssm_scan_fwd_plan(*args, plan: dict, **kw):
+    return ssm_scan_fwd(*args, plan=plan, **kw)
+
+
+def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                     out=None, out_dtype=None, stream=None):
+    """One decode step (see include/ssmscan.h); ``state`` [batch, d_inner, d_state] float32
+    is updated in place.  x, delta, z: [batch, d_inner]; B, C: [batch, d_state]."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be [batch, d_inner]")
+    batch, d_inner = x.shape
+    d_state = state.shape[-1] if state.dim() == 3 else -1
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(_load().ssm_state_update(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(out), batch, d_inner,
+                                    d_state, _dtype_code(x), _dtype_code(out), _stream(stream)))
+    return out
+
+
+def ssm_affine_exclusive_scan(a, b, out_a=None, out_b=None, stream=None):
+    """Exclusive scan of affine pairs (a[k], b[k]) in time order on the GPU (float32)."""
+    import torch
+    n = a.numel()
+    out_a = torch.empty_like(a) if out_a is None else out_a
+    out_b = torch.empty_like(b) if out_b is None else out_b
+    _check(_load().ssm_affine_exclusive_scan(_ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b), n, _stream(stream)))
+    return out_a, out_b

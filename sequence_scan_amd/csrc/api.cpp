@@ -1,0 +1,332 @@
+// C-ABI host layer of libssmscan: argument checks, plan choice, workspace,
+// launches.  Every check runs before anything is enqueued; on any non-OK
+// status nothing has been enqueued and no output has been written.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ssmscan.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ssm_status fail(ssm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+ssm_status ok() {
+  return SSM_OK;
+}
+
+struct Range {
+  const char* name;
+  uintptr_t lo;
+  uintptr_t hi;  // exclusive
+};
+
+Range range(const char* name, const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, p ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  if (a.lo == 0 || b.lo == 0 || a.hi == a.lo || b.hi == b.lo) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
+int64_t esize(ssm_dtype t) { return t == SSM_BF16 ? 2 : 4; }
+
+bool valid_dtype(ssm_dtype t) { return t == SSM_F32 || t == SSM_BF16; }
+
+ssm::DT to_dt(ssm_dtype t) { return t == SSM_BF16 ? ssm::DT::BF16 : ssm::DT::F32; }
+
+ssm_status check_align(const char* name, const void* p) {
+  if (p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+  return SSM_OK;
+}
+
+int device_simds() {
+  int dev = 0;
+  int cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 1024;
+  return cus * 4;
+}
+
+// The plan: prefer a single time chunk (no extra pass) and the largest state
+// group per wave that still gives at least 1.5 wavefronts per SIMD; when even
+// one state per wave cannot fill the chip, cut time into chunks of at least
+// 1024 steps with 4 states per wave.
+void choose_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_plan* p) {
+  const int64_t blocks = batch * ((d_inner + 63) / 64);
+  const int64_t want = simds + simds / 2;
+  int ns = 0;
+  for (int cand : {16, 8, 4, 2, 1}) {
+    if (blocks * (16 / cand) >= want) {
+      ns = cand;
+      break;
+    }
+  }
+  int64_t chunks = 1;
+  if (ns == 0) {
+    ns = 4;
+    const int64_t waves = std::max<int64_t>(1, blocks * 4);
+    chunks = (3 * (int64_t)simds + waves - 1) / waves;
+    chunks = std::min(chunks, std::max<int64_t>(1, seqlen / 1024));
+  }
+  int64_t chunk_len = seqlen > 0 ? (seqlen + chunks - 1) / chunks : 1;
+  if (chunk_len < 1) chunk_len = 1;
+  p->states_per_wave = ns;
+  p->reserved0 = 0;
+  p->chunk_len = chunk_len;
+  p->n_chunks = seqlen > 0 ? (seqlen + chunk_len - 1) / chunk_len : 0;
+  for (auto& r : p->reserved) r = 0;
+}
+
+struct Sizes {
+  int64_t elems;      // batch * seqlen * d_inner
+  int64_t bc;         // batch * seqlen * d_state
+  int64_t state;      // batch * d_inner * d_state
+};
+
+ssm_status check_common(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                        ssm_dtype in_dtype, ssm_dtype out_dtype, Sizes* sz) {
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "negative size (batch=%lld seqlen=%lld d_inner=%lld d_state=%lld)",
+                (long long)batch, (long long)seqlen, (long long)d_inner, (long long)d_state);
+  if (d_state != ssm::kDState)
+    return fail(SSM_ERR_UNSUPPORTED, "d_state=%lld is not supported (this build supports 16)", (long long)d_state);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown dtype (in=%d out=%d)", (int)in_dtype, (int)out_dtype);
+  int64_t t1, t2;
+  if (!mul_ok(batch, seqlen, &t1) || !mul_ok(t1, d_inner, &sz->elems) || !mul_ok(sz->elems, 8, &t2) ||
+      !mul_ok(t1, d_state, &sz->bc) || !mul_ok(batch, d_inner, &t2) || !mul_ok(t2, d_state, &sz->state) ||
+      !mul_ok(sz->state, 8, &t1))
+    return fail(SSM_ERR_BAD_SHAPE, "element count overflows int64");
+  if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch=%lld exceeds 65535", (long long)batch);
+  return SSM_OK;
+}
+
+ssm_status scan_impl(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                     const float* D, const void* z, const float* delta_bias, int softplus, void* out,
+                     float* last_state, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                     ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream, const ssm_plan* plan_in) {
+  Sizes sz;
+  ssm_status st = check_common(batch, seqlen, d_inner, d_state, in_dtype, out_dtype, &sz);
+  if (st != SSM_OK) return st;
+  // a required pointer may be NULL only when its tensor is empty
+  const bool need_e = sz.elems > 0, need_bc = sz.bc > 0, need_a = d_inner > 0;
+  if ((need_e && (!x || !delta || !out)) || (need_a && !A) || (need_bc && (!B || !C))) {
+    const char* which = (need_e && !x) ? "x" : (need_e && !delta) ? "delta" : (need_a && !A) ? "A"
+                      : (need_bc && !B) ? "B" : (need_bc && !C) ? "C" : "out";
+    return fail(SSM_ERR_NULL_ARG, "required pointer %s is NULL", which);
+  }
+  const void* ptrs[] = {x, delta, A, B, C, D, z, delta_bias, out, last_state};
+  const char* names[] = {"x", "delta", "A", "B", "C", "D", "z", "delta_bias", "out", "last_state"};
+  for (int i = 0; i < 10; ++i)
+    if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
+  const int64_t si = esize(in_dtype), so = esize(out_dtype);
+  const Range ins[] = {
+      range("x", x, sz.elems * si),          range("delta", delta, sz.elems * si),
+      range("z", z, sz.elems * si),          range("B", B, sz.bc * si),
+      range("C", C, sz.bc * si),             range("A", A, d_inner * d_state * 4),
+      range("D", D, d_inner * 4),            range("delta_bias", delta_bias, d_inner * 4),
+  };
+  const Range ro = range("out", out, sz.elems * so);
+  const Range rl = range("last_state", last_state, sz.state * 4);
+  for (const Range& r : ins) {
+    if (overlaps(ro, r)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps input %s", r.name);
+    if (overlaps(rl, r)) return fail(SSM_ERR_UNSUPPORTED, "last_state overlaps input %s", r.name);
+  }
+  if (overlaps(ro, rl)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps last_state");
+
+  ssm_plan plan;
+  if (plan_in) {
+    plan = *plan_in;
+    const int ns = plan.states_per_wave;
+    if (ns != 1 && ns != 2 && ns != 4 && ns != 8 && ns != 16)
+      return fail(SSM_ERR_UNSUPPORTED, "plan.states_per_wave=%d not in {1,2,4,8,16}", ns);
+    if (plan.chunk_len < 1) return fail(SSM_ERR_UNSUPPORTED, "plan.chunk_len must be >= 1");
+    plan.n_chunks = seqlen > 0 ? (seqlen + plan.chunk_len - 1) / plan.chunk_len : 0;
+    if (plan.n_chunks > 65535) return fail(SSM_ERR_UNSUPPORTED, "plan gives more than 65535 chunks");
+  } else {
+    choose_plan(batch, seqlen, d_inner, device_simds(), &plan);
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0 || d_inner == 0) return ok();
+  if (seqlen == 0) {
+    if (last_state) {
+      hipError_t e = ssm::launch_fill_zero(last_state, sz.state, s);
+      if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+  }
+
+  ssm::ScanArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.z = z;
+  a.B = B;
+  a.C = C;
+  a.A = A;
+  a.D = D;
+  a.bias = delta_bias;
+  a.out = out;
+  a.last_state = last_state;
+  a.seqlen = seqlen;
+  a.d_inner = d_inner;
+  a.chunk_len = plan.chunk_len;
+  a.n_chunks = (int32_t)plan.n_chunks;
+  a.softplus = softplus ? 1 : 0;
+  a.batch = (int32_t)batch;
+
+  void* ws = nullptr;
+  if (plan.n_chunks > 1) {
+    int64_t n_state, n_sum, bytes;
+    if (!mul_ok(batch * plan.n_chunks, d_inner * d_state, &n_state) ||
+        !mul_ok(batch * plan.n_chunks, d_inner, &n_sum) || !mul_ok(n_state + n_sum, 4, &bytes))
+      return fail(SSM_ERR_BAD_SHAPE, "workspace size overflows int64");
+    hipError_t e = hipMallocAsync(&ws, (size_t)bytes, s);
+    if (e != hipSuccess || ws == nullptr)
+      return fail(SSM_ERR_HIP, "hipMallocAsync(%lld bytes) failed: %s", (long long)bytes, hipGetErrorString(e));
+    a.ws_state = static_cast<float*>(ws);
+    a.ws_dtsum = a.ws_state + n_state;
+  }
+  hipError_t e = ssm::launch_scan(a, to_dt(in_dtype), to_dt(out_dtype), plan.states_per_wave, s);
+  if (ws) {
+    hipError_t e2 = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                        const float* D, const void* z, const float* delta_bias, int softplus, void* out,
+                        float* last_state, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                        ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream) {
+  return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, out, last_state, batch, seqlen, d_inner,
+                   d_state, in_dtype, out_dtype, stream, nullptr);
+}
+
+ssm_status ssm_scan_fwd_plan(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int softplus, void* out,
+                             float* last_state, int64_t batch, int64_t seqlen, int64_t d_inner,
+                             int64_t d_state, ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream,
+                             const ssm_plan* plan) {
+  if (!plan) return fail(SSM_ERR_NULL_ARG, "plan is NULL");
+  return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, out, last_state, batch, seqlen, d_inner,
+                   d_state, in_dtype, out_dtype, stream, plan);
+}
+
+ssm_status ssm_scan_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, ssm_plan* plan) {
+  if (!plan) return fail(SSM_ERR_NULL_ARG, "plan is NULL");
+  Sizes sz;
+  ssm_status st = check_common(batch, seqlen, d_inner, d_state, SSM_F32, SSM_F32, &sz);
+  if (st != SSM_OK) return st;
+  choose_plan(batch, seqlen, d_inner, device_simds(), plan);
+  return SSM_OK;
+}
+
+ssm_status ssm_state_update(float* state, const void* x, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z, const float* delta_bias, int softplus,
+                            void* out, int64_t batch, int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
+                            ssm_dtype out_dtype, void* stream) {
+  Sizes sz;
+  ssm_status st = check_common(batch, 1, d_inner, d_state, in_dtype, out_dtype, &sz);
+  if (st != SSM_OK) return st;
+  const bool need_e = sz.elems > 0, need_bc = sz.bc > 0, need_a = d_inner > 0;
+  if ((need_e && (!state || !x || !delta || !out)) || (need_a && !A) || (need_bc && (!B || !C))) {
+    const char* which = (need_e && !state) ? "state" : (need_e && !x) ? "x" : (need_e && !delta) ? "delta"
+                      : (need_a && !A) ? "A" : (need_bc && !B) ? "B" : (need_bc && !C) ? "C" : "out";
+    return fail(SSM_ERR_NULL_ARG, "required pointer %s is NULL", which);
+  }
+  const void* ptrs[] = {state, x, delta, A, B, C, D, z, delta_bias, out};
+  const char* names[] = {"state", "x", "delta", "A", "B", "C", "D", "z", "delta_bias", "out"};
+  for (int i = 0; i < 10; ++i)
+    if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
+  const int64_t si = esize(in_dtype), so = esize(out_dtype);
+  const Range ins[] = {
+      range("x", x, sz.elems * si),       range("delta", delta, sz.elems * si),
+      range("z", z, sz.elems * si),       range("B", B, sz.bc * si),
+      range("C", C, sz.bc * si),          range("A", A, d_inner * d_state * 4),
+      range("D", D, d_inner * 4),         range("delta_bias", delta_bias, d_inner * 4),
+  };
+  const Range rs = range("state", state, sz.state * 4);
+  const Range ro = range("out", out, sz.elems * so);
+  for (const Range& r : ins) {
+    if (overlaps(ro, r)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps input %s", r.name);
+    if (overlaps(rs, r)) return fail(SSM_ERR_UNSUPPORTED, "state overlaps input %s", r.name);
+  }
+  if (overlaps(ro, rs)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps state");
+  if (batch == 0 || d_inner == 0) return ok();
+  ssm::DecodeArgs a{};
+  a.state = state;
+  a.x = x;
+  a.delta = delta;
+  a.z = z;
+  a.B = B;
+  a.C = C;
+  a.A = A;
+  a.D = D;
+  a.bias = delta_bias;
+  a.out = out;
+  a.d_inner = d_inner;
+  a.pairs = batch * d_inner;
+  a.softplus = softplus ? 1 : 0;
+  hipError_t e = ssm::launch_decode(a, to_dt(in_dtype), to_dt(out_dtype), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ssm_status ssm_affine_exclusive_scan(const float* a, const float* b, float* out_a, float* out_b, int64_t n,
+                                     void* stream) {
+  if (n < 0) return fail(SSM_ERR_BAD_SHAPE, "n=%lld is negative", (long long)n);
+  if (n > 0 && (!a || !b || !out_a || !out_b)) return fail(SSM_ERR_NULL_ARG, "required pointer is NULL");
+  hipError_t e = ssm::launch_affine_exclusive_scan(a, b, out_a, out_b, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* ssm_status_string(ssm_status s) {
+  switch (s) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_NULL_ARG: return "SSM_ERR_NULL_ARG: a required pointer is NULL";
+    case SSM_ERR_BAD_SHAPE: return "SSM_ERR_BAD_SHAPE: a size is negative or overflows";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: dtype, d_state, alignment, aliasing or plan";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime refused an allocation or launch";
+    default: return "unknown ssm_status";
+  }
+}
+
+const char* ssm_last_error(void) { return g_last_error.c_str(); }
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the gfx950
+// kernels (kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr int kDState = 16;   // the one d_state this build supports
+constexpr int kWave = 64;     // gfx950 wavefront size
+
+enum class DT : int { F32 = 0, BF16 = 1 };
+
+struct ScanArgs {
+  const void* x;
+  const void* delta;
+  const void* z;          // nullable
+  const void* B;
+  const void* C;
+  const float* A;         // [d_inner, 16]
+  const float* D;         // nullable
+  const float* bias;      // nullable
+  void* out;
+  float* last_state;      // nullable
+  float* ws_state;        // [batch, n_chunks, d_inner, 16]; chunked runs only
+  float* ws_dtsum;        // [batch, n_chunks, d_inner];    chunked runs only
+  int64_t seqlen;
+  int64_t d_inner;
+  int64_t chunk_len;
+  int32_t n_chunks;
+  int32_t softplus;
+  int32_t batch;
+};
+
+struct DecodeArgs {
+  float* state;
+  const void* x;
+  const void* delta;
+  const void* z;
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* D;
+  const float* bias;
+  void* out;
+  int64_t d_inner;
+  int64_t pairs;          // batch * d_inner
+  int32_t softplus;
+};
+
+// Launchers; each returns the hipGetLastError() of its launches.
+hipError_t launch_scan(const ScanArgs& a, DT in, DT out, int states_per_wave, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, DT in, DT out, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_affine_exclusive_scan(const float* a, const float* b, float* oa, float* ob,
+                                        int64_t n, hipStream_t s);
+
+}  // namespace ssm

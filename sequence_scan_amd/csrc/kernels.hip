@@ -1,0 +1,574 @@
+// gfx950 kernels of libssmscan: chunked selective scan, affine-pair carry
+// pass, decode state update.
+//
+// What is computed (pages: "Mamba и State Space Models", nareshka.ru,
+// "Ключевая инновация" and "Selective Scan (core algorithm)"; "State Space
+// Models: Mamba и альтернатива Transformer", johe.ru, "_scan" for the D skip
+// and "Параллельная форма" for the prefix form; "Модуль 8. Альтернативы
+// Transformer", vladkulikov.com, section 7 for the affine-pair operator):
+//   dt = softplus(delta + bias);  h[n] <- exp(dt A[d,n]) h[n] + dt B_t[n] x
+//   out = (sum_n C_t[n] h[n] + D x) * silu(z)
+//
+// Work decomposition (MI355X-first; see the design notes in the repository):
+//  * A workgroup owns 64 consecutive channels of one batch row and one time
+//    chunk.  Its G = 16 / NS wavefronts each carry NS of the 16 states of all
+//    64 channels (lane = channel), so B_t[n] and C_t[n] are the same for every
+//    lane of a wave and are read as LDS broadcasts; the fp32 state lives in
+//    VGPRs for the whole chunk and never touches HBM mid-sequence.
+//  * Time is processed in tiles of T steps.  Phase 1: each wave converts and
+//    discretises T/G of the tile's steps (softplus, dt*x) into LDS, and the
+//    workgroup stages the tile's B/C rows in LDS as fp32.  Phase 2: every wave
+//    runs the recurrence over the whole tile for its states and leaves a
+//    partial readout per step in LDS.  Phase 3: each wave finishes T/G steps
+//    (sum of the partials in a fixed order, D skip, SiLU gate, store).  The
+//    next tile's HBM loads are issued before phase 2 so they overlap the math.
+//  * Long sequences are cut into chunks.  Pass A reduces every chunk but the
+//    last to its affine pair per state coordinate: the end state from zero and
+//    the step-size sum S (the chunk's decay is exp(A S)).  The carry kernel
+//    scans the pairs in time order with a wavefront DPP scan (lane = chunk).
+//    Pass B re-runs each chunk from its incoming state with the full readout.
+#include "internal.h"
+
+namespace ssm {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// ---------------------------------------------------------------- element io
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+struct Io;
+
+template <>
+struct Io<float> {
+  using raw = float;
+  static __device__ __forceinline__ raw load(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  static __device__ __forceinline__ float cvt(raw r) { return r; }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+};
+
+template <>
+struct Io<uint16_t> {  // bfloat16 bit patterns
+  using raw = uint16_t;
+  static __device__ __forceinline__ raw load(const void* p, int64_t i) {
+    return static_cast<const uint16_t*>(p)[i];
+  }
+  static __device__ __forceinline__ float cvt(raw r) { return bf16_to_f32(r); }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16_rne(v);
+  }
+};
+
+// Unpack a 16-byte vector of B/C elements into fp32.
+template <typename T>
+struct Vec16;
+
+template <>
+struct Vec16<float> {
+  static constexpr int kElems = 4;
+  static __device__ __forceinline__ void unpack(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x);
+    o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z);
+    o[3] = __uint_as_float(v.w);
+  }
+};
+
+template <>
+struct Vec16<uint16_t> {
+  static constexpr int kElems = 8;
+  static __device__ __forceinline__ void unpack(const uint4& v, float* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+// ------------------------------------------------------- pointwise functions
+
+// softplus(u) = log(1 + e^u) = max(u, 0) + log1p(e), e = exp(-|u|) in (0, 1].
+// log1p(e) is log(w) plus the rounding error c of w = 1 + e (c is exact,
+// |c| <= 2^-24), which keeps the result accurate to a few ulp also when e is
+// tiny and w rounds to 1.
+__device__ __forceinline__ float softplus_f(float u) {
+  const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(u) * kLog2e);
+  const float w = 1.0f + e;
+  const float c = e - (w - 1.0f);
+  const float l = __builtin_amdgcn_logf(w);  // log2(w)
+  return __builtin_fmaxf(u, 0.0f) + __builtin_fmaf(l, kLn2, c);
+}
+
+// SiLU(z) = z * sigmoid(z) = z / (1 + e^{-z}).
+__device__ __forceinline__ float silu_f(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// ------------------------------------------------ wavefront affine-pair scan
+
+#define SSM_DPP(old, src, ctrl, rmask)                                                    \
+  __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), \
+                                             (ctrl), (rmask), 0xf, false))
+
+// Inclusive scan over the 64 lanes of a wavefront of affine pairs (a, b),
+// lane order = time order: lane i ends with pair_i o pair_{i-1} o ... o pair_0,
+// where (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2).  Hillis-Steele within each
+// 16-lane row (row_shr 1, 2, 4, 8), then row_bcast:15 and row_bcast:31 join
+// the rows.  Lanes without a predecessor receive the identity (1, 0).  All 64
+// lanes must be active.
+__device__ __forceinline__ void affine_wave_scan(float& a, float& b) {
+#define SSM_SCAN_STEP(ctrl, rmask)                 \
+  {                                                \
+    const float pa = SSM_DPP(1.0f, a, ctrl, rmask); \
+    const float pb = SSM_DPP(0.0f, b, ctrl, rmask); \
+    b = __builtin_fmaf(a, pb, b);                  \
+    a = a * pa;                                    \
+  }
+  SSM_SCAN_STEP(0x111, 0xf)  // row_shr:1
+  SSM_SCAN_STEP(0x112, 0xf)  // row_shr:2
+  SSM_SCAN_STEP(0x114, 0xf)  // row_shr:4
+  SSM_SCAN_STEP(0x118, 0xf)  // row_shr:8
+  SSM_SCAN_STEP(0x142, 0xa)  // row_bcast:15 into rows 1 and 3
+  SSM_SCAN_STEP(0x143, 0xc)  // row_bcast:31 into rows 2 and 3
+#undef SSM_SCAN_STEP
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ------------------------------------------------------------- scan kernel
+
+template <int G>
+struct Tile {
+  static constexpr int T = (G == 1 || G >= 8) ? 16 : 32;  // steps per tile
+};
+
+template <typename Tin, typename Tout, int NS, bool PASS_A>
+__global__ void __launch_bounds__(kWave * (kDState / NS))
+scan_chunk_kernel(ScanArgs a) {
+  constexpr int G = kDState / NS;         // wavefronts per workgroup (state groups)
+  constexpr int T = Tile<G>::T;           // time steps per tile
+  constexpr int SPW = T / G;              // steps each wave prepares / finishes
+  constexpr int NTHR = kWave * G;
+  constexpr int EPV = Vec16<Tin>::kElems; // B/C elements per 16-byte vector
+  constexpr int VPR = kDState / EPV;      // 16-byte vectors per B or C row
+  constexpr int BC_VECS = (PASS_A ? 1 : 2) * T * VPR;
+  constexpr int BC_R = (BC_VECS + NTHR - 1) / NTHR;
+  using In = Io<Tin>;
+
+  __shared__ float2 sh_dtv[T][kWave];                 // (dt, dt * x)
+  __shared__ float sh_B[T][kDState];
+  __shared__ float sh_C[PASS_A ? 1 : T][kDState];
+  __shared__ float sh_y[PASS_A ? 1 : T][G][kWave];    // partial readouts
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  // the wave index is uniform across the wave: keep it (and every row offset
+  // derived from it) in scalar registers
+  const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int b = blockIdx.z;
+  const int k = blockIdx.y;
+  const int K = a.n_chunks;
+  const int64_t Dn = a.d_inner;
+  const int64_t L = a.seqlen;
+  const int64_t d0 = (int64_t)blockIdx.x * kWave;
+  const int64_t d = d0 + lane;
+  const bool dvalid = d < Dn;
+  const bool full_block = d0 + kWave <= Dn;
+  // lanes past the last channel read the last channel (results are never stored)
+  const int loff = dvalid ? lane : (int)(Dn - 1 - d0);
+  const int64_t t_begin = (int64_t)k * a.chunk_len;
+  const int64_t t_end = min(t_begin + a.chunk_len, L);
+  const bool has_z = !PASS_A && a.z != nullptr;
+  const bool softplus = a.softplus != 0;
+  const bool has_D = a.D != nullptr;
+
+  float A2[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) A2[i] = a.A[(d0 + loff) * kDState + g * NS + i] * kLog2e;
+  const float bias = a.bias != nullptr ? a.bias[d0 + loff] : 0.0f;
+  const float Dd = has_D ? a.D[d0 + loff] : 0.0f;
+
+  float h[NS];
+  if (!PASS_A && k > 0) {
+    const float* src = a.ws_state + (((int64_t)b * K + (k - 1)) * Dn + d0 + loff) * kDState + g * NS;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) h[i] = src[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) h[i] = 0.0f;
+  }
+  float dtsum = 0.0f;
+
+  // Row pointers of this chunk: element (t_begin + tt, d0) of batch row b.
+  const int64_t base_e = ((int64_t)b * L + t_begin) * Dn + d0;
+  const Tin* xb = static_cast<const Tin*>(a.x) + base_e;
+  const Tin* db = static_cast<const Tin*>(a.delta) + base_e;
+  const Tin* zb = has_z ? static_cast<const Tin*>(a.z) + base_e : nullptr;
+  Tout* ob = PASS_A ? nullptr : static_cast<Tout*>(a.out) + base_e;
+  const Tin* Bb = static_cast<const Tin*>(a.B) + ((int64_t)b * L + t_begin) * kDState;
+  const Tin* Cb = static_cast<const Tin*>(a.C) + ((int64_t)b * L + t_begin) * kDState;
+
+  typename In::raw rx[SPW], rdt[SPW], rz[SPW];
+  uint4 rbc[BC_R];
+  float xs[SPW], zs[SPW];
+
+  // Issue the HBM loads of the tile at chunk-relative step tt0 into registers.
+  auto issue = [&](int64_t tt0, int nt) {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int s = g * SPW + j;
+      if (s < nt) {                            // wave-uniform
+        const int64_t row = (tt0 + s) * Dn;
+        rx[j] = xb[row + loff];
+        rdt[j] = db[row + loff];
+        if (has_z) rz[j] = zb[row + loff];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < BC_R; ++r) {
+      const int v = tid + r * NTHR;
+      if (v < BC_VECS) {
+        const int which = v / (T * VPR);
+        const int w = v - which * (T * VPR);
+        const int row = w / VPR;
+        const int part = w - row * VPR;
+        if (row < nt) {
+          const Tin* src = (which ? Cb : Bb) + (tt0 + row) * kDState + part * EPV;
+          rbc[r] = *reinterpret_cast<const uint4*>(src);
+        }
+      }
+    }
+  };
+
+  // Phase 1: discretise this wave's steps into LDS; stage B/C rows as fp32.
+  auto commit = [&](int nt) {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int s = g * SPW + j;
+      if (s < nt) {
+        const float x = In::cvt(rx[j]);
+        const float u = In::cvt(rdt[j]) + bias;
+        const float dt = softplus ? softplus_f(u) : u;
+        sh_dtv[s][lane] = make_float2(dt, dt * x);
+        xs[j] = x;
+        zs[j] = has_z ? In::cvt(rz[j]) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < BC_R; ++r) {
+      const int v = tid + r * NTHR;
+      if (v < BC_VECS) {
+        const int which = v / (T * VPR);
+        const int w = v - which * (T * VPR);
+        const int row = w / VPR;
+        const int part = w - row * VPR;
+        if (row < nt) {
+          float f[EPV];
+          Vec16<Tin>::unpack(rbc[r], f);
+          float* dst = which ? &sh_C[PASS_A ? 0 : row][part * EPV] : &sh_B[row][part * EPV];
+#pragma unroll
+          for (int i = 0; i < EPV; ++i) dst[i] = f[i];
+        }
+      }
+    }
+  };
+
+  // Phase 2: the recurrence over one step for this wave's NS states.
+  auto step = [&](int s) {
+    const float2 v = sh_dtv[s][lane];
+    float y = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const float ar = __builtin_amdgcn_exp2f(v.x * A2[i]);
+      h[i] = __builtin_fmaf(ar, h[i], v.y * sh_B[s][g * NS + i]);
+      if (!PASS_A) y = __builtin_fmaf(sh_C[PASS_A ? 0 : s][g * NS + i], h[i], y);
+    }
+    if (PASS_A) {
+      dtsum += v.x;
+    } else {
+      sh_y[PASS_A ? 0 : s][PASS_A ? 0 : g][lane] = y;
+    }
+  };
+
+  // Phase 3: finish this wave's steps: sum partials, D skip, gate, store.
+  auto finish = [&](int64_t tt0, int nt) {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int s = g * SPW + j;
+      if (s < nt) {
+        float y = sh_y[PASS_A ? 0 : s][0][lane];
+#pragma unroll
+        for (int gg = 1; gg < G; ++gg) y += sh_y[PASS_A ? 0 : s][PASS_A ? 0 : gg][lane];
+        if (has_D) y = __builtin_fmaf(Dd, xs[j], y);
+        if (has_z) y = y * silu_f(zs[j]);
+        Tout* orow = ob + (tt0 + s) * Dn;
+        if (full_block || dvalid) Io<Tout>::store(orow, lane, y);
+      }
+    }
+  };
+
+  const int64_t nsteps = t_end - t_begin;
+  if (nsteps > 0) issue(0, (int)min((int64_t)T, nsteps));
+  for (int64_t tt0 = 0; tt0 < nsteps; tt0 += T) {
+    const int nt = (int)min((int64_t)T, nsteps - tt0);
+    commit(nt);
+    if (tt0 + T < nsteps) issue(tt0 + T, (int)min((int64_t)T, nsteps - tt0 - T));
+    __syncthreads();
+    if (nt == T) {
+#pragma unroll
+      for (int s = 0; s < T; ++s) step(s);
+    } else {
+      for (int s = 0; s < nt; ++s) step(s);
+    }
+    __syncthreads();
+    if (!PASS_A) finish(tt0, nt);
+  }
+
+  if (!dvalid) return;
+  if (PASS_A) {
+    float* dst = a.ws_state + (((int64_t)b * K + k) * Dn + d) * kDState + g * NS;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) dst[i] = h[i];
+    if (g == 0) a.ws_dtsum[((int64_t)b * K + k) * Dn + d] = dtsum;
+  } else if (k == K - 1 && a.last_state != nullptr) {
+    float* dst = a.last_state + ((int64_t)b * Dn + d) * kDState + g * NS;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) dst[i] = h[i];
+  }
+}
+
+// ------------------------------------------------------------ carry kernel
+//
+// On entry, slot p < K-1 of ws_state holds chunk p's end state from zero
+// and ws_dtsum its step-size sum S_p; the pair of chunk p for coordinate
+// (d, n) is (exp(A[d,n] S_p), end state).  On exit slot p holds the state
+// entering chunk p + 1: the inclusive composition of pairs 0..p applied to
+// h = 0.  A workgroup takes 64 consecutive (d, n) columns; pairs are loaded
+// 64 at a time (coalesced along columns) into LDS, each wave scans 16
+// columns with lane = chunk, and a per-column carry joins the segments.
+__global__ void __launch_bounds__(256) carry_kernel(float* ws_state, const float* ws_dtsum,
+                                                    const float* A, int64_t Dn, int K) {
+  __shared__ float sa[64][65];
+  __shared__ float sb[64][65];
+  __shared__ float ca[64];
+  __shared__ float cb[64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int b = blockIdx.y;
+  const int64_t ncol = Dn * kDState;
+  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+  const int npairs = K - 1;
+  const float a2 = col < ncol ? A[col] * kLog2e : 0.0f;
+  if (tid < 64) {
+    ca[tid] = 1.0f;
+    cb[tid] = 0.0f;
+  }
+  for (int p0 = 0; p0 < npairs; p0 += 64) {
+    const int np = min(64, npairs - p0);
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int r = w + 4 * i;
+      float av = 1.0f, bv = 0.0f;
+      if (r < np && col < ncol) {
+        const int64_t p = (int64_t)b * K + p0 + r;
+        bv = ws_state[p * ncol + col];
+        const float S = ws_dtsum[p * Dn + (col >> 4)];
+        av = __builtin_amdgcn_exp2f(S * a2);
+      }
+      sa[r][lane] = av;
+      sb[r][lane] = bv;
+    }
+    __syncthreads();
+    for (int j = 0; j < 16; ++j) {
+      const int c = w + 4 * j;
+      float av = sa[lane][c];
+      float bv = sb[lane][c];
+      affine_wave_scan(av, bv);
+      const float cav = ca[c];
+      const float cbv = cb[c];
+      const float rb = __builtin_fmaf(av, cbv, bv);  // (av, bv) o carry
+      const float ra = av * cav;
+      sb[lane][c] = rb;
+      const float na = readlane_f(ra, 63);
+      const float nb = readlane_f(rb, 63);
+      if (lane == 0) {
+        ca[c] = na;
+        cb[c] = nb;
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int r = w + 4 * i;
+      if (r < np && col < ncol) ws_state[((int64_t)b * K + p0 + r) * ncol + col] = sb[r][lane];
+    }
+    __syncthreads();
+  }
+}
+
+// Exclusive affine-pair scan of one array (one wavefront; the combine of the
+// carry kernel, exposed for tests).
+__global__ void __launch_bounds__(64) affine_exclusive_scan_kernel(const float* a, const float* b,
+                                                                   float* oa, float* ob, int64_t n) {
+  const int lane = threadIdx.x;
+  float ca = 1.0f, cb = 0.0f;
+  for (int64_t s0 = 0; s0 < n; s0 += 64) {
+    const int64_t i = s0 + lane;
+    float av = i < n ? a[i] : 1.0f;
+    float bv = i < n ? b[i] : 0.0f;
+    affine_wave_scan(av, bv);
+    const float ia = av * ca;
+    const float ib = __builtin_fmaf(av, cb, bv);
+    const float ea = SSM_DPP(ca, ia, 0x138, 0xf);  // wave_shr:1, lane 0 keeps the carry
+    const float eb = SSM_DPP(cb, ib, 0x138, 0xf);
+    if (i < n) {
+      oa[i] = ea;
+      ob[i] = eb;
+    }
+    ca = readlane_f(ia, 63);
+    cb = readlane_f(ib, 63);
+  }
+}
+
+// ----------------------------------------------------------- decode kernel
+//
+// One (b, d) pair per quad of lanes; lane q of the quad owns states 4q..4q+3
+// (one 16-byte load and store of the fp32 state).  The readout is reduced
+// over the quad with two DPP quad permutes; lane 0 of the quad applies the
+// D skip and the gate and stores out.
+template <typename Tin, typename Tout>
+__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+  using In = Io<Tin>;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e = gid >> 2;
+  const int q = threadIdx.x & 3;
+  if (e >= a.pairs) return;  // whole quads leave together
+  const int64_t d = e % a.d_inner;
+  const int64_t b = e / a.d_inner;
+
+  float4 hs = *reinterpret_cast<const float4*>(a.state + e * kDState + 4 * q);
+  const float4 av = *reinterpret_cast<const float4*>(a.A + d * kDState + 4 * q);
+  float Bv[4], Cv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Bv[i] = In::cvt(In::load(a.B, b * kDState + 4 * q + i));
+    Cv[i] = In::cvt(In::load(a.C, b * kDState + 4 * q + i));
+  }
+  const float x = In::cvt(In::load(a.x, e));
+  const float dl = In::cvt(In::load(a.delta, e));
+  const float u = dl + (a.bias != nullptr ? a.bias[d] : 0.0f);
+  const float dt = a.softplus ? softplus_f(u) : u;
+  const float dtx = dt * x;
+  float h[4] = {hs.x, hs.y, hs.z, hs.w};
+  const float A2[4] = {av.x * kLog2e, av.y * kLog2e, av.z * kLog2e, av.w * kLog2e};
+  float y = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float ar = __builtin_amdgcn_exp2f(dt * A2[i]);
+    h[i] = __builtin_fmaf(ar, h[i], dtx * Bv[i]);
+    y = __builtin_fmaf(Cv[i], h[i], y);
+  }
+  *reinterpret_cast<float4*>(a.state + e * kDState + 4 * q) = make_float4(h[0], h[1], h[2], h[3]);
+  // quad sum in a fixed order: (q0 + q1) + (q2 + q3) on every lane
+  y = y + SSM_DPP(0.0f, y, 0xB1, 0xf);  // quad_perm [1,0,3,2]
+  y = y + SSM_DPP(0.0f, y, 0x4E, 0xf);  // quad_perm [2,3,0,1]
+  if (q == 0) {
+    if (a.D != nullptr) y = __builtin_fmaf(a.D[d], x, y);
+    if (a.z != nullptr) y = y * silu_f(In::cvt(In::load(a.z, e)));
+    Io<Tout>::store(a.out, e, y);
+  }
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+// --------------------------------------------------------------- launchers
+
+template <typename Tin, typename Tout, int NS>
+hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
+  constexpr int G = kDState / NS;
+  const unsigned nblk = (unsigned)((a.d_inner + kWave - 1) / kWave);
+  if (a.n_chunks > 1) {
+    dim3 gridA(nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch);
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, true>), gridA, dim3(kWave * G), 0, s, a);
+    const unsigned ncolblk = (unsigned)((a.d_inner * kDState + 63) / 64);
+    hipLaunchKernelGGL(carry_kernel, dim3(ncolblk, (unsigned)a.batch), dim3(256), 0, s, a.ws_state,
+                       (const float*)a.ws_dtsum, a.A, a.d_inner, a.n_chunks);
+  }
+  dim3 gridB(nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
+  hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false>), gridB, dim3(kWave * G), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_scan_ns(const ScanArgs& a, int ns, hipStream_t s) {
+  switch (ns) {
+    case 1: return launch_scan_t<Tin, Tout, 1>(a, s);
+    case 2: return launch_scan_t<Tin, Tout, 2>(a, s);
+    case 4: return launch_scan_t<Tin, Tout, 4>(a, s);
+    case 8: return launch_scan_t<Tin, Tout, 8>(a, s);
+    case 16: return launch_scan_t<Tin, Tout, 16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scan(const ScanArgs& a, DT in, DT out, int ns, hipStream_t s) {
+  if (in == DT::F32 && out == DT::F32) return launch_scan_ns<float, float>(a, ns, s);
+  if (in == DT::F32 && out == DT::BF16) return launch_scan_ns<float, uint16_t>(a, ns, s);
+  if (in == DT::BF16 && out == DT::F32) return launch_scan_ns<uint16_t, float>(a, ns, s);
+  return launch_scan_ns<uint16_t, uint16_t>(a, ns, s);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, DT in, DT out, hipStream_t s) {
+  const int64_t threads = a.pairs * 4;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  if (in == DT::F32 && out == DT::F32)
+    hipLaunchKernelGGL((decode_kernel<float, float>), dim3(grid), dim3(256), 0, s, a);
+  else if (in == DT::F32 && out == DT::BF16)
+    hipLaunchKernelGGL((decode_kernel<float, uint16_t>), dim3(grid), dim3(256), 0, s, a);
+  else if (in == DT::BF16 && out == DT::F32)
+    hipLaunchKernelGGL((decode_kernel<uint16_t, float>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<uint16_t, uint16_t>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = min((int64_t)4096, (n + 255) / 256);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_affine_exclusive_scan(const float* a, const float* b, float* oa, float* ob,
+                                        int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(affine_exclusive_scan_kernel, dim3(1), dim3(64), 0, s, a, b, oa, ob, n);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

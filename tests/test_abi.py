@@ -1,0 +1,162 @@
+"""C-ABI checks that run without a GPU: exports, versions, status strings, and
+every host-side rejection path (these return before any HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sequence_scan_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(ssm.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(ssm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_function_is_exported():
+    lib = ssm.library()
+    names = header_functions()
+    assert {"ssm_scan_fwd", "ssm_state_update", "ssm_scan_plan", "ssm_scan_fwd_plan",
+            "ssm_affine_exclusive_scan", "ssm_status_string", "ssm_last_error", "ssm_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ssmscan.h but not exported"
+
+
+def test_version_and_strings():
+    assert ssm.ssm_abi_version() == 1
+    for code, name in ssm.STATUS_NAMES.items():
+        assert ssm.ssm_status_string(code).startswith(name)
+    assert "unknown" in ssm.ssm_status_string(99)
+
+
+F32, BF16 = ssm.SSM_F32, ssm.SSM_BF16
+P = 0x10000000  # fake, 16-byte aligned device addresses: never dereferenced on these paths
+
+
+def scan(**kw):
+    a = dict(x=P, delta=P + 0x1000000, A=P + 0x2000000, B=P + 0x3000000, C=P + 0x4000000, D=None, z=None,
+             bias=None, softplus=1, out=P + 0x5000000, last=None, batch=2, seqlen=8, d_inner=64, d_state=16,
+             ind=F32, outd=F32, stream=None)
+    a.update(kw)
+    lib = ssm.library()
+    return lib.ssm_scan_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["softplus"],
+                            a["out"], a["last"], a["batch"], a["seqlen"], a["d_inner"], a["d_state"], a["ind"],
+                            a["outd"], a["stream"])
+
+
+@pytest.mark.parametrize("arg", ["x", "delta", "A", "B", "C", "out"])
+def test_null_required(arg):
+    assert scan(**{arg: None}) == ssm.SSM_ERR_NULL_ARG
+    assert arg in ssm.ssm_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(seqlen=-5), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(d_inner=-64), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(batch=1 << 40, seqlen=1 << 20, d_inner=1 << 10), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(d_state=8), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(d_state=32), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(ind=7), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(outd=-1), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(batch=70000, seqlen=1, d_inner=1), ssm.SSM_ERR_UNSUPPORTED),
+])
+def test_bad_sizes_and_types(kw, code):
+    assert scan(**kw) == code
+    assert ssm.ssm_last_error() != ""
+
+
+@pytest.mark.parametrize("arg", ["x", "delta", "A", "B", "C", "D", "z", "bias", "out", "last"])
+def test_misaligned(arg):
+    kw = {"D": P + 0x6000000, "z": P + 0x7000000, "bias": P + 0x8000000, "last": P + 0x9000000}
+    base = {**kw}
+    cur = {"x": P, "delta": P + 0x1000000, "A": P + 0x2000000, "B": P + 0x3000000, "C": P + 0x4000000,
+           "out": P + 0x5000000, **base}
+    cur[arg] = cur[arg] + 4
+    assert scan(**cur) == ssm.SSM_ERR_UNSUPPORTED
+    assert "aligned" in ssm.ssm_last_error()
+
+
+@pytest.mark.parametrize("target", ["x", "delta", "B", "A"])
+def test_out_aliasing_an_input(target):
+    ptrs = {"x": P, "delta": P + 0x1000000, "A": P + 0x2000000, "B": P + 0x3000000}
+    assert scan(out=ptrs[target] + 16) == ssm.SSM_ERR_UNSUPPORTED
+    assert "overlaps" in ssm.ssm_last_error()
+
+
+def test_last_state_aliasing():
+    assert scan(last=P + 0x1000000 + 64) == ssm.SSM_ERR_UNSUPPORTED
+    assert scan(last=P + 0x5000000 + 32) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_bad_plan_rejected_before_launch():
+    lib = ssm.library()
+    for spw, chunk in ((3, 10), (32, 10), (4, 0), (4, -3)):
+        p = ssm.ssm_plan()
+        p.states_per_wave = spw
+        p.chunk_len = chunk
+        rc = lib.ssm_scan_fwd_plan(P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, None, None, None,
+                                   1, P + 0x5000000, None, 2, 8, 64, 16, F32, F32, None, ctypes.byref(p))
+        assert rc == ssm.SSM_ERR_UNSUPPORTED, (spw, chunk)
+    assert lib.ssm_scan_fwd_plan(P, P, P, P, P, None, None, None, 1, P, None, 1, 1, 1, 16, F32, F32, None,
+                                 None) == ssm.SSM_ERR_NULL_ARG
+
+
+def test_decode_rejections():
+    lib = ssm.library()
+
+    def dec(**kw):
+        a = dict(state=P, x=P + 0x1000000, delta=P + 0x2000000, A=P + 0x3000000, B=P + 0x4000000, C=P + 0x5000000,
+                 D=None, z=None, bias=None, softplus=1, out=P + 0x6000000, batch=4, d_inner=64, d_state=16,
+                 ind=BF16, outd=F32)
+        a.update(kw)
+        return lib.ssm_state_update(a["state"], a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                    a["bias"], a["softplus"], a["out"], a["batch"], a["d_inner"], a["d_state"],
+                                    a["ind"], a["outd"], None)
+    assert dec(state=None) == ssm.SSM_ERR_NULL_ARG
+    assert dec(out=None) == ssm.SSM_ERR_NULL_ARG
+    assert dec(batch=-1) == ssm.SSM_ERR_BAD_SHAPE
+    assert dec(d_state=4) == ssm.SSM_ERR_UNSUPPORTED
+    assert dec(state=P + 8) == ssm.SSM_ERR_UNSUPPORTED
+    assert dec(out=P + 32) == ssm.SSM_ERR_UNSUPPORTED          # out inside state
+    assert dec(state=P + 0x1000000) == ssm.SSM_ERR_UNSUPPORTED  # state on x
+
+
+def test_affine_scan_rejections():
+    lib = ssm.library()
+    assert lib.ssm_affine_exclusive_scan(P, P, P, P, -1, None) == ssm.SSM_ERR_BAD_SHAPE
+    assert lib.ssm_affine_exclusive_scan(None, P, P, P, 3, None) == ssm.SSM_ERR_NULL_ARG
+
+
+def test_plan_choices():
+    # Sizes of the benchmark workloads (MI355X: 256 CUs = 1024 SIMDs).
+    p = ssm.ssm_scan_plan(8, 2048, 5120)
+    assert p["n_chunks"] == 1 and p["states_per_wave"] == 4
+    p = ssm.ssm_scan_plan(1, 262144, 2048)
+    assert p["n_chunks"] > 1 and p["chunk_len"] * p["n_chunks"] >= 262144
+    p = ssm.ssm_scan_plan(1, 0, 64)
+    assert p["n_chunks"] == 0
+    with pytest.raises(ssm.SSMError):
+        ssm.ssm_scan_plan(1, 10, 64, 12)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(ssm, "_lib", None)
+    monkeypatch.setattr(ssm, "LIB_PATH", os.path.join(ROOT, "does-not-exist.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        ssm.library()
+
+
+def test_product_code_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "sequence_scan_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+    hdr = open(ssm.HEADER_PATH).read().lower()
+    assert "oracle" not in hdr

@@ -1,0 +1,220 @@
+"""GPU parity of libssmscan against the fp64 oracle (through the C ABI).
+
+Bars: max per-row relative error (rows = (b, d) over t for out; (b, d) over n
+for the state) <= 1e-5 for the all-fp32 path and <= 2e-3 for bf16 inputs
+with fp32 state; bf16 out equals round-to-nearest-even of fp32 out bitwise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import rne_bf16_of, rowinf, sample_channels, say, slice_channels, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+ssm = pytest.importorskip("sequence_scan_amd")
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    ssm.library()
+
+
+def run_scan(inp, out_dtype=torch.float32, plan=None, softplus=True, use=("D", "z", "delta_bias"),
+             with_state=True):
+    t = to_dev(inp)
+    bsz, L, Dn = inp["x"].shape
+    last = torch.full((bsz, Dn, 16), float("nan"), device="cuda") if with_state else None
+    out = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"],
+                           t["D"] if "D" in use else None, t["z"] if "z" in use else None,
+                           t["delta_bias"] if "delta_bias" in use else None, softplus=softplus,
+                           last_state=last, out_dtype=out_dtype, plan=plan)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), (last.cpu().numpy() if with_state else None)
+
+
+def run_oracle(inp, softplus=True, use=("D", "z", "delta_bias")):
+    return oracle.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                           inp["D"] if "D" in use else None, inp["z"] if "z" in use else None,
+                           inp["delta_bias"] if "delta_bias" in use else None, softplus=softplus)
+
+
+def small_case(dtype="f32", batch=2, seqlen=300, d_inner=200, seed=3, random_params=True):
+    cfg = workloads.ScanConfig("small", batch, d_inner, 16, seqlen, dtype)
+    return workloads.scan_inputs(cfg, seed=seed, random_params=random_params)
+
+
+# ----------------------------------------------------------------- carry combine
+
+def test_affine_scan_worked_example():
+    rows = np.loadtxt(oracle_golden(), comments="#", ndmin=2)
+    for la, lb, ea, eb, ca, cb in rows:
+        say(f"affine exclusive scan ({ea},{eb}) then ({la},{lb})")
+        a = torch.tensor([ea, la, 5.0], dtype=torch.float32, device="cuda")
+        b = torch.tensor([eb, lb, 6.0], dtype=torch.float32, device="cuda")
+        oa, ob = ssm.ssm_affine_exclusive_scan(a, b)
+        torch.cuda.synchronize()
+        assert oa.tolist()[0] == 1.0 and ob.tolist()[0] == 0.0
+        assert (oa.tolist()[1], ob.tolist()[1]) == (ea, eb)
+        assert (oa.tolist()[2], ob.tolist()[2]) == (ca, cb)
+
+
+def oracle_golden():
+    import os
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "affine_pair.txt")
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 200])
+def test_affine_scan_random(n):
+    say(f"affine exclusive scan random n={n}")
+    rng = np.random.default_rng(n)
+    a = rng.uniform(0.5, 1.0, n).astype(np.float32)
+    b = rng.standard_normal(n).astype(np.float32)
+    oa, ob = ssm.ssm_affine_exclusive_scan(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda())
+    torch.cuda.synchronize()
+    ea = np.ones(n)
+    eb = np.zeros(n)
+    acc = (1.0, 0.0)
+    for k in range(n):
+        ea[k], eb[k] = acc
+        la, lb = oracle.affine_compose((a[k], b[k]), acc)
+        acc = (la[0], lb[0])
+    np.testing.assert_allclose(oa.cpu().numpy(), ea, rtol=1e-5)
+    np.testing.assert_allclose(ob.cpu().numpy(), eb, rtol=1e-5, atol=1e-5 * np.max(np.abs(eb)))
+
+
+# ----------------------------------------------------------------- scan parity
+
+def test_tiny_fp32_config():
+    say("tiny_fp32 default plan")
+    inp = workloads.scan_inputs(workloads.SCAN_CONFIGS["tiny_fp32"], seed=0)
+    out, last = run_scan(inp)
+    ref, ref_last = run_oracle(inp)
+    assert rowinf(out, ref, 1) <= TOL_F32
+    assert rowinf(last, ref_last, 2) <= TOL_F32
+
+
+@pytest.mark.parametrize("ns", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("chunk", [300, 7, 64, 129])
+def test_plans(ns, chunk):
+    say(f"plan states_per_wave={ns} chunk_len={chunk}")
+    inp = small_case()
+    out, last = run_scan(inp, plan={"states_per_wave": ns, "chunk_len": chunk})
+    ref, ref_last = run_oracle(inp)
+    e1, e2 = rowinf(out, ref, 1), rowinf(last, ref_last, 2)
+    assert e1 <= TOL_F32 and e2 <= TOL_F32, (e1, e2)
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+@pytest.mark.parametrize("mask", range(8))
+def test_optional_inputs(softplus, mask):
+    use = tuple(n for i, n in enumerate(("D", "z", "delta_bias")) if mask >> i & 1)
+    say(f"optional inputs {use} softplus={softplus}")
+    inp = small_case(batch=1, seqlen=100, d_inner=70, seed=7)
+    if not softplus:  # the step is then used as given: draw it positive
+        rng = np.random.default_rng(9)
+        inp["delta"] = np.exp(rng.uniform(np.log(1e-3), np.log(0.1), inp["delta"].shape)).astype(np.float32)
+        inp["delta_bias"] = rng.uniform(0.0, 0.01, inp["delta_bias"].shape).astype(np.float32)
+    for with_state in (True, False):
+        out, last = run_scan(inp, plan={"states_per_wave": 4, "chunk_len": 33}, softplus=softplus, use=use,
+                             with_state=with_state)
+        ref, ref_last = run_oracle(inp, softplus=softplus, use=use)
+        assert rowinf(out, ref, 1) <= TOL_F32
+        if with_state:
+            assert rowinf(last, ref_last, 2) <= TOL_F32
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_out_dtypes(in_dtype):
+    say(f"in={in_dtype} out fp32 vs bf16")
+    inp = small_case(dtype=in_dtype, seqlen=257, d_inner=130, seed=11)
+    ref, _ = run_oracle(inp)
+    plan = {"states_per_wave": 4, "chunk_len": 100}
+    out32, _ = run_scan(inp, torch.float32, plan=plan)
+    out16, _ = run_scan(inp, torch.bfloat16, plan=plan)
+    assert rowinf(out32, ref, 1) <= (TOL_F32 if in_dtype == "f32" else TOL_BF16)
+    np.testing.assert_array_equal(out16, rne_bf16_of(torch.from_numpy(out32)))
+
+
+def test_bf16_inputs_small():
+    say("bf16 inputs, every plan shape")
+    inp = small_case(dtype="bf16", seed=13)
+    ref, ref_last = run_oracle(inp)
+    for ns in (1, 2, 4, 8, 16):
+        out, last = run_scan(inp, plan={"states_per_wave": ns, "chunk_len": 77})
+        assert rowinf(out, ref, 1) <= TOL_BF16
+        assert rowinf(last, ref_last, 2) <= TOL_BF16
+        # inputs are identical on both sides, so fp32 rounding is all that differs
+        assert rowinf(out, ref, 1) <= 1e-5
+
+
+def test_deterministic():
+    say("determinism")
+    inp = small_case(dtype="bf16", batch=3, seqlen=500, d_inner=256, seed=17)
+    plan = {"states_per_wave": 2, "chunk_len": 128}
+    a, la = run_scan(inp, plan=plan)
+    b, lb = run_scan(inp, plan=plan)
+    assert np.array_equal(a, b, equal_nan=True) and np.array_equal(la, lb)
+
+
+def test_nan_spread():
+    say("NaN spread")
+    inp = small_case(batch=2, seqlen=80, d_inner=70, seed=19)
+    inp["x"] = inp["x"].copy()
+    inp["x"][1, 30, 5] = np.nan
+    out, last = run_scan(inp, plan={"states_per_wave": 4, "chunk_len": 16})
+    ref, ref_last = run_oracle(inp)
+    assert np.array_equal(np.isnan(out), np.isnan(ref))
+    assert np.array_equal(np.isnan(last), np.isnan(ref_last))
+    ok = ~np.isnan(ref)
+    assert np.max(np.abs(out[ok] - ref[ok])) <= 1e-5 * np.max(np.abs(ref[ok]))
+
+
+def test_edge_sizes():
+    say("edge sizes: seqlen 0, batch 0, d_inner 1, seqlen 1")
+    t = to_dev(small_case(batch=1, seqlen=4, d_inner=3))
+    last = torch.full((1, 3, 16), 7.0, device="cuda")
+    empty = torch.empty((1, 0, 3), device="cuda")
+    emptybc = torch.empty((1, 0, 16), device="cuda")
+    ssm.ssm_scan_fwd(empty, empty, t["A"], emptybc, emptybc, last_state=last)
+    torch.cuda.synchronize()
+    assert torch.all(last == 0)
+    e0 = torch.empty((0, 5, 3), device="cuda")
+    ssm.ssm_scan_fwd(e0, e0, t["A"], torch.empty((0, 5, 16), device="cuda"), torch.empty((0, 5, 16), device="cuda"))
+    for L, Dn in ((1, 1), (1, 65), (33, 1)):
+        inp = small_case(batch=2, seqlen=L, d_inner=Dn, seed=L + Dn)
+        out, st = run_scan(inp)
+        ref, ref_st = run_oracle(inp)
+        assert rowinf(out, ref, 1) <= TOL_F32 and rowinf(st, ref_st, 2) <= TOL_F32
+
+
+# ------------------------------------------------------------- full-size configs
+
+@pytest.mark.parametrize("name", ["mamba130m", "mamba2p8b"])
+def test_full_config_sampled(name):
+    cfg = workloads.SCAN_CONFIGS[name]
+    say(f"{name} full size, default plan {ssm.ssm_scan_plan(cfg.batch, cfg.seqlen, cfg.d_inner)}")
+    inp = workloads.scan_inputs(cfg, seed=0)
+    out, last = run_scan(inp)
+    assert np.all(np.isfinite(out))
+    sel = sample_channels(cfg.d_inner, 24)
+    ref, ref_last = run_oracle(slice_channels(inp, sel))
+    assert rowinf(out[:, :, sel], ref, 1) <= TOL_BF16
+    assert rowinf(last[:, sel], ref_last, 2) <= TOL_BF16
+
+
+def test_long_dna_sampled():
+    cfg = workloads.SCAN_CONFIGS["long_dna"]
+    say(f"long_dna full size, default plan {ssm.ssm_scan_plan(cfg.batch, cfg.seqlen, cfg.d_inner)}")
+    inp = workloads.scan_inputs(cfg, seed=0)
+    out, last = run_scan(inp)
+    sel = sample_channels(cfg.d_inner, 8)
+    ref, ref_last = run_oracle(slice_channels(inp, sel))
+    assert rowinf(out[:, :, sel], ref, 1) <= TOL_BF16
+    assert rowinf(last[:, sel], ref_last, 2) <= TOL_BF16
