@@ -5,6 +5,13 @@ Flags: packed-FP32 VALU instructions are disabled (the code is written for
 scalar fp32 VALU), and floating-point contraction is off so that every fused
 multiply-add in the kernels is one written out explicitly (results then do
 not depend on how the compiler schedules a template instance).
+
+Machine sinking is disabled: with ROCm 7.2's compiler the MachineSink pass
+moved the LDS reads of a tile's recurrence past the workgroup barrier that
+ends it (into a successor block created by a later uniform branch), so fast
+waves overwrote tile inputs that slow waves had not read yet.  The IR and the
+post-isel machine code had the correct order.  tests/test_codegen.py checks
+the generated assembly for that symptom (two barriers with no work between).
 """
 from __future__ import annotations
 
@@ -22,7 +29,7 @@ ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-ffp-contract=off", "-Wall", "-Wno-unused-function",
+    "-ffp-contract=off", "-mllvm", "-disable-machine-sink", "-Wall", "-Wno-unused-function",
 ]
 
 

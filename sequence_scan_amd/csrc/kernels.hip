@@ -21,7 +21,8 @@
 //    runs the recurrence over the whole tile for its states and leaves a
 //    partial readout per step in LDS.  Phase 3: each wave finishes T/G steps
 //    (sum of the partials in a fixed order, D skip, SiLU gate, store).  The
-//    next tile's HBM loads are issued before phase 2 so they overlap the math.
+//    HBM loads of the tile after next are issued before phase 2, so two tiles
+//    of reads are in flight behind the arithmetic.
 //  * Long sequences are cut into chunks.  Pass A reduces every chunk but the
 //    last to its affine pair per state coordinate: the end state from zero and
 //    the step-size sum S (the chunk's decay is exp(A S)).  The carry kernel
@@ -150,6 +151,17 @@ __device__ __forceinline__ void affine_wave_scan(float& a, float& b) {
 #undef SSM_SCAN_STEP
 }
 
+// Workgroup barrier pinned in the instruction schedule.  __syncthreads()
+// alone has been seen to let the machine scheduler hoist the s_barrier above
+// the LDS reads that precede it (the IR order was correct), which let fast
+// waves overwrite tile inputs that slower waves were still reading; the
+// scheduling fences on both sides keep every LDS access on its side.
+__device__ __forceinline__ void block_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
@@ -161,7 +173,21 @@ struct Tile {
   static constexpr int T = (G == 1 || G >= 8) ? 16 : 32;  // steps per tile
 };
 
-template <typename Tin, typename Tout, int NS, bool PASS_A>
+// The main loop is straight-line code: loads, LDS staging and stores are all
+// unconditional, so the compiler can count outstanding memory operations
+// exactly and wait only for the tile it needs.  (Any conditional load or
+// store inside the loop makes it fall back to draining the whole memory
+// pipeline at every tile.)  To get there:
+//  * the ragged part of the chunk (nsteps % T steps) is peeled off and run
+//    first as one short tile; every later tile is full;
+//  * lanes past the last channel load, compute and store the last channel's
+//    values, which are bit-identical, so their duplicate stores are benign;
+//  * threads past the B/C staging work stage a duplicate of another thread's
+//    vector (same value, same LDS address);
+//  * two register banks hold the raw inputs of the next two tiles, so each
+//    wave keeps two tiles of HBM reads in flight behind its arithmetic; the
+//    prefetch index is clamped to the last tile, so it always reads valid rows.
+template <typename Tin, typename Tout, int NS, bool PASS_A, bool HAS_Z>
 __global__ void __launch_bounds__(kWave * (kDState / NS))
 scan_chunk_kernel(ScanArgs a) {
   constexpr int G = kDState / NS;         // wavefronts per workgroup (state groups)
@@ -172,6 +198,7 @@ scan_chunk_kernel(ScanArgs a) {
   constexpr int VPR = kDState / EPV;      // 16-byte vectors per B or C row
   constexpr int BC_VECS = (PASS_A ? 1 : 2) * T * VPR;
   constexpr int BC_R = (BC_VECS + NTHR - 1) / NTHR;
+  constexpr bool kZ = HAS_Z && !PASS_A;
   using In = Io<Tin>;
 
   __shared__ float2 sh_dtv[T][kWave];                 // (dt, dt * x)
@@ -190,26 +217,23 @@ scan_chunk_kernel(ScanArgs a) {
   const int64_t Dn = a.d_inner;
   const int64_t L = a.seqlen;
   const int64_t d0 = (int64_t)blockIdx.x * kWave;
-  const int64_t d = d0 + lane;
-  const bool dvalid = d < Dn;
-  const bool full_block = d0 + kWave <= Dn;
-  // lanes past the last channel read the last channel (results are never stored)
-  const int loff = dvalid ? lane : (int)(Dn - 1 - d0);
+  // lanes past the last channel take the last channel's place
+  const int loff = (int)min((int64_t)lane, Dn - 1 - d0);
+  const int64_t dl = d0 + loff;
   const int64_t t_begin = (int64_t)k * a.chunk_len;
   const int64_t t_end = min(t_begin + a.chunk_len, L);
-  const bool has_z = !PASS_A && a.z != nullptr;
   const bool softplus = a.softplus != 0;
   const bool has_D = a.D != nullptr;
 
   float A2[NS];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) A2[i] = a.A[(d0 + loff) * kDState + g * NS + i] * kLog2e;
-  const float bias = a.bias != nullptr ? a.bias[d0 + loff] : 0.0f;
-  const float Dd = has_D ? a.D[d0 + loff] : 0.0f;
+  for (int i = 0; i < NS; ++i) A2[i] = a.A[dl * kDState + g * NS + i] * kLog2e;
+  const float bias = a.bias != nullptr ? a.bias[dl] : 0.0f;
+  const float Dd = has_D ? a.D[dl] : 0.0f;
 
   float h[NS];
   if (!PASS_A && k > 0) {
-    const float* src = a.ws_state + (((int64_t)b * K + (k - 1)) * Dn + d0 + loff) * kDState + g * NS;
+    const float* src = a.ws_state + (((int64_t)b * K + (k - 1)) * Dn + dl) * kDState + g * NS;
 #pragma unroll
     for (int i = 0; i < NS; ++i) h[i] = src[i];
   } else {
@@ -222,73 +246,65 @@ scan_chunk_kernel(ScanArgs a) {
   const int64_t base_e = ((int64_t)b * L + t_begin) * Dn + d0;
   const Tin* xb = static_cast<const Tin*>(a.x) + base_e;
   const Tin* db = static_cast<const Tin*>(a.delta) + base_e;
-  const Tin* zb = has_z ? static_cast<const Tin*>(a.z) + base_e : nullptr;
+  const Tin* zb = kZ ? static_cast<const Tin*>(a.z) + base_e : nullptr;
   Tout* ob = PASS_A ? nullptr : static_cast<Tout*>(a.out) + base_e;
   const Tin* Bb = static_cast<const Tin*>(a.B) + ((int64_t)b * L + t_begin) * kDState;
   const Tin* Cb = static_cast<const Tin*>(a.C) + ((int64_t)b * L + t_begin) * kDState;
 
-  typename In::raw rx[SPW], rdt[SPW], rz[SPW];
-  uint4 rbc[BC_R];
+  struct Bank {
+    typename In::raw rx[SPW], rdt[SPW], rz[SPW];
+    uint4 rbc[BC_R];
+  };
+  Bank bk0, bk1;
   float xs[SPW], zs[SPW];
 
-  // Issue the HBM loads of the tile at chunk-relative step tt0 into registers.
-  auto issue = [&](int64_t tt0, int nt) {
+  // Issue the loads of the tile at chunk-relative step tt0 with nt valid steps
+  // (rows past nt re-read the last valid row).
+  auto issue = [&](Bank& bk, int64_t tt0, int nt) {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
-      const int s = g * SPW + j;
-      if (s < nt) {                            // wave-uniform
-        const int64_t row = (tt0 + s) * Dn;
-        rx[j] = xb[row + loff];
-        rdt[j] = db[row + loff];
-        if (has_z) rz[j] = zb[row + loff];
-      }
+      const int s = min(g * SPW + j, nt - 1);  // wave-uniform
+      const int64_t row = (tt0 + s) * Dn;
+      bk.rx[j] = xb[row + loff];
+      bk.rdt[j] = db[row + loff];
+      if (kZ) bk.rz[j] = zb[row + loff];
     }
 #pragma unroll
     for (int r = 0; r < BC_R; ++r) {
-      const int v = tid + r * NTHR;
-      if (v < BC_VECS) {
-        const int which = v / (T * VPR);
-        const int w = v - which * (T * VPR);
-        const int row = w / VPR;
-        const int part = w - row * VPR;
-        if (row < nt) {
-          const Tin* src = (which ? Cb : Bb) + (tt0 + row) * kDState + part * EPV;
-          rbc[r] = *reinterpret_cast<const uint4*>(src);
-        }
-      }
+      const int v = (tid + r * NTHR) % BC_VECS;
+      const int which = v / (T * VPR);
+      const int w = v - which * (T * VPR);
+      const int row = min(w / VPR, nt - 1);
+      const int part = w % VPR;
+      const Tin* src = (which ? Cb : Bb) + (tt0 + row) * kDState + part * EPV;
+      bk.rbc[r] = *reinterpret_cast<const uint4*>(src);
     }
   };
 
   // Phase 1: discretise this wave's steps into LDS; stage B/C rows as fp32.
-  auto commit = [&](int nt) {
+  auto commit = [&](Bank& bk) {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int s = g * SPW + j;
-      if (s < nt) {
-        const float x = In::cvt(rx[j]);
-        const float u = In::cvt(rdt[j]) + bias;
-        const float dt = softplus ? softplus_f(u) : u;
-        sh_dtv[s][lane] = make_float2(dt, dt * x);
-        xs[j] = x;
-        zs[j] = has_z ? In::cvt(rz[j]) : 0.0f;
-      }
+      const float x = In::cvt(bk.rx[j]);
+      const float u = In::cvt(bk.rdt[j]) + bias;
+      const float dt = softplus ? softplus_f(u) : u;
+      sh_dtv[s][lane] = make_float2(dt, dt * x);
+      xs[j] = x;
+      if (kZ) zs[j] = In::cvt(bk.rz[j]);
     }
 #pragma unroll
     for (int r = 0; r < BC_R; ++r) {
-      const int v = tid + r * NTHR;
-      if (v < BC_VECS) {
-        const int which = v / (T * VPR);
-        const int w = v - which * (T * VPR);
-        const int row = w / VPR;
-        const int part = w - row * VPR;
-        if (row < nt) {
-          float f[EPV];
-          Vec16<Tin>::unpack(rbc[r], f);
-          float* dst = which ? &sh_C[PASS_A ? 0 : row][part * EPV] : &sh_B[row][part * EPV];
+      const int v = (tid + r * NTHR) % BC_VECS;
+      const int which = v / (T * VPR);
+      const int w = v - which * (T * VPR);
+      const int row = w / VPR;
+      const int part = w % VPR;
+      float f[EPV];
+      Vec16<Tin>::unpack(bk.rbc[r], f);
+      float* dst = which ? &sh_C[PASS_A ? 0 : row][part * EPV] : &sh_B[row][part * EPV];
 #pragma unroll
-          for (int i = 0; i < EPV; ++i) dst[i] = f[i];
-        }
-      }
+      for (int i = 0; i < EPV; ++i) dst[i] = f[i];
     }
   };
 
@@ -310,47 +326,68 @@ scan_chunk_kernel(ScanArgs a) {
   };
 
   // Phase 3: finish this wave's steps: sum partials, D skip, gate, store.
-  auto finish = [&](int64_t tt0, int nt) {
+  // Full tiles store unconditionally; the peeled ragged tile (full == false)
+  // skips its steps past nt with a wave-uniform branch.
+  auto finish = [&](int64_t tt0, int nt, bool full) {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int s = g * SPW + j;
-      if (s < nt) {
+      if (full || s < nt) {
         float y = sh_y[PASS_A ? 0 : s][0][lane];
 #pragma unroll
         for (int gg = 1; gg < G; ++gg) y += sh_y[PASS_A ? 0 : s][PASS_A ? 0 : gg][lane];
         if (has_D) y = __builtin_fmaf(Dd, xs[j], y);
-        if (has_z) y = y * silu_f(zs[j]);
-        Tout* orow = ob + (tt0 + s) * Dn;
-        if (full_block || dvalid) Io<Tout>::store(orow, lane, y);
+        if (kZ) y = y * silu_f(zs[j]);
+        Io<Tout>::store(ob + (tt0 + s) * Dn, loff, y);
       }
     }
   };
 
-  const int64_t nsteps = t_end - t_begin;
-  if (nsteps > 0) issue(0, (int)min((int64_t)T, nsteps));
-  for (int64_t tt0 = 0; tt0 < nsteps; tt0 += T) {
-    const int nt = (int)min((int64_t)T, nsteps - tt0);
-    commit(nt);
-    if (tt0 + T < nsteps) issue(tt0 + T, (int)min((int64_t)T, nsteps - tt0 - T));
-    __syncthreads();
-    if (nt == T) {
+  // A full tile: everything straight-line.
+  auto full_tile = [&](Bank& bk, int64_t tt0, int64_t pf0) {
+    commit(bk);
+    issue(bk, pf0, T);
+    block_sync();
 #pragma unroll
-      for (int s = 0; s < T; ++s) step(s);
-    } else {
-      for (int s = 0; s < nt; ++s) step(s);
-    }
-    __syncthreads();
-    if (!PASS_A) finish(tt0, nt);
-  }
+    for (int s = 0; s < T; ++s) step(s);
+    block_sync();
+    if (!PASS_A) finish(tt0, T, true);
+  };
 
-  if (!dvalid) return;
+  const int64_t nsteps = t_end - t_begin;
+  const int tail = (int)(nsteps % T);          // the peeled ragged tile
+  const int64_t nfull = nsteps / T;
+  const int64_t last_full = tail + (nfull - 1) * T;   // start of the last full tile
+  if (tail > 0) {
+    issue(bk0, 0, tail);
+    if (nfull > 0) issue(bk1, tail, T);
+    commit(bk0);
+    if (nfull > 1) issue(bk0, tail + T, T);
+    block_sync();
+    for (int s = 0; s < tail; ++s) step(s);
+    block_sync();
+    if (!PASS_A) finish(0, tail, false);
+  } else {
+    if (nfull > 0) issue(bk1, 0, T);
+    if (nfull > 1) issue(bk0, T, T);
+  }
+  // full tiles f = 0, 1, ...: tile f's inputs are in bk1 for even f and bk0
+  // for odd f; each tile prefetches tile f + 2 into the bank it just used
+  int64_t f = 0;
+  for (; f + 1 < nfull; f += 2) {
+    const int64_t t0 = tail + f * T;
+    full_tile(bk1, t0, min(t0 + 2 * T, last_full));
+    full_tile(bk0, t0 + T, min(t0 + 3 * T, last_full));
+  }
+  if (f < nfull) full_tile(bk1, tail + f * T, last_full);
+
   if (PASS_A) {
-    float* dst = a.ws_state + (((int64_t)b * K + k) * Dn + d) * kDState + g * NS;
+    float* dst = a.ws_state + (((int64_t)b * K + k) * Dn + dl) * kDState + g * NS;
 #pragma unroll
     for (int i = 0; i < NS; ++i) dst[i] = h[i];
-    if (g == 0) a.ws_dtsum[((int64_t)b * K + k) * Dn + d] = dtsum;
+    if (g == 0) a.ws_dtsum[((int64_t)b * K + k) * Dn + dl] = dtsum;
   } else if (k == K - 1 && a.last_state != nullptr) {
-    float* dst = a.last_state + ((int64_t)b * Dn + d) * kDState + g * NS;
+    float* dst = a.last_state + ((int64_t)b * Dn + dl) * kDState + g * NS;
 #pragma unroll
     for (int i = 0; i < NS; ++i) dst[i] = h[i];
   }
@@ -398,7 +435,7 @@ __global__ void __launch_bounds__(256) carry_kernel(float* ws_state, const float
       sa[r][lane] = av;
       sb[r][lane] = bv;
     }
-    __syncthreads();
+    block_sync();
     for (int j = 0; j < 16; ++j) {
       const int c = w + 4 * j;
       float av = sa[lane][c];
@@ -416,13 +453,13 @@ __global__ void __launch_bounds__(256) carry_kernel(float* ws_state, const float
         cb[c] = nb;
       }
     }
-    __syncthreads();
+    block_sync();
 #pragma unroll 4
     for (int i = 0; i < 16; ++i) {
       const int r = w + 4 * i;
       if (r < np && col < ncol) ws_state[((int64_t)b * K + p0 + r) * ncol + col] = sb[r][lane];
     }
-    __syncthreads();
+    block_sync();
   }
 }
 
@@ -512,13 +549,16 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
   const unsigned nblk = (unsigned)((a.d_inner + kWave - 1) / kWave);
   if (a.n_chunks > 1) {
     dim3 gridA(nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch);
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, true>), gridA, dim3(kWave * G), 0, s, a);
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, true, false>), gridA, dim3(kWave * G), 0, s, a);
     const unsigned ncolblk = (unsigned)((a.d_inner * kDState + 63) / 64);
     hipLaunchKernelGGL(carry_kernel, dim3(ncolblk, (unsigned)a.batch), dim3(256), 0, s, a.ws_state,
                        (const float*)a.ws_dtsum, a.A, a.d_inner, a.n_chunks);
   }
   dim3 gridB(nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
-  hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false>), gridB, dim3(kWave * G), 0, s, a);
+  if (a.z != nullptr)
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, true>), gridB, dim3(kWave * G), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, false>), gridB, dim3(kWave * G), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,56 @@
+"""Checks of the generated gfx950 assembly (CPU only; needs hipcc).
+
+The scan kernel's correctness depends on every LDS access staying on its side
+of the workgroup barriers.  A compiler that moves a whole phase of LDS reads
+past a barrier leaves two barriers with nothing between them; this test
+rejects such a build.  It also checks that no kernel spills to scratch memory.
+"""
+import re
+import shutil
+
+import pytest
+
+from sequence_scan_amd import build as lib_build
+
+pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / "kernels.s"
+    lib_build.asm(str(out))
+    return out.read_text()
+
+
+def kernels(asm_text):
+    for m in re.finditer(r"^(_Z\S+):\s*;", asm_text, re.M):
+        end = asm_text.find(".Lfunc_end", m.end())
+        yield m.group(1), asm_text[m.end():end]
+
+
+def test_no_collapsed_barriers(asm):
+    bad = []
+    for name, body in kernels(asm):
+        ins = [ln.split()[0] for ln in body.splitlines() if re.match(r"^\s+[a-z_]+", ln)]
+        last = None
+        for i, op in enumerate(ins):
+            if op == "s_barrier":
+                if last is not None and not any(x.startswith(("ds_", "v_", "global_")) for x in ins[last + 1:i]):
+                    bad.append(name)
+                last = i
+    assert not bad, f"barriers with no work between them in: {sorted(set(bad))}"
+
+
+def test_every_scan_kernel_synchronises(asm):
+    names = [n for n, _ in kernels(asm) if "scan_chunk_kernel" in n]
+    assert len(names) >= 40
+    for name, body in kernels(asm):
+        # 16 states per wave means one wave per workgroup: no barrier is needed
+        if "scan_chunk_kernel" in name and "Li16E" not in name:
+            assert body.count("s_barrier") >= 4, name
+
+
+def test_no_scratch_spills(asm):
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm, re.S):
+        priv = re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", m.group(2))
+        assert priv and int(priv.group(1)) == 0, f"{m.group(1)} uses scratch"
