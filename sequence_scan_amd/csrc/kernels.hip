@@ -28,6 +28,8 @@
 //    the step-size sum S (the chunk's decay is exp(A S)).  The carry kernel
 //    scans the pairs in time order with a wavefront DPP scan (lane = chunk).
 //    Pass B re-runs each chunk from its incoming state with the full readout.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ssm {
@@ -171,7 +173,77 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 template <int G>
 struct Tile {
   static constexpr int T = (G == 1 || G >= 8) ? 16 : 32;  // steps per tile
+  // channels per prologue/epilogue item on the wide path (8 x bf16 = 16 B)
+  static constexpr int CW = (T / G) < 8 ? (T / G) : 8;
 };
+
+// CW contiguous input elements of one row, as raw 32-bit words.
+template <typename Tin, int CW>
+struct Raw {
+  static constexpr int kBytes = CW * (int)sizeof(Tin);
+  static constexpr int kWords = kBytes >= 4 ? kBytes / 4 : 1;
+  uint32_t w[kWords];
+  __device__ __forceinline__ void load(const Tin* p) {
+    if constexpr (kBytes == 2) {
+      w[0] = *reinterpret_cast<const uint16_t*>(p);
+    } else if constexpr (kBytes == 4) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (kBytes == 8) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < kBytes / 16; ++q) {
+        const uint4 v = reinterpret_cast<const uint4*>(p)[q];
+        w[4 * q] = v.x;
+        w[4 * q + 1] = v.y;
+        w[4 * q + 2] = v.z;
+        w[4 * q + 3] = v.w;
+      }
+    }
+  }
+  __device__ __forceinline__ float get(int k) const {
+    if constexpr (sizeof(Tin) == 4) {
+      return __uint_as_float(w[k]);
+    } else {
+      const uint32_t word = w[k >> 1];
+      return (k & 1) ? __uint_as_float(word & 0xffff0000u) : __uint_as_float(word << 16);
+    }
+  }
+};
+
+// Store CW contiguous outputs of one row.
+template <typename Tout, int CW>
+__device__ __forceinline__ void store_row(Tout* p, const float* v) {
+  if constexpr (sizeof(Tout) == 4) {
+    if constexpr (CW % 4 == 0) {
+#pragma unroll
+      for (int q = 0; q < CW / 4; ++q)
+        reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    } else if constexpr (CW == 2) {
+      *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    } else {
+      p[0] = v[0];
+    }
+  } else {
+    if constexpr (CW == 1) {
+      p[0] = f32_to_bf16_rne(v[0]);
+    } else {
+      uint32_t w[CW / 2];
+#pragma unroll
+      for (int q = 0; q < CW / 2; ++q)
+        w[q] = (uint32_t)f32_to_bf16_rne(v[2 * q]) | ((uint32_t)f32_to_bf16_rne(v[2 * q + 1]) << 16);
+      if constexpr (CW == 8) {
+        *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else if constexpr (CW == 4) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(p) = w[0];
+      }
+    }
+  }
+}
 
 // The main loop is straight-line code: loads, LDS staging and stores are all
 // unconditional, so the compiler can count outstanding memory operations
@@ -180,36 +252,48 @@ struct Tile {
 // pipeline at every tile.)  To get there:
 //  * the ragged part of the chunk (nsteps % T steps) is peeled off and run
 //    first as one short tile; every later tile is full;
-//  * lanes past the last channel load, compute and store the last channel's
-//    values, which are bit-identical, so their duplicate stores are benign;
+//  * lanes past the last channel compute the last channel's values, which
+//    are bit-identical, and items past it repeat the last item's work, so
+//    their duplicate stores are benign;
 //  * threads past the B/C staging work stage a duplicate of another thread's
 //    vector (same value, same LDS address);
 //  * two register banks hold the raw inputs of the next two tiles, so each
-//    wave keeps two tiles of HBM reads in flight behind its arithmetic; the
+//    thread keeps two tiles of HBM reads in flight behind its arithmetic; the
 //    prefetch index is clamped to the last tile, so it always reads valid rows.
-template <typename Tin, typename Tout, int NS, bool PASS_A, bool HAS_Z>
+//
+// Phases 1 and 3 are elementwise over (step, channel), so they use their own
+// thread mapping: with WIDE, thread item (row r, chunk c) covers CW
+// consecutive channels of one step, read and written with 16-byte accesses
+// (1 KiB per wavefront instruction); without WIDE (d_inner not a multiple of
+// 8), CW = 1 and an item is one channel.  Phase 2 keeps lane = channel.
+template <typename Tin, typename Tout, int NS, bool PASS_A, bool HAS_Z, bool WIDE>
 __global__ void __launch_bounds__(kWave * (kDState / NS))
 scan_chunk_kernel(ScanArgs a) {
   constexpr int G = kDState / NS;         // wavefronts per workgroup (state groups)
   constexpr int T = Tile<G>::T;           // time steps per tile
-  constexpr int SPW = T / G;              // steps each wave prepares / finishes
   constexpr int NTHR = kWave * G;
+  constexpr int CW = WIDE ? Tile<G>::CW : 1;   // channels per item
+  constexpr int CPR = kWave / CW;         // items per row
+  constexpr int IPT = T * CPR / NTHR;     // items per thread
+  static_assert(IPT >= 1 && IPT * NTHR == T * CPR, "tile does not split evenly");
   constexpr int EPV = Vec16<Tin>::kElems; // B/C elements per 16-byte vector
   constexpr int VPR = kDState / EPV;      // 16-byte vectors per B or C row
   constexpr int BC_VECS = (PASS_A ? 1 : 2) * T * VPR;
   constexpr int BC_R = (BC_VECS + NTHR - 1) / NTHR;
   constexpr bool kZ = HAS_Z && !PASS_A;
-  using In = Io<Tin>;
+  using R = Raw<Tin, CW>;
 
-  __shared__ float2 sh_dtv[T][kWave];                 // (dt, dt * x)
+  // Rows are padded by one element: the prologue/epilogue items (CW
+  // consecutive channels per thread, 64 / CW threads per row) then spread
+  // over all LDS banks, while lane = channel accesses stay consecutive.
+  __shared__ float2 sh_dtv[T][kWave + 1];             // (dt, dt * x)
   __shared__ float sh_B[T][kDState];
   __shared__ float sh_C[PASS_A ? 1 : T][kDState];
-  __shared__ float sh_y[PASS_A ? 1 : T][G][kWave];    // partial readouts
+  __shared__ float sh_y[PASS_A ? 1 : T][G * kWave + 1];  // partial readouts, [row][wave][channel]
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  // the wave index is uniform across the wave: keep it (and every row offset
-  // derived from it) in scalar registers
+  // the wave index is uniform across the wave: keep it in a scalar register
   const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int b = blockIdx.z;
   const int k = blockIdx.y;
@@ -217,8 +301,9 @@ scan_chunk_kernel(ScanArgs a) {
   const int64_t Dn = a.d_inner;
   const int64_t L = a.seqlen;
   const int64_t d0 = (int64_t)blockIdx.x * kWave;
-  // lanes past the last channel take the last channel's place
-  const int loff = (int)min((int64_t)lane, Dn - 1 - d0);
+  const int nvalid = (int)min((int64_t)kWave, Dn - d0);   // channels of this block
+  // phase 2: lanes past the last channel take the last channel's place
+  const int loff = min(lane, nvalid - 1);
   const int64_t dl = d0 + loff;
   const int64_t t_begin = (int64_t)k * a.chunk_len;
   const int64_t t_end = min(t_begin + a.chunk_len, L);
@@ -228,8 +313,22 @@ scan_chunk_kernel(ScanArgs a) {
   float A2[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) A2[i] = a.A[dl * kDState + g * NS + i] * kLog2e;
-  const float bias = a.bias != nullptr ? a.bias[dl] : 0.0f;
-  const float Dd = has_D ? a.D[dl] : 0.0f;
+
+  // phases 1 and 3: this thread's items (row, first channel), fixed for the kernel
+  int irow[IPT], icol[IPT];
+  float ibias[IPT][CW], iD[IPT][CW];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int idx = tid + it * NTHR;
+    irow[it] = idx / CPR;
+    icol[it] = min(idx % CPR, (nvalid + CW - 1) / CW - 1) * CW;  // clamp to the last valid item
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+      const int64_t dq = d0 + min(icol[it] + q, nvalid - 1);
+      ibias[it][q] = a.bias != nullptr ? a.bias[dq] : 0.0f;
+      iD[it][q] = has_D ? a.D[dq] : 0.0f;
+    }
+  }
 
   float h[NS];
   if (!PASS_A && k > 0) {
@@ -252,22 +351,21 @@ scan_chunk_kernel(ScanArgs a) {
   const Tin* Cb = static_cast<const Tin*>(a.C) + ((int64_t)b * L + t_begin) * kDState;
 
   struct Bank {
-    typename In::raw rx[SPW], rdt[SPW], rz[SPW];
+    R rx[IPT], rdt[IPT], rz[IPT];
     uint4 rbc[BC_R];
   };
   Bank bk0, bk1;
-  float xs[SPW], zs[SPW];
+  R xs[IPT], zs[IPT];   // raw x and z of the tile being finished
 
   // Issue the loads of the tile at chunk-relative step tt0 with nt valid steps
   // (rows past nt re-read the last valid row).
   auto issue = [&](Bank& bk, int64_t tt0, int nt) {
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int s = min(g * SPW + j, nt - 1);  // wave-uniform
-      const int64_t row = (tt0 + s) * Dn;
-      bk.rx[j] = xb[row + loff];
-      bk.rdt[j] = db[row + loff];
-      if (kZ) bk.rz[j] = zb[row + loff];
+    for (int it = 0; it < IPT; ++it) {
+      const int64_t off = (tt0 + min(irow[it], nt - 1)) * Dn + icol[it];
+      bk.rx[it].load(xb + off);
+      bk.rdt[it].load(db + off);
+      if (kZ) bk.rz[it].load(zb + off);
     }
 #pragma unroll
     for (int r = 0; r < BC_R; ++r) {
@@ -281,17 +379,19 @@ scan_chunk_kernel(ScanArgs a) {
     }
   };
 
-  // Phase 1: discretise this wave's steps into LDS; stage B/C rows as fp32.
+  // Phase 1: discretise this thread's items into LDS; stage B/C rows as fp32.
   auto commit = [&](Bank& bk) {
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int s = g * SPW + j;
-      const float x = In::cvt(bk.rx[j]);
-      const float u = In::cvt(bk.rdt[j]) + bias;
-      const float dt = softplus ? softplus_f(u) : u;
-      sh_dtv[s][lane] = make_float2(dt, dt * x);
-      xs[j] = x;
-      if (kZ) zs[j] = In::cvt(bk.rz[j]);
+    for (int it = 0; it < IPT; ++it) {
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        const float x = bk.rx[it].get(q);
+        const float u = bk.rdt[it].get(q) + ibias[it][q];
+        const float dt = softplus ? softplus_f(u) : u;
+        sh_dtv[irow[it]][icol[it] + q] = make_float2(dt, dt * x);
+      }
+      xs[it] = bk.rx[it];
+      if (kZ) zs[it] = bk.rz[it];
     }
 #pragma unroll
     for (int r = 0; r < BC_R; ++r) {
@@ -308,38 +408,63 @@ scan_chunk_kernel(ScanArgs a) {
     }
   };
 
-  // Phase 2: the recurrence over one step for this wave's NS states.
-  auto step = [&](int s) {
-    const float2 v = sh_dtv[s][lane];
-    float y = 0.0f;
+  // Phase 2: the recurrence for this wave's NS states over steps [0, n).
+  // Software-pipelined by one step: the transitions exp(dt * A) of step s + 1
+  // do not depend on the state, so they are computed while step s updates it,
+  // which keeps each exp's latency off the h dependency chain.
+  auto run_steps = [&](auto n_c) {
+    const int n = n_c;
+    float2 v = sh_dtv[0][loff];
+    float ar[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const float ar = __builtin_amdgcn_exp2f(v.x * A2[i]);
-      h[i] = __builtin_fmaf(ar, h[i], v.y * sh_B[s][g * NS + i]);
-      if (!PASS_A) y = __builtin_fmaf(sh_C[PASS_A ? 0 : s][g * NS + i], h[i], y);
-    }
-    if (PASS_A) {
-      dtsum += v.x;
-    } else {
-      sh_y[PASS_A ? 0 : s][PASS_A ? 0 : g][lane] = y;
+    for (int i = 0; i < NS; ++i) ar[i] = __builtin_amdgcn_exp2f(v.x * A2[i]);
+#pragma unroll
+    for (int s = 0; s < n; ++s) {
+      float2 vn = v;
+      float an[NS];
+      if (s + 1 < n) {
+        vn = sh_dtv[s + 1][loff];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) an[i] = __builtin_amdgcn_exp2f(vn.x * A2[i]);
+      }
+      float y = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        h[i] = __builtin_fmaf(ar[i], h[i], v.y * sh_B[s][g * NS + i]);
+        if (!PASS_A) y = __builtin_fmaf(sh_C[PASS_A ? 0 : s][g * NS + i], h[i], y);
+      }
+      if (PASS_A) {
+        dtsum += v.x;
+      } else {
+        sh_y[PASS_A ? 0 : s][(PASS_A ? 0 : g) * kWave + lane] = y;
+      }
+      if (s + 1 < n) {
+        v = vn;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) ar[i] = an[i];
+      }
     }
   };
 
-  // Phase 3: finish this wave's steps: sum partials, D skip, gate, store.
-  // Full tiles store unconditionally; the peeled ragged tile (full == false)
-  // skips its steps past nt with a wave-uniform branch.
+  // Phase 3: finish this thread's items: sum partials in a fixed order, D
+  // skip, gate, store.  Full tiles store unconditionally; the peeled ragged
+  // tile (full == false) skips rows past nt.
   auto finish = [&](int64_t tt0, int nt, bool full) {
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int s = g * SPW + j;
-      if (full || s < nt) {
-        float y = sh_y[PASS_A ? 0 : s][0][lane];
+    for (int it = 0; it < IPT; ++it) {
+      const int r = irow[it];
+      float y[CW];
 #pragma unroll
-        for (int gg = 1; gg < G; ++gg) y += sh_y[PASS_A ? 0 : s][PASS_A ? 0 : gg][lane];
-        if (has_D) y = __builtin_fmaf(Dd, xs[j], y);
-        if (kZ) y = y * silu_f(zs[j]);
-        Io<Tout>::store(ob + (tt0 + s) * Dn, loff, y);
+      for (int q = 0; q < CW; ++q) {
+        const int col = icol[it] + q;
+        float acc = sh_y[PASS_A ? 0 : r][col];
+#pragma unroll
+        for (int gg = 1; gg < G; ++gg) acc += sh_y[PASS_A ? 0 : r][(PASS_A ? 0 : gg) * kWave + col];
+        if (has_D) acc = __builtin_fmaf(iD[it][q], xs[it].get(q), acc);
+        if (kZ) acc = acc * silu_f(zs[it].get(q));
+        y[q] = acc;
       }
+      if (full || r < nt) store_row<Tout, CW>(ob + (tt0 + r) * Dn + icol[it], y);
     }
   };
 
@@ -348,8 +473,7 @@ scan_chunk_kernel(ScanArgs a) {
     commit(bk);
     issue(bk, pf0, T);
     block_sync();
-#pragma unroll
-    for (int s = 0; s < T; ++s) step(s);
+    run_steps(std::integral_constant<int, T>());
     block_sync();
     if (!PASS_A) finish(tt0, T, true);
   };
@@ -364,7 +488,7 @@ scan_chunk_kernel(ScanArgs a) {
     commit(bk0);
     if (nfull > 1) issue(bk0, tail + T, T);
     block_sync();
-    for (int s = 0; s < tail; ++s) step(s);
+    run_steps(tail);
     block_sync();
     if (!PASS_A) finish(0, tail, false);
   } else {
@@ -543,23 +667,30 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
 
 // --------------------------------------------------------------- launchers
 
-template <typename Tin, typename Tout, int NS>
-hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
+template <typename Tin, typename Tout, int NS, bool WIDE>
+hipError_t launch_scan_w(const ScanArgs& a, hipStream_t s) {
   constexpr int G = kDState / NS;
   const unsigned nblk = (unsigned)((a.d_inner + kWave - 1) / kWave);
   if (a.n_chunks > 1) {
     dim3 gridA(nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch);
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, true, false>), gridA, dim3(kWave * G), 0, s, a);
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, true, false, WIDE>), gridA, dim3(kWave * G), 0, s, a);
     const unsigned ncolblk = (unsigned)((a.d_inner * kDState + 63) / 64);
     hipLaunchKernelGGL(carry_kernel, dim3(ncolblk, (unsigned)a.batch), dim3(256), 0, s, a.ws_state,
                        (const float*)a.ws_dtsum, a.A, a.d_inner, a.n_chunks);
   }
   dim3 gridB(nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
   if (a.z != nullptr)
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, true>), gridB, dim3(kWave * G), 0, s, a);
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, true, WIDE>), gridB, dim3(kWave * G), 0, s, a);
   else
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, false>), gridB, dim3(kWave * G), 0, s, a);
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, false, WIDE>), gridB, dim3(kWave * G), 0, s, a);
   return hipGetLastError();
+}
+
+// The wide prologue/epilogue needs rows that split into aligned groups of 8.
+template <typename Tin, typename Tout, int NS>
+hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
+  if (a.d_inner % 8 == 0) return launch_scan_w<Tin, Tout, NS, true>(a, s);
+  return launch_scan_w<Tin, Tout, NS, false>(a, s);
 }
 
 template <typename Tin, typename Tout>
