@@ -39,13 +39,31 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def measured_traffic(key):
+    """HBM bytes per launch recorded from the FETCH_SIZE / WRITE_SIZE counters
+    (scaled by a plain copy's reading) in profiles/*.md, or None when no record
+    exists for `key` or the kernel source has changed since it was taken."""
+    import glob
+    import hashlib
+    with open(os.path.join(ROOT, "sequence_scan_amd", "csrc", "kernels.hip"), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for row in f:
+                if row.startswith("traffic-record: "):
+                    rec = json.loads(row[len("traffic-record: "):])
+                    if rec.get("kernel_source_sha256") == sha and key in rec:
+                        return rec[key]["hbm_bytes"]
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba2p8b",
-                    choices=["mamba2p8b", "mamba130m", "long_dna", "tiny_fp32", "decode"])
+                    choices=["mamba2p8b", "mamba130m", "long_dna", "tiny_fp32", "decode", "copy"])
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -196,6 +214,18 @@ def main():
     import sequence_scan_amd as ssm
     ssm.library()
 
+    if args.workload == "copy":
+        # a plain device-to-device copy of known size: the reference point for
+        # the hardware byte counters and the achievable streaming bandwidth
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        ms, _ = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
+        nbytes = 2 * n * 4
+        print(json.dumps({"metric": "device copy bandwidth (read + write)", "value": round(nbytes / (ms / 1e3) / 1e9, 1),
+                          "unit": "GB/s", "bytes_per_copy": nbytes, "ms_per_copy": round(ms, 4), "n_gpus": 1}), flush=True)
+        return
+
     if args.workload == "decode":
         d = decode_case(args.decode_steps)
         print(json.dumps({"metric": "decode tokens/sec at batch 256", "value": round(d["tokens_per_s"], 1),
@@ -216,13 +246,17 @@ def main():
     tflops = states * FLOPS_PER_STATE_UPDATE / (k_avg / 1e3) / 1e12
     k_gbs = nbytes / (k_avg / 1e3) / 1e9
     single_launch = plan_used.get("n_chunks", 1) in (1, None)
+    traffic = None
+    if single_launch and args.out_dtype == "f32" and not args.plan:
+        traffic = measured_traffic(f"scan_{cfg.name}")
     roofline = {
         "bound": "alu",
         "achieved": round(tflops, 2),
         "peak": round(VALU_PEAK_TFLOPS, 2),
         "unit": "TFLOP/s",
         "frac": round(tflops / VALU_PEAK_TFLOPS, 4),
-        "traffic": None,
+        "traffic": traffic,
+        "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading)",
         "kernel": "scan_chunk_kernel (pass B)" if single_launch else "ssm_scan_fwd (all passes)",
         "flops_per_state_update": FLOPS_PER_STATE_UPDATE,
         "state_updates_per_launch": states,

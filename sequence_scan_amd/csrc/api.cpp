@@ -74,30 +74,23 @@ int device_simds() {
   return cus * 4;
 }
 
-// The plan: prefer a single time chunk (no extra pass) and the largest state
-// group per wave that still gives at least 1.5 wavefronts per SIMD; when even
-// one state per wave cannot fill the chip, cut time into chunks of at least
-// 1024 steps with 4 states per wave.
+// The plan (from measurements on MI355X): 4 states per wave (a workgroup of
+// 4 wavefronts per 64 channels) is the fastest split on every workload
+// measured, down to 0.75 wavefronts per SIMD.  When the channel blocks give
+// fewer than half a wavefront per SIMD, the sequence is also cut into chunks
+// until there are about 12 wavefronts per SIMD, with chunks of at least 1024
+// steps: the extra reduction pass costs less than idle SIMDs.
 void choose_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_plan* p) {
   const int64_t blocks = batch * ((d_inner + 63) / 64);
-  const int64_t want = simds + simds / 2;
-  int ns = 0;
-  for (int cand : {16, 8, 4, 2, 1}) {
-    if (blocks * (16 / cand) >= want) {
-      ns = cand;
-      break;
-    }
-  }
+  const int64_t waves = std::max<int64_t>(1, blocks * 4);
   int64_t chunks = 1;
-  if (ns == 0) {
-    ns = 4;
-    const int64_t waves = std::max<int64_t>(1, blocks * 4);
-    chunks = (3 * (int64_t)simds + waves - 1) / waves;
+  if (waves < simds / 2) {
+    chunks = (12 * (int64_t)simds + waves - 1) / waves;
     chunks = std::min(chunks, std::max<int64_t>(1, seqlen / 1024));
   }
   int64_t chunk_len = seqlen > 0 ? (seqlen + chunks - 1) / chunks : 1;
   if (chunk_len < 1) chunk_len = 1;
-  p->states_per_wave = ns;
+  p->states_per_wave = 4;
   p->reserved0 = 0;
   p->chunk_len = chunk_len;
   p->n_chunks = seqlen > 0 ? (seqlen + chunk_len - 1) / chunk_len : 0;

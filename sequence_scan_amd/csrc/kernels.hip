@@ -616,10 +616,35 @@ __global__ void __launch_bounds__(64) affine_exclusive_scan_kernel(const float* 
 // One (b, d) pair per quad of lanes; lane q of the quad owns states 4q..4q+3
 // (one 16-byte load and store of the fp32 state).  The readout is reduced
 // over the quad with two DPP quad permutes; lane 0 of the quad applies the
-// D skip and the gate and stores out.
+// D skip and the gate and stores out.  The per-step inputs are read with
+// non-temporal loads and out is stored non-temporally: they are touched once,
+// and keeping them out of the caches leaves room for the state, which every
+// step reads and writes again.
+template <typename Tin>
+__device__ __forceinline__ float nt_load(const void* p, int64_t i) {
+  if constexpr (sizeof(Tin) == 4) {
+    return __builtin_nontemporal_load(static_cast<const float*>(p) + i);
+  } else {
+    return bf16_to_f32(__builtin_nontemporal_load(static_cast<const uint16_t*>(p) + i));
+  }
+}
+
+template <typename Tin>
+__device__ __forceinline__ void load4(const void* p, int64_t i, float* o) {
+  if constexpr (sizeof(Tin) == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+}
+
 template <typename Tin, typename Tout>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
-  using In = Io<Tin>;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t e = gid >> 2;
   const int q = threadIdx.x & 3;
@@ -630,13 +655,10 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   float4 hs = *reinterpret_cast<const float4*>(a.state + e * kDState + 4 * q);
   const float4 av = *reinterpret_cast<const float4*>(a.A + d * kDState + 4 * q);
   float Bv[4], Cv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    Bv[i] = In::cvt(In::load(a.B, b * kDState + 4 * q + i));
-    Cv[i] = In::cvt(In::load(a.C, b * kDState + 4 * q + i));
-  }
-  const float x = In::cvt(In::load(a.x, e));
-  const float dl = In::cvt(In::load(a.delta, e));
+  load4<Tin>(a.B, b * kDState + 4 * q, Bv);
+  load4<Tin>(a.C, b * kDState + 4 * q, Cv);
+  const float x = nt_load<Tin>(a.x, e);
+  const float dl = nt_load<Tin>(a.delta, e);
   const float u = dl + (a.bias != nullptr ? a.bias[d] : 0.0f);
   const float dt = a.softplus ? softplus_f(u) : u;
   const float dtx = dt * x;
@@ -655,8 +677,12 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   y = y + SSM_DPP(0.0f, y, 0x4E, 0xf);  // quad_perm [2,3,0,1]
   if (q == 0) {
     if (a.D != nullptr) y = __builtin_fmaf(a.D[d], x, y);
-    if (a.z != nullptr) y = y * silu_f(In::cvt(In::load(a.z, e)));
-    Io<Tout>::store(a.out, e, y);
+    if (a.z != nullptr) y = y * silu_f(nt_load<Tin>(a.z, e));
+    if constexpr (sizeof(Tout) == 4) {
+      __builtin_nontemporal_store(y, static_cast<float*>(a.out) + e);
+    } else {
+      __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<uint16_t*>(a.out) + e);
+    }
   }
 }
 
