@@ -35,6 +35,10 @@
 namespace ssm {
 namespace {
 
+// Every lambda of a kernel body must be inlined: an outlined call would pass
+// the state and the register banks through scratch memory.
+#define SSM_INLINE __attribute__((always_inline))
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -359,7 +363,7 @@ scan_chunk_kernel(ScanArgs a) {
 
   // Issue the loads of the tile at chunk-relative step tt0 with nt valid steps
   // (rows past nt re-read the last valid row).
-  auto issue = [&](Bank& bk, int64_t tt0, int nt) {
+  auto issue = [&](Bank& bk, int64_t tt0, int nt) SSM_INLINE {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int64_t off = (tt0 + min(irow[it], nt - 1)) * Dn + icol[it];
@@ -380,16 +384,25 @@ scan_chunk_kernel(ScanArgs a) {
   };
 
   // Phase 1: discretise this thread's items into LDS; stage B/C rows as fp32.
-  auto commit = [&](Bank& bk) {
+  // The softplus switch is taken once per tile (a uniform branch around the
+  // whole item loop), never per element.
+  auto discretise = [&](Bank& bk, auto sp_c) SSM_INLINE {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
         const float x = bk.rx[it].get(q);
         const float u = bk.rdt[it].get(q) + ibias[it][q];
-        const float dt = softplus ? softplus_f(u) : u;
+        const float dt = decltype(sp_c)::value ? softplus_f(u) : u;
         sh_dtv[irow[it]][icol[it] + q] = make_float2(dt, dt * x);
       }
+    }
+  };
+  auto commit = [&](Bank& bk) SSM_INLINE {
+    if (softplus) discretise(bk, std::true_type());
+    else discretise(bk, std::false_type());
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
       xs[it] = bk.rx[it];
       if (kZ) zs[it] = bk.rz[it];
     }
@@ -412,7 +425,7 @@ scan_chunk_kernel(ScanArgs a) {
   // Software-pipelined by one step: the transitions exp(dt * A) of step s + 1
   // do not depend on the state, so they are computed while step s updates it,
   // which keeps each exp's latency off the h dependency chain.
-  auto run_steps = [&](auto n_c) {
+  auto run_steps = [&](auto n_c) SSM_INLINE {
     const int n = n_c;
     float2 v = sh_dtv[0][loff];
     float ar[NS];
@@ -446,36 +459,50 @@ scan_chunk_kernel(ScanArgs a) {
     }
   };
 
-  // Phase 3: finish this thread's items: sum partials in a fixed order, D
-  // skip, gate, store.  Full tiles store unconditionally; the peeled ragged
-  // tile (full == false) skips rows past nt.
-  auto finish = [&](int64_t tt0, int nt, bool full) {
+  // Phase 3: finish this thread's items into registers: sum the partials in
+  // a fixed order, D skip, gate.  The D switch is taken once per tile.
+  float yv[IPT][CW];
+  auto finish_items = [&](auto d_c) SSM_INLINE {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int r = irow[it];
-      float y[CW];
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
         const int col = icol[it] + q;
         float acc = sh_y[PASS_A ? 0 : r][col];
 #pragma unroll
         for (int gg = 1; gg < G; ++gg) acc += sh_y[PASS_A ? 0 : r][(PASS_A ? 0 : gg) * kWave + col];
-        if (has_D) acc = __builtin_fmaf(iD[it][q], xs[it].get(q), acc);
+        if (decltype(d_c)::value) acc = __builtin_fmaf(iD[it][q], xs[it].get(q), acc);
         if (kZ) acc = acc * silu_f(zs[it].get(q));
-        y[q] = acc;
+        yv[it][q] = acc;
       }
-      if (full || r < nt) store_row<Tout, CW>(ob + (tt0 + r) * Dn + icol[it], y);
     }
   };
+  auto finish = [&]() SSM_INLINE {
+    if (has_D) finish_items(std::true_type());
+    else finish_items(std::false_type());
+  };
+  // Store the finished tile that starts at chunk-relative step tt0.  Full
+  // tiles store unconditionally; the peeled ragged tile (full == false)
+  // skips rows past nt.
+  auto store = [&](int64_t tt0, int nt, bool full) SSM_INLINE {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it)
+      if (full || irow[it] < nt) store_row<Tout, CW>(ob + (tt0 + irow[it]) * Dn + icol[it], yv[it]);
+  };
 
-  // A full tile: everything straight-line.
-  auto full_tile = [&](Bank& bk, int64_t tt0, int64_t pf0) {
+  // A full tile, straight-line.  The outputs of the previous full tile
+  // (at step prev0, when has_prev) are stored only after this tile's inputs
+  // have been committed: the wait for those inputs then never includes the
+  // acknowledgement of stores issued just before it.
+  auto full_tile = [&](Bank& bk, int64_t tt0, int64_t pf0, auto has_prev_c, int64_t prev0) SSM_INLINE {
     commit(bk);
+    if (!PASS_A && decltype(has_prev_c)::value) store(prev0, T, true);
     issue(bk, pf0, T);
     block_sync();
     run_steps(std::integral_constant<int, T>());
     block_sync();
-    if (!PASS_A) finish(tt0, T, true);
+    if (!PASS_A) finish();
   };
 
   const int64_t nsteps = t_end - t_begin;
@@ -490,20 +517,28 @@ scan_chunk_kernel(ScanArgs a) {
     block_sync();
     run_steps(tail);
     block_sync();
-    if (!PASS_A) finish(0, tail, false);
+    if (!PASS_A) {
+      finish();
+      store(0, tail, false);
+    }
   } else {
     if (nfull > 0) issue(bk1, 0, T);
     if (nfull > 1) issue(bk0, T, T);
   }
   // full tiles f = 0, 1, ...: tile f's inputs are in bk1 for even f and bk0
-  // for odd f; each tile prefetches tile f + 2 into the bank it just used
-  int64_t f = 0;
-  for (; f + 1 < nfull; f += 2) {
-    const int64_t t0 = tail + f * T;
-    full_tile(bk1, t0, min(t0 + 2 * T, last_full));
-    full_tile(bk0, t0 + T, min(t0 + 3 * T, last_full));
+  // for odd f; each tile prefetches tile f + 2 into the bank it just used and
+  // stores the outputs of tile f - 1
+  if (nfull > 0) {
+    full_tile(bk1, tail, min(tail + 2 * T, last_full), std::false_type(), 0);
+    int64_t f = 1;
+    for (; f + 1 < nfull; f += 2) {
+      const int64_t t0 = tail + f * T;
+      full_tile(bk0, t0, min(t0 + 2 * T, last_full), std::true_type(), t0 - T);
+      full_tile(bk1, t0 + T, min(t0 + 3 * T, last_full), std::true_type(), t0);
+    }
+    if (f < nfull) full_tile(bk0, tail + f * T, last_full, std::true_type(), tail + (f - 1) * T);
+    if (!PASS_A) store(last_full, T, true);
   }
-  if (f < nfull) full_tile(bk1, tail + f * T, last_full);
 
   if (PASS_A) {
     float* dst = a.ws_state + (((int64_t)b * K + k) * Dn + dl) * kDState + g * NS;

@@ -3,7 +3,8 @@
 The scan kernel's correctness depends on every LDS access staying on its side
 of the workgroup barriers.  A compiler that moves a whole phase of LDS reads
 past a barrier leaves two barriers with nothing between them; this test
-rejects such a build.  It also checks that no kernel spills to scratch memory.
+rejects such a build.  It also checks that no kernel spills to scratch memory
+or calls an outlined function.
 """
 import re
 import shutil
@@ -54,3 +55,10 @@ def test_no_scratch_spills(asm):
     for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm, re.S):
         priv = re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", m.group(2))
         assert priv and int(priv.group(1)) == 0, f"{m.group(1)} uses scratch"
+
+
+def test_no_outlined_calls(asm):
+    # every helper of a kernel body is inlined: a call would move live state
+    # through the calling convention's stack
+    for name, body in kernels(asm):
+        assert "s_swappc" not in body and "s_setpc" not in body, f"{name} makes a call"
