@@ -7,8 +7,10 @@ the whole batch with inputs resident in HBM.  Prints ONE JSON line:
 
   value       GB/s of algorithmic traffic (x, delta, z, B, C read once + out
               written once) over the K timed steps;
-  roofline    the scan kernel against its binding ceiling (the fp32 VALU rate),
-              with its HBM fraction beside it;
+  roofline    the scan kernel against its binding ceiling, the VALU rate for
+              its instruction mix (24 SIMD-cycles per wavefront of 64 state
+              updates), with the plain fp32 FMA rate and the HBM fraction
+              beside it;
   cpu_baseline the fp64 oracle on the host cores over the same workload;
   decode      512 consecutive ssm_state_update steps at batch 256, d_inner 8192:
               tokens/s (the second half of the metric).
@@ -29,10 +31,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, AMD spec
-# fp32 vector VALU without packed-FP32 instructions (the build disables them):
-# 256 CUs x 4 SIMD x 16 lanes x 2 flop (FMA) x 2.4 GHz
-VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+SIMDS, CLOCK_HZ = 256 * 4, 2.4e9  # 256 CUs x 4 SIMD16 at the 2.4 GHz peak engine clock
+# fp32 FMA rate without packed-FP32 instructions (the build disables them):
+# a wave64 VALU instruction occupies a SIMD16 for 4 cycles
+FMA_PEAK_TFLOPS = SIMDS * 16 * 2 * CLOCK_HZ / 1e12
 FLOPS_PER_STATE_UPDATE = 7       # mul (dt*A), exp, mul (dt*x*B), FMA (update, 2), FMA (readout, 2)
+# The instruction-mix ceiling of one state update: four 4-cycle VALU
+# instructions plus one v_exp_f32, which occupies the VALU for 8 cycles
+# (measured: it does not overlap other VALU work), so 24 SIMD-cycles per
+# wavefront of 64 updates.
+CYCLES_PER_WAVE_UPDATE = 24
+MIX_PEAK_TFLOPS = SIMDS * CLOCK_HZ * 64 / CYCLES_PER_WAVE_UPDATE * FLOPS_PER_STATE_UPDATE / 1e12
 
 
 def log(msg):
@@ -252,13 +261,16 @@ def main():
     roofline = {
         "bound": "alu",
         "achieved": round(tflops, 2),
-        "peak": round(VALU_PEAK_TFLOPS, 2),
+        "peak": round(MIX_PEAK_TFLOPS, 2),
         "unit": "TFLOP/s",
-        "frac": round(tflops / VALU_PEAK_TFLOPS, 4),
+        "frac": round(tflops / MIX_PEAK_TFLOPS, 4),
         "traffic": traffic,
         "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading)",
         "kernel": "scan_chunk_kernel (pass B)" if single_launch else "ssm_scan_fwd (all passes)",
         "flops_per_state_update": FLOPS_PER_STATE_UPDATE,
+        "peak_basis": "1024 SIMDs x 2.4 GHz x 64 lanes / 24 cycles per wavefront state update x 7 flops",
+        "fp32_fma_peak": round(FMA_PEAK_TFLOPS, 2),
+        "fp32_fma_frac": round(tflops / FMA_PEAK_TFLOPS, 4),
         "state_updates_per_launch": states,
         "avg_launch_us": round(k_avg * 1e3, 2),
         "hbm": {"achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -122,6 +122,18 @@ __device__ __forceinline__ float softplus_f(float u) {
   return __builtin_fmaxf(u, 0.0f) + __builtin_fmaf(l, kLn2, c);
 }
 
+// The same in log2 units: softplus(u) * log2(e) from a = u * log2(e),
+// = max(a, 0) + log2(1 + 2^-|a|), with the rounding error c of w = 1 + 2^-|a|
+// added back as c * log2(e).  The scan works with step sizes in these units:
+// exp(dt A) = exp2(dt2 A) with dt2 = dt log2(e).
+__device__ __forceinline__ float softplus2_f(float a) {
+  const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(a));
+  const float w = 1.0f + e;
+  const float c = e - (w - 1.0f);
+  const float l = __builtin_amdgcn_logf(w);  // log2(w)
+  return __builtin_fmaxf(a, 0.0f) + __builtin_fmaf(c, kLog2e, l);
+}
+
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^{-z}).
 __device__ __forceinline__ float silu_f(float z) {
   const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
@@ -314,13 +326,13 @@ scan_chunk_kernel(ScanArgs a) {
   const bool softplus = a.softplus != 0;
   const bool has_D = a.D != nullptr;
 
-  float A2[NS];
+  float Ad[NS];  // this lane's A[d, n]; step sizes are in log2 units (dt2)
 #pragma unroll
-  for (int i = 0; i < NS; ++i) A2[i] = a.A[dl * kDState + g * NS + i] * kLog2e;
+  for (int i = 0; i < NS; ++i) Ad[i] = a.A[dl * kDState + g * NS + i];
 
   // phases 1 and 3: this thread's items (row, first channel), fixed for the kernel
   int irow[IPT], icol[IPT];
-  float ibias[IPT][CW], iD[IPT][CW];
+  float ibias[IPT][CW], iD[IPT][CW];  // bias in log2 units, D
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
     const int idx = tid + it * NTHR;
@@ -329,7 +341,7 @@ scan_chunk_kernel(ScanArgs a) {
 #pragma unroll
     for (int q = 0; q < CW; ++q) {
       const int64_t dq = d0 + min(icol[it] + q, nvalid - 1);
-      ibias[it][q] = a.bias != nullptr ? a.bias[dq] : 0.0f;
+      ibias[it][q] = a.bias != nullptr ? a.bias[dq] * kLog2e : 0.0f;
       iD[it][q] = has_D ? a.D[dq] : 0.0f;
     }
   }
@@ -359,7 +371,8 @@ scan_chunk_kernel(ScanArgs a) {
     uint4 rbc[BC_R];
   };
   Bank bk0, bk1;
-  R xs[IPT], zs[IPT];   // raw x and z of the tile being finished
+  float xs[IPT][CW];    // x of the tile being finished
+  R zs[IPT];            // raw z of the tile being finished
 
   // Issue the loads of the tile at chunk-relative step tt0 with nt valid steps
   // (rows past nt re-read the last valid row).
@@ -383,18 +396,21 @@ scan_chunk_kernel(ScanArgs a) {
     }
   };
 
-  // Phase 1: discretise this thread's items into LDS; stage B/C rows as fp32.
-  // The softplus switch is taken once per tile (a uniform branch around the
-  // whole item loop), never per element.
+  // Phase 1: discretise this thread's items into LDS as (dt2, dt2 * x), the
+  // step size in log2 units and the input term's factor (the ln 2 that
+  // dt2 * x carries is folded into the staged B rows); stage B/C rows as
+  // fp32.  The softplus switch is taken once per tile (a uniform branch
+  // around the whole item loop), never per element.
   auto discretise = [&](Bank& bk, auto sp_c) SSM_INLINE {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
         const float x = bk.rx[it].get(q);
-        const float u = bk.rdt[it].get(q) + ibias[it][q];
-        const float dt = decltype(sp_c)::value ? softplus_f(u) : u;
-        sh_dtv[irow[it]][icol[it] + q] = make_float2(dt, dt * x);
+        const float u2 = __builtin_fmaf(bk.rdt[it].get(q), kLog2e, ibias[it][q]);
+        const float dt2 = decltype(sp_c)::value ? softplus2_f(u2) : u2;
+        sh_dtv[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * x);
+        xs[it][q] = x;
       }
     }
   };
@@ -403,7 +419,6 @@ scan_chunk_kernel(ScanArgs a) {
     else discretise(bk, std::false_type());
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
-      xs[it] = bk.rx[it];
       if (kZ) zs[it] = bk.rz[it];
     }
 #pragma unroll
@@ -416,8 +431,9 @@ scan_chunk_kernel(ScanArgs a) {
       float f[EPV];
       Vec16<Tin>::unpack(bk.rbc[r], f);
       float* dst = which ? &sh_C[PASS_A ? 0 : row][part * EPV] : &sh_B[row][part * EPV];
+      const float scale = which ? 1.0f : kLn2;  // B carries the ln 2 of dt2 * x
 #pragma unroll
-      for (int i = 0; i < EPV; ++i) dst[i] = f[i];
+      for (int i = 0; i < EPV; ++i) dst[i] = f[i] * scale;
     }
   };
 
@@ -430,7 +446,7 @@ scan_chunk_kernel(ScanArgs a) {
     float2 v = sh_dtv[0][loff];
     float ar[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) ar[i] = __builtin_amdgcn_exp2f(v.x * A2[i]);
+    for (int i = 0; i < NS; ++i) ar[i] = __builtin_amdgcn_exp2f(v.x * Ad[i]);
 #pragma unroll
     for (int s = 0; s < n; ++s) {
       float2 vn = v;
@@ -438,7 +454,7 @@ scan_chunk_kernel(ScanArgs a) {
       if (s + 1 < n) {
         vn = sh_dtv[s + 1][loff];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) an[i] = __builtin_amdgcn_exp2f(vn.x * A2[i]);
+        for (int i = 0; i < NS; ++i) an[i] = __builtin_amdgcn_exp2f(vn.x * Ad[i]);
       }
       float y = 0.0f;
 #pragma unroll
@@ -472,7 +488,7 @@ scan_chunk_kernel(ScanArgs a) {
         float acc = sh_y[PASS_A ? 0 : r][col];
 #pragma unroll
         for (int gg = 1; gg < G; ++gg) acc += sh_y[PASS_A ? 0 : r][(PASS_A ? 0 : gg) * kWave + col];
-        if (decltype(d_c)::value) acc = __builtin_fmaf(iD[it][q], xs[it].get(q), acc);
+        if (decltype(d_c)::value) acc = __builtin_fmaf(iD[it][q], xs[it][q], acc);
         if (kZ) acc = acc * silu_f(zs[it].get(q));
         yv[it][q] = acc;
       }
@@ -555,8 +571,8 @@ scan_chunk_kernel(ScanArgs a) {
 // ------------------------------------------------------------ carry kernel
 //
 // On entry, slot p < K-1 of ws_state holds chunk p's end state from zero
-// and ws_dtsum its step-size sum S_p; the pair of chunk p for coordinate
-// (d, n) is (exp(A[d,n] S_p), end state).  On exit slot p holds the state
+// and ws_dtsum its step-size sum S_p in log2 units (the scan kernel's dt2);
+// the pair of chunk p for coordinate (d, n) is (exp2(A[d,n] S_p), end state).  On exit slot p holds the state
 // entering chunk p + 1: the inclusive composition of pairs 0..p applied to
 // h = 0.  A workgroup takes 64 consecutive (d, n) columns; pairs are loaded
 // 64 at a time (coalesced along columns) into LDS, each wave scans 16
@@ -574,7 +590,7 @@ __global__ void __launch_bounds__(256) carry_kernel(float* ws_state, const float
   const int64_t ncol = Dn * kDState;
   const int64_t col = (int64_t)blockIdx.x * 64 + lane;
   const int npairs = K - 1;
-  const float a2 = col < ncol ? A[col] * kLog2e : 0.0f;
+  const float a2 = col < ncol ? A[col] : 0.0f;  // S is a sum of log2-unit step sizes
   if (tid < 64) {
     ca[tid] = 1.0f;
     cb[tid] = 0.0f;
