@@ -48,6 +48,13 @@ class OracleLib:
         lib.oracle_scan_fwd.restype = ctypes.c_int
         lib.oracle_scan_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp,
                                         _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+        lib.oracle_scan_fwd_from.restype = ctypes.c_int
+        lib.oracle_scan_fwd_from.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp,
+                                             _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+        lib.oracle_conv1d_fwd.restype = ctypes.c_int
+        lib.oracle_conv1d_fwd.argtypes = [_dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, _i64, _i64, _i64, _i64]
+        lib.oracle_conv1d_update.restype = ctypes.c_int
+        lib.oracle_conv1d_update.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int, _dp, _i64, _i64, _i64]
         lib.oracle_state_update.restype = ctypes.c_int
         lib.oracle_state_update.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int,
                                             _dp, _i64, _i64, _i64]
@@ -60,15 +67,15 @@ class OracleLib:
         self.lib = lib
 
     def scan_fwd(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
-                 chunk: int = 0, nthreads: int | None = None, return_state: bool = True):
-        """Sequential fp64 scan from a zero state.
+                 chunk: int = 0, nthreads: int | None = None, return_state: bool = True, h0=None):
+        """Sequential fp64 scan from the state h0 [batch, d_inner, d_state] (None: zero).
 
         x, delta, z: [batch, L, d_inner]; B, C: [batch, L, d_state]; A: [d_inner, d_state];
         D, delta_bias: [d_inner].  Returns (out [batch, L, d_inner], last_state
         [batch, d_inner, d_state] or None), float64.  ``chunk > 0`` runs the chunked
         form: per-chunk affine pairs composed in time order, then each chunk re-run."""
         x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
-        D, z, delta_bias = map(_f64, (D, z, delta_bias))
+        D, z, delta_bias, h0 = map(_f64, (D, z, delta_bias, h0))
         if x.ndim != 3:
             raise ValueError("x must be [batch, L, d_inner]")
         batch, L, Dn = x.shape
@@ -79,11 +86,13 @@ class OracleLib:
             raise ValueError("bad A/B/C shape")
         if (D is not None and D.shape != (Dn,)) or (delta_bias is not None and delta_bias.shape != (Dn,)):
             raise ValueError("bad D/delta_bias shape")
+        if h0 is not None and h0.shape != (batch, Dn, N):
+            raise ValueError("h0 must be [batch, d_inner, d_state]")
         out = np.empty((batch, L, Dn), dtype=np.float64)
         last = np.empty((batch, Dn, N), dtype=np.float64) if return_state else None
-        rc = self.lib.oracle_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                      _ptr(delta_bias), int(bool(softplus)), _ptr(out), _ptr(last),
-                                      batch, L, Dn, N, int(chunk), int(nthreads or default_threads()))
+        rc = self.lib.oracle_scan_fwd_from(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                           _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(out), _ptr(last),
+                                           batch, L, Dn, N, int(chunk), int(nthreads or default_threads()))
         if rc != 0:
             raise ValueError("oracle_scan_fwd rejected its arguments")
         return out, last
@@ -116,6 +125,43 @@ class OracleLib:
         b = np.empty(n)
         self.lib.oracle_affine_compose(_ptr(a2), _ptr(b2), _ptr(a1), _ptr(b1), _ptr(a), _ptr(b), n)
         return a, b
+
+    def conv1d_fwd(self, x, weight, bias=None, silu=True, conv_state=None, return_state=True):
+        """Causal depthwise conv1d (+ bias, + SiLU).  x: [batch, L, d_inner]; weight:
+        [d_inner, d_conv]; bias: [d_inner]; conv_state: [batch, d_inner, d_conv], the
+        d_conv most recent earlier inputs, oldest first (None: zeros).  Returns (out
+        [batch, L, d_inner], new conv_state or None) as float64."""
+        x, w, bias, st = map(_f64, (x, weight, bias, conv_state))
+        batch, L, Dn = x.shape
+        K = w.shape[1]
+        if w.shape != (Dn, K) or (bias is not None and bias.shape != (Dn,)):
+            raise ValueError("bad weight/bias shape")
+        if st is not None and st.shape != (batch, Dn, K):
+            raise ValueError("conv_state must be [batch, d_inner, d_conv]")
+        out = np.empty((batch, L, Dn), dtype=np.float64)
+        st_out = np.empty((batch, Dn, K), dtype=np.float64) if return_state else None
+        rc = self.lib.oracle_conv1d_fwd(_ptr(x), _ptr(w), _ptr(bias), int(bool(silu)), _ptr(st), _ptr(out),
+                                        _ptr(st_out), batch, L, Dn, K)
+        if rc != 0:
+            raise ValueError("oracle_conv1d_fwd rejected its arguments")
+        return out, st_out
+
+    def conv1d_update(self, conv_state, x, weight, bias=None, silu=True):
+        """One decode step of the convolution.  conv_state: [batch, d_inner, d_conv];
+        x: [batch, d_inner].  Returns (out [batch, d_inner], new conv_state); the
+        argument itself is not modified."""
+        st = np.array(conv_state, dtype=np.float64, order="C", copy=True)
+        x, w, bias = map(_f64, (x, weight, bias))
+        batch, Dn = x.shape
+        K = w.shape[1]
+        if st.shape != (batch, Dn, K) or w.shape != (Dn, K):
+            raise ValueError("bad conv_state/weight shape")
+        out = np.empty((batch, Dn), dtype=np.float64)
+        rc = self.lib.oracle_conv1d_update(_ptr(st), _ptr(x), _ptr(w), _ptr(bias), int(bool(silu)), _ptr(out),
+                                           batch, Dn, K)
+        if rc != 0:
+            raise ValueError("oracle_conv1d_update rejected its arguments")
+        return out, st
 
     def step_size(self, delta, delta_bias=None, softplus=True):
         """dt = softplus(delta + bias), or delta + bias; delta: [rows, d_inner]."""
@@ -154,3 +200,11 @@ def affine_compose(*args, **kw):
 
 def step_size(*args, **kw):
     return load().step_size(*args, **kw)
+
+
+def conv1d_fwd(*args, **kw):
+    return load().conv1d_fwd(*args, **kw)
+
+
+def conv1d_update(*args, **kw):
+    return load().conv1d_update(*args, **kw)

@@ -47,7 +47,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI 1
+#define ORACLE_ABI 2
 
 int oracle_abi_version(void) { return ORACLE_ABI; }
 
@@ -79,6 +79,7 @@ typedef struct {
   const double *x, *delta, *A, *B, *C, *D, *z, *bias;
   int softplus_on;
   double *out, *last_state;
+  const double* h0; /* [batch, Dn, N] initial state, or NULL for zero */
   int64_t batch, L, Dn, N, chunk;
   int64_t row_begin, row_end; /* rows are r = b * Dn + d */
 } job_t;
@@ -87,7 +88,7 @@ static void scan_rows(const job_t* j) {
   double* h = (double*)calloc((size_t)j->N, sizeof(double));
   for (int64_t r = j->row_begin; r < j->row_end; ++r) {
     int64_t b = r / j->Dn, d = r % j->Dn;
-    for (int64_t n = 0; n < j->N; ++n) h[n] = 0.0;
+    for (int64_t n = 0; n < j->N; ++n) h[n] = j->h0 ? j->h0[(b * j->Dn + d) * j->N + n] : 0.0;
     for (int64_t t = 0; t < j->L; ++t) {
       int64_t e = (b * j->L + t) * j->Dn + d;          /* [batch, L, d_inner] */
       const double* Bt = j->B + (b * j->L + t) * j->N; /* [batch, L, d_state] */
@@ -135,8 +136,9 @@ static void scan_rows_chunked(const job_t* j) {
         }
       }
     }
-    /* pass 2: compose the pairs in time order; chunk k starts from acc applied to h = 0 */
-    for (int64_t n = 0; n < N; ++n) { acc_a[n] = 1.0; acc_b[n] = 0.0; }
+    /* pass 2: compose the pairs in time order; chunk k starts from acc applied to
+     * h = 0, where acc starts as the constant map to the initial state */
+    for (int64_t n = 0; n < N; ++n) { acc_a[n] = 0.0; acc_b[n] = j->h0 ? j->h0[(b * j->Dn + d) * N + n] : 0.0; }
     for (int64_t k = 0; k < nch; ++k) {
       for (int64_t n = 0; n < N; ++n) h[n] = acc_b[n]; /* acc(0) = acc_a*0 + acc_b */
       int64_t t1 = (k + 1) * Tc < L ? (k + 1) * Tc : L;
@@ -191,22 +193,36 @@ static int run_threads(job_t base, int nthreads) {
   return 0;
 }
 
-/* Full forward scan.  Shapes: x, delta, z, out [batch, L, Dn]; B, C [batch, L, N];
- * A [Dn, N]; D, bias [Dn]; last_state [batch, Dn, N].  D, z, bias, last_state may be
- * NULL.  chunk > 0 selects the chunked form with chunks of that many steps.
- * Returns 0, or -1 on bad arguments. */
+/* Full forward scan from the initial state h0 [batch, Dn, N] (NULL: zero).
+ * Shapes: x, delta, z, out [batch, L, Dn]; B, C [batch, L, N]; A [Dn, N]; D, bias
+ * [Dn]; last_state [batch, Dn, N].  D, z, bias, last_state may be NULL.  chunk > 0
+ * selects the chunked form with chunks of that many steps.  Returns 0, or -1 on
+ * bad arguments.  Continuing a sequence from a stored state is the recurrence
+ * itself (the decode cache of "Модуль 8", sections 7 and 14, vladkulikov.com). */
+int oracle_scan_fwd_from(const double* x, const double* delta, const double* A, const double* B,
+                         const double* C, const double* D, const double* z, const double* bias,
+                         int softplus_on, const double* h0, double* out, double* last_state,
+                         int64_t batch, int64_t L, int64_t Dn, int64_t N, int64_t chunk, int nthreads) {
+  if (!x || !delta || !A || !B || !C || !out) return -1;
+  if (batch < 0 || L < 0 || Dn < 0 || N <= 0 || chunk < 0) return -1;
+  if (L == 0) {
+    if (last_state) {
+      if (h0) memcpy(last_state, h0, sizeof(double) * (size_t)(batch * Dn * N));
+      else memset(last_state, 0, sizeof(double) * (size_t)(batch * Dn * N));
+    }
+    return 0;
+  }
+  job_t j = {x, delta, A, B, C, D, z, bias, softplus_on, out, last_state, h0, batch, L, Dn, N, chunk, 0, 0};
+  return run_threads(j, nthreads);
+}
+
+/* The scan from a zero state. */
 int oracle_scan_fwd(const double* x, const double* delta, const double* A, const double* B,
                     const double* C, const double* D, const double* z, const double* bias,
                     int softplus_on, double* out, double* last_state, int64_t batch, int64_t L,
                     int64_t Dn, int64_t N, int64_t chunk, int nthreads) {
-  if (!x || !delta || !A || !B || !C || !out) return -1;
-  if (batch < 0 || L < 0 || Dn < 0 || N <= 0 || chunk < 0) return -1;
-  if (L == 0) {
-    if (last_state) memset(last_state, 0, sizeof(double) * (size_t)(batch * Dn * N));
-    return 0;
-  }
-  job_t j = {x, delta, A, B, C, D, z, bias, softplus_on, out, last_state, batch, L, Dn, N, chunk, 0, 0};
-  return run_threads(j, nthreads);
+  return oracle_scan_fwd_from(x, delta, A, B, C, D, z, bias, softplus_on, NULL, out, last_state,
+                              batch, L, Dn, N, chunk, nthreads);
 }
 
 /* One decode step: state [batch, Dn, N] is read and overwritten; x, delta, z, out
@@ -243,4 +259,64 @@ void oracle_step_size(const double* delta, const double* bias, int softplus_on, 
                       int64_t rows, int64_t Dn) {
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t d = 0; d < Dn; ++d) out[r * Dn + d] = step_size(delta[r * Dn + d], bias, d, softplus_on);
+}
+
+/* ------------------------------------------------------------------ conv1d
+ *
+ * The block's short causal depthwise convolution ("Mamba и State Space
+ * Models", nareshka.ru, section "Реализация MambaBlock": a Conv1d with one
+ * filter of width K per channel, padding K - 1, output cut to the first L
+ * steps; "State Space Models: Mamba и альтернатива Transformer", johe.ru,
+ * MambaBlock: the same convolution followed by SiLU):
+ *
+ *   out[b,t,d] = act(bias[d] + sum_{k<K} w[d,k] * x[b, t-K+1+k, d])
+ *
+ * act is SiLU or the identity.  Inputs before t = 0 come from the cache
+ * conv_state_in [batch, Dn, K], which holds the K most recent earlier inputs,
+ * oldest first (entry k is the input at time k - K), or are zero when it is
+ * NULL ("Модуль 8", vladkulikov.com, sections 6 and 14: the decode cache keeps
+ * the last d_conv inputs of the convolution branch, [batch, d_inner, d_conv]).
+ * conv_state_out receives the K most recent inputs after the call.
+ */
+static double conv_input(const double* x, const double* state_in, int64_t b, int64_t t, int64_t d,
+                         int64_t L, int64_t Dn, int64_t K) {
+  if (t >= 0) return x[(b * L + t) * Dn + d];
+  return state_in ? state_in[(b * Dn + d) * K + (t + K)] : 0.0;
+}
+
+int oracle_conv1d_fwd(const double* x, const double* w, const double* bias, int silu_on,
+                      const double* state_in, double* out, double* state_out, int64_t batch,
+                      int64_t L, int64_t Dn, int64_t K) {
+  if (!x || !w || !out || batch < 0 || L < 0 || Dn < 0 || K <= 0) return -1;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t d = 0; d < Dn; ++d) {
+        double acc = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < K; ++k)
+          acc += w[d * K + k] * conv_input(x, state_in, b, t - K + 1 + k, d, L, Dn, K);
+        out[(b * L + t) * Dn + d] = silu_on ? silu(acc) : acc;
+      }
+  if (state_out)
+    for (int64_t b = 0; b < batch; ++b)
+      for (int64_t d = 0; d < Dn; ++d)
+        for (int64_t k = 0; k < K; ++k)
+          state_out[(b * Dn + d) * K + k] = conv_input(x, state_in, b, L - K + k, d, L, Dn, K);
+  return 0;
+}
+
+/* One decode step of the convolution: the cache drops its oldest input and
+ * appends x; the output is the filter applied to the updated cache. */
+int oracle_conv1d_update(double* state, const double* x, const double* w, const double* bias,
+                         int silu_on, double* out, int64_t batch, int64_t Dn, int64_t K) {
+  if (!state || !x || !w || !out || batch < 0 || Dn < 0 || K <= 0) return -1;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t d = 0; d < Dn; ++d) {
+      double* st = state + (b * Dn + d) * K;
+      for (int64_t k = 0; k + 1 < K; ++k) st[k] = st[k + 1];
+      st[K - 1] = x[b * Dn + d];
+      double acc = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += w[d * K + k] * st[k];
+      out[b * Dn + d] = silu_on ? silu(acc) : acc;
+    }
+  return 0;
 }

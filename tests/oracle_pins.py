@@ -21,7 +21,12 @@ Sources of the statements:
     3 "Фильтр": with stable diagonal dynamics each coordinate decays on its
     own; section 4: a NaN spreads to all later steps.
   * "Mamba и State Space Models" (nareshka.ru), "Ключевая инновация": the
-    selective recurrence and the readout after the update.
+    selective recurrence and the readout after the update; "Реализация
+    MambaBlock": the block's depthwise Conv1d with padding d_conv - 1, cut to
+    the sequence length (a causal filter), which johe.ru's MambaBlock follows
+    with SiLU; vladkulikov.com sections 6 and 14: the decode cache keeps the
+    last d_conv inputs of that branch and the SSM state, so a sequence can be
+    continued from both.
 """
 from __future__ import annotations
 
@@ -327,8 +332,126 @@ def pin_optional_inputs(orc):
     _close(nobias, full, 1e-13, "bias folded into delta")
 
 
+def pin_initial_state_free_response(orc):
+    """From a stored state h0 with no input (x = 0) the output is the state's free
+    decay read out: y_t = (sum_n C_t[n] exp(A_n sum_{s<=t} dt_s) h0[n]) * SiLU(z_t),
+    a closed form with cumulative step sums (no recurrence)."""
+    rng = np.random.default_rng(41)
+    batch, L, Dn, N = 2, 23, 3, 5
+    c = _rand_case(rng, batch, L, Dn, N)
+    c["x"] = np.zeros_like(c["x"])
+    h0 = rng.standard_normal((batch, Dn, N))
+    dt = _softplus(c["delta"] + c["delta_bias"][None, None, :])   # [b, t, d]
+    S = np.cumsum(dt, axis=1)
+    ref = np.einsum("btn,btdn,bdn->btd", c["C"], np.exp(S[..., None] * c["A"][None, None]), h0)
+    ref = ref * _silu(c["z"])
+    for chunk in (0, 5):
+        out, last = orc.scan_fwd(**c, h0=h0, chunk=chunk)
+        _close(out, ref, 1e-12, f"free response from h0 (chunk {chunk})")
+        _close(last, np.exp(S[:, -1, :, None] * c["A"][None]) * h0, 1e-12, "final state of the free response")
+
+
+def pin_initial_state_continuation(orc):
+    """Scanning L1 steps, then L2 more from the stored state, is one scan of L1 + L2
+    steps (bitwise: the same arithmetic in the same order); the chunked form from
+    h0 agrees with the sequential one."""
+    rng = np.random.default_rng(43)
+    batch, L1, L2, Dn, N = 2, 9, 14, 3, 4
+    c = _rand_case(rng, batch, L1 + L2, Dn, N)
+    full, full_last = orc.scan_fwd(**c)
+    first = {k: (v[:, :L1] if k in ("x", "delta", "z", "B", "C") else v) for k, v in c.items()}
+    second = {k: (v[:, L1:] if k in ("x", "delta", "z", "B", "C") else v) for k, v in c.items()}
+    o1, h1 = orc.scan_fwd(**first)
+    o2, h2 = orc.scan_fwd(**second, h0=h1)
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), full), "continuation differs from one scan"
+    assert np.array_equal(h2, full_last), "continued final state differs"
+    o2c, h2c = orc.scan_fwd(**second, h0=h1, chunk=4)
+    _close(o2c, o2, 1e-12, "chunked continuation")
+    _close(h2c, h2, 1e-12, "chunked continuation state")
+    # an empty continuation returns the stored state unchanged
+    empty = {k: (v[:, :0] if k in ("x", "delta", "z", "B", "C") else v) for k, v in c.items()}
+    _, h_empty = orc.scan_fwd(**empty, h0=h1)
+    assert np.array_equal(h_empty, h1)
+
+
+def _conv_reference(x, w, bias, silu_on, hist=None):
+    """Causal depthwise convolution per channel with numpy's convolve: the filter
+    reversed (Conv1d correlates), full convolution, first L outputs; optional K
+    earlier inputs prepended."""
+    batch, L, Dn = x.shape
+    K = w.shape[1]
+    out = np.empty_like(x)
+    for b in range(batch):
+        for d in range(Dn):
+            seq = x[b, :, d] if hist is None else np.concatenate([hist[b, d, :], x[b, :, d]])
+            full = np.convolve(seq, w[d, ::-1])
+            lin = full[(0 if hist is None else K):][:L] + (0.0 if bias is None else bias[d])
+            out[b, :, d] = _silu(lin) if silu_on else lin
+    return out
+
+
+def pin_conv1d_numpy(orc):
+    """The convolution equals numpy's convolve with the reversed filter (Conv1d
+    with padding K - 1 cut to L steps), plus bias, through SiLU; with a cache of
+    earlier inputs, the same on the joined sequence."""
+    rng = np.random.default_rng(47)
+    batch, L, Dn, K = 2, 19, 3, 4
+    x = rng.standard_normal((batch, L, Dn))
+    w = rng.standard_normal((Dn, K))
+    bias = rng.standard_normal(Dn)
+    for silu_on in (True, False):
+        out, _ = orc.conv1d_fwd(x, w, bias, silu=silu_on)
+        _close(out, _conv_reference(x, w, bias, silu_on), 1e-12, f"conv1d vs numpy (silu {silu_on})")
+    hist = rng.standard_normal((batch, Dn, K))
+    out, _ = orc.conv1d_fwd(x, w, None, silu=True, conv_state=hist)
+    _close(out, _conv_reference(x, w, None, True, hist), 1e-12, "conv1d with a cache vs numpy")
+
+
+def pin_conv1d_impulse(orc):
+    """A unit impulse at t0 (no bias, no activation) returns the filter reversed:
+    out[t0 + j] = w[K - 1 - j] for j < K, and 0 elsewhere."""
+    batch, L, Dn, K, t0 = 1, 12, 2, 4, 3
+    x = np.zeros((batch, L, Dn))
+    x[0, t0, :] = 1.0
+    w = np.array([[1.0, 2.0, 3.0, 4.0], [-0.5, 0.25, 8.0, -2.0]])
+    out, st = orc.conv1d_fwd(x, w, None, silu=False)
+    ref = np.zeros_like(x)
+    for j in range(K):
+        ref[0, t0 + j, :] = w[:, K - 1 - j]
+    assert np.array_equal(out, ref), "impulse response is not the reversed filter"
+    assert np.array_equal(st, np.zeros((batch, Dn, K))), "cache after the impulse has left it"
+
+
+def pin_conv1d_decode_and_continuation(orc):
+    """L decode steps from a zero cache equal one prefill (bitwise), and so does a
+    prefill of L1 steps continued by a prefill of L2 steps from the returned cache;
+    a sequence shorter than the filter leaves a zero-padded cache."""
+    rng = np.random.default_rng(53)
+    batch, L1, L2, Dn, K = 2, 6, 9, 3, 4
+    x = rng.standard_normal((batch, L1 + L2, Dn))
+    w = rng.standard_normal((Dn, K))
+    bias = rng.standard_normal(Dn)
+    full, full_st = orc.conv1d_fwd(x, w, bias)
+    st = np.zeros((batch, Dn, K))
+    outs = []
+    for t in range(L1 + L2):
+        o, st = orc.conv1d_update(st, x[:, t], w, bias)
+        outs.append(o)
+    assert np.array_equal(np.stack(outs, axis=1), full), "decode steps differ from the prefill"
+    assert np.array_equal(st, full_st), "decode cache differs from the prefill cache"
+    o1, s1 = orc.conv1d_fwd(x[:, :L1], w, bias)
+    o2, s2 = orc.conv1d_fwd(x[:, L1:], w, bias, conv_state=s1)
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), full), "continued prefill differs"
+    assert np.array_equal(s2, full_st)
+    _, s_short = orc.conv1d_fwd(x[:, :2], w, bias)
+    ref = np.zeros((batch, Dn, K))
+    ref[:, :, K - 2:] = np.transpose(x[:, :2], (0, 2, 1))
+    assert np.array_equal(s_short, ref), "short-sequence cache is not zero-padded"
+
+
 ALL_PINS = [
     pin_affine_worked_example, pin_step_size, pin_lti_convolution, pin_semiseparable, pin_delta_zero,
     pin_impulse_closed_form, pin_chunked_composition, pin_decode_equals_scan, pin_invariants,
-    pin_decay, pin_nan_propagation, pin_optional_inputs,
+    pin_decay, pin_nan_propagation, pin_optional_inputs, pin_initial_state_free_response,
+    pin_initial_state_continuation, pin_conv1d_numpy, pin_conv1d_impulse, pin_conv1d_decode_and_continuation,
 ]

@@ -41,6 +41,20 @@ MUTANTS = {
                          "j->last_state[(d * j->N + n) * 0 + (b * j->Dn + d) * j->N + (j->N - 1 - n)] = h[n];"),
     "gate_before_skip": ("  if (D) y += D[d] * x;\n  if (zp) y *= silu(*zp);",
                          "  if (zp) y *= silu(*zp);\n  if (D) y += D[d] * x;"),
+    "h0_ignored": ("h[n] = j->h0 ? j->h0[(b * j->Dn + d) * j->N + n] : 0.0;", "h[n] = 0.0;"),
+    "h0_chunked_ignored": ("acc_b[n] = j->h0 ? j->h0[(b * j->Dn + d) * N + n] : 0.0; }",
+                           "acc_b[n] = 0.0; }"),
+    "conv_filter_not_reversed": ("acc += w[d * K + k] * conv_input(x, state_in, b, t - K + 1 + k, d, L, Dn, K);",
+                                 "acc += w[d * K + (K - 1 - k)] * conv_input(x, state_in, b, t - K + 1 + k, d, L, Dn, K);"),
+    "conv_not_causal": ("conv_input(x, state_in, b, t - K + 1 + k, d, L, Dn, K);",
+                        "conv_input(x, state_in, b, t + k, d, L, Dn, K);"),
+    "conv_state_off_by_one": ("return state_in ? state_in[(b * Dn + d) * K + (t + K)] : 0.0;",
+                              "return state_in ? state_in[(b * Dn + d) * K + (t + K - 1 < 0 ? 0 : t + K - 1)] : 0.0;"),
+    "conv_update_no_shift": ("for (int64_t k = 0; k + 1 < K; ++k) st[k] = st[k + 1];", ""),
+    "conv_bias_dropped": ("double acc = bias ? bias[d] : 0.0;\n        for (int64_t k = 0; k < K; ++k)\n          acc +=",
+                          "double acc = 0.0;\n        for (int64_t k = 0; k < K; ++k)\n          acc +="),
+    "conv_state_out_oldest_last": ("state_out[(b * Dn + d) * K + k] = conv_input(x, state_in, b, L - K + k, d, L, Dn, K);",
+                                   "state_out[(b * Dn + d) * K + k] = conv_input(x, state_in, b, L - 1 - k, d, L, Dn, K);"),
 }
 
 
