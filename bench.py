@@ -76,6 +76,7 @@ def parse():
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--plan", default=None, help="states_per_wave,chunk_len (tuning only)")
     return ap.parse_args()
@@ -212,6 +213,45 @@ def decode_case(steps):
     }
 
 
+def conv_case(batch, seqlen, d_inner, reps=20):
+    """The conv1d front-end on a layer's shape: prefill (bf16 in, bf16 out, the
+    scan's input) and one decode step at batch 256, d_inner 8192."""
+    import torch
+
+    import sequence_scan_amd as ssm
+    import workloads
+
+    inp = workloads.conv_inputs(batch, seqlen, d_inner, 4, "bf16", seed=0, with_state=True)
+    x = torch.from_numpy(inp["x"]).to(torch.bfloat16).cuda()
+    w = torch.from_numpy(inp["weight"]).cuda()
+    b = torch.from_numpy(inp["bias"]).cuda()
+    st = torch.from_numpy(inp["conv_state"]).to(torch.bfloat16).cuda()
+    st_out = torch.empty_like(st)
+    out = torch.empty_like(x)
+    run = lambda: ssm.ssm_conv1d_fwd(x, w, b, conv_state_in=st, out=out, conv_state_out=st_out)
+    avg, med, mn = per_launch_ms(run, reps)
+    nbytes = workloads.conv_algorithmic_bytes(batch, seqlen, d_inner, 4, "bf16", "bf16")
+    res = {"workload": f"conv1d prefill batch {batch}, seqlen {seqlen}, d_inner {d_inner}, d_conv 4, bf16 in/out, SiLU",
+           "us_per_call": round(avg * 1e3, 2), "bytes_per_call": nbytes,
+           "GBps": round(nbytes / (avg / 1e3) / 1e9, 1), "hbm_frac": round(nbytes / (avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del x, out, inp
+    dcfg = workloads.DECODE_CONFIG
+    dinp = workloads.conv_inputs(dcfg.batch, 1, dcfg.d_inner, 4, "bf16", seed=1, with_state=True)
+    xs = torch.from_numpy(dinp["x"][:, 0]).to(torch.bfloat16).cuda()
+    ws = torch.from_numpy(dinp["weight"]).cuda()
+    bs = torch.from_numpy(dinp["bias"]).cuda()
+    cache = torch.from_numpy(dinp["conv_state"]).to(torch.bfloat16).cuda()
+    dout = torch.empty_like(xs)
+    step = lambda: ssm.ssm_conv1d_update(cache, xs, ws, bs, out=dout)
+    davg, _, _ = per_launch_ms(step, 50)
+    e = dcfg.batch * dcfg.d_inner
+    dbytes = e * (2 * 4 * 2 + 2 + 2)  # cache read + written (4 bf16), x read, out written
+    res["decode_step"] = {"workload": f"conv1d decode step batch {dcfg.batch}, d_inner {dcfg.d_inner}, bf16",
+                          "us_per_step": round(davg * 1e3, 2), "bytes_per_step": dbytes,
+                          "GBps": round(dbytes / (davg / 1e3) / 1e9, 1)}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -305,6 +345,8 @@ def main():
     del inp
     if not args.no_decode and args.workload == "mamba2p8b":
         line["decode"] = decode_case(args.decode_steps)
+    if not args.no_conv and args.workload == "mamba2p8b":
+        line["conv1d"] = conv_case(cfg.batch, cfg.seqlen, cfg.d_inner)
     print(json.dumps(line), flush=True)
 
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
@@ -127,6 +127,71 @@ ssm_status ssm_scan_fwd_plan(const void* x, const void* delta, const float* A, c
                              int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                              ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream,
                              const ssm_plan* plan);
+
+/*
+ * Forward scan continuing from a stored state: the recurrence starts from
+ * h = initial_state instead of zero, which continues a sequence scanned
+ * earlier (chunked prefill, or a prompt after a cached prefix; pages
+ * "Модуль 8. Альтернативы Transformer", sections 7 and 14: the inference cache
+ * holds ssm_state [batch, d_inner, d_state], and the scan is the same
+ * recurrence run from it).  Scanning L1 steps and then L2 steps from the
+ * returned last_state gives the same outputs as one scan of L1 + L2 steps.
+ *   initial_state: [batch, d_inner, d_state] fp32, or NULL for a zero state.
+ * last_state may be the same buffer as initial_state (the state is then
+ * replaced in place), but must not overlap it otherwise; out must not overlap
+ * it.  plan may be NULL (the planner's choice).  With seqlen == 0 a non-NULL
+ * last_state receives the initial state.  Everything else as for
+ * ssm_scan_fwd.
+ */
+ssm_status ssm_scan_fwd_from(const void* x, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z,
+                             const float* delta_bias, int softplus, const float* initial_state,
+                             void* out, float* last_state, int64_t batch, int64_t seqlen,
+                             int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
+                             ssm_dtype out_dtype, void* stream, const ssm_plan* plan);
+
+/*
+ * The block's short causal depthwise convolution that feeds the scan (page
+ * "Mamba и State Space Models", nareshka.ru, section "Реализация MambaBlock":
+ * a Conv1d with one width-d_conv filter per channel and padding d_conv - 1,
+ * cut to the sequence length; page "State Space Models: Mamba и альтернатива
+ * Transformer", johe.ru, MambaBlock: SiLU after it):
+ *
+ *   out[b,t,d] = act(bias[d] + sum_{k < d_conv} weight[d,k] * x[b, t-d_conv+1+k, d])
+ *
+ * act is SiLU when `silu` is nonzero, else the identity.  Inputs before t = 0
+ * are taken from conv_state_in, or are zero when it is NULL.
+ *   x, out          : [batch, seqlen, d_inner] (in_dtype / out_dtype)
+ *   weight          : [d_inner, d_conv] fp32;  bias: [d_inner] fp32 or NULL
+ *   conv_state_in   : [batch, d_inner, d_conv] in in_dtype, or NULL: the d_conv
+ *                     most recent earlier inputs of each channel, oldest first
+ *                     (page "Модуль 8", sections 6 and 14: the decode cache keeps
+ *                     the last d_conv inputs of the convolution branch)
+ *   conv_state_out  : same layout, or NULL: receives the d_conv most recent
+ *                     inputs after this call (zero-padded, or taken from
+ *                     conv_state_in, when seqlen < d_conv); it may be the same
+ *                     buffer as conv_state_in.
+ * d_conv is 2, 3 or 4 (else SSM_ERR_UNSUPPORTED).  Pointers 16-byte aligned;
+ * out and conv_state_out must not overlap any input or each other (except the
+ * in-place cache).  Errors and asynchrony as for ssm_scan_fwd.
+ */
+ssm_status ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int silu,
+                          const void* conv_state_in, void* out, void* conv_state_out,
+                          int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_conv,
+                          ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream);
+
+/*
+ * One decode step of the convolution: for every (b, d) the cache conv_state
+ * [batch, d_inner, d_conv] (in_dtype, read and overwritten in place) drops its
+ * oldest input and appends x[b, d]; out[b, d] is the filter applied to the
+ * updated cache, plus bias, through SiLU when `silu` is nonzero.  Running
+ * seqlen steps from a zero cache gives the outputs and the cache of one
+ * ssm_conv1d_fwd call.  x, out: [batch, d_inner].  Other arguments and errors
+ * as for ssm_conv1d_fwd; out must not overlap conv_state or any input.
+ */
+ssm_status ssm_conv1d_update(void* conv_state, const void* x, const float* weight, const float* bias,
+                             int silu, void* out, int64_t batch, int64_t d_inner, int64_t d_conv,
+                             ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream);
 
 /*
  * The affine-pair operator on its own, for checking the carry pass's combine

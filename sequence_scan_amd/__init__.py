@@ -7,7 +7,8 @@ streams.  There is no fallback: if ``libssmscan.so`` is missing or cannot be
 loaded, every call raises.
 
 Functions carry the C names: ``ssm_scan_fwd``, ``ssm_state_update``,
-``ssm_scan_fwd_plan``, ``ssm_scan_plan``, ``ssm_affine_exclusive_scan``,
+``ssm_scan_fwd_plan``, ``ssm_scan_fwd_from``, ``ssm_scan_plan``,
+``ssm_conv1d_fwd``, ``ssm_conv1d_update``, ``ssm_affine_exclusive_scan``,
 ``ssm_status_string``, ``ssm_last_error``, ``ssm_abi_version``.
 """
 from __future__ import annotations
@@ -60,6 +61,16 @@ def _load():
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_plan.argtypes = scan_args + [ctypes.POINTER(ssm_plan)]
     lib.ssm_scan_fwd_plan.restype = ctypes.c_int
+    lib.ssm_scan_fwd_from.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                      _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp,
+                                      ctypes.POINTER(ssm_plan)]
+    lib.ssm_scan_fwd_from.restype = ctypes.c_int
+    lib.ssm_conv1d_fwd.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                   ctypes.c_int, ctypes.c_int, _vp]
+    lib.ssm_conv1d_fwd.restype = ctypes.c_int
+    lib.ssm_conv1d_update.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i64, _i64, _i64,
+                                      ctypes.c_int, ctypes.c_int, _vp]
+    lib.ssm_conv1d_update.restype = ctypes.c_int
     lib.ssm_state_update.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                      _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
     lib.ssm_state_update.restype = ctypes.c_int
@@ -164,6 +175,73 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: b
 
 def ssm_scan_fwd_plan(*args, plan: dict, **kw):
     return ssm_scan_fwd(*args, plan=plan, **kw)
+
+
+def _plan_struct(plan: Optional[dict]):
+    if plan is None:
+        return None
+    p = ssm_plan()
+    p.states_per_wave = int(plan["states_per_wave"])
+    p.chunk_len = int(plan["chunk_len"])
+    return ctypes.byref(p)
+
+
+def ssm_scan_fwd_from(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                      initial_state=None, out=None, last_state=None, out_dtype=None, stream=None,
+                      plan: Optional[dict] = None):
+    """Forward scan continuing from ``initial_state`` [batch, d_inner, d_state] float32
+    (None: zero); ``last_state`` may be the same tensor (replaced in place).  Other
+    arguments as for ``ssm_scan_fwd``.  Returns out."""
+    import torch
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, d_inner]")
+    batch, seqlen, d_inner = x.shape
+    d_state = A.shape[-1] if A.dim() == 2 else -1
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(_load().ssm_scan_fwd_from(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                     _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(out),
+                                     _ptr(last_state), batch, seqlen, d_inner, d_state, _dtype_code(x),
+                                     _dtype_code(out), _stream(stream), _plan_struct(plan)))
+    return out
+
+
+def ssm_conv1d_fwd(x, weight, bias=None, silu: bool = True, conv_state_in=None, out=None,
+                   conv_state_out=None, out_dtype=None, stream=None):
+    """Causal depthwise conv1d (+ bias, + SiLU) over x [batch, seqlen, d_inner]; weight
+    [d_inner, d_conv] and bias [d_inner] float32; the caches [batch, d_inner, d_conv]
+    have x's dtype.  Returns out (allocated if None, dtype ``out_dtype`` or x's)."""
+    import torch
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be [batch, seqlen, d_inner] and weight [d_inner, d_conv]")
+    batch, seqlen, d_inner = x.shape
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    for c in (conv_state_in, conv_state_out):
+        if c is not None and c.dtype != x.dtype:
+            raise TypeError("conv caches must have x's dtype")
+    _check(_load().ssm_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), int(bool(silu)), _ptr(conv_state_in),
+                                  _ptr(out), _ptr(conv_state_out), batch, seqlen, d_inner, weight.shape[1],
+                                  _dtype_code(x), _dtype_code(out), _stream(stream)))
+    return out
+
+
+def ssm_conv1d_update(conv_state, x, weight, bias=None, silu: bool = True, out=None, out_dtype=None,
+                      stream=None):
+    """One decode step of the convolution; ``conv_state`` [batch, d_inner, d_conv] (x's
+    dtype) is updated in place.  x: [batch, d_inner].  Returns out."""
+    import torch
+    if x.dim() != 2 or weight.dim() != 2:
+        raise ValueError("x must be [batch, d_inner] and weight [d_inner, d_conv]")
+    if conv_state.dtype != x.dtype:
+        raise TypeError("conv_state must have x's dtype")
+    batch, d_inner = x.shape
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(_load().ssm_conv1d_update(_ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias), int(bool(silu)),
+                                     _ptr(out), batch, d_inner, weight.shape[1], _dtype_code(x), _dtype_code(out),
+                                     _stream(stream)))
+    return out
 
 
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,

@@ -121,10 +121,28 @@ ssm_status check_common(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t 
   return SSM_OK;
 }
 
+ssm_status conv_check(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_conv, ssm_dtype in_dtype,
+                      ssm_dtype out_dtype) {
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_conv < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "negative size (batch=%lld seqlen=%lld d_inner=%lld d_conv=%lld)",
+                (long long)batch, (long long)seqlen, (long long)d_inner, (long long)d_conv);
+  if (d_conv < 2 || d_conv > 4)
+    return fail(SSM_ERR_UNSUPPORTED, "d_conv=%lld is not supported (2, 3 or 4)", (long long)d_conv);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown dtype (in=%d out=%d)", (int)in_dtype, (int)out_dtype);
+  int64_t t1, t2;
+  if (!mul_ok(batch, seqlen, &t1) || !mul_ok(t1, d_inner, &t2) || !mul_ok(t2, 8, &t1) ||
+      !mul_ok(batch, d_inner, &t1) || !mul_ok(t1, d_conv * 8, &t2))
+    return fail(SSM_ERR_BAD_SHAPE, "element count overflows int64");
+  if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch=%lld exceeds 65535", (long long)batch);
+  return SSM_OK;
+}
+
 ssm_status scan_impl(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                     const float* D, const void* z, const float* delta_bias, int softplus, void* out,
-                     float* last_state, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                     ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream, const ssm_plan* plan_in) {
+                     const float* D, const void* z, const float* delta_bias, int softplus, const float* h0,
+                     void* out, float* last_state, int64_t batch, int64_t seqlen, int64_t d_inner,
+                     int64_t d_state, ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream,
+                     const ssm_plan* plan_in) {
   Sizes sz;
   ssm_status st = check_common(batch, seqlen, d_inner, d_state, in_dtype, out_dtype, &sz);
   if (st != SSM_OK) return st;
@@ -135,9 +153,10 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
                       : (need_bc && !B) ? "B" : (need_bc && !C) ? "C" : "out";
     return fail(SSM_ERR_NULL_ARG, "required pointer %s is NULL", which);
   }
-  const void* ptrs[] = {x, delta, A, B, C, D, z, delta_bias, out, last_state};
-  const char* names[] = {"x", "delta", "A", "B", "C", "D", "z", "delta_bias", "out", "last_state"};
-  for (int i = 0; i < 10; ++i)
+  const void* ptrs[] = {x, delta, A, B, C, D, z, delta_bias, out, last_state, h0};
+  const char* names[] = {"x", "delta", "A", "B", "C", "D", "z", "delta_bias", "out", "last_state",
+                         "initial_state"};
+  for (int i = 0; i < 11; ++i)
     if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
   const int64_t si = esize(in_dtype), so = esize(out_dtype);
   const Range ins[] = {
@@ -148,11 +167,16 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   };
   const Range ro = range("out", out, sz.elems * so);
   const Range rl = range("last_state", last_state, sz.state * 4);
+  const Range rh = range("initial_state", h0, sz.state * 4);
   for (const Range& r : ins) {
     if (overlaps(ro, r)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps input %s", r.name);
     if (overlaps(rl, r)) return fail(SSM_ERR_UNSUPPORTED, "last_state overlaps input %s", r.name);
   }
   if (overlaps(ro, rl)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps last_state");
+  if (overlaps(ro, rh)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps initial_state");
+  // the final state may replace the initial one in place, but not overlap it otherwise
+  const bool h0_in_place = h0 != nullptr && static_cast<const void*>(h0) == static_cast<const void*>(last_state);
+  if (!h0_in_place && overlaps(rl, rh)) return fail(SSM_ERR_UNSUPPORTED, "last_state partly overlaps initial_state");
 
   ssm_plan plan;
   if (plan_in) {
@@ -170,8 +194,9 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch == 0 || d_inner == 0) return ok();
   if (seqlen == 0) {
-    if (last_state) {
-      hipError_t e = ssm::launch_fill_zero(last_state, sz.state, s);
+    if (last_state && !h0_in_place) {
+      hipError_t e = h0 ? ssm::launch_copy_f32(last_state, h0, sz.state, s)
+                        : ssm::launch_fill_zero(last_state, sz.state, s);
       if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     }
     return ok();
@@ -188,6 +213,7 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   a.bias = delta_bias;
   a.out = out;
   a.last_state = last_state;
+  a.h0 = h0;
   a.seqlen = seqlen;
   a.d_inner = d_inner;
   a.chunk_len = plan.chunk_len;
@@ -196,18 +222,28 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   a.batch = (int32_t)batch;
 
   void* ws = nullptr;
+  hipError_t e = hipSuccess;
   if (plan.n_chunks > 1) {
+    // With several chunks, the workgroups that read the initial state are not
+    // the ones that write the final state: an in-place initial state is read
+    // from a copy in the workspace.
+    const int64_t n_h0 = h0_in_place ? sz.state : 0;
     int64_t n_state, n_sum, bytes;
     if (!mul_ok(batch * plan.n_chunks, d_inner * d_state, &n_state) ||
-        !mul_ok(batch * plan.n_chunks, d_inner, &n_sum) || !mul_ok(n_state + n_sum, 4, &bytes))
+        !mul_ok(batch * plan.n_chunks, d_inner, &n_sum) || !mul_ok(n_state + n_sum + n_h0, 4, &bytes))
       return fail(SSM_ERR_BAD_SHAPE, "workspace size overflows int64");
-    hipError_t e = hipMallocAsync(&ws, (size_t)bytes, s);
+    e = hipMallocAsync(&ws, (size_t)bytes, s);
     if (e != hipSuccess || ws == nullptr)
       return fail(SSM_ERR_HIP, "hipMallocAsync(%lld bytes) failed: %s", (long long)bytes, hipGetErrorString(e));
     a.ws_state = static_cast<float*>(ws);
     a.ws_dtsum = a.ws_state + n_state;
+    if (n_h0 > 0) {
+      float* copy = a.ws_dtsum + n_sum;
+      e = ssm::launch_copy_f32(copy, h0, n_h0, s);
+      a.h0 = copy;
+    }
   }
-  hipError_t e = ssm::launch_scan(a, to_dt(in_dtype), to_dt(out_dtype), plan.states_per_wave, s);
+  if (e == hipSuccess) e = ssm::launch_scan(a, to_dt(in_dtype), to_dt(out_dtype), plan.states_per_wave, s);
   if (ws) {
     hipError_t e2 = hipFreeAsync(ws, s);
     if (e == hipSuccess) e = e2;
@@ -224,8 +260,8 @@ ssm_status ssm_scan_fwd(const void* x, const void* delta, const float* A, const 
                         const float* D, const void* z, const float* delta_bias, int softplus, void* out,
                         float* last_state, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                         ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream) {
-  return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, out, last_state, batch, seqlen, d_inner,
-                   d_state, in_dtype, out_dtype, stream, nullptr);
+  return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, nullptr, out, last_state, batch, seqlen,
+                   d_inner, d_state, in_dtype, out_dtype, stream, nullptr);
 }
 
 ssm_status ssm_scan_fwd_plan(const void* x, const void* delta, const float* A, const void* B, const void* C,
@@ -234,8 +270,17 @@ ssm_status ssm_scan_fwd_plan(const void* x, const void* delta, const float* A, c
                              int64_t d_state, ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream,
                              const ssm_plan* plan) {
   if (!plan) return fail(SSM_ERR_NULL_ARG, "plan is NULL");
-  return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, out, last_state, batch, seqlen, d_inner,
-                   d_state, in_dtype, out_dtype, stream, plan);
+  return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, nullptr, out, last_state, batch, seqlen,
+                   d_inner, d_state, in_dtype, out_dtype, stream, plan);
+}
+
+ssm_status ssm_scan_fwd_from(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int softplus,
+                             const float* initial_state, void* out, float* last_state, int64_t batch,
+                             int64_t seqlen, int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
+                             ssm_dtype out_dtype, void* stream, const ssm_plan* plan) {
+  return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, out, last_state, batch, seqlen,
+                   d_inner, d_state, in_dtype, out_dtype, stream, plan);
 }
 
 ssm_status ssm_scan_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, ssm_plan* plan) {
@@ -294,6 +339,90 @@ ssm_status ssm_state_update(float* state, const void* x, const void* delta, cons
   a.pairs = batch * d_inner;
   a.softplus = softplus ? 1 : 0;
   hipError_t e = ssm::launch_decode(a, to_dt(in_dtype), to_dt(out_dtype), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ssm_status ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int silu,
+                          const void* conv_state_in, void* out, void* conv_state_out, int64_t batch,
+                          int64_t seqlen, int64_t d_inner, int64_t d_conv, ssm_dtype in_dtype,
+                          ssm_dtype out_dtype, void* stream) {
+  ssm_status st = conv_check(batch, seqlen, d_inner, d_conv, in_dtype, out_dtype);
+  if (st != SSM_OK) return st;
+  const int64_t elems = batch * seqlen * d_inner, cache = batch * d_inner * d_conv;
+  if ((elems > 0 && (!x || !out)) || (d_inner > 0 && !weight))
+    return fail(SSM_ERR_NULL_ARG, "required pointer %s is NULL", (elems > 0 && !x) ? "x" : !weight ? "weight" : "out");
+  const void* ptrs[] = {x, weight, bias, conv_state_in, out, conv_state_out};
+  const char* names[] = {"x", "weight", "bias", "conv_state_in", "out", "conv_state_out"};
+  for (int i = 0; i < 6; ++i)
+    if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
+  const int64_t si = esize(in_dtype), so = esize(out_dtype);
+  const Range ins[] = {range("x", x, elems * si), range("weight", weight, d_inner * d_conv * 4),
+                       range("bias", bias, d_inner * 4), range("conv_state_in", conv_state_in, cache * si)};
+  const Range ro = range("out", out, elems * so);
+  const Range rs = range("conv_state_out", conv_state_out, cache * si);
+  const bool in_place = conv_state_out != nullptr && conv_state_out == conv_state_in;
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(ro, ins[i])) return fail(SSM_ERR_UNSUPPORTED, "out overlaps input %s", ins[i].name);
+    // the outgoing cache may replace the incoming one in place (i == 3)
+    if (overlaps(rs, ins[i]) && !(in_place && i == 3))
+      return fail(SSM_ERR_UNSUPPORTED, "conv_state_out overlaps input %s", ins[i].name);
+  }
+  if (overlaps(ro, rs)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps conv_state_out");
+  if (batch == 0 || d_inner == 0) return ok();
+  ssm::ConvArgs a{};
+  a.x = x;
+  a.w = weight;
+  a.bias = bias;
+  a.state_in = conv_state_in;
+  a.out = out;
+  a.state_out = conv_state_out;
+  a.seqlen = seqlen;
+  a.d_inner = d_inner;
+  a.batch = (int32_t)batch;
+  a.silu = silu ? 1 : 0;
+  hipError_t e = ssm::launch_conv1d(a, to_dt(in_dtype), to_dt(out_dtype), (int)d_conv, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ssm_status ssm_conv1d_update(void* conv_state, const void* x, const float* weight, const float* bias, int silu,
+                             void* out, int64_t batch, int64_t d_inner, int64_t d_conv, ssm_dtype in_dtype,
+                             ssm_dtype out_dtype, void* stream) {
+  ssm_status st = conv_check(batch, 1, d_inner, d_conv, in_dtype, out_dtype);
+  if (st != SSM_OK) return st;
+  const int64_t elems = batch * d_inner, cache = batch * d_inner * d_conv;
+  if (elems > 0 && (!conv_state || !x || !out || !weight))
+    return fail(SSM_ERR_NULL_ARG, "required pointer %s is NULL",
+                !conv_state ? "conv_state" : !x ? "x" : !weight ? "weight" : "out");
+  const void* ptrs[] = {conv_state, x, weight, bias, out};
+  const char* names[] = {"conv_state", "x", "weight", "bias", "out"};
+  for (int i = 0; i < 5; ++i)
+    if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
+  const int64_t si = esize(in_dtype), so = esize(out_dtype);
+  const Range ins[] = {range("x", x, elems * si), range("weight", weight, d_inner * d_conv * 4),
+                       range("bias", bias, d_inner * 4)};
+  const Range ro = range("out", out, elems * so);
+  const Range rs = range("conv_state", conv_state, cache * si);
+  for (const Range& r : ins) {
+    if (overlaps(ro, r)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps input %s", r.name);
+    if (overlaps(rs, r)) return fail(SSM_ERR_UNSUPPORTED, "conv_state overlaps input %s", r.name);
+  }
+  if (overlaps(ro, rs)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps conv_state");
+  if (elems == 0) return ok();
+  ssm::ConvArgs a{};
+  a.x = x;
+  a.w = weight;
+  a.bias = bias;
+  a.state_in = conv_state;
+  a.out = out;
+  a.state_out = conv_state;
+  a.seqlen = 1;
+  a.d_inner = d_inner;
+  a.batch = (int32_t)batch;
+  a.silu = silu ? 1 : 0;
+  hipError_t e =
+      ssm::launch_conv1d_update(a, to_dt(in_dtype), to_dt(out_dtype), (int)d_conv, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

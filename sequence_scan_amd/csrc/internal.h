@@ -23,6 +23,7 @@ struct ScanArgs {
   const float* bias;      // nullable
   void* out;
   float* last_state;      // nullable
+  const float* h0;        // nullable: initial state [batch, d_inner, 16]
   float* ws_state;        // [batch, n_chunks, d_inner, 16]; chunked runs only
   float* ws_dtsum;        // [batch, n_chunks, d_inner];    chunked runs only
   int64_t seqlen;
@@ -49,10 +50,29 @@ struct DecodeArgs {
   int32_t softplus;
 };
 
+// Causal depthwise conv1d (+ bias, + SiLU) over [batch, seqlen, d_inner].
+struct ConvArgs {
+  const void* x;
+  const float* w;         // [d_inner, K]
+  const float* bias;      // nullable
+  const void* state_in;   // nullable: [batch, d_inner, K] in the input dtype
+  void* out;
+  void* state_out;        // nullable: [batch, d_inner, K] in the input dtype
+  int64_t seqlen;
+  int64_t d_inner;
+  int32_t batch;
+  int32_t silu;
+};
+
 // Launchers; each returns the hipGetLastError() of its launches.
 hipError_t launch_scan(const ScanArgs& a, DT in, DT out, int states_per_wave, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, DT in, DT out, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+// K is the filter width (2, 3 or 4).  The forward launch writes out, then
+// (stream-ordered) the new cache; the update reads and rewrites the cache.
+hipError_t launch_conv1d(const ConvArgs& a, DT in, DT out, int K, hipStream_t s);
+hipError_t launch_conv1d_update(const ConvArgs& a, DT in, DT out, int K, hipStream_t s);
 hipError_t launch_affine_exclusive_scan(const float* a, const float* b, float* oa, float* ob,
                                         int64_t n, hipStream_t s);
 

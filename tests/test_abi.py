@@ -20,14 +20,15 @@ def header_functions():
 def test_every_declared_function_is_exported():
     lib = ssm.library()
     names = header_functions()
-    assert {"ssm_scan_fwd", "ssm_state_update", "ssm_scan_plan", "ssm_scan_fwd_plan",
-            "ssm_affine_exclusive_scan", "ssm_status_string", "ssm_last_error", "ssm_abi_version"} <= set(names)
+    assert {"ssm_scan_fwd", "ssm_state_update", "ssm_scan_plan", "ssm_scan_fwd_plan", "ssm_scan_fwd_from",
+            "ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_affine_exclusive_scan", "ssm_status_string",
+            "ssm_last_error", "ssm_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssmscan.h but not exported"
 
 
 def test_version_and_strings():
-    assert ssm.ssm_abi_version() == 1
+    assert ssm.ssm_abi_version() == 2
     for code, name in ssm.STATUS_NAMES.items():
         assert ssm.ssm_status_string(code).startswith(name)
     assert "unknown" in ssm.ssm_status_string(99)
@@ -160,3 +161,54 @@ def test_product_code_never_touches_the_oracle():
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
     hdr = open(ssm.HEADER_PATH).read().lower()
     assert "oracle" not in hdr
+
+
+def test_scan_from_state_rejections():
+    lib = ssm.library()
+
+    def run(h0, last, out=P + 0x5000000):
+        return lib.ssm_scan_fwd_from(P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, None, None, None,
+                                     1, h0, out, last, 2, 8, 64, 16, F32, F32, None, None)
+    assert run(P + 0x6000000 + 4, None) == ssm.SSM_ERR_UNSUPPORTED           # misaligned initial state
+    assert "aligned" in ssm.ssm_last_error()
+    assert run(P + 0x6000000, P + 0x6000000 + 16) == ssm.SSM_ERR_UNSUPPORTED  # partial overlap
+    assert "initial_state" in ssm.ssm_last_error()
+    assert run(P + 0x5000000, None) == ssm.SSM_ERR_UNSUPPORTED                # out over the initial state
+    bad = ssm.ssm_plan()
+    bad.states_per_wave, bad.chunk_len = 3, 8
+    assert lib.ssm_scan_fwd_from(P, P, P, P, P, None, None, None, 1, None, P + 0x5000000, None, 1, 8, 64, 16,
+                                 F32, F32, None, ctypes.byref(bad)) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_conv1d_rejections():
+    lib = ssm.library()
+
+    def fwd(**kw):
+        a = dict(x=P, w=P + 0x1000000, bias=None, silu=1, sin=None, out=P + 0x2000000, sout=None, batch=2, seqlen=8,
+                 d_inner=64, d_conv=4, ind=BF16, outd=BF16)
+        a.update(kw)
+        return lib.ssm_conv1d_fwd(a["x"], a["w"], a["bias"], a["silu"], a["sin"], a["out"], a["sout"], a["batch"],
+                                  a["seqlen"], a["d_inner"], a["d_conv"], a["ind"], a["outd"], None)
+    assert fwd(x=None) == ssm.SSM_ERR_NULL_ARG
+    assert fwd(w=None) == ssm.SSM_ERR_NULL_ARG
+    assert fwd(out=None) == ssm.SSM_ERR_NULL_ARG
+    assert fwd(seqlen=-1) == ssm.SSM_ERR_BAD_SHAPE
+    for k in (0, 1, 5, 8):
+        assert fwd(d_conv=k) == ssm.SSM_ERR_UNSUPPORTED, k
+    assert fwd(ind=5) == ssm.SSM_ERR_UNSUPPORTED
+    assert fwd(out=P + 8) == ssm.SSM_ERR_UNSUPPORTED                        # misaligned and on x
+    assert fwd(out=P + 0x40) == ssm.SSM_ERR_UNSUPPORTED                      # out overlaps x
+    assert "overlaps" in ssm.ssm_last_error()
+    assert fwd(sin=P + 0x3000000, sout=P + 0x3000000 + 16) == ssm.SSM_ERR_UNSUPPORTED  # partial cache overlap
+    assert fwd(sout=P + 0x2000000) == ssm.SSM_ERR_UNSUPPORTED               # cache over out
+
+    def upd(**kw):
+        a = dict(st=P, x=P + 0x1000000, w=P + 0x2000000, bias=None, silu=1, out=P + 0x3000000, batch=4, d_inner=64,
+                 d_conv=4, ind=BF16, outd=F32)
+        a.update(kw)
+        return lib.ssm_conv1d_update(a["st"], a["x"], a["w"], a["bias"], a["silu"], a["out"], a["batch"],
+                                     a["d_inner"], a["d_conv"], a["ind"], a["outd"], None)
+    assert upd(st=None) == ssm.SSM_ERR_NULL_ARG
+    assert upd(d_conv=6) == ssm.SSM_ERR_UNSUPPORTED
+    assert upd(out=P + 16) == ssm.SSM_ERR_UNSUPPORTED                       # out inside the cache
+    assert upd(st=P + 0x1000000) == ssm.SSM_ERR_UNSUPPORTED                 # cache on x

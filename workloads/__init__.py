@@ -44,7 +44,7 @@ __all__ = [
 ]
 
 # Tensor ids used as the first spawn key (stable; never renumber).
-_T_BIAS, _T_X, _T_DT, _T_Z, _T_B, _T_C, _T_W, _T_TOK, _T_BETA, _T_A, _T_D = range(11)
+_T_BIAS, _T_X, _T_DT, _T_Z, _T_B, _T_C, _T_W, _T_TOK, _T_BETA, _T_A, _T_D, _T_CW, _T_CB, _T_CS, _T_H0 = range(15)
 _BLOCK_ELEMS = 1 << 20
 
 
@@ -246,6 +246,33 @@ def decode_inputs(cfg: DecodeConfig, seed: int = 0, steps: int | None = None,
     }
 
 
+def conv_inputs(batch: int, seqlen: int, d_inner: int, d_conv: int = 4, dtype: str = "bf16", seed: int = 0,
+                with_state: bool = False):
+    """Inputs of the block's causal depthwise convolution.
+
+    x ~ N(0, 1) [batch, seqlen, d_inner] and, with ``with_state``, a cache of earlier
+    inputs ~ N(0, 1) [batch, d_inner, d_conv], both rounded to ``dtype``; weight
+    [d_inner, d_conv] and bias [d_inner] ~ U(-1/sqrt(d_conv), 1/sqrt(d_conv)) in fp32,
+    the default initialisation range of a depthwise Conv1d (fan-in d_conv).
+    """
+    bound = 1.0 / np.sqrt(d_conv)
+    uni = lambda g, n: g.uniform(-bound, bound, n)
+    out = {
+        "x": _to_dtype(_normal((batch, seqlen, d_inner), seed, _T_X), dtype),
+        "weight": _fill((d_inner, d_conv), seed, _T_CW, uni),
+        "bias": _fill((d_inner,), seed, _T_CB, uni),
+        "dtype": dtype,
+    }
+    if with_state:
+        out["conv_state"] = _to_dtype(_normal((batch, d_inner, d_conv), seed, _T_CS), dtype)
+    return out
+
+
+def initial_state(batch: int, d_inner: int, d_state: int = 16, seed: int = 0) -> np.ndarray:
+    """A stored scan state [batch, d_inner, d_state] ~ N(0, 1), fp32."""
+    return _normal((batch, d_inner, d_state), seed, _T_H0)
+
+
 def _esize(dtype: str) -> int:
     return {"f32": 4, "bf16": 2}[dtype]
 
@@ -264,3 +291,9 @@ def decode_algorithmic_bytes(batch, d_inner, d_state, in_dtype, out_dtype, with_
     e = batch * d_inner
     nread = 3 if with_z else 2
     return e * (2 * 4 * d_state + nread * si + so) + 2 * batch * d_state * si
+
+
+def conv_algorithmic_bytes(batch, seqlen, d_inner, d_conv, in_dtype, out_dtype) -> int:
+    """Bytes a convolution prefill must move: x read once, out written once (the
+    filter, bias and caches, a few KiB per channel group, are excluded)."""
+    return batch * seqlen * d_inner * (_esize(in_dtype) + _esize(out_dtype))
