@@ -229,10 +229,11 @@ def conv_case(batch, seqlen, d_inner, reps=20):
     st_out = torch.empty_like(st)
     out = torch.empty_like(x)
     run = lambda: ssm.ssm_conv1d_fwd(x, w, b, conv_state_in=st, out=out, conv_state_out=st_out)
-    avg, med, mn = per_launch_ms(run, reps)
+    avg, _ = time_steps(run, reps, 3)  # back-to-back calls, events around the loop
     nbytes = workloads.conv_algorithmic_bytes(batch, seqlen, d_inner, 4, "bf16", "bf16")
     res = {"workload": f"conv1d prefill batch {batch}, seqlen {seqlen}, d_inner {d_inner}, d_conv 4, bf16 in/out, SiLU",
-           "us_per_call": round(avg * 1e3, 2), "bytes_per_call": nbytes,
+           "us_per_call": round(avg * 1e3, 2), "timing": "back-to-back calls (prefill kernel + cache kernel)",
+           "bytes_per_call": nbytes,
            "GBps": round(nbytes / (avg / 1e3) / 1e9, 1), "hbm_frac": round(nbytes / (avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     del x, out, inp
     dcfg = workloads.DECODE_CONFIG
@@ -243,7 +244,7 @@ def conv_case(batch, seqlen, d_inner, reps=20):
     cache = torch.from_numpy(dinp["conv_state"]).to(torch.bfloat16).cuda()
     dout = torch.empty_like(xs)
     step = lambda: ssm.ssm_conv1d_update(cache, xs, ws, bs, out=dout)
-    davg, _, _ = per_launch_ms(step, 50)
+    davg, _ = time_steps(step, 200, 10)  # 200 consecutive steps, events around the loop
     e = dcfg.batch * dcfg.d_inner
     dbytes = e * (2 * 4 * 2 + 2 + 2)  # cache read + written (4 bf16), x read, out written
     res["decode_step"] = {"workload": f"conv1d decode step batch {dcfg.batch}, d_inner {dcfg.d_inner}, bf16",
