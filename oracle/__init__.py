@@ -51,6 +51,8 @@ class OracleLib:
         lib.oracle_scan_fwd_from.restype = ctypes.c_int
         lib.oracle_scan_fwd_from.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp,
                                              _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+        lib.oracle_scan_bwd.restype = ctypes.c_int
+        lib.oracle_scan_bwd.argtypes = [_dp] * 8 + [ctypes.c_int] + [_dp] * 12 + [_i64] * 4
         lib.oracle_conv1d_fwd.restype = ctypes.c_int
         lib.oracle_conv1d_fwd.argtypes = [_dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, _i64, _i64, _i64, _i64]
         lib.oracle_conv1d_update.restype = ctypes.c_int
@@ -125,6 +127,35 @@ class OracleLib:
         b = np.empty(n)
         self.lib.oracle_affine_compose(_ptr(a2), _ptr(b2), _ptr(a1), _ptr(b1), _ptr(a), _ptr(b), n)
         return a, b
+
+    def scan_bwd(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None,
+                 dout=None, dlast=None):
+        """Gradients of the scan for the output gradient dout [batch, L, d_inner] (and
+        optionally dlast [batch, d_inner, d_state], the gradient of the final state).
+        Returns a dict of float64 arrays: dx, ddelta, dA, dB, dC, and dD, dz,
+        ddelta_bias, dh0 for the optional inputs that were given."""
+        x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
+        D, z, delta_bias, h0, dout, dlast = map(_f64, (D, z, delta_bias, h0, dout, dlast))
+        batch, L, Dn = x.shape
+        N = A.shape[1]
+        if dout is None or dout.shape != x.shape:
+            raise ValueError("dout must match x")
+        g = {k: np.empty(x.shape) for k in ("dx", "ddelta")}
+        g["dA"] = np.empty((Dn, N))
+        g["dB"] = np.empty((batch, L, N))
+        g["dC"] = np.empty((batch, L, N))
+        g["dD"] = np.empty(Dn) if D is not None else None
+        g["dz"] = np.empty(x.shape) if z is not None else None
+        g["ddelta_bias"] = np.empty(Dn) if delta_bias is not None else None
+        g["dh0"] = np.empty((batch, Dn, N)) if h0 is not None else None
+        rc = self.lib.oracle_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(dout), _ptr(dlast),
+                                      _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                                      _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]),
+                                      batch, L, Dn, N)
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd rejected its arguments")
+        return {k: v for k, v in g.items() if v is not None}
 
     def conv1d_fwd(self, x, weight, bias=None, silu=True, conv_state=None, return_state=True):
         """Causal depthwise conv1d (+ bias, + SiLU).  x: [batch, L, d_inner]; weight:
@@ -208,3 +239,7 @@ def conv1d_fwd(*args, **kw):
 
 def conv1d_update(*args, **kw):
     return load().conv1d_update(*args, **kw)
+
+
+def scan_bwd(*args, **kw):
+    return load().scan_bwd(*args, **kw)

@@ -320,3 +320,94 @@ int oracle_conv1d_update(double* state, const double* x, const double* w, const 
     }
   return 0;
 }
+
+/* ---------------------------------------------------------------- backward
+ *
+ * Gradients of the scan by reverse-mode differentiation of the recurrence
+ * above (the pages give the forward recurrence only; the gradients follow
+ * from it by the chain rule).  With u = delta + bias, dt = softplus(u) (or u),
+ * a_t = exp(dt_t A), h_t = a_t h_{t-1} + dt_t B_t x_t, y_t = C_t . h_t + D x_t,
+ * out_t = y_t SiLU(z_t), and g_t = dL/dout_t:
+ *   dy_t  = g_t SiLU(z_t);          dz_t = g_t y_t SiLU'(z_t)
+ *   dh_t  = dy_t C_t + a_{t+1} dh_{t+1}   (dh after the last step: dlast)
+ *   dx_t  = dy_t D + dt_t (B_t . dh_t)
+ *   ddt_t = sum_n dh_t[n] (A_n a_t[n] h_{t-1}[n] + B_t[n] x_t)
+ *   ddelta_t = ddt_t softplus'(u_t) (= sigmoid(u_t)), or ddt_t
+ *   dB_t[n] += dh_t[n] dt_t x_t,  dC_t[n] += dy_t h_t[n]   (summed over d)
+ *   dA[d,n] += dh_t[n] a_t[n] h_{t-1}[n] dt_t;  dD[d] += dy_t x_t;
+ *   dbias[d] += ddelta_t;  dh0 = a_0 dh_0        (summed over b and t)
+ * Every output is overwritten.  The reduced gradients (dB, dC over channels;
+ * dA, dD, dbias over batch rows) are summed row by row in a fixed order on
+ * one thread, so the result does not depend on the thread count.
+ */
+static double sigmoid(double u) { return 1.0 / (1.0 + exp(-u)); }
+
+int oracle_scan_bwd(const double* x, const double* delta, const double* A, const double* B,
+                    const double* C, const double* D, const double* z, const double* bias,
+                    int softplus_on, const double* h0, const double* dout, const double* dlast,
+                    double* dx, double* ddelta, double* dA, double* dB, double* dC, double* dD,
+                    double* dz, double* dbias, double* dh0, int64_t batch, int64_t L, int64_t Dn,
+                    int64_t N) {
+  if (!x || !delta || !A || !B || !C || !dout || !dx || !ddelta || !dA || !dB || !dC) return -1;
+  if (batch < 0 || L < 0 || Dn < 0 || N <= 0) return -1;
+  memset(dA, 0, sizeof(double) * (size_t)(Dn * N));
+  memset(dB, 0, sizeof(double) * (size_t)(batch * L * N));
+  memset(dC, 0, sizeof(double) * (size_t)(batch * L * N));
+  if (dD) memset(dD, 0, sizeof(double) * (size_t)Dn);
+  if (dbias) memset(dbias, 0, sizeof(double) * (size_t)Dn);
+  double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N)); /* h_{t-1} for t = 0..L */
+  double* dh = (double*)malloc(sizeof(double) * (size_t)N);
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t d = 0; d < Dn; ++d) {
+      const double* A_d = A + d * N;
+      /* forward: hs[t] = state before step t, hs[L] = final state */
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        int64_t e = (b * L + t) * Dn + d;
+        const double* Bt = B + (b * L + t) * N;
+        double dt = step_size(delta[e], bias, d, softplus_on);
+        for (int64_t n = 0; n < N; ++n)
+          hs[(t + 1) * N + n] = exp(dt * A_d[n]) * hs[t * N + n] + (dt * Bt[n]) * x[e];
+      }
+      /* reverse */
+      for (int64_t n = 0; n < N; ++n) dh[n] = dlast ? dlast[(b * Dn + d) * N + n] : 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        int64_t e = (b * L + t) * Dn + d;
+        const double* Bt = B + (b * L + t) * N;
+        const double* Ct = C + (b * L + t) * N;
+        double u = delta[e] + (bias ? bias[d] : 0.0);
+        double dt = softplus_on ? softplus(u) : u;
+        double dy = dout[e];
+        if (z) {
+          double y = 0.0;
+          for (int64_t n = 0; n < N; ++n) y += Ct[n] * hs[(t + 1) * N + n];
+          if (D) y += D[d] * x[e];
+          double zz = z[e], s = sigmoid(zz);
+          dz[e] = dout[e] * y * (s * (1.0 + zz * (1.0 - s)));
+          dy = dout[e] * silu(zz);
+        }
+        double sB = 0.0, ddt = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          double a = exp(dt * A_d[n]);
+          dh[n] += dy * Ct[n];                                  /* dh_t */
+          double hprev = hs[t * N + n];
+          dC[(b * L + t) * N + n] += dy * hs[(t + 1) * N + n];
+          dB[(b * L + t) * N + n] += dh[n] * dt * x[e];
+          sB += dh[n] * Bt[n];
+          ddt += dh[n] * (A_d[n] * a * hprev + Bt[n] * x[e]);
+          dA[d * N + n] += dh[n] * a * hprev * dt;
+          dh[n] *= a;                                           /* a_t dh_t, carried to step t-1 */
+        }
+        dx[e] = (D ? dy * D[d] : 0.0) + dt * sB;
+        double dd = softplus_on ? ddt * sigmoid(u) : ddt;
+        ddelta[e] = dd;
+        if (dD) dD[d] += dy * x[e];
+        if (dbias) dbias[d] += dd;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < N; ++n) dh0[(b * Dn + d) * N + n] = dh[n];
+    }
+  free(hs);
+  free(dh);
+  return 0;
+}

@@ -27,6 +27,8 @@ Sources of the statements:
     with SiLU; vladkulikov.com sections 6 and 14: the decode cache keeps the
     last d_conv inputs of that branch and the SSM state, so a sequence can be
     continued from both.
+  * The pages give no gradients; the backward is pinned to the forward by
+    central finite differences.
 """
 from __future__ import annotations
 
@@ -449,9 +451,61 @@ def pin_conv1d_decode_and_continuation(orc):
     assert np.array_equal(s_short, ref), "short-sequence cache is not zero-padded"
 
 
+def _fd_grads(orc, case, h0, g, glast, softplus, keys, eps=1e-6):
+    """Central finite differences of L = sum(g * out) + sum(glast * last_state),
+    computed with the forward scan only."""
+    def loss(c, hh):
+        out, last = orc.scan_fwd(**c, h0=hh, softplus=softplus)
+        return float(np.sum(out * g) + np.sum(last * glast))
+    res = {}
+    for k in keys:
+        base = h0 if k == "h0" else case[k]
+        num = np.zeros_like(base)
+        for i in np.ndindex(base.shape):
+            vals = []
+            for sgn in (1.0, -1.0):
+                c = {kk: v.copy() for kk, v in case.items()}
+                hh = None if h0 is None else h0.copy()
+                tgt = hh if k == "h0" else c[k]
+                tgt[i] += sgn * eps
+                vals.append(loss(c, hh))
+            num[i] = (vals[0] - vals[1]) / (2 * eps)
+        res[k] = num
+    return res
+
+
+def pin_backward_finite_differences(orc):
+    """Every gradient of the backward equals the central finite difference of the
+    (pinned) forward scan: L = sum(dout * out) + sum(dlast * last_state), for x,
+    delta, z, B, C, A, D, delta_bias and the initial state; softplus on and off,
+    with and without the optional inputs."""
+    rng = np.random.default_rng(59)
+    batch, L, Dn, N = 2, 6, 3, 3
+    names = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD",
+             "delta_bias": "ddelta_bias", "h0": "dh0"}
+    for softplus, optional in ((True, True), (False, True), (True, False)):
+        c = _rand_case(rng, batch, L, Dn, N)
+        if not softplus:
+            c["delta"] = rng.uniform(0.01, 0.5, c["delta"].shape)
+            c["delta_bias"] = rng.uniform(0.0, 0.1, Dn)
+        if not optional:
+            for k in ("z", "D", "delta_bias"):
+                c.pop(k)
+        h0 = rng.standard_normal((batch, Dn, N)) if optional else None
+        g = rng.standard_normal((batch, L, Dn))
+        glast = rng.standard_normal((batch, Dn, N))
+        got = orc.scan_bwd(**c, softplus=softplus, h0=h0, dout=g, dlast=glast)
+        keys = list(c) + (["h0"] if h0 is not None else [])
+        num = _fd_grads(orc, c, h0, g, glast, softplus, keys)
+        for k in keys:
+            _close(got[names[k]], num[k], 1e-7, f"d{k} vs finite differences (softplus {softplus})")
+        assert set(got) == {names[k] for k in keys}, "gradients of absent inputs must be absent"
+
+
 ALL_PINS = [
     pin_affine_worked_example, pin_step_size, pin_lti_convolution, pin_semiseparable, pin_delta_zero,
     pin_impulse_closed_form, pin_chunked_composition, pin_decode_equals_scan, pin_invariants,
     pin_decay, pin_nan_propagation, pin_optional_inputs, pin_initial_state_free_response,
     pin_initial_state_continuation, pin_conv1d_numpy, pin_conv1d_impulse, pin_conv1d_decode_and_continuation,
+    pin_backward_finite_differences,
 ]

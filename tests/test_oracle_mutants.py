@@ -53,6 +53,17 @@ MUTANTS = {
     "conv_update_no_shift": ("for (int64_t k = 0; k + 1 < K; ++k) st[k] = st[k + 1];", ""),
     "conv_bias_dropped": ("double acc = bias ? bias[d] : 0.0;\n        for (int64_t k = 0; k < K; ++k)\n          acc +=",
                           "double acc = 0.0;\n        for (int64_t k = 0; k < K; ++k)\n          acc +="),
+    "bwd_carry_before_input": ("dh[n] += dy * Ct[n];                                  /* dh_t */",
+                               "dh[n] = dh[n] * exp(dt * A_d[n]) + dy * Ct[n];"),
+    "bwd_dB_drops_dt": ("dB[(b * L + t) * N + n] += dh[n] * dt * x[e];", "dB[(b * L + t) * N + n] += dh[n] * x[e];"),
+    "bwd_dC_uses_hprev": ("dC[(b * L + t) * N + n] += dy * hs[(t + 1) * N + n];",
+                          "dC[(b * L + t) * N + n] += dy * hs[t * N + n];"),
+    "bwd_ddt_drops_input": ("ddt += dh[n] * (A_d[n] * a * hprev + Bt[n] * x[e]);", "ddt += dh[n] * (A_d[n] * a * hprev);"),
+    "bwd_dA_drops_dt": ("dA[d * N + n] += dh[n] * a * hprev * dt;", "dA[d * N + n] += dh[n] * a * hprev;"),
+    "bwd_dx_drops_skip": ("dx[e] = (D ? dy * D[d] : 0.0) + dt * sB;", "dx[e] = dt * sB;"),
+    "bwd_softplus_derivative": ("double dd = softplus_on ? ddt * sigmoid(u) : ddt;", "double dd = ddt;"),
+    "bwd_silu_derivative": ("dz[e] = dout[e] * y * (s * (1.0 + zz * (1.0 - s)));", "dz[e] = dout[e] * y * s;"),
+    "bwd_dlast_ignored": ("dh[n] = dlast ? dlast[(b * Dn + d) * N + n] : 0.0;", "dh[n] = 0.0;"),
     "conv_state_out_oldest_last": ("state_out[(b * Dn + d) * K + k] = conv_input(x, state_in, b, L - K + k, d, L, Dn, K);",
                                    "state_out[(b * Dn + d) * K + k] = conv_input(x, state_in, b, L - 1 - k, d, L, Dn, K);"),
 }
