@@ -77,6 +77,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--plan", default=None, help="states_per_wave,chunk_len (tuning only)")
     return ap.parse_args()
@@ -253,6 +254,34 @@ def conv_case(batch, seqlen, d_inner, reps=20):
     return res
 
 
+def backward_case(cfg, steps=5):
+    """ssm_scan_bwd on the layer's shape (bf16 inputs and gradients, all optional
+    inputs), timed as back-to-back calls."""
+    import torch
+
+    import sequence_scan_amd as ssm
+    import workloads
+
+    inp = workloads.scan_inputs(cfg, seed=0)
+    t = {k: (torch.from_numpy(v).to(torch.bfloat16) if k in ("x", "delta", "z", "B", "C") else torch.from_numpy(v)).cuda()
+         for k, v in inp.items() if k != "dtype"}
+    del inp
+    dout = torch.randn(t["x"].shape, device="cuda").to(torch.bfloat16)
+    run = lambda: ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                                   softplus=True, dout=dout)
+    ms, _ = time_steps(run, steps, 2)
+    # VALU cycles per wavefront state update: the checkpoint forward (3 VALU +
+    # exp = 20), the tile's forward again with the readout (4 + exp = 24), the
+    # reverse step (11 VALU + exp = 52) and the lane reductions of dB, dC (~12)
+    cyc = 20 + 24 + 52 + 12
+    updates = cfg.batch * cfg.seqlen * cfg.d_inner * cfg.d_state
+    floor_us = updates / 64 * cyc / (SIMDS * CLOCK_HZ) * 1e6
+    return {"workload": f"ssm_scan_bwd {cfg.name}: batch {cfg.batch}, seqlen {cfg.seqlen}, d_inner {cfg.d_inner}, "
+                        "bf16 inputs and gradients, softplus, D, z",
+            "us_per_call": round(ms * 1e3, 1), "alu_floor_us": round(floor_us, 1),
+            "alu_frac": round(floor_us / (ms * 1e3), 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -348,6 +377,8 @@ def main():
         line["decode"] = decode_case(args.decode_steps)
     if not args.no_conv and args.workload == "mamba2p8b":
         line["conv1d"] = conv_case(cfg.batch, cfg.seqlen, cfg.d_inner)
+    if not args.no_backward and args.workload == "mamba2p8b":
+        line["backward"] = backward_case(cfg)
     print(json.dumps(line), flush=True)
 
 

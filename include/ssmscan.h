@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
@@ -149,6 +149,39 @@ ssm_status ssm_scan_fwd_from(const void* x, const void* delta, const float* A, c
                              void* out, float* last_state, int64_t batch, int64_t seqlen,
                              int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
                              ssm_dtype out_dtype, void* stream, const ssm_plan* plan);
+
+/*
+ * Backward of the scan: the gradients of a loss L with respect to every input
+ * of ssm_scan_fwd_from, given dout = dL/dout (and optionally dlast_state =
+ * dL/dlast_state).  The pages give the forward recurrence only; the gradients
+ * are its chain rule in reverse time:
+ *   dh_t = C_t dy_t + exp(dt_{t+1} A) dh_{t+1}  (dh after the last step = dlast_state),
+ *   with dy_t = dout_t SiLU(z_t) (or dout_t), and from it dx, ddelta, dz, dA,
+ *   dB, dC, dD, ddelta_bias and dinitial_state.
+ * The forward inputs (x .. softplus, initial_state) are those of the forward
+ * call; the forward outputs are not needed (the states are recomputed).
+ *   dout          : [batch, seqlen, d_inner] in grad_dtype
+ *   dlast_state   : [batch, d_inner, d_state] fp32, or NULL (zero)
+ *   dx, ddelta, dz: [batch, seqlen, d_inner] in grad_dtype (dz iff z != NULL)
+ *   dB, dC        : [batch, seqlen, d_state] in grad_dtype
+ *   dA            : [d_inner, d_state] fp32;  dD, ddelta_bias: [d_inner] fp32,
+ *                   required exactly when D, delta_bias are given
+ *   dinitial_state: [batch, d_inner, d_state] fp32 or NULL (not computed)
+ * Every gradient is overwritten (not accumulated).  Reductions (dB, dC over
+ * channels; dA, dD, ddelta_bias over rows) run in a fixed order: results are
+ * bitwise reproducible.  A workspace of about batch * seqlen * d_inner * 4 +
+ * batch * seqlen * ceil(d_inner / 64) * 128 bytes is taken with hipMallocAsync
+ * on `stream` and released with hipFreeAsync.  Outputs must not overlap any
+ * input or each other.  Sizes, dtypes, alignment and errors as for
+ * ssm_scan_fwd (grad_dtype in place of out_dtype).
+ */
+ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* delta_bias,
+                        int softplus, const float* initial_state, const void* dout,
+                        const float* dlast_state, void* dx, void* ddelta, float* dA, void* dB,
+                        void* dC, float* dD, void* dz, float* ddelta_bias, float* dinitial_state,
+                        int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                        ssm_dtype in_dtype, ssm_dtype grad_dtype, void* stream);
 
 /*
  * The block's short causal depthwise convolution that feeds the scan (page

@@ -8,7 +8,7 @@ loaded, every call raises.
 
 Functions carry the C names: ``ssm_scan_fwd``, ``ssm_state_update``,
 ``ssm_scan_fwd_plan``, ``ssm_scan_fwd_from``, ``ssm_scan_plan``,
-``ssm_conv1d_fwd``, ``ssm_conv1d_update``, ``ssm_affine_exclusive_scan``,
+``ssm_scan_bwd``, ``ssm_conv1d_fwd``, ``ssm_conv1d_update``, ``ssm_affine_exclusive_scan``,
 ``ssm_status_string``, ``ssm_last_error``, ``ssm_abi_version``.
 """
 from __future__ import annotations
@@ -65,6 +65,8 @@ def _load():
                                       _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp,
                                       ctypes.POINTER(ssm_plan)]
     lib.ssm_scan_fwd_from.restype = ctypes.c_int
+    lib.ssm_scan_bwd.argtypes = [_vp] * 8 + [ctypes.c_int] + [_vp] * 12 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int, _vp]
+    lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_conv1d_fwd.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                    ctypes.c_int, ctypes.c_int, _vp]
     lib.ssm_conv1d_fwd.restype = ctypes.c_int
@@ -204,6 +206,42 @@ def ssm_scan_fwd_from(x, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
                                      _ptr(last_state), batch, seqlen, d_inner, d_state, _dtype_code(x),
                                      _dtype_code(out), _stream(stream), _plan_struct(plan)))
     return out
+
+
+def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, initial_state=None,
+                 dout=None, dlast_state=None, want_dinitial_state: bool = False, grad_dtype=None, stream=None):
+    """Gradients of the scan (see include/ssmscan.h).  Forward inputs as for
+    ``ssm_scan_fwd_from``; ``dout`` [batch, seqlen, d_inner] (its dtype is the gradient
+    dtype unless ``grad_dtype`` is given); ``dlast_state`` optional.  Returns a dict with
+    dx, ddelta, dA, dB, dC and, for the inputs given, dD, dz, ddelta_bias, and
+    dinitial_state when ``want_dinitial_state``."""
+    import torch
+    if x.dim() != 3 or dout is None:
+        raise ValueError("x must be [batch, seqlen, d_inner] and dout given")
+    batch, seqlen, d_inner = x.shape
+    d_state = A.shape[-1] if A.dim() == 2 else -1
+    gdt = grad_dtype or dout.dtype
+    if dout.dtype != gdt:
+        raise TypeError("dout must have the gradient dtype")
+    dev = x.device
+    g = {"dx": torch.empty(x.shape, dtype=gdt, device=dev), "ddelta": torch.empty(x.shape, dtype=gdt, device=dev),
+         "dA": torch.empty(A.shape, dtype=torch.float32, device=dev),
+         "dB": torch.empty(B.shape, dtype=gdt, device=dev), "dC": torch.empty(C.shape, dtype=gdt, device=dev)}
+    if D is not None:
+        g["dD"] = torch.empty(D.shape, dtype=torch.float32, device=dev)
+    if z is not None:
+        g["dz"] = torch.empty(x.shape, dtype=gdt, device=dev)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty(delta_bias.shape, dtype=torch.float32, device=dev)
+    if want_dinitial_state:
+        g["dinitial_state"] = torch.empty((batch, d_inner, d_state), dtype=torch.float32, device=dev)
+    _check(_load().ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(dout),
+                                _ptr(dlast_state), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                                _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                                _ptr(g.get("dinitial_state")), batch, seqlen, d_inner, d_state, _dtype_code(x),
+                                _dtype_code(g["dx"]), _stream(stream)))
+    return g
 
 
 def ssm_conv1d_fwd(x, weight, bias=None, silu: bool = True, conv_state_in=None, out=None,

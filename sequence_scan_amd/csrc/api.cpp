@@ -343,6 +343,115 @@ ssm_status ssm_state_update(float* state, const void* x, const void* delta, cons
   return ok();
 }
 
+ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                        const float* D, const void* z, const float* delta_bias, int softplus,
+                        const float* initial_state, const void* dout, const float* dlast_state, void* dx,
+                        void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                        float* dinitial_state, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                        ssm_dtype in_dtype, ssm_dtype grad_dtype, void* stream) {
+  Sizes sz;
+  ssm_status st = check_common(batch, seqlen, d_inner, d_state, in_dtype, grad_dtype, &sz);
+  if (st != SSM_OK) return st;
+  const bool need_e = sz.elems > 0, need_bc = sz.bc > 0, need_a = d_inner > 0;
+  struct Req { const char* name; const void* p; bool need; };
+  const Req req[] = {{"x", x, need_e}, {"delta", delta, need_e}, {"dout", dout, need_e}, {"dx", dx, need_e},
+                     {"ddelta", ddelta, need_e}, {"A", A, need_a}, {"dA", dA, need_a}, {"B", B, need_bc},
+                     {"C", C, need_bc}, {"dB", dB, need_bc}, {"dC", dC, need_bc},
+                     {"dD", dD, need_a && D != nullptr}, {"dz", dz, need_e && z != nullptr},
+                     {"ddelta_bias", ddelta_bias, need_a && delta_bias != nullptr}};
+  for (const Req& r : req)
+    if (r.need && r.p == nullptr) return fail(SSM_ERR_NULL_ARG, "required pointer %s is NULL", r.name);
+  if ((dD != nullptr && D == nullptr) || (dz != nullptr && z == nullptr) ||
+      (ddelta_bias != nullptr && delta_bias == nullptr))
+    return fail(SSM_ERR_UNSUPPORTED, "a gradient was requested for an input the forward did not have");
+  const void* ptrs[] = {x, delta, A, B, C, D, z, delta_bias, initial_state, dout, dlast_state, dx, ddelta, dA,
+                        dB, dC, dD, dz, ddelta_bias, dinitial_state};
+  const char* names[] = {"x", "delta", "A", "B", "C", "D", "z", "delta_bias", "initial_state", "dout",
+                         "dlast_state", "dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias",
+                         "dinitial_state"};
+  for (int i = 0; i < 20; ++i)
+    if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
+  const int64_t si = esize(in_dtype), sg = esize(grad_dtype);
+  const Range ins[] = {
+      range("x", x, sz.elems * si),          range("delta", delta, sz.elems * si),
+      range("z", z, sz.elems * si),          range("B", B, sz.bc * si),
+      range("C", C, sz.bc * si),             range("A", A, d_inner * d_state * 4),
+      range("D", D, d_inner * 4),            range("delta_bias", delta_bias, d_inner * 4),
+      range("initial_state", initial_state, sz.state * 4), range("dout", dout, sz.elems * sg),
+      range("dlast_state", dlast_state, sz.state * 4),
+  };
+  const Range outs[] = {
+      range("dx", dx, sz.elems * sg),        range("ddelta", ddelta, sz.elems * sg),
+      range("dz", dz, sz.elems * sg),        range("dB", dB, sz.bc * sg),
+      range("dC", dC, sz.bc * sg),           range("dA", dA, d_inner * d_state * 4),
+      range("dD", dD, d_inner * 4),          range("ddelta_bias", ddelta_bias, d_inner * 4),
+      range("dinitial_state", dinitial_state, sz.state * 4),
+  };
+  for (int i = 0; i < 9; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return fail(SSM_ERR_UNSUPPORTED, "%s overlaps input %s", outs[i].name, r.name);
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outs[j]))
+        return fail(SSM_ERR_UNSUPPORTED, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (d_inner == 0) return ok();
+  if (batch == 0 || seqlen == 0) {
+    // no steps: the parameter gradients are zero and the state's gradient
+    // passes through unchanged
+    e = ssm::launch_fill_zero(dA, d_inner * d_state, s);
+    if (e == hipSuccess && dD) e = ssm::launch_fill_zero(dD, d_inner, s);
+    if (e == hipSuccess && ddelta_bias) e = ssm::launch_fill_zero(ddelta_bias, d_inner, s);
+    if (e == hipSuccess && dinitial_state && sz.state > 0)
+      e = dlast_state ? ssm::launch_copy_f32(dinitial_state, dlast_state, sz.state, s)
+                      : ssm::launch_fill_zero(dinitial_state, sz.state, s);
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
+  const int64_t nblk = (d_inner + 63) / 64;
+  const int64_t ntiles = (seqlen + ssm::kBwdTile - 1) / ssm::kBwdTile;
+  int64_t n_ck, n_bc, n_a, n_dd, bytes;
+  if (!mul_ok(batch * nblk, ntiles * 64 * d_state, &n_ck) || !mul_ok(sz.bc / d_state, nblk * 2 * d_state, &n_bc) ||
+      !mul_ok(sz.state, 1, &n_a) || !mul_ok(batch * d_inner, 2, &n_dd) ||
+      !mul_ok(n_ck + n_bc + n_a + n_dd, 4, &bytes))
+    return fail(SSM_ERR_BAD_SHAPE, "workspace size overflows int64");
+  void* ws = nullptr;
+  e = hipMallocAsync(&ws, (size_t)bytes, s);
+  if (e != hipSuccess || ws == nullptr)
+    return fail(SSM_ERR_HIP, "hipMallocAsync(%lld bytes) failed: %s", (long long)bytes, hipGetErrorString(e));
+  ssm::BwdArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.z = z;
+  a.B = B;
+  a.C = C;
+  a.A = A;
+  a.D = D;
+  a.bias = delta_bias;
+  a.h0 = initial_state;
+  a.dout = dout;
+  a.dlast = dlast_state;
+  a.dx = dx;
+  a.ddelta = ddelta;
+  a.dz = dz;
+  a.ws_ckpt = static_cast<float*>(ws);
+  a.ws_bc = a.ws_ckpt + n_ck;
+  a.ws_a = a.ws_bc + n_bc;
+  a.ws_dd = a.ws_a + n_a;
+  a.dh0 = dinitial_state;
+  a.seqlen = seqlen;
+  a.d_inner = d_inner;
+  a.batch = (int32_t)batch;
+  a.softplus = softplus ? 1 : 0;
+  a.nblk = (int32_t)nblk;
+  e = ssm::launch_scan_bwd(a, to_dt(in_dtype), to_dt(grad_dtype), dA, dB, dC, dD, ddelta_bias, s);
+  hipError_t e2 = hipFreeAsync(ws, s);
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 ssm_status ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int silu,
                           const void* conv_state_in, void* out, void* conv_state_out, int64_t batch,
                           int64_t seqlen, int64_t d_inner, int64_t d_conv, ssm_dtype in_dtype,

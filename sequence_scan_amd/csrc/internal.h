@@ -64,6 +64,36 @@ struct ConvArgs {
   int32_t silu;
 };
 
+// Backward of the scan.  Elementwise gradients and dout share one dtype.
+struct BwdArgs {
+  const void* x;
+  const void* delta;
+  const void* z;          // nullable
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* D;         // nullable
+  const float* bias;      // nullable
+  const float* h0;        // nullable
+  const void* dout;
+  const float* dlast;     // nullable
+  void* dx;
+  void* ddelta;
+  void* dz;               // non-null iff z is
+  float* ws_ckpt;         // [batch, nblk, ntiles, 64, 16] states entering each tile
+  float* ws_bc;           // [batch, seqlen, nblk, 2, 16] per-block dB (before the ln 2), dC
+  float* ws_a;            // [batch, d_inner, 16] per-row dA
+  float* ws_dd;           // [batch, d_inner, 2] per-row dD, dbias
+  float* dh0;             // nullable: [batch, d_inner, 16]
+  int64_t seqlen;
+  int64_t d_inner;
+  int32_t batch;
+  int32_t softplus;
+  int32_t nblk;           // ceil(d_inner / 64)
+};
+
+constexpr int kBwdTile = 16;  // steps per backward tile (and per checkpoint)
+
 // Launchers; each returns the hipGetLastError() of its launches.
 hipError_t launch_scan(const ScanArgs& a, DT in, DT out, int states_per_wave, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, DT in, DT out, hipStream_t s);
@@ -73,6 +103,10 @@ hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t 
 // (stream-ordered) the new cache; the update reads and rewrites the cache.
 hipError_t launch_conv1d(const ConvArgs& a, DT in, DT out, int K, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvArgs& a, DT in, DT out, int K, hipStream_t s);
+// Backward: the per-block kernel, then the fixed-order reductions into dA, dB,
+// dC, dD and dbias (dD / dbias may be NULL when the forward had none).
+hipError_t launch_scan_bwd(const BwdArgs& a, DT in, DT grad, float* dA, void* dB, void* dC, float* dD,
+                           float* dbias, hipStream_t s);
 hipError_t launch_affine_exclusive_scan(const float* a, const float* b, float* oa, float* ob,
                                         int64_t n, hipStream_t s);
 

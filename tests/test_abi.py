@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_strings():
-    assert ssm.ssm_abi_version() == 2
+    assert ssm.ssm_abi_version() == 3
     for code, name in ssm.STATUS_NAMES.items():
         assert ssm.ssm_status_string(code).startswith(name)
     assert "unknown" in ssm.ssm_status_string(99)
@@ -212,3 +212,28 @@ def test_conv1d_rejections():
     assert upd(d_conv=6) == ssm.SSM_ERR_UNSUPPORTED
     assert upd(out=P + 16) == ssm.SSM_ERR_UNSUPPORTED                       # out inside the cache
     assert upd(st=P + 0x1000000) == ssm.SSM_ERR_UNSUPPORTED                 # cache on x
+
+
+def test_scan_bwd_rejections():
+    lib = ssm.library()
+    base = dict(x=P, delta=P + 0x1000000, A=P + 0x2000000, B=P + 0x3000000, C=P + 0x4000000, D=None, z=None, bias=None,
+                h0=None, dout=P + 0x5000000, dlast=None, dx=P + 0x6000000, ddelta=P + 0x7000000, dA=P + 0x8000000,
+                dB=P + 0x9000000, dC=P + 0xa000000, dD=None, dz=None, dbias=None, dh0=None, batch=2, seqlen=8,
+                d_inner=64, d_state=16, ind=F32, gd=F32)
+
+    def bwd(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.ssm_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], 1, a["h0"],
+                                a["dout"], a["dlast"], a["dx"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"],
+                                a["dz"], a["dbias"], a["dh0"], a["batch"], a["seqlen"], a["d_inner"], a["d_state"],
+                                a["ind"], a["gd"], None)
+    for k in ("dout", "dx", "ddelta", "dA", "dB", "dC"):
+        assert bwd(**{k: None}) == ssm.SSM_ERR_NULL_ARG, k
+    assert bwd(D=P + 0xb000000) == ssm.SSM_ERR_NULL_ARG                     # D given, dD missing
+    assert bwd(dz=P + 0xb000000) == ssm.SSM_ERR_UNSUPPORTED                 # dz without z
+    assert bwd(d_state=8) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd(dx=P + 0x6000000 + 4) == ssm.SSM_ERR_UNSUPPORTED             # misaligned
+    assert bwd(dx=P + 0x1000000) == ssm.SSM_ERR_UNSUPPORTED                 # dx over delta
+    assert bwd(dB=P + 0x6000000 + 64) == ssm.SSM_ERR_UNSUPPORTED            # two gradients overlap
+    assert "overlaps" in ssm.ssm_last_error()
