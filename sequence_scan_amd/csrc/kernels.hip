@@ -993,7 +993,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
   __shared__ float sh_y[T][G * kWave + 1];     // forward readout partials
   __shared__ float sh_s1[T][G * kWave + 1];    // partial dh . B'
   __shared__ float sh_s2[T][G * kWave + 1];    // partial sum dh A a h_{t-1}
-  __shared__ float sh_red[G][kWave][8] __attribute__((aligned(16)));  // per-lane dB', dC contributions
+  __shared__ float sh_red[G][kWave * 9];        // per-lane dB', dC contributions, stride 9
   __shared__ float sh_bc[T][2][kDState];       // the tile's dB', dC of this block
 
   const int tid = threadIdx.x;
@@ -1037,36 +1037,57 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
   const Tin* Cb = static_cast<const Tin*>(a.C) + b * L * kDState;
   float* ck = a.ws_ckpt + ((b * a.nblk + blk) * ntiles) * (int64_t)(kWave * kDState);
 
-  // stage the B (x ln 2) and C rows of the tile at step t0 (rows past nt repeat)
-  auto stage_bc = [&](int64_t t0, int nt, bool with_c) SSM_INLINE {
-    const int r = tid / kDState, n = tid % kDState;  // 256 threads = 16 rows x 16 states
-    const int64_t t = t0 + min(r, nt - 1);
-    sh_B[r][n] = ld_in(Bb + t * kDState + n) * kLn2;
-    if (with_c) sh_C[r][n] = ld_in(Cb + t * kDState + n);
+  // Raw inputs of one tile, loaded one tile ahead of their use (rows past
+  // the tile's end repeat its last row, so every load is unconditional).
+  struct Bank {
+    R rx[IPT], rd[IPT], rz[IPT];
+    RG rg[IPT];
+    float bv, cv;   // this thread's B, C element (256 threads = 16 rows x 16 states)
+  };
+  auto tile_rows = [&](int64_t k) SSM_INLINE { return (int)min((int64_t)T, L - k * T); };
+  auto load = [&](Bank& bk, int64_t k, bool full) SSM_INLINE {
+    const int64_t t0 = k * T;
+    const int nt = tile_rows(k);
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int64_t off = (t0 + min(irow[it], nt - 1)) * Dn + icol[it];
+      bk.rx[it].load(xb + off);
+      bk.rd[it].load(db + off);
+      if (full) {
+        bk.rg[it].load(gb + off);
+        if (HAS_Z) bk.rz[it].load(zb + off);
+      }
+    }
+    const int64_t t = t0 + min(tid / kDState, nt - 1);
+    bk.bv = ld_in(Bb + t * kDState + tid % kDState);
+    if (full) bk.cv = ld_in(Cb + t * kDState + tid % kDState);
+  };
+  auto stage_bc = [&](const Bank& bk, bool with_c) SSM_INLINE {
+    const int r = tid / kDState, n = tid % kDState;
+    sh_B[r][n] = bk.bv * kLn2;
+    if (with_c) sh_C[r][n] = bk.cv;
   };
 
   // ---- phase 1: forward, storing the state entering each tile
   float h[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) h[i] = a.h0 != nullptr ? a.h0[(b * Dn + dl) * kDState + g * NS + i] : 0.0f;
+  Bank cur, nxt;
+  load(cur, 0, false);
   for (int64_t k = 0; k < ntiles; ++k) {
-    const int64_t t0 = k * T;
-    const int nt = (int)min((int64_t)T, L - t0);
+    const int nt = tile_rows(k);
     *reinterpret_cast<float4*>(ck + (k * kWave + lane) * kDState + g * NS) = make_float4(h[0], h[1], h[2], h[3]);
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
-      const int64_t off = (t0 + min(irow[it], nt - 1)) * Dn + icol[it];
-      R rx, rd;
-      rx.load(xb + off);
-      rd.load(db + off);
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
-        const float u2 = __builtin_fmaf(rd.get(q), kLog2e, ibias2[it][q]);
+        const float u2 = __builtin_fmaf(cur.rd[it].get(q), kLog2e, ibias2[it][q]);
         const float dt2 = softplus ? softplus2_f(u2) : u2;
-        sh_dtu[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * rx.get(q));
+        sh_dtu[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * cur.rx[it].get(q));
       }
     }
-    stage_bc(t0, nt, false);
+    stage_bc(cur, false);
+    if (k + 1 < ntiles) load(nxt, k + 1, false);
     block_sync();
     for (int s = 0; s < nt; ++s) {
       const float2 v = sh_dtu[s][loff];
@@ -1075,6 +1096,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
         h[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(v.x * Ad[i]), h[i], v.y * sh_B[s][g * NS + i]);
     }
     block_sync();
+    cur = nxt;
   }
 
   // ---- phase 2: the tiles in reverse
@@ -1090,29 +1112,24 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < CW; ++q) dDacc[it][q] = dBacc[it][q] = 0.0f;
 
+  load(cur, ntiles - 1, true);
+  float4 hc = *reinterpret_cast<const float4*>(ck + ((ntiles - 1) * kWave + lane) * kDState + g * NS);
   for (int64_t k = ntiles - 1; k >= 0; --k) {
     const int64_t t0 = k * T;
-    const int nt = (int)min((int64_t)T, L - t0);
+    const int nt = tile_rows(k);
     float xv[IPT][CW], dyv[IPT][CW], dt2v[IPT][CW], sgv[IPT][CW], gv[IPT][CW], zv[IPT][CW];
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
-      const int64_t off = (t0 + min(irow[it], nt - 1)) * Dn + icol[it];
-      R rx, rd, rz;
-      RG rg;
-      rx.load(xb + off);
-      rd.load(db + off);
-      rg.load(gb + off);
-      if (HAS_Z) rz.load(zb + off);
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
-        const float x = rx.get(q);
-        const float u = rd.get(q) + ibias[it][q];
-        const float u2 = __builtin_fmaf(rd.get(q), kLog2e, ibias2[it][q]);
+        const float x = cur.rx[it].get(q);
+        const float u = cur.rd[it].get(q) + ibias[it][q];
+        const float u2 = __builtin_fmaf(cur.rd[it].get(q), kLog2e, ibias2[it][q]);
         const float dt2 = softplus ? softplus2_f(u2) : u2;
-        const float gg = rg.get(q);
+        const float gg = cur.rg[it].get(q);
         float dy = gg;
         if (HAS_Z) {
-          const float z = rz.get(q);
+          const float z = cur.rz[it].get(q);
           zv[it][q] = z;
           dy = gg * silu_f(z);
         }
@@ -1125,9 +1142,12 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
         sh_dy[irow[it]][icol[it] + q] = dy;
       }
     }
-    stage_bc(t0, nt, true);
-    const float4 hc = *reinterpret_cast<const float4*>(ck + (k * kWave + lane) * kDState + g * NS);
+    stage_bc(cur, true);
     h[0] = hc.x; h[1] = hc.y; h[2] = hc.z; h[3] = hc.w;
+    if (k > 0) {
+      load(nxt, k - 1, true);
+      hc = *reinterpret_cast<const float4*>(ck + ((k - 1) * kWave + lane) * kDState + g * NS);
+    }
     block_sync();
 
     // forward within the tile: each step's incoming state, and readout partials
@@ -1175,18 +1195,23 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
         // lanes 8p .. 8p + 7; three DPP steps (two within the quad, then
         // row_half_mirror, which swaps the two quads of each 8-lane half)
         // leave the total in all 8 lanes of group j.
-        float* red = &sh_red[g][0][0];
-        *reinterpret_cast<float4*>(red + lane * 8) = make_float4(cb[0], cb[1], cb[2], cb[3]);
-        *reinterpret_cast<float4*>(red + lane * 8 + 4) = make_float4(cc[0], cc[1], cc[2], cc[3]);
+        // (a lane's 8 values sit at stride 9: 9 is odd, so both the writes
+        // and the column reads below touch 64 distinct banks)
+        float* red = &sh_red[g][0];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          red[lane * 9 + i] = cb[i];
+          red[lane * 9 + NS + i] = cc[i];
+        }
         __builtin_amdgcn_wave_barrier();
         const int j = lane >> 3, p = lane & 7;
         float acc = 0.0f;
         if (nvalid == kWave) {
 #pragma unroll
-          for (int m = 0; m < 8; ++m) acc += red[(p * 8 + m) * 8 + j];
+          for (int m = 0; m < 8; ++m) acc += red[(p * 8 + m) * 9 + j];
         } else {  // lanes past the last channel hold duplicates: leave them out
 #pragma unroll
-          for (int m = 0; m < 8; ++m) acc += (p * 8 + m < nvalid) ? red[(p * 8 + m) * 8 + j] : 0.0f;
+          for (int m = 0; m < 8; ++m) acc += (p * 8 + m < nvalid) ? red[(p * 8 + m) * 9 + j] : 0.0f;
         }
         acc += SSM_DPP(0.0f, acc, 0xb1, 0xf);   // quad_perm [1,0,3,2]
         acc += SSM_DPP(0.0f, acc, 0x4e, 0xf);   // quad_perm [2,3,0,1]
@@ -1237,6 +1262,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
       a.ws_bc[((b * L + t0 + s) * a.nblk + blk) * (2 * kDState) + w] = (&sh_bc[s][0][0])[w];
     }
     block_sync();
+    cur = nxt;
   }
 
   // per-row parameter gradients and the initial state's gradient
