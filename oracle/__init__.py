@@ -49,8 +49,8 @@ class OracleLib:
         lib.oracle_scan_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp,
                                         _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
         lib.oracle_scan_fwd_from.restype = ctypes.c_int
-        lib.oracle_scan_fwd_from.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp,
-                                             _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
+        lib.oracle_scan_fwd_from.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int, ctypes.c_int,
+                                             _dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
         lib.oracle_scan_bwd.restype = ctypes.c_int
         lib.oracle_scan_bwd.argtypes = [_dp] * 8 + [ctypes.c_int] + [_dp] * 12 + [_i64] * 4
         lib.oracle_conv1d_fwd.restype = ctypes.c_int
@@ -59,7 +59,7 @@ class OracleLib:
         lib.oracle_conv1d_update.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int, _dp, _i64, _i64, _i64]
         lib.oracle_state_update.restype = ctypes.c_int
         lib.oracle_state_update.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int,
-                                            _dp, _i64, _i64, _i64]
+                                            ctypes.c_int, _dp, _i64, _i64, _i64]
         lib.oracle_affine_compose.restype = None
         lib.oracle_affine_compose.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64]
         lib.oracle_step_size.restype = None
@@ -69,13 +69,16 @@ class OracleLib:
         self.lib = lib
 
     def scan_fwd(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
-                 chunk: int = 0, nthreads: int | None = None, return_state: bool = True, h0=None):
+                 chunk: int = 0, nthreads: int | None = None, return_state: bool = True, h0=None,
+                 zoh: bool = False):
         """Sequential fp64 scan from the state h0 [batch, d_inner, d_state] (None: zero).
 
         x, delta, z: [batch, L, d_inner]; B, C: [batch, L, d_state]; A: [d_inner, d_state];
         D, delta_bias: [d_inner].  Returns (out [batch, L, d_inner], last_state
         [batch, d_inner, d_state] or None), float64.  ``chunk > 0`` runs the chunked
-        form: per-chunk affine pairs composed in time order, then each chunk re-run."""
+        form: per-chunk affine pairs composed in time order, then each chunk re-run.
+        ``zoh`` uses the exact zero-order-hold input coefficient (e^{dt A} - 1) / A
+        in place of dt."""
         x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
         D, z, delta_bias, h0 = map(_f64, (D, z, delta_bias, h0))
         if x.ndim != 3:
@@ -93,13 +96,15 @@ class OracleLib:
         out = np.empty((batch, L, Dn), dtype=np.float64)
         last = np.empty((batch, Dn, N), dtype=np.float64) if return_state else None
         rc = self.lib.oracle_scan_fwd_from(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                           _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(out), _ptr(last),
+                                           _ptr(delta_bias), int(bool(softplus)), int(bool(zoh)), _ptr(h0),
+                                           _ptr(out), _ptr(last),
                                            batch, L, Dn, N, int(chunk), int(nthreads or default_threads()))
         if rc != 0:
             raise ValueError("oracle_scan_fwd rejected its arguments")
         return out, last
 
-    def state_update(self, state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True):
+    def state_update(self, state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True,
+                     zoh: bool = False):
         """One decode step.  state: [batch, d_inner, d_state]; x, delta, z: [batch, d_inner];
         B, C: [batch, d_state].  Returns (out [batch, d_inner], new_state) as float64; the
         ``state`` argument itself is not modified."""
@@ -113,7 +118,7 @@ class OracleLib:
         out = np.empty((batch, Dn), dtype=np.float64)
         rc = self.lib.oracle_state_update(_ptr(st), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
                                           _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
-                                          _ptr(out), batch, Dn, N)
+                                          int(bool(zoh)), _ptr(out), batch, Dn, N)
         if rc != 0:
             raise ValueError("oracle_state_update rejected its arguments")
         return out, st

@@ -12,7 +12,8 @@
  *     for t = 0 .. L-1:
  *       u   = delta[b,t,d] + bias[d]                (bias optional, 0 if absent)
  *       dt  = softplus(u) if softplus_on else u     (softplus(u) = log(1 + e^u))
- *       for n: h[n] = exp(dt * A[d,n]) * h[n] + (dt * B[b,t,n]) * x[b,t,d]
+ *       for n: h[n] = exp(dt * A[d,n]) * h[n] + (c[n] * B[b,t,n]) * x[b,t,d]
+ *                c[n] = dt, or (exp(dt * A[d,n]) - 1) / A[d,n] in zoh mode
  *       y   = sum_n C[b,t,n] * h[n]
  *       y  += D[d] * x[b,t,d]                       (optional skip)
  *       y  *= z * sigmoid(z), z = z[b,t,d]          (optional SiLU gate)
@@ -37,6 +38,11 @@
  *    step written first; the chunked mode below joins chunks with it.
  *  - Same page, sections 7 and 14: the decode step is the same recurrence for
  *    one token, continuing from the stored ssm_state [batch, d_inner, d_state].
+ *  - Same page, sections 4 and 5: the exact zero-order-hold discretisation
+ *    holds the input constant over the step, so the input coefficient is the
+ *    integral of e^{sA} over s in [0, dt]: (e^{dt A} - 1) / A per diagonal
+ *    coordinate, with the limit dt at A = 0.  Mamba's own parametrisation
+ *    uses dt in its place (zoh off).
  *
  * Threads split independent (b, d) rows only; the order of the arithmetic
  * within a row is exactly the loop above.
@@ -47,7 +53,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI 2
+#define ORACLE_ABI 3
 
 int oracle_abi_version(void) { return ORACLE_ABI; }
 
@@ -64,10 +70,19 @@ static double step_size(double delta, const double* bias, int64_t d, int softplu
   return softplus_on ? softplus(u) : u;
 }
 
+/* The coefficient of B_t[n] x_t in the update of a coordinate with diagonal
+ * entry a: dt, or with zoh the integral of e^{sa} over [0, dt], which is
+ * (e^{dt a} - 1) / a for a != 0 and dt at a = 0. */
+static double input_coef(double dt, double a, int zoh) {
+  if (!zoh) return dt;
+  if (a == 0.0) return dt;
+  return expm1(dt * a) / a;
+}
+
 /* One recurrence step of one channel: updates h[0..N) in place and returns y. */
-static double scan_step(double* h, double x, double dt, const double* A_d, const double* B_t,
+static double scan_step(double* h, double x, double dt, int zoh, const double* A_d, const double* B_t,
                         const double* C_t, const double* D, int64_t d, const double* zp, int64_t N) {
-  for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A_d[n]) * h[n] + (dt * B_t[n]) * x;
+  for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A_d[n]) * h[n] + (input_coef(dt, A_d[n], zoh) * B_t[n]) * x;
   double y = 0.0;
   for (int64_t n = 0; n < N; ++n) y += C_t[n] * h[n];
   if (D) y += D[d] * x;
@@ -77,7 +92,7 @@ static double scan_step(double* h, double x, double dt, const double* A_d, const
 
 typedef struct {
   const double *x, *delta, *A, *B, *C, *D, *z, *bias;
-  int softplus_on;
+  int softplus_on, zoh;
   double *out, *last_state;
   const double* h0; /* [batch, Dn, N] initial state, or NULL for zero */
   int64_t batch, L, Dn, N, chunk;
@@ -94,7 +109,7 @@ static void scan_rows(const job_t* j) {
       const double* Bt = j->B + (b * j->L + t) * j->N; /* [batch, L, d_state] */
       const double* Ct = j->C + (b * j->L + t) * j->N;
       double dt = step_size(j->delta[e], j->bias, d, j->softplus_on);
-      double y = scan_step(h, j->x[e], dt, j->A + d * j->N, Bt, Ct, j->D, d, j->z ? j->z + e : NULL, j->N);
+      double y = scan_step(h, j->x[e], dt, j->zoh, j->A + d * j->N, Bt, Ct, j->D, d, j->z ? j->z + e : NULL, j->N);
       j->out[e] = y;
     }
     if (j->last_state)
@@ -132,7 +147,7 @@ static void scan_rows_chunked(const job_t* j) {
         for (int64_t n = 0; n < N; ++n) {
           double a = exp(dt * A_d[n]);
           Pk[n] = a * Pk[n];
-          Ek[n] = a * Ek[n] + (dt * Bt[n]) * j->x[e];
+          Ek[n] = a * Ek[n] + (input_coef(dt, A_d[n], j->zoh) * Bt[n]) * j->x[e];
         }
       }
     }
@@ -147,7 +162,7 @@ static void scan_rows_chunked(const job_t* j) {
         const double* Bt = j->B + (b * L + t) * N;
         const double* Ct = j->C + (b * L + t) * N;
         double dt = step_size(j->delta[e], j->bias, d, j->softplus_on);
-        j->out[e] = scan_step(h, j->x[e], dt, A_d, Bt, Ct, j->D, d, j->z ? j->z + e : NULL, N);
+        j->out[e] = scan_step(h, j->x[e], dt, j->zoh, A_d, Bt, Ct, j->D, d, j->z ? j->z + e : NULL, N);
       }
       for (int64_t n = 0; n < N; ++n) { /* acc = (P_k, E_k) o acc */
         double a2 = P[k * N + n], b2 = E[k * N + n];
@@ -193,7 +208,8 @@ static int run_threads(job_t base, int nthreads) {
   return 0;
 }
 
-/* Full forward scan from the initial state h0 [batch, Dn, N] (NULL: zero).
+/* Full forward scan from the initial state h0 [batch, Dn, N] (NULL: zero);
+ * zoh selects the exact zero-order-hold input coefficient.
  * Shapes: x, delta, z, out [batch, L, Dn]; B, C [batch, L, N]; A [Dn, N]; D, bias
  * [Dn]; last_state [batch, Dn, N].  D, z, bias, last_state may be NULL.  chunk > 0
  * selects the chunked form with chunks of that many steps.  Returns 0, or -1 on
@@ -201,7 +217,7 @@ static int run_threads(job_t base, int nthreads) {
  * itself (the decode cache of "Модуль 8", sections 7 and 14, vladkulikov.com). */
 int oracle_scan_fwd_from(const double* x, const double* delta, const double* A, const double* B,
                          const double* C, const double* D, const double* z, const double* bias,
-                         int softplus_on, const double* h0, double* out, double* last_state,
+                         int softplus_on, int zoh, const double* h0, double* out, double* last_state,
                          int64_t batch, int64_t L, int64_t Dn, int64_t N, int64_t chunk, int nthreads) {
   if (!x || !delta || !A || !B || !C || !out) return -1;
   if (batch < 0 || L < 0 || Dn < 0 || N <= 0 || chunk < 0) return -1;
@@ -212,7 +228,7 @@ int oracle_scan_fwd_from(const double* x, const double* delta, const double* A, 
     }
     return 0;
   }
-  job_t j = {x, delta, A, B, C, D, z, bias, softplus_on, out, last_state, h0, batch, L, Dn, N, chunk, 0, 0};
+  job_t j = {x, delta, A, B, C, D, z, bias, softplus_on, zoh, out, last_state, h0, batch, L, Dn, N, chunk, 0, 0};
   return run_threads(j, nthreads);
 }
 
@@ -221,7 +237,7 @@ int oracle_scan_fwd(const double* x, const double* delta, const double* A, const
                     const double* C, const double* D, const double* z, const double* bias,
                     int softplus_on, double* out, double* last_state, int64_t batch, int64_t L,
                     int64_t Dn, int64_t N, int64_t chunk, int nthreads) {
-  return oracle_scan_fwd_from(x, delta, A, B, C, D, z, bias, softplus_on, NULL, out, last_state,
+  return oracle_scan_fwd_from(x, delta, A, B, C, D, z, bias, softplus_on, 0, NULL, out, last_state,
                               batch, L, Dn, N, chunk, nthreads);
 }
 
@@ -229,7 +245,7 @@ int oracle_scan_fwd(const double* x, const double* delta, const double* A, const
  * [batch, Dn]; B, C [batch, N].  Same arithmetic as one step of the scan. */
 int oracle_state_update(double* state, const double* x, const double* delta, const double* A,
                         const double* B, const double* C, const double* D, const double* z,
-                        const double* bias, int softplus_on, double* out, int64_t batch,
+                        const double* bias, int softplus_on, int zoh, double* out, int64_t batch,
                         int64_t Dn, int64_t N) {
   if (!state || !x || !delta || !A || !B || !C || !out) return -1;
   if (batch < 0 || Dn < 0 || N <= 0) return -1;
@@ -237,7 +253,7 @@ int oracle_state_update(double* state, const double* x, const double* delta, con
     for (int64_t d = 0; d < Dn; ++d) {
       int64_t e = b * Dn + d;
       double dt = step_size(delta[e], bias, d, softplus_on);
-      out[e] = scan_step(state + e * N, x[e], dt, A + d * N, B + b * N, C + b * N, D, d,
+      out[e] = scan_step(state + e * N, x[e], dt, zoh, A + d * N, B + b * N, C + b * N, D, d,
                          z ? z + e : NULL, N);
     }
   return 0;

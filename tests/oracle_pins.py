@@ -29,6 +29,10 @@ Sources of the statements:
     continued from both.
   * The pages give no gradients; the backward is pinned to the forward by
     central finite differences.
+  * "Модуль 8", sections 4 and 5: the exact zero-order-hold coefficient is the
+    integral of e^{sA} over the step, with the limit dt at A = 0, and the
+    page's worked example (tests/golden/zoh_worked_example.txt); holding the
+    input constant makes the discrete state equal the continuous solution.
 """
 from __future__ import annotations
 
@@ -215,26 +219,28 @@ def pin_chunked_composition(orc):
 
 def pin_decode_equals_scan(orc):
     """L decode steps from a zero state reproduce one scan bitwise, and
-    prefill(L1) followed by L2 decode steps equals scan(L1 + L2) bitwise."""
+    prefill(L1) followed by L2 decode steps equals scan(L1 + L2) bitwise; with
+    the small-step and with the zero-order-hold input coefficient."""
     rng = np.random.default_rng(51)
     batch, L, Dn, N = 3, 17, 4, 5
     c = _rand_case(rng, batch, L, Dn, N)
-    ref, ref_last = orc.scan_fwd(**c)
-    state = np.zeros((batch, Dn, N))
-    for t in range(L):
-        y, state = orc.state_update(state, c["x"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t],
-                                    c["D"], c["z"][:, t], c["delta_bias"])
-        assert np.array_equal(y, ref[:, t]), f"decode step {t} differs from the scan"
-    assert np.array_equal(state, ref_last), "decode final state differs from the scan"
-    L1 = 9
-    pre = {k: (v[:, :L1] if k in ("x", "delta", "z", "B", "C") else v) for k, v in c.items()}
-    out1, st = orc.scan_fwd(**pre)
-    assert np.array_equal(out1, ref[:, :L1])
-    for t in range(L1, L):
-        y, st = orc.state_update(st, c["x"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t],
-                                 c["D"], c["z"][:, t], c["delta_bias"])
-        assert np.array_equal(y, ref[:, t]), f"continued decode step {t} differs"
-    assert np.array_equal(st, ref_last)
+    for zoh in (False, True):
+        ref, ref_last = orc.scan_fwd(**c, zoh=zoh)
+        state = np.zeros((batch, Dn, N))
+        for t in range(L):
+            y, state = orc.state_update(state, c["x"][:, t], c["delta"][:, t], c["A"], c["B"][:, t],
+                                        c["C"][:, t], c["D"], c["z"][:, t], c["delta_bias"], zoh=zoh)
+            assert np.array_equal(y, ref[:, t]), f"decode step {t} differs from the scan (zoh {zoh})"
+        assert np.array_equal(state, ref_last), f"decode final state differs from the scan (zoh {zoh})"
+        L1 = 9
+        pre = {k: (v[:, :L1] if k in ("x", "delta", "z", "B", "C") else v) for k, v in c.items()}
+        out1, st = orc.scan_fwd(**pre, zoh=zoh)
+        assert np.array_equal(out1, ref[:, :L1])
+        for t in range(L1, L):
+            y, st = orc.state_update(st, c["x"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t],
+                                     c["D"], c["z"][:, t], c["delta_bias"], zoh=zoh)
+            assert np.array_equal(y, ref[:, t]), f"continued decode step {t} differs (zoh {zoh})"
+        assert np.array_equal(st, ref_last)
 
 
 def pin_invariants(orc):
@@ -502,10 +508,88 @@ def pin_backward_finite_differences(orc):
         assert set(got) == {names[k] for k in keys}, "gradients of absent inputs must be absent"
 
 
+def pin_zoh_worked_example(orc):
+    """The pages' worked example: for a = -1, B = 1 the small-step coefficient dt
+    exceeds the exact zero-order-hold one by 10 % at dt = 0.193747558.  One step
+    from zero with x = 1 and C = 1 reads out the input coefficient itself."""
+    rows = np.loadtxt(os.path.join(GOLDEN, "zoh_worked_example.txt"), comments="#", ndmin=2)
+    for a, bv, dt, eps in rows:
+        args = dict(x=np.ones((1, 1, 1)), delta=np.full((1, 1, 1), dt), A=np.array([[a]]),
+                    B=np.full((1, 1, 1), bv), C=np.ones((1, 1, 1)), softplus=False)
+        y_zoh, _ = orc.scan_fwd(**args, zoh=True)
+        y_dt, _ = orc.scan_fwd(**args)
+        assert y_dt[0, 0, 0] == dt * bv, "the small-step coefficient is dt B"
+        got = y_dt[0, 0, 0] / y_zoh[0, 0, 0] - 1.0
+        # dt is printed to 9 digits and d(eps)/d(dt) is about 0.53 there
+        assert abs(got - eps) <= 1e-9, f"relative error of dt B against ZOH: {got!r}, page: {eps}"
+
+
+def pin_zoh_held_input_is_exact(orc):
+    """With x and B held constant, zero-order hold reproduces the continuous system:
+    after steps dt_1..dt_t from zero the state is (e^{A S_t} - 1) / A * B x, with
+    S_t the elapsed time (S_t B x where A = 0), whatever the step sizes; so merging
+    pairs of steps leaves the state unchanged.  Sequential and chunked forms.  The
+    small-step coefficient fails this (control)."""
+    rng = np.random.default_rng(61)
+    batch, L, Dn, N = 2, 36, 3, 5
+    A = -np.exp(rng.uniform(-1.0, 2.5, (Dn, N)))
+    A[0, 0] = 0.0
+    A[1, 1] = -1e-7
+    xv = rng.standard_normal((batch, Dn))
+    Bv = rng.standard_normal((batch, N))
+    Cv = rng.standard_normal((batch, N))
+    x = np.repeat(xv[:, None, :], L, axis=1)
+    B = np.repeat(Bv[:, None, :], L, axis=1)
+    C = np.repeat(Cv[:, None, :], L, axis=1)
+    delta = rng.uniform(0.001, 0.4, (batch, L, Dn))
+    S = np.cumsum(delta, axis=1)                                    # [b, t, d]
+    AS = S[..., None] * A[None, None]                               # [b, t, d, n]
+    safeA = np.where(A == 0.0, 1.0, A)
+    # (e^{AS} - 1) / A, by its power series S sum_k (AS)^k / (k+1)! where |AS| is small
+    series = S[..., None] * sum(AS ** k / math.factorial(k + 1) for k in range(8))
+    coef = np.where(np.abs(AS) < 1e-2, series, (np.exp(AS) - 1.0) / safeA[None, None])
+    h_ref = coef * Bv[:, None, None, :] * xv[:, None, :, None]       # [b, t, d, n]
+    y_ref = np.einsum("btdn,bn->btd", h_ref, Cv)
+    for chunk in (0, 5):
+        out, last = orc.scan_fwd(x, delta, A, B, C, softplus=False, zoh=True, chunk=chunk)
+        _close(out, y_ref, 1e-12, f"held-input outputs (chunk {chunk})")
+        _close(last, h_ref[:, -1], 1e-12, f"held-input final state (chunk {chunk})")
+    merged = delta[:, 0::2] + delta[:, 1::2]
+    _, last2 = orc.scan_fwd(x[:, : L // 2], merged, A, B[:, : L // 2], C[:, : L // 2], softplus=False, zoh=True)
+    _close(last2, h_ref[:, -1], 1e-12, "state after merged steps")
+    _, last_dt = orc.scan_fwd(x, delta, A, B, C, softplus=False)
+    assert float(np.max(np.abs(last_dt - h_ref[:, -1]))) > 1e-3 * float(np.max(np.abs(h_ref[:, -1]))), \
+        "control: the small-step form is not exact for a held input"
+
+
+def pin_zoh_integral_definition(orc):
+    """One step's coefficient is the integral of e^{sA} over s in [0, dt]: against
+    composite Simpson quadrature at several (dt, A), up to |dt A| = 40; at A = 0 it
+    is dt exactly (the same as the small-step form) and it is continuous there."""
+    dts = np.array([1e-3, 0.05, 0.3, 1.0, 4.0])
+    A = np.array([[-10.0, -1.0, -0.25, -3e-4, 0.0, -1e-12, 0.5]])
+    batch, N = dts.size, A.shape[1]
+    args = dict(x=np.ones((batch, 1, 1)), delta=dts.reshape(batch, 1, 1), A=A,
+                B=np.ones((batch, 1, N)), C=np.zeros((batch, 1, N)), softplus=False)
+    _, h = orc.scan_fwd(**args, zoh=True)
+    _, h_dt = orc.scan_fwd(**args)
+    m = 20000                                                      # Simpson panels (even)
+    for i, dt in enumerate(dts):
+        s = np.linspace(0.0, dt, m + 1)
+        w = np.ones(m + 1)
+        w[1:-1:2], w[2:-1:2] = 4.0, 2.0
+        for n in range(N):
+            quad = float(np.sum(w * np.exp(s * A[0, n]))) * dt / (3.0 * m)
+            assert abs(h[i, 0, n] - quad) <= 1e-10 * quad, f"dt={dt} A={A[0, n]}: {h[i, 0, n]!r} vs {quad!r}"
+        assert h[i, 0, 4] == h_dt[i, 0, 4] == dt, "A = 0: the coefficient is dt"
+        assert abs(h[i, 0, 5] - dt) <= 1e-11 * dt, "continuity at A -> 0"
+
+
 ALL_PINS = [
     pin_affine_worked_example, pin_step_size, pin_lti_convolution, pin_semiseparable, pin_delta_zero,
     pin_impulse_closed_form, pin_chunked_composition, pin_decode_equals_scan, pin_invariants,
     pin_decay, pin_nan_propagation, pin_optional_inputs, pin_initial_state_free_response,
     pin_initial_state_continuation, pin_conv1d_numpy, pin_conv1d_impulse, pin_conv1d_decode_and_continuation,
-    pin_backward_finite_differences,
+    pin_backward_finite_differences, pin_zoh_worked_example, pin_zoh_held_input_is_exact,
+    pin_zoh_integral_definition,
 ]

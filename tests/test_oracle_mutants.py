@@ -16,19 +16,19 @@ import oracle_pins
 MUTANTS = {
     "drop_D_skip": ("if (D) y += D[d] * x;", ""),
     "exp_sign": ("h[n] = exp(dt * A_d[n]) * h[n]", "h[n] = exp(-dt * A_d[n]) * h[n]"),
-    "drop_dt_in_input": ("(dt * B_t[n]) * x", "(B_t[n]) * x"),
+    "drop_dt_in_input": ("(input_coef(dt, A_d[n], zoh) * B_t[n]) * x", "(B_t[n]) * x"),
     "A_same_for_all_n": ("h[n] = exp(dt * A_d[n])", "h[n] = exp(dt * A_d[0])"),
     "readout_uses_B": ("y += C_t[n] * h[n]", "y += B_t[n] * h[n]"),
-    "B_state_index": ("(dt * B_t[n]) * x", "(dt * B_t[N - 1 - n]) * x"),
+    "B_state_index": ("(input_coef(dt, A_d[n], zoh) * B_t[n]) * x", "(input_coef(dt, A_d[n], zoh) * B_t[N - 1 - n]) * x"),
     "gate_sigmoid": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     "softplus_drop_max": ("return fmax(u, 0.0) + log1p(exp(-fabs(u)));", "return log1p(exp(-fabs(u)));"),
     "softplus_sign": ("log1p(exp(-fabs(u)))", "log1p(exp(fabs(u)))"),
     "bias_ignored": ("double u = delta + (bias ? bias[d] : 0.0);", "double u = delta;"),
     "readout_before_update": (
-        "  for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A_d[n]) * h[n] + (dt * B_t[n]) * x;\n"
+        "  for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A_d[n]) * h[n] + (input_coef(dt, A_d[n], zoh) * B_t[n]) * x;\n"
         "  double y = 0.0;\n  for (int64_t n = 0; n < N; ++n) y += C_t[n] * h[n];\n",
         "  double y = 0.0;\n  for (int64_t n = 0; n < N; ++n) y += C_t[n] * h[n];\n"
-        "  for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A_d[n]) * h[n] + (dt * B_t[n]) * x;\n"),
+        "  for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A_d[n]) * h[n] + (input_coef(dt, A_d[n], zoh) * B_t[n]) * x;\n"),
     "B_previous_step": ("const double* Bt = j->B + (b * j->L + t) * j->N;",
                         "const double* Bt = j->B + (b * j->L + (t > 0 ? t - 1 : 0)) * j->N;"),
     "x_batch_index": ("int64_t e = (b * j->L + t) * j->Dn + d;          /* [batch, L, d_inner] */",
@@ -64,6 +64,13 @@ MUTANTS = {
     "bwd_softplus_derivative": ("double dd = softplus_on ? ddt * sigmoid(u) : ddt;", "double dd = ddt;"),
     "bwd_silu_derivative": ("dz[e] = dout[e] * y * (s * (1.0 + zz * (1.0 - s)));", "dz[e] = dout[e] * y * s;"),
     "bwd_dlast_ignored": ("dh[n] = dlast ? dlast[(b * Dn + d) * N + n] : 0.0;", "dh[n] = 0.0;"),
+    "zoh_ignored": ("  if (!zoh) return dt;\n  if (a == 0.0)", "  return dt;\n  if (a == 0.0)"),
+    "zoh_sign": ("return expm1(dt * a) / a;", "return expm1(-dt * a) / -a;"),
+    "zoh_extra_factor": ("return expm1(dt * a) / a;", "return expm1(dt * a) / a * exp(0.5 * dt * a);"),
+    "zoh_limit_zero": ("if (a == 0.0) return dt;", "if (a == 0.0) return 0.0;"),
+    "zoh_chunked_pass1": ("Ek[n] = a * Ek[n] + (input_coef(dt, A_d[n], j->zoh) * Bt[n]) * j->x[e];",
+                          "Ek[n] = a * Ek[n] + (dt * Bt[n]) * j->x[e];"),
+    "zoh_decode_ignored": ("out[e] = scan_step(state + e * N, x[e], dt, zoh,", "out[e] = scan_step(state + e * N, x[e], dt, 0,"),
     "conv_state_out_oldest_last": ("state_out[(b * Dn + d) * K + k] = conv_input(x, state_in, b, L - K + k, d, L, Dn, K);",
                                    "state_out[(b * Dn + d) * K + k] = conv_input(x, state_in, b, L - 1 - k, d, L, Dn, K);"),
 }
