@@ -53,9 +53,8 @@ def measured_traffic(key):
     (scaled by a plain copy's reading) in profiles/*.md, or None when no record
     exists for `key` or the kernel source has changed since it was taken."""
     import glob
-    import hashlib
-    with open(os.path.join(ROOT, "sequence_scan_amd", "csrc", "kernels.hip"), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    from sequence_scan_amd import build as lib_build
+    sha = lib_build.kernel_source_sha256()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as f:
             for row in f:

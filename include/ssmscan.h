@@ -10,7 +10,7 @@
  * for the recurrent decode step and the shape of ssm_state):
  *
  *   for every batch row b and channel d, from a zero state h = 0:
- *     dt  = softplus(delta[b,t,d] + bias[d])     (or delta + bias if softplus == 0)
+ *     dt  = softplus(delta[b,t,d] + bias[d])     (or delta + bias without SSM_SOFTPLUS)
  *     h[n] = exp(dt * A[d,n]) * h[n] + dt * B[b,t,n] * x[b,t,d]     n < d_state
  *     y   = sum_n C[b,t,n] * h[n] + D[d] * x[b,t,d]
  *     out[b,t,d] = y * z[b,t,d] * sigmoid(z[b,t,d])                  (SiLU gate)
@@ -50,7 +50,24 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
+
+/*
+ * Bits of the step-flags argument (named `softplus` in the calls below):
+ *   SSM_SOFTPLUS  dt = softplus(delta + bias); without it dt = delta + bias
+ *                 as given (the caller guarantees a meaningful step).
+ *   SSM_ZOH       the exact zero-order-hold input coefficient: the update adds
+ *                 (e^{dt A[d,n]} - 1) / A[d,n] * B_t[n] * x in place of
+ *                 dt * B_t[n] * x, with its limit dt where A[d,n] = 0 (page
+ *                 "Модуль 8. Альтернативы Transformer", vladkulikov.com,
+ *                 section 4: the input is held constant over the step, so its
+ *                 coefficient is the integral of e^{sA} over [0, dt]; section 5
+ *                 shows the two coefficients differ by 10 % at dt A = -0.19).
+ *                 Forward calls only; the backward rejects it.
+ * Any other bit is rejected with SSM_ERR_UNSUPPORTED.
+ */
+#define SSM_SOFTPLUS 1
+#define SSM_ZOH 2
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
@@ -72,8 +89,8 @@ typedef enum {
  *   z           -- no gate (out = y);
  *   delta_bias  -- bias 0;
  *   last_state  -- final state h after step seqlen-1 is not stored.
- * softplus: nonzero applies softplus to delta + bias; zero uses delta + bias as
- *   the step size as given (the caller guarantees it is a meaningful step).
+ * softplus: step flags, SSM_SOFTPLUS and/or SSM_ZOH (0: dt = delta + bias as
+ *   given, with the dt input coefficient).
  * Sizes: batch, seqlen, d_inner >= 0 (a zero size is a valid empty call;
  *   with seqlen == 0 a non-NULL last_state is set to zero); d_state == 16.
  * Alignment: every pointer 16-byte aligned.
@@ -159,7 +176,8 @@ ssm_status ssm_scan_fwd_from(const void* x, const void* delta, const float* A, c
  *   with dy_t = dout_t SiLU(z_t) (or dout_t), and from it dx, ddelta, dz, dA,
  *   dB, dC, dD, ddelta_bias and dinitial_state.
  * The forward inputs (x .. softplus, initial_state) are those of the forward
- * call; the forward outputs are not needed (the states are recomputed).
+ * call (step flags: SSM_SOFTPLUS or 0; SSM_ZOH is rejected); the forward
+ * outputs are not needed (the states are recomputed).
  *   dout          : [batch, seqlen, d_inner] in grad_dtype
  *   dlast_state   : [batch, d_inner, d_state] fp32, or NULL (zero)
  *   dx, ddelta, dz: [batch, seqlen, d_inner] in grad_dtype (dz iff z != NULL)

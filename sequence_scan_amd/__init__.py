@@ -23,6 +23,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ssmscan.h")
 
 SSM_F32 = 0
 SSM_BF16 = 1
+SSM_SOFTPLUS = 1  # step flags: dt = softplus(delta + bias)
+SSM_ZOH = 2       # step flags: exact zero-order-hold input coefficient
 SSM_OK, SSM_ERR_NULL_ARG, SSM_ERR_BAD_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP = range(5)
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_BAD_SHAPE", 3: "SSM_ERR_UNSUPPORTED",
                 4: "SSM_ERR_HIP"}
@@ -100,6 +102,11 @@ def _check(status: int):
         raise SSMError(status, _load().ssm_last_error().decode())
 
 
+def _flags(softplus, zoh) -> int:
+    """The step-flags word of the C ABI."""
+    return (SSM_SOFTPLUS if softplus else 0) | (SSM_ZOH if zoh else 0)
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.float32:
@@ -145,14 +152,16 @@ def ssm_scan_plan(batch: int, seqlen: int, d_inner: int, d_state: int = D_STATE)
 
 
 def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
-                 out=None, last_state=None, out_dtype=None, stream=None, plan: Optional[dict] = None):
+                 out=None, last_state=None, out_dtype=None, stream=None, plan: Optional[dict] = None,
+                 zoh: bool = False):
     """Forward selective scan from a zero state (see include/ssmscan.h).
 
     x, delta, z: [batch, seqlen, d_inner]; B, C: [batch, seqlen, d_state] (all float32 or
     all bfloat16); A: [d_inner, d_state], D, delta_bias: [d_inner] (float32).  ``out``
     (allocated if None, dtype ``out_dtype`` or x's) and ``last_state`` (float32
     [batch, d_inner, d_state], optional) are written on the current stream.  ``plan`` =
-    {"states_per_wave": .., "chunk_len": ..} forces an execution plan.  Returns out.
+    {"states_per_wave": .., "chunk_len": ..} forces an execution plan.  ``zoh`` selects the
+    exact zero-order-hold input coefficient (e^{dt A} - 1) / A in place of dt.  Returns out.
     """
     import torch
     if x.dim() != 3:
@@ -163,7 +172,7 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: b
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     lib = _load()
     args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-            int(bool(softplus)), _ptr(out), _ptr(last_state), batch, seqlen, d_inner, d_state,
+            _flags(softplus, zoh), _ptr(out), _ptr(last_state), batch, seqlen, d_inner, d_state,
             _dtype_code(x), _dtype_code(out), _stream(stream))
     if plan is None:
         _check(lib.ssm_scan_fwd(*args))
@@ -190,7 +199,7 @@ def _plan_struct(plan: Optional[dict]):
 
 def ssm_scan_fwd_from(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
                       initial_state=None, out=None, last_state=None, out_dtype=None, stream=None,
-                      plan: Optional[dict] = None):
+                      plan: Optional[dict] = None, zoh: bool = False):
     """Forward scan continuing from ``initial_state`` [batch, d_inner, d_state] float32
     (None: zero); ``last_state`` may be the same tensor (replaced in place).  Other
     arguments as for ``ssm_scan_fwd``.  Returns out."""
@@ -202,7 +211,7 @@ def ssm_scan_fwd_from(x, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     _check(_load().ssm_scan_fwd_from(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                     _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(out),
+                                     _ptr(delta_bias), _flags(softplus, zoh), _ptr(initial_state), _ptr(out),
                                      _ptr(last_state), batch, seqlen, d_inner, d_state, _dtype_code(x),
                                      _dtype_code(out), _stream(stream), _plan_struct(plan)))
     return out
@@ -283,7 +292,7 @@ def ssm_conv1d_update(conv_state, x, weight, bias=None, silu: bool = True, out=N
 
 
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
-                     out=None, out_dtype=None, stream=None):
+                     out=None, out_dtype=None, stream=None, zoh: bool = False):
     """One decode step (see include/ssmscan.h); ``state`` [batch, d_inner, d_state] float32
     is updated in place.  x, delta, z: [batch, d_inner]; B, C: [batch, d_state]."""
     import torch
@@ -294,7 +303,7 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, 
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     _check(_load().ssm_state_update(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                    _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(out), batch, d_inner,
+                                    _ptr(z), _ptr(delta_bias), _flags(softplus, zoh), _ptr(out), batch, d_inner,
                                     d_state, _dtype_code(x), _dtype_code(out), _stream(stream)))
     return out
 

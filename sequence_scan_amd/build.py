@@ -18,11 +18,30 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
-HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(os.path.dirname(HERE), "include", "ssmscan.h")]
+# Device translation units, as (source, extra defines, object name).  The
+# scan kernel template is instantiated by scan_inst.hip once per (input dtype,
+# output dtype, input coefficient): eight units that compile in parallel.
+def _scan_units():
+    units = []
+    for zoh in (0, 1):
+        for tin, nin in (("float", "f32"), ("uint16_t", "bf16")):
+            for tout, nout in (("float", "f32"), ("uint16_t", "bf16")):
+                fn = f"launch_scan_{nin}_{nout}" + ("_zoh" if zoh else "")
+                units.append((os.path.join(CSRC, "scan_inst.hip"),
+                              [f"-DSSM_INST_TIN={tin}", f"-DSSM_INST_TOUT={tout}", f"-DSSM_INST_ZOH={zoh}",
+                               f"-DSSM_INST_FN={fn}"], fn))
+    return units
+
+
+DEVICE_UNITS = _scan_units() + [(os.path.join(CSRC, f), [], f.split(".")[0]) for f in ("scan.hip", "conv.hip", "bwd.hip")]
+HOST_UNITS = [(os.path.join(CSRC, "api.cpp"), [], "api")]
+SOURCES = sorted({u[0] for u in DEVICE_UNITS + HOST_UNITS})
+HEADERS = [os.path.join(CSRC, f) for f in ("internal.h", "device.h", "scan_kernel.h")] + [
+    os.path.join(os.path.dirname(HERE), "include", "ssmscan.h")]
 LIB = os.path.join(HERE, "libssmscan.so")
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
@@ -33,28 +52,64 @@ FLAGS = [
 ]
 
 
+def kernel_source_sha256() -> str:
+    """One hash over every device source and header (in a fixed order): the
+    identity of the kernels that a profile was taken of."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in sorted({u[0] for u in DEVICE_UNITS} | set(HEADERS)):
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _run_all(cmds, verbose):
+    """Run the compiler commands in parallel; raise with the output of any failure."""
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    failed = []
+    for cmd, p in zip(cmds, procs):
+        out, _ = p.communicate()
+        # the host pass does not know the packed-fp32 target feature; that warning is expected
+        noise = [ln for ln in out.splitlines() if ln.strip() and "packed-fp32-ops" not in ln]
+        if p.returncode != 0:
+            failed.append(" ".join(cmd) + "\n" + "\n".join(noise))
+        elif verbose and noise:
+            print("\n".join(noise))
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n\n".join(failed))
+
+
 def build(verbose: bool = False) -> str:
     """Compile unconditionally; returns the path of libssmscan.so."""
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = ["hipcc", *FLAGS, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass does not know the packed-fp32 target feature; that warning is expected
-    noise = [ln for ln in (r.stdout + r.stderr).splitlines() if ln.strip() and "packed-fp32-ops" not in ln]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(noise))
-    if verbose and noise:
-        print("\n".join(noise))
+    with tempfile.TemporaryDirectory(prefix="ssmscan_build_") as od:
+        units = DEVICE_UNITS + HOST_UNITS
+        objs = [os.path.join(od, name + ".o") for _, _, name in units]
+        comp = [f for f in FLAGS if f != "-shared"]
+        _run_all([["hipcc", *comp, *defs, "-c", src, "-o", obj] for (src, defs, _), obj in zip(units, objs)], verbose)
+        # -z defs: a launcher declared but built in no unit fails here, not at load time
+        _run_all([["hipcc", *FLAGS, "-Wl,-z,defs", *objs, "-o", tmp]], verbose)
     os.replace(tmp, LIB)
     return LIB
 
 
 def asm(out_path: str) -> str:
-    """Write the gfx950 assembly of the kernels (for inspection)."""
-    cmd = ["hipcc", *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "--cuda-device-only", "-S",
-           SOURCES[0], "-o", out_path]
-    subprocess.run(cmd, check=True, capture_output=True)
+    """Write the gfx950 assembly of every device translation unit, concatenated
+    (for inspection and the code-generation checks)."""
+    with tempfile.TemporaryDirectory(prefix="ssmscan_asm_") as od:
+        outs = [os.path.join(od, name + ".s") for _, _, name in DEVICE_UNITS]
+        flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
+        _run_all([["hipcc", *flags, *defs, "--cuda-device-only", "-S", src, "-o", o]
+                  for (src, defs, _), o in zip(DEVICE_UNITS, outs)], False)
+        with open(out_path, "w") as f:
+            for o in outs:
+                with open(o) as g:
+                    f.write(g.read())
     return out_path
 
 

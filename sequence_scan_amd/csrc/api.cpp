@@ -138,6 +138,15 @@ ssm_status conv_check(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_
   return SSM_OK;
 }
 
+// The step flags word: SSM_SOFTPLUS and SSM_ZOH are its only bits.
+ssm_status check_flags(int flags, bool allow_zoh) {
+  if ((flags & ~(SSM_SOFTPLUS | SSM_ZOH)) != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "step flags %d: only SSM_SOFTPLUS (1) and SSM_ZOH (2) are defined", flags);
+  if (!allow_zoh && (flags & SSM_ZOH) != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "the backward is defined for the dt input coefficient only, not SSM_ZOH");
+  return SSM_OK;
+}
+
 ssm_status scan_impl(const void* x, const void* delta, const float* A, const void* B, const void* C,
                      const float* D, const void* z, const float* delta_bias, int softplus, const float* h0,
                      void* out, float* last_state, int64_t batch, int64_t seqlen, int64_t d_inner,
@@ -146,6 +155,7 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   Sizes sz;
   ssm_status st = check_common(batch, seqlen, d_inner, d_state, in_dtype, out_dtype, &sz);
   if (st != SSM_OK) return st;
+  if ((st = check_flags(softplus, true)) != SSM_OK) return st;
   // a required pointer may be NULL only when its tensor is empty
   const bool need_e = sz.elems > 0, need_bc = sz.bc > 0, need_a = d_inner > 0;
   if ((need_e && (!x || !delta || !out)) || (need_a && !A) || (need_bc && (!B || !C))) {
@@ -218,7 +228,8 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   a.d_inner = d_inner;
   a.chunk_len = plan.chunk_len;
   a.n_chunks = (int32_t)plan.n_chunks;
-  a.softplus = softplus ? 1 : 0;
+  a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
+  a.zoh = (softplus & SSM_ZOH) ? 1 : 0;
   a.batch = (int32_t)batch;
 
   void* ws = nullptr;
@@ -299,6 +310,7 @@ ssm_status ssm_state_update(float* state, const void* x, const void* delta, cons
   Sizes sz;
   ssm_status st = check_common(batch, 1, d_inner, d_state, in_dtype, out_dtype, &sz);
   if (st != SSM_OK) return st;
+  if ((st = check_flags(softplus, true)) != SSM_OK) return st;
   const bool need_e = sz.elems > 0, need_bc = sz.bc > 0, need_a = d_inner > 0;
   if ((need_e && (!state || !x || !delta || !out)) || (need_a && !A) || (need_bc && (!B || !C))) {
     const char* which = (need_e && !state) ? "state" : (need_e && !x) ? "x" : (need_e && !delta) ? "delta"
@@ -337,7 +349,8 @@ ssm_status ssm_state_update(float* state, const void* x, const void* delta, cons
   a.out = out;
   a.d_inner = d_inner;
   a.pairs = batch * d_inner;
-  a.softplus = softplus ? 1 : 0;
+  a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
+  a.zoh = (softplus & SSM_ZOH) ? 1 : 0;
   hipError_t e = ssm::launch_decode(a, to_dt(in_dtype), to_dt(out_dtype), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -352,6 +365,7 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
   Sizes sz;
   ssm_status st = check_common(batch, seqlen, d_inner, d_state, in_dtype, grad_dtype, &sz);
   if (st != SSM_OK) return st;
+  if ((st = check_flags(softplus, false)) != SSM_OK) return st;
   const bool need_e = sz.elems > 0, need_bc = sz.bc > 0, need_a = d_inner > 0;
   struct Req { const char* name; const void* p; bool need; };
   const Req req[] = {{"x", x, need_e}, {"delta", delta, need_e}, {"dout", dout, need_e}, {"dx", dx, need_e},
@@ -443,7 +457,7 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
   a.seqlen = seqlen;
   a.d_inner = d_inner;
   a.batch = (int32_t)batch;
-  a.softplus = softplus ? 1 : 0;
+  a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
   a.nblk = (int32_t)nblk;
   e = ssm::launch_scan_bwd(a, to_dt(in_dtype), to_dt(grad_dtype), dA, dB, dC, dD, ddelta_bias, s);
   hipError_t e2 = hipFreeAsync(ws, s);

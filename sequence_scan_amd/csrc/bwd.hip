@@ -1,0 +1,422 @@
+// gfx950 kernels of libssmscan: the scan's backward (recompute-and-reverse
+// gradients) and its fixed-order reductions.
+#include "device.h"
+
+namespace ssm {
+namespace {
+
+// ---------------------------------------------------------- backward kernel
+//
+// Reverse-mode gradients of the scan (the chain rule applied to the
+// recurrence; the pages give the forward only).  With dt2 = dt log2(e) as in
+// the forward kernel, a_t = exp2(dt2_t A), u2_t = dt2_t x_t and B' = B ln 2:
+//   dy_t   = dout_t SiLU(z_t)                   dz_t = dout_t y_t SiLU'(z_t)
+//   dh_t   = dy_t C_t + a_{t+1} dh_{t+1}        (carry from dlast)
+//   dx_t   = dy_t D + dt2_t (dh_t . B'_t)
+//   ddt_t  = sum_n dh_t A a_t h_{t-1} + x_t log2(e) (dh_t . B'_t)
+//   ddelta = ddt sigmoid(delta + bias) (softplus) or ddt
+//   dB_t  += ln 2 dh_t u2_t,   dC_t += dy_t h_t   (over channels)
+//   dA    += ln 2 dh_t a_t h_{t-1} dt2_t          (over steps and rows)
+// A workgroup owns 64 channels of one batch row (4 wavefronts x 4 states per
+// lane, as in the forward).  Phase 1 runs the forward and stores the state
+// entering every tile of kBwdTile steps.  Phase 2 walks the tiles backwards:
+// it recomputes the tile's forward from its checkpoint (keeping each step's
+// incoming state in registers), then runs the reverse recurrence.  Sums over a
+// channel's 16 states go through LDS partials, summed in a fixed order; dB and
+// dC are reduced over the wavefront's 64 channels through a wave-local LDS
+// transpose and 3 DPP steps, and stored per channel block for a second,
+// fixed-order reduction kernel: the result does not depend on timing.
+
+template <typename Tin, typename Tg, bool HAS_Z, int CW>
+__global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
+  constexpr int NS = 4, G = 4, T = kBwdTile, NTHR = 256;
+  constexpr int CPR = kWave / CW;
+  constexpr int IPT = T * CPR / NTHR;
+  static_assert(IPT >= 1 && IPT * NTHR == T * CPR, "tile does not split evenly");
+  using R = Raw<Tin, CW>;
+  using RG = Raw<Tg, CW>;
+  constexpr int RS = kWave + 4;  // staging row stride (16-byte aligned rows)
+
+  __shared__ float2 sh_dtu[T][kWave + 1];      // (dt2, u2)
+  __shared__ float sh_dy[T][kWave + 1];
+  __shared__ float sh_B[T][kDState];           // B ln 2
+  __shared__ float sh_C[T][kDState];
+  __shared__ float sh_y[T][G * kWave + 1];     // forward readout partials
+  __shared__ float sh_s1[T][G * kWave + 1];    // partial dh . B'
+  __shared__ float sh_s2[T][G * kWave + 1];    // partial sum dh A a h_{t-1}
+  __shared__ float sh_red[G][kWave * 9];        // per-lane dB', dC contributions, stride 9
+  __shared__ float sh_bc[T][2][kDState];       // the tile's dB', dC of this block
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int64_t b = blockIdx.y;
+  const int blk = blockIdx.x;
+  const int64_t Dn = a.d_inner, L = a.seqlen;
+  const int64_t d0 = (int64_t)blk * kWave;
+  const int nvalid = (int)min((int64_t)kWave, Dn - d0);
+  const int loff = min(lane, nvalid - 1);
+  const int64_t dl = d0 + loff;
+  const bool softplus = a.softplus != 0;
+  const int64_t ntiles = (L + T - 1) / T;
+
+  float Ad[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) Ad[i] = a.A[dl * kDState + g * NS + i];
+
+  int irow[IPT], icol[IPT];
+  float ibias[IPT][CW], ibias2[IPT][CW], iD[IPT][CW];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int idx = tid + it * NTHR;
+    irow[it] = idx / CPR;
+    icol[it] = min(idx % CPR, (nvalid + CW - 1) / CW - 1) * CW;
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+      const int64_t dq = d0 + min(icol[it] + q, nvalid - 1);
+      ibias[it][q] = a.bias != nullptr ? a.bias[dq] : 0.0f;
+      ibias2[it][q] = ibias[it][q] * kLog2e;
+      iD[it][q] = a.D != nullptr ? a.D[dq] : 0.0f;
+    }
+  }
+  const int64_t row0 = b * L * Dn + d0;
+  const Tin* xb = static_cast<const Tin*>(a.x) + row0;
+  const Tin* db = static_cast<const Tin*>(a.delta) + row0;
+  const Tin* zb = HAS_Z ? static_cast<const Tin*>(a.z) + row0 : nullptr;
+  const Tg* gb = static_cast<const Tg*>(a.dout) + row0;
+  const Tin* Bb = static_cast<const Tin*>(a.B) + b * L * kDState;
+  const Tin* Cb = static_cast<const Tin*>(a.C) + b * L * kDState;
+  float* ck = a.ws_ckpt + ((b * a.nblk + blk) * ntiles) * (int64_t)(kWave * kDState);
+
+  // Raw inputs of one tile, loaded one tile ahead of their use (rows past
+  // the tile's end repeat its last row, so every load is unconditional).
+  struct Bank {
+    R rx[IPT], rd[IPT], rz[IPT];
+    RG rg[IPT];
+    float bv, cv;   // this thread's B, C element (256 threads = 16 rows x 16 states)
+  };
+  auto tile_rows = [&](int64_t k) SSM_INLINE { return (int)min((int64_t)T, L - k * T); };
+  auto load = [&](Bank& bk, int64_t k, bool full) SSM_INLINE {
+    const int64_t t0 = k * T;
+    const int nt = tile_rows(k);
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int64_t off = (t0 + min(irow[it], nt - 1)) * Dn + icol[it];
+      bk.rx[it].load(xb + off);
+      bk.rd[it].load(db + off);
+      if (full) {
+        bk.rg[it].load(gb + off);
+        if (HAS_Z) bk.rz[it].load(zb + off);
+      }
+    }
+    const int64_t t = t0 + min(tid / kDState, nt - 1);
+    bk.bv = ld_in(Bb + t * kDState + tid % kDState);
+    if (full) bk.cv = ld_in(Cb + t * kDState + tid % kDState);
+  };
+  auto stage_bc = [&](const Bank& bk, bool with_c) SSM_INLINE {
+    const int r = tid / kDState, n = tid % kDState;
+    sh_B[r][n] = bk.bv * kLn2;
+    if (with_c) sh_C[r][n] = bk.cv;
+  };
+
+  // ---- phase 1: forward, storing the state entering each tile
+  float h[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) h[i] = a.h0 != nullptr ? a.h0[(b * Dn + dl) * kDState + g * NS + i] : 0.0f;
+  Bank cur, nxt;
+  load(cur, 0, false);
+  for (int64_t k = 0; k < ntiles; ++k) {
+    const int nt = tile_rows(k);
+    *reinterpret_cast<float4*>(ck + (k * kWave + lane) * kDState + g * NS) = make_float4(h[0], h[1], h[2], h[3]);
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        const float u2 = __builtin_fmaf(cur.rd[it].get(q), kLog2e, ibias2[it][q]);
+        const float dt2 = softplus ? softplus2_f(u2) : u2;
+        sh_dtu[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * cur.rx[it].get(q));
+      }
+    }
+    stage_bc(cur, false);
+    if (k + 1 < ntiles) load(nxt, k + 1, false);
+    block_sync();
+    for (int s = 0; s < nt; ++s) {
+      const float2 v = sh_dtu[s][loff];
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        h[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(v.x * Ad[i]), h[i], v.y * sh_B[s][g * NS + i]);
+    }
+    block_sync();
+    cur = nxt;
+  }
+
+  // ---- phase 2: the tiles in reverse
+  float carry[NS], dAacc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    carry[i] = a.dlast != nullptr ? a.dlast[(b * Dn + dl) * kDState + g * NS + i] : 0.0f;
+    dAacc[i] = 0.0f;
+  }
+  float dDacc[IPT][CW], dBacc[IPT][CW];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it)
+#pragma unroll
+    for (int q = 0; q < CW; ++q) dDacc[it][q] = dBacc[it][q] = 0.0f;
+
+  load(cur, ntiles - 1, true);
+  float4 hc = *reinterpret_cast<const float4*>(ck + ((ntiles - 1) * kWave + lane) * kDState + g * NS);
+  for (int64_t k = ntiles - 1; k >= 0; --k) {
+    const int64_t t0 = k * T;
+    const int nt = tile_rows(k);
+    float xv[IPT][CW], dyv[IPT][CW], dt2v[IPT][CW], sgv[IPT][CW], gv[IPT][CW], zv[IPT][CW];
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        const float x = cur.rx[it].get(q);
+        const float u = cur.rd[it].get(q) + ibias[it][q];
+        const float u2 = __builtin_fmaf(cur.rd[it].get(q), kLog2e, ibias2[it][q]);
+        const float dt2 = softplus ? softplus2_f(u2) : u2;
+        const float gg = cur.rg[it].get(q);
+        float dy = gg;
+        if (HAS_Z) {
+          const float z = cur.rz[it].get(q);
+          zv[it][q] = z;
+          dy = gg * silu_f(z);
+        }
+        xv[it][q] = x;
+        gv[it][q] = gg;
+        dyv[it][q] = dy;
+        dt2v[it][q] = dt2;
+        sgv[it][q] = softplus ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u * kLog2e)) : 1.0f;
+        sh_dtu[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * x);
+        sh_dy[irow[it]][icol[it] + q] = dy;
+      }
+    }
+    stage_bc(cur, true);
+    h[0] = hc.x; h[1] = hc.y; h[2] = hc.z; h[3] = hc.w;
+    if (k > 0) {
+      load(nxt, k - 1, true);
+      hc = *reinterpret_cast<const float4*>(ck + ((k - 1) * kWave + lane) * kDState + g * NS);
+    }
+    block_sync();
+
+    // forward within the tile: each step's incoming state, and readout partials
+    float hp[T][NS];
+#pragma unroll
+    for (int s = 0; s < T; ++s) {
+      if (s < nt) {
+        const float2 v = sh_dtu[s][loff];
+        float y = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          hp[s][i] = h[i];
+          h[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(v.x * Ad[i]), h[i], v.y * sh_B[s][g * NS + i]);
+          y = __builtin_fmaf(sh_C[s][g * NS + i], h[i], y);
+        }
+        sh_y[s][g * kWave + lane] = y;
+      }
+    }
+
+    // reverse within the tile
+#pragma unroll
+    for (int s = T - 1; s >= 0; --s) {
+      if (s < nt) {
+        const float2 v = sh_dtu[s][loff];
+        const float dy = sh_dy[s][loff];
+        float s1 = 0.0f, s2 = 0.0f, cb[NS], cc[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const float aa = __builtin_amdgcn_exp2f(v.x * Ad[i]);
+          const float Bs = sh_B[s][g * NS + i];
+          const float dh = __builtin_fmaf(dy, sh_C[s][g * NS + i], carry[i]);
+          const float hs = __builtin_fmaf(aa, hp[s][i], v.y * Bs);
+          cc[i] = dy * hs;
+          cb[i] = dh * v.y;
+          s1 = __builtin_fmaf(dh, Bs, s1);
+          const float qv = dh * aa * hp[s][i];
+          s2 = __builtin_fmaf(qv, Ad[i], s2);
+          dAacc[i] = __builtin_fmaf(qv, v.x, dAacc[i]);
+          carry[i] = aa * dh;
+        }
+        sh_s1[s][g * kWave + lane] = s1;
+        sh_s2[s][g * kWave + lane] = s2;
+        // dB', dC of this step over the wavefront's 64 channels: every lane
+        // stages its 8 contributions; lane 8j + p sums contribution j of
+        // lanes 8p .. 8p + 7; three DPP steps (two within the quad, then
+        // row_half_mirror, which swaps the two quads of each 8-lane half)
+        // leave the total in all 8 lanes of group j.
+        // (a lane's 8 values sit at stride 9: 9 is odd, so both the writes
+        // and the column reads below touch 64 distinct banks)
+        float* red = &sh_red[g][0];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          red[lane * 9 + i] = cb[i];
+          red[lane * 9 + NS + i] = cc[i];
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int j = lane >> 3, p = lane & 7;
+        float acc = 0.0f;
+        if (nvalid == kWave) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m) acc += red[(p * 8 + m) * 9 + j];
+        } else {  // lanes past the last channel hold duplicates: leave them out
+#pragma unroll
+          for (int m = 0; m < 8; ++m) acc += (p * 8 + m < nvalid) ? red[(p * 8 + m) * 9 + j] : 0.0f;
+        }
+        acc += SSM_DPP(0.0f, acc, 0xb1, 0xf);   // quad_perm [1,0,3,2]
+        acc += SSM_DPP(0.0f, acc, 0x4e, 0xf);   // quad_perm [2,3,0,1]
+        acc += SSM_DPP(0.0f, acc, 0x141, 0xf);  // row_half_mirror
+        if (p == 0) sh_bc[s][j >> 2][g * NS + (j & 3)] = acc;
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    block_sync();
+
+    // per element: dz, dx, ddelta; per channel: dD, dbias
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int r = irow[it];
+      if (r < nt) {
+        float ox[CW], od[CW], oz[CW];
+#pragma unroll
+        for (int q = 0; q < CW; ++q) {
+          const int col = icol[it] + q;
+          float S1 = 0.0f, S2 = 0.0f, y = 0.0f;
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) {
+            S1 += sh_s1[r][gg * kWave + col];
+            S2 += sh_s2[r][gg * kWave + col];
+            if (HAS_Z) y += sh_y[r][gg * kWave + col];
+          }
+          if (HAS_Z) {
+            y = __builtin_fmaf(iD[it][q], xv[it][q], y);
+            const float z = zv[it][q];
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+            oz[q] = gv[it][q] * y * (sg * __builtin_fmaf(z, 1.0f - sg, 1.0f));
+          }
+          ox[q] = __builtin_fmaf(dyv[it][q], iD[it][q], dt2v[it][q] * S1);
+          const float ddt = __builtin_fmaf(xv[it][q] * kLog2e, S1, S2);
+          od[q] = ddt * sgv[it][q];
+          dDacc[it][q] = __builtin_fmaf(dyv[it][q], xv[it][q], dDacc[it][q]);
+          dBacc[it][q] += od[q];
+        }
+        const int64_t off = (t0 + r) * Dn + icol[it];
+        store_row<Tg, CW>(static_cast<Tg*>(a.dx) + row0 + off, ox);
+        store_row<Tg, CW>(static_cast<Tg*>(a.ddelta) + row0 + off, od);
+        if (HAS_Z) store_row<Tg, CW>(static_cast<Tg*>(a.dz) + row0 + off, oz);
+      }
+    }
+    // this tile's dB', dC of the block
+    for (int i = tid; i < nt * 2 * kDState; i += NTHR) {
+      const int s = i / (2 * kDState), w = i % (2 * kDState);
+      a.ws_bc[((b * L + t0 + s) * a.nblk + blk) * (2 * kDState) + w] = (&sh_bc[s][0][0])[w];
+    }
+    block_sync();
+    cur = nxt;
+  }
+
+  // per-row parameter gradients and the initial state's gradient
+  if (lane < nvalid) {
+    *reinterpret_cast<float4*>(a.ws_a + (b * Dn + dl) * kDState + g * NS) =
+        make_float4(dAacc[0] * kLn2, dAacc[1] * kLn2, dAacc[2] * kLn2, dAacc[3] * kLn2);
+    if (a.dh0 != nullptr)
+      *reinterpret_cast<float4*>(a.dh0 + (b * Dn + dl) * kDState + g * NS) =
+          make_float4(carry[0], carry[1], carry[2], carry[3]);
+  }
+  // dD and dbias: the items of one channel are summed over rows in row order
+  float* sred = &sh_s1[0][0];  // free after the last tile: [T][64] x 2
+#pragma unroll
+  for (int it = 0; it < IPT; ++it)
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+      sred[irow[it] * kWave + icol[it] + q] = dDacc[it][q];
+      sred[T * kWave + irow[it] * kWave + icol[it] + q] = dBacc[it][q];
+    }
+  block_sync();
+  if (tid < kWave && tid < nvalid) {
+    float sD = 0.0f, sB = 0.0f;
+    for (int r = 0; r < T; ++r) {
+      sD += sred[r * kWave + tid];
+      sB += sred[T * kWave + r * kWave + tid];
+    }
+    a.ws_dd[(b * Dn + d0 + tid) * 2] = sD;
+    a.ws_dd[(b * Dn + d0 + tid) * 2 + 1] = sB;
+  }
+}
+
+// dB, dC: sum the per-block partials in block order (dB also takes the ln 2).
+template <typename Tg>
+__global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(const float* ws_bc, Tg* dB, Tg* dC, int64_t rows,
+                                                            int nblk) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * 2 * kDState) return;
+  const int64_t row = i / (2 * kDState);
+  const int w = (int)(i % (2 * kDState));
+  float acc = 0.0f;
+  for (int k = 0; k < nblk; ++k) acc += ws_bc[(row * nblk + k) * (2 * kDState) + w];
+  Tg* dst = w < kDState ? dB : dC;
+  const float v = w < kDState ? acc * kLn2 : acc;
+  const int64_t o = row * kDState + (w % kDState);
+  if constexpr (sizeof(Tg) == 4) dst[o] = v;
+  else dst[o] = f32_to_bf16_rne(v);
+}
+
+// dA, dD, dbias: sum the per-row partials over the batch in row order.
+__global__ void __launch_bounds__(256) bwd_reduce_params_kernel(const float* ws_a, const float* ws_dd, float* dA,
+                                                                float* dD, float* dbias, int64_t batch,
+                                                                int64_t Dn) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < Dn * kDState) {
+    float acc = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) acc += ws_a[b * Dn * kDState + i];
+    dA[i] = acc;
+  }
+  if (i < Dn) {
+    float sD = 0.0f, sB = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) {
+      sD += ws_dd[(b * Dn + i) * 2];
+      sB += ws_dd[(b * Dn + i) * 2 + 1];
+    }
+    if (dD != nullptr) dD[i] = sD;
+    if (dbias != nullptr) dbias[i] = sB;
+  }
+}
+
+}  // namespace
+
+namespace {
+
+template <typename Tin, typename Tg>
+void launch_scan_bwd_t(const BwdArgs& a, float* dA, void* dB, void* dC, float* dD, float* dbias, hipStream_t s) {
+  const dim3 grid((unsigned)a.nblk, (unsigned)a.batch);
+  if (a.seqlen > 0) {
+    if (a.d_inner % 4 == 0) {
+      if (a.z != nullptr) hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, true, 4>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, false, 4>), grid, dim3(256), 0, s, a);
+    } else {
+      if (a.z != nullptr) hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, true, 1>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, false, 1>), grid, dim3(256), 0, s, a);
+    }
+    const int64_t rows = (int64_t)a.batch * a.seqlen;
+    const int64_t n = rows * 2 * kDState;
+    hipLaunchKernelGGL((bwd_reduce_bc_kernel<Tg>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.ws_bc,
+                       static_cast<Tg*>(dB), static_cast<Tg*>(dC), rows, a.nblk);
+  }
+  const int64_t np = a.d_inner * kDState;
+  hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s, a.ws_a, a.ws_dd,
+                     dA, dD, dbias, (int64_t)a.batch, a.d_inner);
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const BwdArgs& a, DT in, DT grad, float* dA, void* dB, void* dC, float* dD,
+                           float* dbias, hipStream_t s) {
+  if (in == DT::F32 && grad == DT::F32) launch_scan_bwd_t<float, float>(a, dA, dB, dC, dD, dbias, s);
+  else if (in == DT::F32 && grad == DT::BF16) launch_scan_bwd_t<float, uint16_t>(a, dA, dB, dC, dD, dbias, s);
+  else if (in == DT::BF16 && grad == DT::F32) launch_scan_bwd_t<uint16_t, float>(a, dA, dB, dC, dD, dbias, s);
+  else launch_scan_bwd_t<uint16_t, uint16_t>(a, dA, dB, dC, dD, dbias, s);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

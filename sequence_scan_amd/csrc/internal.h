@@ -32,6 +32,7 @@ struct ScanArgs {
   int32_t n_chunks;
   int32_t softplus;
   int32_t batch;
+  int32_t zoh;            // exact zero-order-hold input coefficient
 };
 
 struct DecodeArgs {
@@ -48,6 +49,7 @@ struct DecodeArgs {
   int64_t d_inner;
   int64_t pairs;          // batch * d_inner
   int32_t softplus;
+  int32_t zoh;            // exact zero-order-hold input coefficient
 };
 
 // Causal depthwise conv1d (+ bias, + SiLU) over [batch, seqlen, d_inner].
@@ -96,6 +98,18 @@ constexpr int kBwdTile = 16;  // steps per backward tile (and per checkpoint)
 
 // Launchers; each returns the hipGetLastError() of its launches.
 hipError_t launch_scan(const ScanArgs& a, DT in, DT out, int states_per_wave, hipStream_t s);
+// What launch_scan dispatches to: the kernel instances of one (input dtype,
+// output dtype, input coefficient) each (scan_inst.hip), and the chunk carry
+// pass they share.
+hipError_t launch_scan_f32_f32(const ScanArgs& a, int states_per_wave, hipStream_t s);
+hipError_t launch_scan_f32_bf16(const ScanArgs& a, int states_per_wave, hipStream_t s);
+hipError_t launch_scan_bf16_f32(const ScanArgs& a, int states_per_wave, hipStream_t s);
+hipError_t launch_scan_bf16_bf16(const ScanArgs& a, int states_per_wave, hipStream_t s);
+hipError_t launch_scan_f32_f32_zoh(const ScanArgs& a, int states_per_wave, hipStream_t s);
+hipError_t launch_scan_f32_bf16_zoh(const ScanArgs& a, int states_per_wave, hipStream_t s);
+hipError_t launch_scan_bf16_f32_zoh(const ScanArgs& a, int states_per_wave, hipStream_t s);
+hipError_t launch_scan_bf16_bf16_zoh(const ScanArgs& a, int states_per_wave, hipStream_t s);
+hipError_t launch_carry(const ScanArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, DT in, DT out, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);

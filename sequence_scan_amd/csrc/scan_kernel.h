@@ -1,0 +1,384 @@
+// The chunked selective-scan kernel of libssmscan (template) and its launch
+// templates, included by scan_inst.hip, which the build compiles once per
+// (input dtype, output dtype, input coefficient).
+#ifndef SSMSCAN_SCAN_KERNEL_H
+#define SSMSCAN_SCAN_KERNEL_H
+
+#include "device.h"
+
+namespace ssm {
+namespace {
+
+// The main loop is straight-line code: loads, LDS staging and stores are all
+// unconditional, so the compiler can count outstanding memory operations
+// exactly and wait only for the tile it needs.  (Any conditional load or
+// store inside the loop makes it fall back to draining the whole memory
+// pipeline at every tile.)  To get there:
+//  * the ragged part of the chunk (nsteps % T steps) is peeled off and run
+//    first as one short tile; every later tile is full;
+//  * lanes past the last channel compute the last channel's values, which
+//    are bit-identical, and items past it repeat the last item's work, so
+//    their duplicate stores are benign;
+//  * threads past the B/C staging work stage a duplicate of another thread's
+//    vector (same value, same LDS address);
+//  * two register banks hold the raw inputs of the next two tiles, so each
+//    thread keeps two tiles of HBM reads in flight behind its arithmetic; the
+//    prefetch index is clamped to the last tile, so it always reads valid rows.
+//
+// Phases 1 and 3 are elementwise over (step, channel), so they use their own
+// thread mapping: with WIDE, thread item (row r, chunk c) covers CW
+// consecutive channels of one step, read and written with 16-byte accesses
+// (1 KiB per wavefront instruction); without WIDE (d_inner not a multiple of
+// 8), CW = 1 and an item is one channel.  Phase 2 keeps lane = channel.
+//
+// ZOH selects the exact zero-order-hold input coefficient: per state the
+// update adds zoh_ratio(a) * (dt2 x) * B with a = exp2(dt2 A), which is
+// (e^{dt A} - 1) / A * x * B (B is then staged without the ln 2 factor).
+template <typename Tin, typename Tout, int NS, bool PASS_A, bool HAS_Z, bool WIDE, bool ZOH>
+__global__ void __launch_bounds__(kWave * (kDState / NS))
+scan_chunk_kernel(ScanArgs a) {
+  constexpr int G = kDState / NS;         // wavefronts per workgroup (state groups)
+  constexpr int T = Tile<G>::T;           // time steps per tile
+  constexpr int NTHR = kWave * G;
+  constexpr int CW = WIDE ? Tile<G>::CW : 1;   // channels per item
+  constexpr int CPR = kWave / CW;         // items per row
+  constexpr int IPT = T * CPR / NTHR;     // items per thread
+  static_assert(IPT >= 1 && IPT * NTHR == T * CPR, "tile does not split evenly");
+  constexpr int EPV = Vec16<Tin>::kElems; // B/C elements per 16-byte vector
+  constexpr int VPR = kDState / EPV;      // 16-byte vectors per B or C row
+  constexpr int BC_VECS = (PASS_A ? 1 : 2) * T * VPR;
+  constexpr int BC_R = (BC_VECS + NTHR - 1) / NTHR;
+  constexpr bool kZ = HAS_Z && !PASS_A;
+  using R = Raw<Tin, CW>;
+
+  // Rows are padded by one element: the prologue/epilogue items (CW
+  // consecutive channels per thread, 64 / CW threads per row) then spread
+  // over all LDS banks, while lane = channel accesses stay consecutive.
+  __shared__ float2 sh_dtv[T][kWave + 1];             // (dt, dt * x)
+  __shared__ float sh_B[T][kDState];
+  __shared__ float sh_C[PASS_A ? 1 : T][kDState];
+  __shared__ float sh_y[PASS_A ? 1 : T][G * kWave + 1];  // partial readouts, [row][wave][channel]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  // the wave index is uniform across the wave: keep it in a scalar register
+  const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int b = blockIdx.z;
+  const int k = blockIdx.y;
+  const int K = a.n_chunks;
+  const int64_t Dn = a.d_inner;
+  const int64_t L = a.seqlen;
+  const int64_t d0 = (int64_t)blockIdx.x * kWave;
+  const int nvalid = (int)min((int64_t)kWave, Dn - d0);   // channels of this block
+  // phase 2: lanes past the last channel take the last channel's place
+  const int loff = min(lane, nvalid - 1);
+  const int64_t dl = d0 + loff;
+  const int64_t t_begin = (int64_t)k * a.chunk_len;
+  const int64_t t_end = min(t_begin + a.chunk_len, L);
+  const bool softplus = a.softplus != 0;
+  const bool has_D = a.D != nullptr;
+
+  float Ad[NS];  // this lane's A[d, n]; step sizes are in log2 units (dt2)
+#pragma unroll
+  for (int i = 0; i < NS; ++i) Ad[i] = a.A[dl * kDState + g * NS + i];
+
+  // phases 1 and 3: this thread's items (row, first channel), fixed for the kernel
+  int irow[IPT], icol[IPT];
+  float ibias[IPT][CW], iD[IPT][CW];  // bias in log2 units, D
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int idx = tid + it * NTHR;
+    irow[it] = idx / CPR;
+    icol[it] = min(idx % CPR, (nvalid + CW - 1) / CW - 1) * CW;  // clamp to the last valid item
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+      const int64_t dq = d0 + min(icol[it] + q, nvalid - 1);
+      ibias[it][q] = a.bias != nullptr ? a.bias[dq] * kLog2e : 0.0f;
+      iD[it][q] = has_D ? a.D[dq] : 0.0f;
+    }
+  }
+
+  float h[NS];
+  if (!PASS_A && k > 0) {
+    const float* src = a.ws_state + (((int64_t)b * K + (k - 1)) * Dn + dl) * kDState + g * NS;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) h[i] = src[i];
+  } else if (k == 0 && a.h0 != nullptr) {  // continuing from a stored state
+    const float* src = a.h0 + ((int64_t)b * Dn + dl) * kDState + g * NS;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) h[i] = src[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) h[i] = 0.0f;
+  }
+  float dtsum = 0.0f;
+
+  // Row pointers of this chunk: element (t_begin + tt, d0) of batch row b.
+  const int64_t base_e = ((int64_t)b * L + t_begin) * Dn + d0;
+  const Tin* xb = static_cast<const Tin*>(a.x) + base_e;
+  const Tin* db = static_cast<const Tin*>(a.delta) + base_e;
+  const Tin* zb = kZ ? static_cast<const Tin*>(a.z) + base_e : nullptr;
+  Tout* ob = PASS_A ? nullptr : static_cast<Tout*>(a.out) + base_e;
+  const Tin* Bb = static_cast<const Tin*>(a.B) + ((int64_t)b * L + t_begin) * kDState;
+  const Tin* Cb = static_cast<const Tin*>(a.C) + ((int64_t)b * L + t_begin) * kDState;
+
+  struct Bank {
+    R rx[IPT], rdt[IPT], rz[IPT];
+    uint4 rbc[BC_R];
+  };
+  Bank bk0, bk1;
+  float xs[IPT][CW];    // x of the tile being finished
+  R zs[IPT];            // raw z of the tile being finished
+
+  // Issue the loads of the tile at chunk-relative step tt0 with nt valid steps
+  // (rows past nt re-read the last valid row).
+  auto issue = [&](Bank& bk, int64_t tt0, int nt) SSM_INLINE {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int64_t off = (tt0 + min(irow[it], nt - 1)) * Dn + icol[it];
+      bk.rx[it].load(xb + off);
+      bk.rdt[it].load(db + off);
+      if (kZ) bk.rz[it].load(zb + off);
+    }
+#pragma unroll
+    for (int r = 0; r < BC_R; ++r) {
+      const int v = (tid + r * NTHR) % BC_VECS;
+      const int which = v / (T * VPR);
+      const int w = v - which * (T * VPR);
+      const int row = min(w / VPR, nt - 1);
+      const int part = w % VPR;
+      const Tin* src = (which ? Cb : Bb) + (tt0 + row) * kDState + part * EPV;
+      bk.rbc[r] = *reinterpret_cast<const uint4*>(src);
+    }
+  };
+
+  // Phase 1: discretise this thread's items into LDS as (dt2, dt2 * x), the
+  // step size in log2 units and the input term's factor (the ln 2 that
+  // dt2 * x carries is folded into the staged B rows); stage B/C rows as
+  // fp32.  The softplus switch is taken once per tile (a uniform branch
+  // around the whole item loop), never per element.
+  auto discretise = [&](Bank& bk, auto sp_c) SSM_INLINE {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        const float x = bk.rx[it].get(q);
+        const float u2 = __builtin_fmaf(bk.rdt[it].get(q), kLog2e, ibias[it][q]);
+        const float dt2 = decltype(sp_c)::value ? softplus2_f(u2) : u2;
+        sh_dtv[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * x);
+        xs[it][q] = x;
+      }
+    }
+  };
+  auto commit = [&](Bank& bk) SSM_INLINE {
+    if (softplus) discretise(bk, std::true_type());
+    else discretise(bk, std::false_type());
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      if (kZ) zs[it] = bk.rz[it];
+    }
+#pragma unroll
+    for (int r = 0; r < BC_R; ++r) {
+      const int v = (tid + r * NTHR) % BC_VECS;
+      const int which = v / (T * VPR);
+      const int w = v - which * (T * VPR);
+      const int row = w / VPR;
+      const int part = w % VPR;
+      float f[EPV];
+      Vec16<Tin>::unpack(bk.rbc[r], f);
+      float* dst = which ? &sh_C[PASS_A ? 0 : row][part * EPV] : &sh_B[row][part * EPV];
+      // B carries the ln 2 of dt2 * x; with ZOH, zoh_ratio carries it
+      const float scale = (which || ZOH) ? 1.0f : kLn2;
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) dst[i] = f[i] * scale;
+    }
+  };
+
+  // Phase 2: the recurrence for this wave's NS states over steps [0, n).
+  // Software-pipelined by one step: the transitions exp(dt * A) of step s + 1
+  // (and with ZOH their input ratios) do not depend on the state, so they are
+  // computed while step s updates it, which keeps each exp's latency off the
+  // h dependency chain.
+  constexpr int NR = ZOH ? NS : 1;
+  auto run_steps = [&](auto n_c) SSM_INLINE {
+    const int n = n_c;
+    float2 v = sh_dtv[0][loff];
+    float ar[NS], rr[NR];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const float u2 = v.x * Ad[i];
+      ar[i] = __builtin_amdgcn_exp2f(u2);
+      if constexpr (ZOH) rr[i] = zoh_ratio(ar[i], u2);
+    }
+#pragma unroll
+    for (int s = 0; s < n; ++s) {
+      float2 vn = v;
+      float an[NS], rn[NR];
+      if (s + 1 < n) {
+        vn = sh_dtv[s + 1][loff];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const float u2 = vn.x * Ad[i];
+          an[i] = __builtin_amdgcn_exp2f(u2);
+          if constexpr (ZOH) rn[i] = zoh_ratio(an[i], u2);
+        }
+      }
+      float y = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const float in = v.y * sh_B[s][g * NS + i];
+        if constexpr (ZOH) h[i] = __builtin_fmaf(ar[i], h[i], rr[i] * in);
+        else h[i] = __builtin_fmaf(ar[i], h[i], in);
+        if (!PASS_A) y = __builtin_fmaf(sh_C[PASS_A ? 0 : s][g * NS + i], h[i], y);
+      }
+      if (PASS_A) {
+        dtsum += v.x;
+      } else {
+        sh_y[PASS_A ? 0 : s][(PASS_A ? 0 : g) * kWave + lane] = y;
+      }
+      if (s + 1 < n) {
+        v = vn;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          ar[i] = an[i];
+          if constexpr (ZOH) rr[i] = rn[i];
+        }
+      }
+    }
+  };
+
+  // Phase 3: finish this thread's items into registers: sum the partials in
+  // a fixed order, D skip, gate.  The D switch is taken once per tile.
+  float yv[IPT][CW];
+  auto finish_items = [&](auto d_c) SSM_INLINE {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int r = irow[it];
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        const int col = icol[it] + q;
+        float acc = sh_y[PASS_A ? 0 : r][col];
+#pragma unroll
+        for (int gg = 1; gg < G; ++gg) acc += sh_y[PASS_A ? 0 : r][(PASS_A ? 0 : gg) * kWave + col];
+        if (decltype(d_c)::value) acc = __builtin_fmaf(iD[it][q], xs[it][q], acc);
+        if (kZ) acc = acc * silu_f(zs[it].get(q));
+        yv[it][q] = acc;
+      }
+    }
+  };
+  auto finish = [&]() SSM_INLINE {
+    if (has_D) finish_items(std::true_type());
+    else finish_items(std::false_type());
+  };
+  // Store the finished tile that starts at chunk-relative step tt0.  Full
+  // tiles store unconditionally; the peeled ragged tile (full == false)
+  // skips rows past nt.
+  auto store = [&](int64_t tt0, int nt, bool full) SSM_INLINE {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it)
+      if (full || irow[it] < nt) store_row<Tout, CW>(ob + (tt0 + irow[it]) * Dn + icol[it], yv[it]);
+  };
+
+  // A full tile, straight-line.  The outputs of the previous full tile
+  // (at step prev0, when has_prev) are stored only after this tile's inputs
+  // have been committed: the wait for those inputs then never includes the
+  // acknowledgement of stores issued just before it.
+  auto full_tile = [&](Bank& bk, int64_t tt0, int64_t pf0, auto has_prev_c, int64_t prev0) SSM_INLINE {
+    commit(bk);
+    if (!PASS_A && decltype(has_prev_c)::value) store(prev0, T, true);
+    issue(bk, pf0, T);
+    block_sync();
+    run_steps(std::integral_constant<int, T>());
+    block_sync();
+    if (!PASS_A) finish();
+  };
+
+  const int64_t nsteps = t_end - t_begin;
+  const int tail = (int)(nsteps % T);          // the peeled ragged tile
+  const int64_t nfull = nsteps / T;
+  const int64_t last_full = tail + (nfull - 1) * T;   // start of the last full tile
+  if (tail > 0) {
+    issue(bk0, 0, tail);
+    if (nfull > 0) issue(bk1, tail, T);
+    commit(bk0);
+    if (nfull > 1) issue(bk0, tail + T, T);
+    block_sync();
+    run_steps(tail);
+    block_sync();
+    if (!PASS_A) {
+      finish();
+      store(0, tail, false);
+    }
+  } else {
+    if (nfull > 0) issue(bk1, 0, T);
+    if (nfull > 1) issue(bk0, T, T);
+  }
+  // full tiles f = 0, 1, ...: tile f's inputs are in bk1 for even f and bk0
+  // for odd f; each tile prefetches tile f + 2 into the bank it just used and
+  // stores the outputs of tile f - 1
+  if (nfull > 0) {
+    full_tile(bk1, tail, min(tail + 2 * T, last_full), std::false_type(), 0);
+    int64_t f = 1;
+    for (; f + 1 < nfull; f += 2) {
+      const int64_t t0 = tail + f * T;
+      full_tile(bk0, t0, min(t0 + 2 * T, last_full), std::true_type(), t0 - T);
+      full_tile(bk1, t0 + T, min(t0 + 3 * T, last_full), std::true_type(), t0);
+    }
+    if (f < nfull) full_tile(bk0, tail + f * T, last_full, std::true_type(), tail + (f - 1) * T);
+    if (!PASS_A) store(last_full, T, true);
+  }
+
+  if (PASS_A) {
+    float* dst = a.ws_state + (((int64_t)b * K + k) * Dn + dl) * kDState + g * NS;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) dst[i] = h[i];
+    if (g == 0) a.ws_dtsum[((int64_t)b * K + k) * Dn + dl] = dtsum;
+  } else if (k == K - 1 && a.last_state != nullptr) {
+    float* dst = a.last_state + ((int64_t)b * Dn + dl) * kDState + g * NS;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) dst[i] = h[i];
+  }
+}
+
+
+template <typename Tin, typename Tout, int NS, bool WIDE, bool ZOH>
+hipError_t launch_scan_w(const ScanArgs& a, hipStream_t s) {
+  constexpr int G = kDState / NS;
+  const unsigned nblk = (unsigned)((a.d_inner + kWave - 1) / kWave);
+  if (a.n_chunks > 1) {
+    dim3 gridA(nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch);
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, true, false, WIDE, ZOH>), gridA, dim3(kWave * G), 0, s, a);
+    const hipError_t e = launch_carry(a, s);
+    if (e != hipSuccess) return e;
+  }
+  dim3 gridB(nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
+  if (a.z != nullptr)
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, true, WIDE, ZOH>), gridB, dim3(kWave * G), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, false, WIDE, ZOH>), gridB, dim3(kWave * G), 0, s, a);
+  return hipGetLastError();
+}
+
+// The wide prologue/epilogue needs rows that split into aligned groups of 8.
+template <typename Tin, typename Tout, int NS, bool ZOH>
+hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
+  if (a.d_inner % 8 == 0) return launch_scan_w<Tin, Tout, NS, true, ZOH>(a, s);
+  return launch_scan_w<Tin, Tout, NS, false, ZOH>(a, s);
+}
+
+template <typename Tin, typename Tout, bool ZOH>
+hipError_t launch_scan_ns(const ScanArgs& a, int ns, hipStream_t s) {
+  switch (ns) {
+    case 1: return launch_scan_t<Tin, Tout, 1, ZOH>(a, s);
+    case 2: return launch_scan_t<Tin, Tout, 2, ZOH>(a, s);
+    case 4: return launch_scan_t<Tin, Tout, 4, ZOH>(a, s);
+    case 8: return launch_scan_t<Tin, Tout, 8, ZOH>(a, s);
+    case 16: return launch_scan_t<Tin, Tout, 16, ZOH>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+}  // namespace ssm
+
+#endif  // SSMSCAN_SCAN_KERNEL_H

@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_strings():
-    assert ssm.ssm_abi_version() == 3
+    assert ssm.ssm_abi_version() == 4
     for code, name in ssm.STATUS_NAMES.items():
         assert ssm.ssm_status_string(code).startswith(name)
     assert "unknown" in ssm.ssm_status_string(99)
@@ -219,12 +219,13 @@ def test_scan_bwd_rejections():
     base = dict(x=P, delta=P + 0x1000000, A=P + 0x2000000, B=P + 0x3000000, C=P + 0x4000000, D=None, z=None, bias=None,
                 h0=None, dout=P + 0x5000000, dlast=None, dx=P + 0x6000000, ddelta=P + 0x7000000, dA=P + 0x8000000,
                 dB=P + 0x9000000, dC=P + 0xa000000, dD=None, dz=None, dbias=None, dh0=None, batch=2, seqlen=8,
-                d_inner=64, d_state=16, ind=F32, gd=F32)
+                d_inner=64, d_state=16, ind=F32, gd=F32, flags=1)
 
     def bwd(**kw):
         a = dict(base)
         a.update(kw)
-        return lib.ssm_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], 1, a["h0"],
+        return lib.ssm_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["flags"],
+                                a["h0"],
                                 a["dout"], a["dlast"], a["dx"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"],
                                 a["dz"], a["dbias"], a["dh0"], a["batch"], a["seqlen"], a["d_inner"], a["d_state"],
                                 a["ind"], a["gd"], None)
@@ -237,3 +238,23 @@ def test_scan_bwd_rejections():
     assert bwd(dx=P + 0x1000000) == ssm.SSM_ERR_UNSUPPORTED                 # dx over delta
     assert bwd(dB=P + 0x6000000 + 64) == ssm.SSM_ERR_UNSUPPORTED            # two gradients overlap
     assert "overlaps" in ssm.ssm_last_error()
+    for flags in (ssm.SSM_ZOH, ssm.SSM_ZOH | ssm.SSM_SOFTPLUS):             # the backward of ZOH is not defined
+        assert bwd(flags=flags) == ssm.SSM_ERR_UNSUPPORTED
+        assert "SSM_ZOH" in ssm.ssm_last_error()
+    assert bwd(flags=4) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_step_flags():
+    """SSM_SOFTPLUS and SSM_ZOH are the only bits of the step-flags word; valid
+    words pass the checks (shown on empty calls, which enqueue nothing)."""
+    lib = ssm.library()
+    for bad in (4, 8, -1, 1 << 20, 7):
+        assert scan(softplus=bad) == ssm.SSM_ERR_UNSUPPORTED, bad
+        assert "flags" in ssm.ssm_last_error()
+        assert lib.ssm_state_update(P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, P + 0x5000000,
+                                    None, None, None, bad, P + 0x6000000, 4, 64, 16, F32, F32,
+                                    None) == ssm.SSM_ERR_UNSUPPORTED
+    for good in (0, ssm.SSM_SOFTPLUS, ssm.SSM_ZOH, ssm.SSM_SOFTPLUS | ssm.SSM_ZOH):
+        assert scan(softplus=good, batch=0) == ssm.SSM_OK, good
+        assert lib.ssm_state_update(P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, P + 0x5000000,
+                                    None, None, None, good, P + 0x6000000, 0, 64, 16, F32, F32, None) == ssm.SSM_OK
