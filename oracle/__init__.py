@@ -64,6 +64,10 @@ class OracleLib:
         lib.oracle_affine_compose.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64]
         lib.oracle_step_size.restype = None
         lib.oracle_step_size.argtypes = [_dp, _dp, ctypes.c_int, _dp, _i64, _i64]
+        lib.oracle_ssd_fwd.restype = ctypes.c_int
+        lib.oracle_ssd_fwd.argtypes = [_dp] * 8 + [ctypes.c_int] + [_dp] * 3 + [_i64] * 6 + [ctypes.c_int]
+        lib.oracle_ssd_state_update.restype = ctypes.c_int
+        lib.oracle_ssd_state_update.argtypes = [_dp] * 9 + [ctypes.c_int, _dp] + [_i64] * 5
         lib.oracle_abi_version.restype = ctypes.c_int
         self.path = path
         self.lib = lib
@@ -121,6 +125,52 @@ class OracleLib:
                                           int(bool(zoh)), _ptr(out), batch, Dn, N)
         if rc != 0:
             raise ValueError("oracle_state_update rejected its arguments")
+        return out, st
+
+    def ssd_fwd(self, x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, h0=None,
+                nthreads: int | None = None, return_state: bool = True):
+        """Mamba-2 (SSD) scan, sequential fp64, from h0 [batch, nheads, headdim, d_state]
+        (None: zero).  x, z: [batch, L, nheads, headdim]; dt: [batch, L, nheads]; B, C:
+        [batch, L, ngroups, d_state]; A, dt_bias: [nheads]; D: [nheads * headdim].
+        Returns (out [batch, L, nheads, headdim], last_state or None), float64."""
+        x, dt, A, B, C = map(_f64, (x, dt, A, B, C))
+        D, z, dt_bias, h0 = map(_f64, (D, z, dt_bias, h0))
+        if x.ndim != 4 or B.ndim != 4:
+            raise ValueError("x must be [batch, L, nheads, headdim] and B [batch, L, ngroups, d_state]")
+        batch, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        if dt.shape != (batch, L, H) or A.shape != (H,) or B.shape != (batch, L, G, N) or C.shape != B.shape:
+            raise ValueError("bad dt/A/B/C shape")
+        if (z is not None and z.shape != x.shape) or (D is not None and D.shape != (H * P,)):
+            raise ValueError("bad z/D shape")
+        if (dt_bias is not None and dt_bias.shape != (H,)) or (h0 is not None and h0.shape != (batch, H, P, N)):
+            raise ValueError("bad dt_bias/h0 shape")
+        out = np.empty(x.shape, dtype=np.float64)
+        last = np.empty((batch, H, P, N), dtype=np.float64) if return_state else None
+        rc = self.lib.oracle_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                                     int(bool(softplus)), _ptr(h0), _ptr(out), _ptr(last), batch, L, H, P, G, N,
+                                     int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle_ssd_fwd rejected its arguments")
+        return out, last
+
+    def ssd_state_update(self, state, x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True):
+        """One Mamba-2 decode step.  state: [batch, nheads, headdim, d_state]; x, z:
+        [batch, nheads, headdim]; dt: [batch, nheads]; B, C: [batch, ngroups, d_state].
+        Returns (out, new_state) as float64; ``state`` itself is not modified."""
+        st = np.array(state, dtype=np.float64, order="C", copy=True)
+        x, dt, A, B, C = map(_f64, (x, dt, A, B, C))
+        D, z, dt_bias = map(_f64, (D, z, dt_bias))
+        batch, H, P = x.shape
+        G, N = B.shape[1], B.shape[2]
+        if st.shape != (batch, H, P, N) or dt.shape != (batch, H) or C.shape != B.shape:
+            raise ValueError("bad state/dt/B/C shape")
+        out = np.empty(x.shape, dtype=np.float64)
+        rc = self.lib.oracle_ssd_state_update(_ptr(st), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                              _ptr(z), _ptr(dt_bias), int(bool(softplus)), _ptr(out), batch, H, P,
+                                              G, N)
+        if rc != 0:
+            raise ValueError("oracle_ssd_state_update rejected its arguments")
         return out, st
 
     def affine_compose(self, later, earlier):
@@ -248,3 +298,11 @@ def conv1d_update(*args, **kw):
 
 def scan_bwd(*args, **kw):
     return load().scan_bwd(*args, **kw)
+
+
+def ssd_fwd(*args, **kw):
+    return load().ssd_fwd(*args, **kw)
+
+
+def ssd_state_update(*args, **kw):
+    return load().ssd_state_update(*args, **kw)

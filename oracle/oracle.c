@@ -38,6 +38,9 @@
  *    step written first; the chunked mode below joins chunks with it.
  *  - Same page, sections 7 and 14: the decode step is the same recurrence for
  *    one token, continuing from the stored ssm_state [batch, d_inner, d_state].
+ *  - "Mamba и State Space Models", section "Mamba-2: State Space Duality", and
+ *    "Модуль 8", sections 7 and 14: the Mamba-2 form (scalar A per head, state
+ *    [batch, nheads, headdim, d_state]); see the SSD section at the end.
  *  - Same page, sections 4 and 5: the exact zero-order-hold discretisation
  *    holds the input constant over the step, so the input coefficient is the
  *    integral of e^{sA} over s in [0, dt]: (e^{dt A} - 1) / A per diagonal
@@ -53,7 +56,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI 3
+#define ORACLE_ABI 4
 
 int oracle_abi_version(void) { return ORACLE_ABI; }
 
@@ -425,5 +428,133 @@ int oracle_scan_bwd(const double* x, const double* delta, const double* A, const
     }
   free(hs);
   free(dh);
+  return 0;
+}
+
+/* ------------------------------------------------------------- Mamba-2 SSD
+ *
+ * The Mamba-2 form of the same recurrence ("Mamba и State Space Models",
+ * nareshka.ru, section "Mamba-2: State Space Duality": A is one scalar per
+ * head, A = -exp(A_log); "Модуль 8", vladkulikov.com, section 7: with the
+ * transition a_t I the state is h_t = a_t h_{t-1} + B_t x_t and y_t = C_t^T h_t;
+ * section 14: the state is [batch, nheads, headdim, d_state], and the input
+ * term is written dt B x).  Channels are heads x headdim; every channel p of
+ * head h shares the head's step dt[b,t,h], its scalar A[h], and the B/C rows
+ * of the head's group (heads split into ngroups contiguous blocks):
+ *
+ *   for every batch row b, head h, channel p < headdim, from h0 (or zero):
+ *     g   = h / (nheads / ngroups)
+ *     dt  = softplus(dt_in[b,t,h] + dt_bias[h])   (or dt_in + dt_bias)
+ *     for n: s[n] = exp(dt * A[h]) * s[n] + (dt * B[b,t,g,n]) * x[b,t,h,p]
+ *     y   = sum_n C[b,t,g,n] * s[n]  (+ D[h*headdim+p] * x)  (* SiLU(z[b,t,h,p]))
+ *
+ * Layouts: x, z, out [batch, L, nheads, headdim]; dt [batch, L, nheads];
+ * B, C [batch, L, ngroups, N]; A, dt_bias [nheads]; D [nheads * headdim];
+ * h0, last_state [batch, nheads, headdim, N].
+ */
+typedef struct {
+  const double *x, *dt, *A, *B, *C, *D, *z, *bias, *h0;
+  int softplus_on;
+  double *out, *last_state;
+  int64_t batch, L, H, P, G, N;
+  int64_t row_begin, row_end; /* rows are r = (b * H + h) * P + p */
+} ssd_job_t;
+
+static void* ssd_rows(void* arg) {
+  const ssd_job_t* j = (const ssd_job_t*)arg;
+  double* s = (double*)calloc((size_t)j->N, sizeof(double));
+  for (int64_t r = j->row_begin; r < j->row_end; ++r) {
+    const int64_t p = r % j->P, h = (r / j->P) % j->H, b = r / (j->P * j->H);
+    const int64_t g = h / (j->H / j->G);
+    const int64_t ch = h * j->P + p; /* channel index within a step */
+    for (int64_t n = 0; n < j->N; ++n) s[n] = j->h0 ? j->h0[r * j->N + n] : 0.0;
+    for (int64_t t = 0; t < j->L; ++t) {
+      const int64_t e = (b * j->L + t) * j->H * j->P + ch;
+      const double* Bt = j->B + ((b * j->L + t) * j->G + g) * j->N;
+      const double* Ct = j->C + ((b * j->L + t) * j->G + g) * j->N;
+      const double dt = step_size(j->dt[(b * j->L + t) * j->H + h], j->bias, h, j->softplus_on);
+      const double a = exp(dt * j->A[h]);
+      const double x = j->x[e];
+      double y = 0.0;
+      for (int64_t n = 0; n < j->N; ++n) {
+        s[n] = a * s[n] + (dt * Bt[n]) * x;
+        y += Ct[n] * s[n];
+      }
+      if (j->D) y += j->D[ch] * x;
+      if (j->z) y *= silu(j->z[e]);
+      j->out[e] = y;
+    }
+    if (j->last_state)
+      for (int64_t n = 0; n < j->N; ++n) j->last_state[r * j->N + n] = s[n];
+  }
+  free(s);
+  return NULL;
+}
+
+int oracle_ssd_fwd(const double* x, const double* dt, const double* A, const double* B, const double* C,
+                   const double* D, const double* z, const double* dt_bias, int softplus_on, const double* h0,
+                   double* out, double* last_state, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t G,
+                   int64_t N, int nthreads) {
+  if (!x || !dt || !A || !B || !C || !out) return -1;
+  if (batch < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G != 0) return -1;
+  const int64_t rows = batch * H * P;
+  if (L == 0) {
+    if (last_state) {
+      if (h0) memcpy(last_state, h0, sizeof(double) * (size_t)(rows * N));
+      else memset(last_state, 0, sizeof(double) * (size_t)(rows * N));
+    }
+    return 0;
+  }
+  if (rows == 0) return 0;
+  ssd_job_t base = {x, dt, A, B, C, D, z, dt_bias, h0, softplus_on, out, last_state, batch, L, H, P, G, N, 0, rows};
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > rows) nthreads = (int)rows;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  ssd_job_t* jobs = (ssd_job_t*)malloc(sizeof(ssd_job_t) * (size_t)nthreads);
+  int started = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = base;
+    jobs[i].row_begin = rows * i / nthreads;
+    jobs[i].row_end = rows * (i + 1) / nthreads;
+  }
+  for (int i = 0; i < nthreads; ++i) {
+    if (pthread_create(&th[i], NULL, ssd_rows, &jobs[i]) != 0) break;
+    ++started;
+  }
+  for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+  for (int i = started; i < nthreads; ++i) ssd_rows(&jobs[i]);
+  free(th);
+  free(jobs);
+  return 0;
+}
+
+/* One decode step of the Mamba-2 form: state [batch, H, P, N] is read and
+ * overwritten; x, z, out [batch, H, P]; dt [batch, H]; B, C [batch, G, N]. */
+int oracle_ssd_state_update(double* state, const double* x, const double* dt, const double* A,
+                            const double* B, const double* C, const double* D, const double* z,
+                            const double* dt_bias, int softplus_on, double* out, int64_t batch, int64_t H,
+                            int64_t P, int64_t G, int64_t N) {
+  if (!state || !x || !dt || !A || !B || !C || !out) return -1;
+  if (batch < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G != 0) return -1;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t g = h / (H / G);
+      const double d = step_size(dt[b * H + h], dt_bias, h, softplus_on);
+      const double a = exp(d * A[h]);
+      const double* Bt = B + (b * G + g) * N;
+      const double* Ct = C + (b * G + g) * N;
+      for (int64_t p = 0; p < P; ++p) {
+        const int64_t e = (b * H + h) * P + p;
+        double* s = state + e * N;
+        double y = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          s[n] = a * s[n] + (d * Bt[n]) * x[e];
+          y += Ct[n] * s[n];
+        }
+        if (D) y += D[h * P + p] * x[e];
+        if (z) y *= silu(z[e]);
+        out[e] = y;
+      }
+    }
   return 0;
 }

@@ -29,6 +29,13 @@ Sources of the statements:
     continued from both.
   * The pages give no gradients; the backward is pinned to the forward by
     central finite differences.
+  * Mamba-2 ("Mamba и State Space Models", "Mamba-2: State Space Duality";
+    "Модуль 8", section 7): with a scalar transition per head, one operator
+    has three forms, the recurrence, the semi-separable matrix
+    M_ij = C_i^T B_j prod_{r=j+1..i} a_r, and the chunked matrix form that
+    works inside chunks with matrix products and passes the state between
+    them; with one B/C group it is the Mamba-1 scan with A and dt repeated
+    over a head's channels.
   * "Модуль 8", sections 4 and 5: the exact zero-order-hold coefficient is the
     integral of e^{sA} over the step, with the limit dt at A = 0, and the
     page's worked example (tests/golden/zoh_worked_example.txt); holding the
@@ -585,11 +592,141 @@ def pin_zoh_integral_definition(orc):
         assert abs(h[i, 0, 5] - dt) <= 1e-11 * dt, "continuity at A -> 0"
 
 
+def _ssd_case(rng, batch, L, H, P, G, N):
+    return dict(
+        x=rng.standard_normal((batch, L, H, P)),
+        dt=rng.uniform(-4.0, 0.5, (batch, L, H)),
+        A=-np.exp(rng.uniform(-1.0, 1.5, H)),
+        B=rng.standard_normal((batch, L, G, N)),
+        C=rng.standard_normal((batch, L, G, N)),
+        D=rng.standard_normal(H * P),
+        z=rng.standard_normal((batch, L, H, P)),
+        dt_bias=rng.uniform(-1.0, 1.0, H),
+    )
+
+
+def pin_ssd_semiseparable(orc):
+    """The Mamba-2 scan is multiplication by the semi-separable matrix
+    M_ij = C_i^T B_j prod_{r=j+1..i} a_r (a_r = exp(dt_r A_h)) applied to dt x, plus
+    the initial state's decay C_i^T prod_{r<=i} a_r h0, the D skip and the gate:
+    brute force over (i, j) with numpy, per batch row and head, groups included."""
+    rng = np.random.default_rng(71)
+    batch, L, H, P, G, N = 2, 9, 4, 3, 2, 5
+    c = _ssd_case(rng, batch, L, H, P, G, N)
+    h0 = rng.standard_normal((batch, H, P, N))
+    dt = _softplus(c["dt"] + c["dt_bias"][None, None, :])          # [b, t, h]
+    ref = np.zeros((batch, L, H, P))
+    ref_last = np.zeros((batch, H, P, N))
+    for b in range(batch):
+        for h in range(H):
+            g = h // (H // G)
+            a = np.exp(dt[b, :, h] * c["A"][h])
+            Bm, Cm = c["B"][b, :, g], c["C"][b, :, g]                # [L, N]
+            M = np.zeros((L, L))
+            for i in range(L):
+                for j in range(i + 1):
+                    M[i, j] = (Cm[i] @ Bm[j]) * np.prod(a[j + 1:i + 1])
+            u = dt[b, :, h, None] * c["x"][b, :, h]                   # [L, P]
+            decay0 = np.array([np.prod(a[:i + 1]) for i in range(L)])
+            y = M @ u + decay0[:, None] * (Cm @ h0[b, h].T)
+            y = y + c["D"][h * P:(h + 1) * P][None, :] * c["x"][b, :, h]
+            ref[b, :, h] = y * _silu(c["z"][b, :, h])
+            # final state: sum_j prod_{r>j} a_r dt_j x_j B_j^T, plus the decayed h0
+            w = np.array([np.prod(a[j + 1:]) for j in range(L)])
+            ref_last[b, h] = (u * w[:, None]).T @ Bm + np.prod(a) * h0[b, h]
+    out, last = orc.ssd_fwd(**c, h0=h0)
+    _close(out, ref, 1e-12, "SSD against the semi-separable matrix")
+    _close(last, ref_last, 1e-12, "SSD final state")
+
+
+def _ssd_chunked(c, h0, Q):
+    """The chunked matrix form in numpy: inside a chunk, Y = (L o C B^T) (dt x) with
+    L_ij = exp(s_i - s_j) for j <= i (s = cumulative dt A within the chunk), plus the
+    incoming state read out with decay exp(s_i); the state passed to the next chunk
+    is exp(s_end) state + sum_j exp(s_end - s_j) dt_j x_j B_j^T."""
+    batch, L, H, P = c["x"].shape
+    G = c["B"].shape[2]
+    dt = _softplus(c["dt"] + c["dt_bias"][None, None, :])
+    out = np.zeros((batch, L, H, P))
+    last = np.zeros_like(h0)
+    for b in range(batch):
+        for h in range(H):
+            g = h // (H // G)
+            S = h0[b, h].copy()                                      # [P, N]
+            for t0 in range(0, L, Q):
+                t1 = min(t0 + Q, L)
+                d = dt[b, t0:t1, h]
+                s = np.cumsum(d * c["A"][h])
+                Bm, Cm = c["B"][b, t0:t1, g], c["C"][b, t0:t1, g]
+                X = c["x"][b, t0:t1, h]
+                Lm = np.tril(np.exp(s[:, None] - s[None, :]))
+                y = (Lm * (Cm @ Bm.T)) @ (d[:, None] * X) + np.exp(s)[:, None] * (Cm @ S.T)
+                S = np.exp(s[-1]) * S + (np.exp(s[-1] - s)[:, None] * d[:, None] * X).T @ Bm
+                y = y + c["D"][h * P:(h + 1) * P][None, :] * X
+                out[b, t0:t1, h] = y * _silu(c["z"][b, t0:t1, h])
+            last[b, h] = S
+    return out, last
+
+
+def pin_ssd_chunked_matrix_form(orc):
+    """The chunked matrix form (matrix products inside chunks, the state passed
+    between them) equals the recurrence for chunk lengths that do and do not
+    divide L."""
+    rng = np.random.default_rng(73)
+    batch, L, H, P, G, N = 2, 13, 4, 3, 1, 6
+    c = _ssd_case(rng, batch, L, H, P, G, N)
+    h0 = rng.standard_normal((batch, H, P, N))
+    out, last = orc.ssd_fwd(**c, h0=h0)
+    for Q in (1, 3, 4, L, L + 2):
+        ref, ref_last = _ssd_chunked(c, h0, Q)
+        _close(out, ref, 1e-12, f"chunked form Q={Q}")
+        _close(last, ref_last, 1e-12, f"chunked form state Q={Q}")
+
+
+def pin_ssd_is_mamba1_with_shared_parameters(orc):
+    """With one B/C group, the Mamba-2 scan is the Mamba-1 scan over heads x headdim
+    channels with A[d, n] = A[head] and the head's dt on every channel, bitwise."""
+    rng = np.random.default_rng(75)
+    batch, L, H, P, N = 2, 11, 3, 4, 5
+    c = _ssd_case(rng, batch, L, H, P, 1, N)
+    h0 = rng.standard_normal((batch, H, P, N))
+    out, last = orc.ssd_fwd(**c, h0=h0)
+    Dn = H * P
+    ref, ref_last = orc.scan_fwd(
+        c["x"].reshape(batch, L, Dn), np.repeat(c["dt"], P, axis=2), np.repeat(c["A"], P)[:, None] * np.ones((1, N)),
+        c["B"][:, :, 0], c["C"][:, :, 0], c["D"], c["z"].reshape(batch, L, Dn), np.repeat(c["dt_bias"], P),
+        h0=h0.reshape(batch, Dn, N))
+    assert np.array_equal(out.reshape(batch, L, Dn), ref), "SSD differs from the Mamba-1 scan"
+    assert np.array_equal(last.reshape(batch, Dn, N), ref_last), "SSD final state differs"
+
+
+def pin_ssd_decode_and_continuation(orc):
+    """L Mamba-2 decode steps reproduce one scan bitwise, and scanning L1 steps then
+    L2 from the stored state is one scan of L1 + L2 steps."""
+    rng = np.random.default_rng(77)
+    batch, L, H, P, G, N = 2, 10, 4, 3, 2, 5
+    c = _ssd_case(rng, batch, L, H, P, G, N)
+    ref, ref_last = orc.ssd_fwd(**c)
+    st = np.zeros((batch, H, P, N))
+    for t in range(L):
+        y, st = orc.ssd_state_update(st, c["x"][:, t], c["dt"][:, t], c["A"], c["B"][:, t], c["C"][:, t], c["D"],
+                                     c["z"][:, t], c["dt_bias"])
+        assert np.array_equal(y, ref[:, t]), f"SSD decode step {t} differs from the scan"
+    assert np.array_equal(st, ref_last)
+    L1 = 4
+    cut = ("x", "dt", "z", "B", "C")
+    o1, h1 = orc.ssd_fwd(**{k: (v[:, :L1] if k in cut else v) for k, v in c.items()})
+    o2, h2 = orc.ssd_fwd(**{k: (v[:, L1:] if k in cut else v) for k, v in c.items()}, h0=h1)
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), ref)
+    assert np.array_equal(h2, ref_last)
+
+
 ALL_PINS = [
     pin_affine_worked_example, pin_step_size, pin_lti_convolution, pin_semiseparable, pin_delta_zero,
     pin_impulse_closed_form, pin_chunked_composition, pin_decode_equals_scan, pin_invariants,
     pin_decay, pin_nan_propagation, pin_optional_inputs, pin_initial_state_free_response,
     pin_initial_state_continuation, pin_conv1d_numpy, pin_conv1d_impulse, pin_conv1d_decode_and_continuation,
     pin_backward_finite_differences, pin_zoh_worked_example, pin_zoh_held_input_is_exact,
-    pin_zoh_integral_definition,
+    pin_zoh_integral_definition, pin_ssd_semiseparable, pin_ssd_chunked_matrix_form,
+    pin_ssd_is_mamba1_with_shared_parameters, pin_ssd_decode_and_continuation,
 ]

@@ -71,6 +71,16 @@ MUTANTS = {
     "zoh_chunked_pass1": ("Ek[n] = a * Ek[n] + (input_coef(dt, A_d[n], j->zoh) * Bt[n]) * j->x[e];",
                           "Ek[n] = a * Ek[n] + (dt * Bt[n]) * j->x[e];"),
     "zoh_decode_ignored": ("out[e] = scan_step(state + e * N, x[e], dt, zoh,", "out[e] = scan_step(state + e * N, x[e], dt, 0,"),
+    "ssd_group_index": ("const int64_t g = h / (j->H / j->G);", "const int64_t g = h % j->G;"),
+    "ssd_A_of_group": ("const double a = exp(dt * j->A[h]);", "const double a = exp(dt * j->A[g]);"),
+    "ssd_dt_of_channel": ("step_size(j->dt[(b * j->L + t) * j->H + h]", "step_size(j->dt[(b * j->L + t) * j->H + ch % j->H]"),
+    "ssd_D_per_head": ("if (j->D) y += j->D[ch] * x;", "if (j->D) y += j->D[h] * x;"),
+    "ssd_state_transposed": ("j->last_state[r * j->N + n] = s[n];",
+                             "j->last_state[((r / j->P) * j->N + n) * j->P + r % j->P] = s[n];"),
+    "ssd_readout_before_update": ("        s[n] = a * s[n] + (dt * Bt[n]) * x;\n        y += Ct[n] * s[n];",
+                                  "        y += Ct[n] * s[n];\n        s[n] = a * s[n] + (dt * Bt[n]) * x;"),
+    "ssd_h0_ignored": ("s[n] = j->h0 ? j->h0[r * j->N + n] : 0.0;", "s[n] = 0.0;"),
+    "ssd_decode_group": ("      const int64_t g = h / (H / G);\n      const double d", "      const int64_t g = h % G;\n      const double d"),
     "conv_state_out_oldest_last": ("state_out[(b * Dn + d) * K + k] = conv_input(x, state_in, b, L - K + k, d, L, Dn, K);",
                                    "state_out[(b * Dn + d) * K + k] = conv_input(x, state_in, b, L - 1 - k, d, L, Dn, K);"),
 }
