@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 /*
  * Bits of the step-flags argument (named `softplus` in the calls below):
@@ -243,6 +243,57 @@ ssm_status ssm_conv1d_fwd(const void* x, const float* weight, const float* bias,
 ssm_status ssm_conv1d_update(void* conv_state, const void* x, const float* weight, const float* bias,
                              int silu, void* out, int64_t batch, int64_t d_inner, int64_t d_conv,
                              ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream);
+
+/*
+ * Mamba-2 (SSD) form of the scan (page "Mamba и State Space Models",
+ * nareshka.ru, section "Mamba-2: State Space Duality": A is one scalar per
+ * head; page "Модуль 8. Альтернативы Transformer", vladkulikov.com, section 7:
+ * with the transition a_t I the scan is the semi-separable matrix
+ * M_ij = C_i^T B_j prod_{r=j+1..i} a_r applied to dt x, computed chunk by chunk
+ * with matrix products and the state passed between chunks; section 14: the
+ * state is [batch, nheads, headdim, d_state] and the input term is dt B x).
+ * Channels are heads x headdim; the heads are split into ngroups contiguous
+ * blocks that share B and C:
+ *
+ *   for batch row b, head h (group g = h / (nheads / ngroups)), channel p:
+ *     dt  = softplus(dt_in[b,t,h] + dt_bias[h])   (or dt_in + dt_bias)
+ *     s[p,n] = exp(dt * A[h]) * s[p,n] + dt * B[b,t,g,n] * x[b,t,h,p]
+ *     out[b,t,h,p] = (sum_n C[b,t,g,n] s[p,n] + D[h*headdim + p] x) * SiLU(z)
+ *
+ * Layouts (row-major, last index fastest):
+ *   x, z, out             : [batch, seqlen, nheads, headdim]
+ *   dt                    : [batch, seqlen, nheads]
+ *   B, C                  : [batch, seqlen, ngroups, d_state]
+ *   A, dt_bias            : [nheads] fp32;  D: [nheads * headdim] fp32
+ *   initial/last_state    : [batch, nheads, headdim, d_state] fp32
+ * Supported: in_dtype bf16 (x, dt, z, B, C; the chunk products run on bf16
+ * matrix cores with fp32 accumulation), out fp32 or bf16; headdim 64;
+ * d_state 64 or 128; nheads a multiple of ngroups.  softplus: 0 or
+ * SSM_SOFTPLUS.  Optional (NULL): D, z, dt_bias, initial_state (zero),
+ * last_state.  last_state may be the same buffer as initial_state; no other
+ * overlap of an output with anything is allowed.  Every pointer 16-byte
+ * aligned, except dt (element alignment).  The chunk form sums in a
+ * different order than the recurrence:
+ * results agree with it to rounding, not bitwise.
+ */
+ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias, int softplus,
+                       const float* initial_state, void* out, float* last_state, int64_t batch, int64_t seqlen,
+                       int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state, ssm_dtype in_dtype,
+                       ssm_dtype out_dtype, void* stream);
+
+/*
+ * One Mamba-2 decode step for every (b, h, p), continuing from `state`
+ * [batch, nheads, headdim, d_state] fp32, read and overwritten in place
+ * (pages as above; "Модуль 8", section 7: decode is the recurrent step with a
+ * fixed-size state).  x, z, out: [batch, nheads, headdim]; dt: [batch, nheads];
+ * B, C: [batch, ngroups, d_state].  in_dtype fp32 or bf16; any headdim >= 1;
+ * d_state 64 or 128; other rules as for ssm_ssd_fwd.
+ */
+ssm_status ssm_ssd_state_update(float* state, const void* x, const void* dt, const float* A, const void* B,
+                                const void* C, const float* D, const void* z, const float* dt_bias, int softplus,
+                                void* out, int64_t batch, int64_t nheads, int64_t headdim, int64_t ngroups,
+                                int64_t d_state, ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream);
 
 /*
  * The affine-pair operator on its own, for checking the carry pass's combine

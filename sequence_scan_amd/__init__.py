@@ -78,6 +78,12 @@ def _load():
     lib.ssm_state_update.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                      _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp]
     lib.ssm_state_update.restype = ctypes.c_int
+    lib.ssm_ssd_fwd.argtypes = [_vp] * 8 + [ctypes.c_int, _vp, _vp, _vp] + [_i64] * 6 + [ctypes.c_int, ctypes.c_int,
+                                                                                         _vp]
+    lib.ssm_ssd_fwd.restype = ctypes.c_int
+    lib.ssm_ssd_state_update.argtypes = [_vp] * 9 + [ctypes.c_int, _vp] + [_i64] * 5 + [ctypes.c_int, ctypes.c_int,
+                                                                                      _vp]
+    lib.ssm_ssd_state_update.restype = ctypes.c_int
     lib.ssm_scan_plan.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(ssm_plan)]
     lib.ssm_scan_plan.restype = ctypes.c_int
     lib.ssm_affine_exclusive_scan.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp]
@@ -316,3 +322,41 @@ def ssm_affine_exclusive_scan(a, b, out_a=None, out_b=None, stream=None):
     out_b = torch.empty_like(b) if out_b is None else out_b
     _check(_load().ssm_affine_exclusive_scan(_ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b), n, _stream(stream)))
     return out_a, out_b
+
+
+def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True, initial_state=None,
+                out=None, last_state=None, out_dtype=None, stream=None):
+    """Mamba-2 (SSD) scan (see include/ssmscan.h).  x, z: [batch, seqlen, nheads, headdim]
+    (bfloat16); dt: [batch, seqlen, nheads]; B, C: [batch, seqlen, ngroups, d_state]; A,
+    dt_bias: [nheads] and D: [nheads * headdim] (float32); states [batch, nheads, headdim,
+    d_state] float32.  Returns out (allocated if None, dtype ``out_dtype`` or x's)."""
+    import torch
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim] and B [batch, seqlen, ngroups, d_state]")
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, d_state = B.shape[2], B.shape[3]
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(_load().ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                               _flags(softplus, False), _ptr(initial_state), _ptr(out), _ptr(last_state), batch,
+                               seqlen, nheads, headdim, ngroups, d_state, _dtype_code(x), _dtype_code(out),
+                               _stream(stream)))
+    return out
+
+
+def ssm_ssd_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True, out=None,
+                         out_dtype=None, stream=None):
+    """One Mamba-2 decode step; ``state`` [batch, nheads, headdim, d_state] float32 is
+    updated in place.  x, z: [batch, nheads, headdim]; dt: [batch, nheads]; B, C:
+    [batch, ngroups, d_state].  Returns out."""
+    import torch
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [batch, nheads, headdim] and B [batch, ngroups, d_state]")
+    batch, nheads, headdim = x.shape
+    ngroups, d_state = B.shape[1], B.shape[2]
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(_load().ssm_ssd_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                        _ptr(dt_bias), _flags(softplus, False), _ptr(out), batch, nheads, headdim,
+                                        ngroups, d_state, _dtype_code(x), _dtype_code(out), _stream(stream)))
+    return out

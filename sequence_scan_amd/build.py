@@ -37,7 +37,7 @@ def _scan_units():
     return units
 
 
-DEVICE_UNITS = _scan_units() + [(os.path.join(CSRC, f), [], f.split(".")[0]) for f in ("scan.hip", "conv.hip", "bwd.hip")]
+DEVICE_UNITS = _scan_units() + [(os.path.join(CSRC, f), [], f.split(".")[0]) for f in ("scan.hip", "conv.hip", "bwd.hip", "ssd.hip")]
 HOST_UNITS = [(os.path.join(CSRC, "api.cpp"), [], "api")]
 SOURCES = sorted({u[0] for u in DEVICE_UNITS + HOST_UNITS})
 HEADERS = [os.path.join(CSRC, f) for f in ("internal.h", "device.h", "scan_kernel.h")] + [

@@ -59,9 +59,9 @@ bool valid_dtype(ssm_dtype t) { return t == SSM_F32 || t == SSM_BF16; }
 
 ssm::DT to_dt(ssm_dtype t) { return t == SSM_BF16 ? ssm::DT::BF16 : ssm::DT::F32; }
 
-ssm_status check_align(const char* name, const void* p) {
-  if (p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0)
-    return fail(SSM_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+ssm_status check_align(const char* name, const void* p, uintptr_t bytes = 16) {
+  if (p != nullptr && (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "%s is not %d-byte aligned", name, (int)bytes);
   return SSM_OK;
 }
 
@@ -261,6 +261,44 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   }
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Sizes of the Mamba-2 (SSD) calls.
+struct SsdSizes {
+  int64_t elems;   // batch * seqlen * nheads * headdim
+  int64_t steps;   // batch * seqlen * nheads (dt)
+  int64_t bc;      // batch * seqlen * ngroups * d_state
+  int64_t state;   // batch * nheads * headdim * d_state
+};
+
+ssm_status ssd_check(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                     int64_t d_state, ssm_dtype in_dtype, ssm_dtype out_dtype, int flags, bool scan, SsdSizes* sz) {
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || ngroups < 0 || d_state < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "negative size (batch=%lld seqlen=%lld nheads=%lld headdim=%lld ngroups=%lld "
+                "d_state=%lld)", (long long)batch, (long long)seqlen, (long long)nheads, (long long)headdim,
+                (long long)ngroups, (long long)d_state);
+  if (ngroups < 1 || nheads < 1 || nheads % ngroups != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "nheads=%lld must be a positive multiple of ngroups=%lld", (long long)nheads,
+                (long long)ngroups);
+  if (d_state != 64 && d_state != 128)
+    return fail(SSM_ERR_UNSUPPORTED, "d_state=%lld is not supported (64 or 128)", (long long)d_state);
+  if (scan && headdim != 64) return fail(SSM_ERR_UNSUPPORTED, "headdim=%lld is not supported (64)", (long long)headdim);
+  if (!scan && headdim < 1) return fail(SSM_ERR_UNSUPPORTED, "headdim=%lld must be positive", (long long)headdim);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown dtype (in=%d out=%d)", (int)in_dtype, (int)out_dtype);
+  if (scan && in_dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "the SSD scan takes bf16 inputs (its products run on bf16 matrix cores)");
+  if ((flags & ~SSM_SOFTPLUS) != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "step flags %d: the SSD calls take SSM_SOFTPLUS only", flags);
+  int64_t t1, t2, t3;
+  if (!mul_ok(batch, seqlen, &t1) || !mul_ok(t1, nheads, &sz->steps) || !mul_ok(sz->steps, headdim, &sz->elems) ||
+      !mul_ok(sz->elems, 8, &t2) || !mul_ok(t1, ngroups * d_state, &sz->bc) || !mul_ok(batch, nheads, &t2) ||
+      !mul_ok(t2, headdim * d_state, &sz->state) || !mul_ok(sz->state, 8, &t3))
+    return fail(SSM_ERR_BAD_SHAPE, "element count overflows int64");
+  if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch=%lld exceeds 65535", (long long)batch);
+  if (nheads > INT32_MAX || headdim > INT32_MAX || ngroups > INT32_MAX)
+    return fail(SSM_ERR_UNSUPPORTED, "nheads, headdim and ngroups must fit in 32 bits");
+  return SSM_OK;
 }
 
 }  // namespace
@@ -555,6 +593,137 @@ ssm_status ssm_affine_exclusive_scan(const float* a, const float* b, float* out_
   if (n < 0) return fail(SSM_ERR_BAD_SHAPE, "n=%lld is negative", (long long)n);
   if (n > 0 && (!a || !b || !out_a || !out_b)) return fail(SSM_ERR_NULL_ARG, "required pointer is NULL");
   hipError_t e = ssm::launch_affine_exclusive_scan(a, b, out_a, out_b, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias, int softplus,
+                       const float* initial_state, void* out, float* last_state, int64_t batch, int64_t seqlen,
+                       int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state, ssm_dtype in_dtype,
+                       ssm_dtype out_dtype, void* stream) {
+  SsdSizes sz;
+  ssm_status st = ssd_check(batch, seqlen, nheads, headdim, ngroups, d_state, in_dtype, out_dtype, softplus, true,
+                            &sz);
+  if (st != SSM_OK) return st;
+  const bool need_e = sz.elems > 0, need_bc = sz.bc > 0;
+  struct Req { const char* name; const void* p; bool need; };
+  const Req req[] = {{"x", x, need_e}, {"dt", dt, need_e}, {"out", out, need_e}, {"A", A, need_e},
+                     {"B", B, need_bc}, {"C", C, need_bc}};
+  for (const Req& r : req)
+    if (r.need && r.p == nullptr) return fail(SSM_ERR_NULL_ARG, "required pointer %s is NULL", r.name);
+  const void* ptrs[] = {x, A, B, C, D, z, dt_bias, out, last_state, initial_state};
+  const char* names[] = {"x", "A", "B", "C", "D", "z", "dt_bias", "out", "last_state", "initial_state"};
+  for (int i = 0; i < 10; ++i)
+    if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
+  // dt is read one element at a time: element alignment suffices
+  if ((st = check_align("dt", dt, (uintptr_t)esize(in_dtype))) != SSM_OK) return st;
+  const int64_t si = esize(in_dtype), so = esize(out_dtype);
+  const Range ins[] = {
+      range("x", x, sz.elems * si),     range("dt", dt, sz.steps * si),     range("z", z, sz.elems * si),
+      range("B", B, sz.bc * si),        range("C", C, sz.bc * si),          range("A", A, nheads * 4),
+      range("D", D, nheads * headdim * 4), range("dt_bias", dt_bias, nheads * 4),
+  };
+  const Range ro = range("out", out, sz.elems * so);
+  const Range rl = range("last_state", last_state, sz.state * 4);
+  const Range rh = range("initial_state", initial_state, sz.state * 4);
+  for (const Range& r : ins) {
+    if (overlaps(ro, r)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps input %s", r.name);
+    if (overlaps(rl, r)) return fail(SSM_ERR_UNSUPPORTED, "last_state overlaps input %s", r.name);
+  }
+  if (overlaps(ro, rl)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps last_state");
+  if (overlaps(ro, rh)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps initial_state");
+  // each workgroup reads its own slice of the initial state before it writes
+  // the same slice of the final state, so the two may be one buffer
+  const bool in_place = initial_state != nullptr &&
+                        static_cast<const void*>(initial_state) == static_cast<const void*>(last_state);
+  if (!in_place && overlaps(rl, rh)) return fail(SSM_ERR_UNSUPPORTED, "last_state partly overlaps initial_state");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0) return ok();
+  if (seqlen == 0) {
+    if (last_state && !in_place) {
+      hipError_t e = initial_state ? ssm::launch_copy_f32(last_state, initial_state, sz.state, s)
+                                   : ssm::launch_fill_zero(last_state, sz.state, s);
+      if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+  }
+  ssm::SsdArgs a{};
+  a.x = x;
+  a.dt = dt;
+  a.z = z;
+  a.B = B;
+  a.C = C;
+  a.A = A;
+  a.D = D;
+  a.bias = dt_bias;
+  a.h0 = initial_state;
+  a.out = out;
+  a.state = last_state;
+  a.seqlen = seqlen;
+  a.batch = (int32_t)batch;
+  a.nheads = (int32_t)nheads;
+  a.headdim = (int32_t)headdim;
+  a.ngroups = (int32_t)ngroups;
+  a.d_state = (int32_t)d_state;
+  a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
+  hipError_t e = ssm::launch_ssd(a, to_dt(out_dtype), s);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ssm_status ssm_ssd_state_update(float* state, const void* x, const void* dt, const float* A, const void* B,
+                                const void* C, const float* D, const void* z, const float* dt_bias, int softplus,
+                                void* out, int64_t batch, int64_t nheads, int64_t headdim, int64_t ngroups,
+                                int64_t d_state, ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream) {
+  SsdSizes sz;
+  ssm_status st = ssd_check(batch, 1, nheads, headdim, ngroups, d_state, in_dtype, out_dtype, softplus, false, &sz);
+  if (st != SSM_OK) return st;
+  const bool need_e = sz.elems > 0;
+  struct Req { const char* name; const void* p; bool need; };
+  const Req req[] = {{"state", state, need_e}, {"x", x, need_e}, {"dt", dt, need_e}, {"out", out, need_e},
+                     {"A", A, need_e}, {"B", B, need_e}, {"C", C, need_e}};
+  for (const Req& r : req)
+    if (r.need && r.p == nullptr) return fail(SSM_ERR_NULL_ARG, "required pointer %s is NULL", r.name);
+  const void* ptrs[] = {state, x, A, B, C, D, z, dt_bias, out};
+  const char* names[] = {"state", "x", "A", "B", "C", "D", "z", "dt_bias", "out"};
+  for (int i = 0; i < 9; ++i)
+    if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
+  if ((st = check_align("dt", dt, (uintptr_t)esize(in_dtype))) != SSM_OK) return st;
+  const int64_t si = esize(in_dtype), so = esize(out_dtype);
+  const Range ins[] = {
+      range("x", x, sz.elems * si),     range("dt", dt, sz.steps * si),     range("z", z, sz.elems * si),
+      range("B", B, sz.bc * si),        range("C", C, sz.bc * si),          range("A", A, nheads * 4),
+      range("D", D, nheads * headdim * 4), range("dt_bias", dt_bias, nheads * 4),
+  };
+  const Range rs = range("state", state, sz.state * 4);
+  const Range ro = range("out", out, sz.elems * so);
+  for (const Range& r : ins) {
+    if (overlaps(ro, r)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps input %s", r.name);
+    if (overlaps(rs, r)) return fail(SSM_ERR_UNSUPPORTED, "state overlaps input %s", r.name);
+  }
+  if (overlaps(ro, rs)) return fail(SSM_ERR_UNSUPPORTED, "out overlaps state");
+  if (batch == 0) return ok();
+  ssm::SsdArgs a{};
+  a.x = x;
+  a.dt = dt;
+  a.z = z;
+  a.B = B;
+  a.C = C;
+  a.A = A;
+  a.D = D;
+  a.bias = dt_bias;
+  a.out = out;
+  a.state = state;
+  a.seqlen = 1;
+  a.batch = (int32_t)batch;
+  a.nheads = (int32_t)nheads;
+  a.headdim = (int32_t)headdim;
+  a.ngroups = (int32_t)ngroups;
+  a.d_state = (int32_t)d_state;
+  a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
+  hipError_t e = ssm::launch_ssd_update(a, to_dt(in_dtype), to_dt(out_dtype), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -66,6 +66,31 @@ struct ConvArgs {
   int32_t silu;
 };
 
+// The Mamba-2 (SSD) scan and its decode step.  x, z, out: [batch, L, nheads,
+// headdim]; dt: [batch, L, nheads]; B, C: [batch, L, ngroups, d_state]; A,
+// dt_bias: [nheads]; D: [nheads * headdim]; states [batch, nheads, headdim,
+// d_state] fp32.  The decode step uses the same struct with seqlen 1.
+struct SsdArgs {
+  const void* x;
+  const void* dt;
+  const void* z;          // nullable
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* D;         // nullable
+  const float* bias;      // nullable
+  const float* h0;        // nullable (scan only)
+  void* out;
+  float* state;           // scan: last_state (nullable); decode: the state, in place
+  int64_t seqlen;
+  int32_t batch;
+  int32_t nheads;
+  int32_t headdim;
+  int32_t ngroups;
+  int32_t d_state;
+  int32_t softplus;
+};
+
 // Backward of the scan.  Elementwise gradients and dout share one dtype.
 struct BwdArgs {
   const void* x;
@@ -121,6 +146,9 @@ hipError_t launch_conv1d_update(const ConvArgs& a, DT in, DT out, int K, hipStre
 // dC, dD and dbias (dD / dbias may be NULL when the forward had none).
 hipError_t launch_scan_bwd(const BwdArgs& a, DT in, DT grad, float* dA, void* dB, void* dC, float* dD,
                            float* dbias, hipStream_t s);
+// The SSD scan (bf16 inputs, headdim 64, d_state 64 or 128) and decode step.
+hipError_t launch_ssd(const SsdArgs& a, DT out, hipStream_t s);
+hipError_t launch_ssd_update(const SsdArgs& a, DT in, DT out, hipStream_t s);
 hipError_t launch_affine_exclusive_scan(const float* a, const float* b, float* oa, float* ob,
                                         int64_t n, hipStream_t s);
 

@@ -1,0 +1,403 @@
+// gfx950 kernels of libssmscan: the Mamba-2 (SSD) scan in chunked matrix form
+// on MFMA, and its decode step.
+//
+// What is computed (pages: "Mamba и State Space Models", nareshka.ru, section
+// "Mamba-2: State Space Duality": A is one scalar per head; "Модуль 8.
+// Альтернативы Transformer", vladkulikov.com, section 7: with the transition
+// a_t I the operator is the semi-separable matrix M_ij = C_i^T B_j
+// prod_{r=j+1..i} a_r, which can be applied chunk by chunk with matrix
+// products inside a chunk and the state passed between chunks; section 14:
+// the state is [batch, nheads, headdim, d_state] and the input term dt B x):
+//   for head h (group g = h / (nheads / ngroups)), channel p, step t:
+//     dt = softplus(dt_in[b,t,h] + bias[h]);  a = exp(dt A[h])
+//     s[p,n] <- a s[p,n] + dt B[b,t,g,n] x[b,t,h,p]
+//     out[b,t,h,p] = (sum_n C[b,t,g,n] s[p,n] + D[h P + p] x) * silu(z)
+//
+// Chunked form used here, per (batch row, head) and chunk of Q = 64 steps with
+// cumulative log-decay c_i = sum_{r<=i} dt_r A (log2 units, from the chunk start):
+//   G   = C B^T                                   (Q x Q, over d_state)
+//   W   = G o [j <= i] exp(c_i - c_j) dt_j          (causal decay mask)
+//   Y   = diag(exp(c_i)) C S^T + W X              (S: state entering the chunk)
+//   S  <- exp(c_end) S + (X o exp(c_end - c_j) dt_j)^T B
+// Every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  B, C
+// and X are bf16 inputs, exact as operands.  W, the scaled X and the state are
+// computed in fp32 and enter as two bf16 operands, hi = bf16(v) and
+// lo = bf16(v - hi), whose products are summed: about 16 significant bits.
+//
+// Work decomposition (MI355X-first): a workgroup of four wavefronts owns one
+// (batch row, head) and walks its chunks in order, so the state never leaves
+// the chip: it lives in MFMA accumulators (the P x N tile split over the four
+// waves) and is copied to LDS as bf16 hi/lo once per chunk, as an operand of
+// the next chunk's readout.  Each wave owns one 32 x 32 tile of G and of Y and
+// N/64 32 x 32 tiles of the state.  The HBM reads of the next chunk are issued
+// before the current chunk's arithmetic.
+#include "device.h"
+
+namespace ssm {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// 16 bytes as a native vector (HIP's uint4 is a struct, whose copies the
+// compiler routes through private memory here)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kQ = 64;    // steps per chunk
+constexpr int kP = 64;    // channels per head (headdim)
+constexpr int kPad = 8;   // bf16 row padding: 16 bytes
+
+// Row of accumulator register r of lane l in a 32 x 32 MFMA tile (the column
+// is l % 32).
+__device__ __forceinline__ int frag_row(int r, int l) { return (r >> 2) * 8 + (l >> 5) * 4 + (r & 3); }
+
+// Eight consecutive bf16 of a k-contiguous LDS row: one MFMA operand.
+__device__ __forceinline__ bf16x8_t ld_op(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v as a pair of bf16 whose sum carries about 16 significant bits.
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16_rne(v);
+  lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
+}
+
+template <int N, typename Tout>
+__global__ void __launch_bounds__(256) ssd_chunk_kernel(SsdArgs a) {
+  constexpr int NV = N / 32;          // 16-byte vectors of a B or C chunk per thread
+  constexpr int NT = N / 64;          // state tiles per wave
+  constexpr int SN = N + kPad;        // row strides (elements)
+  constexpr int SQ = kQ + kPad;
+  constexpr int SP = kP + kPad;
+  __shared__ uint16_t sC[kQ * SN] __attribute__((aligned(16)));      // C[i][n]
+  __shared__ uint16_t sB[kQ * SN] __attribute__((aligned(16)));      // B[j][n]
+  __shared__ uint16_t sBt[N * SQ] __attribute__((aligned(16)));      // B[j][n] at [n][j]
+  __shared__ uint16_t sXt[kP * SQ] __attribute__((aligned(16)));     // x[j][p] at [p][j]
+  __shared__ uint16_t sXs[2][kP * SQ] __attribute__((aligned(16)));  // scaled x, hi/lo, [p][j]
+  __shared__ uint16_t sW[2][kQ * SQ] __attribute__((aligned(16)));   // W[i][j], hi/lo
+  __shared__ uint16_t sH[2][kP * SN] __attribute__((aligned(16)));   // state S[p][n], hi/lo
+  __shared__ uint16_t sZ[kQ * SP] __attribute__((aligned(16)));      // z[i][p]
+  __shared__ float s_dt[kQ];                                          // step sizes
+  __shared__ float s_cum[kQ];                                         // cumulative log2 decay
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int H = a.nheads;
+  const int G = a.ngroups;
+  const int g = h / (H / G);
+  const int64_t L = a.seqlen;
+  const int64_t xrow = (int64_t)H * kP;     // elements between consecutive steps of x, z, out
+  const int64_t bcrow = (int64_t)G * N;     // ... of B and C
+  const uint16_t* xb = static_cast<const uint16_t*>(a.x) + (int64_t)b * L * xrow + (int64_t)h * kP;
+  const uint16_t* zb = a.z ? static_cast<const uint16_t*>(a.z) + (int64_t)b * L * xrow + (int64_t)h * kP : nullptr;
+  const uint16_t* dtb = static_cast<const uint16_t*>(a.dt) + (int64_t)b * L * H + h;
+  const uint16_t* Bb = static_cast<const uint16_t*>(a.B) + (int64_t)b * L * bcrow + (int64_t)g * N;
+  const uint16_t* Cb = static_cast<const uint16_t*>(a.C) + (int64_t)b * L * bcrow + (int64_t)g * N;
+  Tout* ob = static_cast<Tout*>(a.out) + (int64_t)b * L * xrow + (int64_t)h * kP;
+  const float A2 = a.A[h] * kLog2e;
+  const float bias = a.bias ? a.bias[h] : 0.0f;
+  const bool softplus = a.softplus != 0;
+  const bool has_z = zb != nullptr;
+  const float* Dh = a.D ? a.D + (int64_t)h * kP : nullptr;
+
+  // tiles of this wave
+  const int ib = w >> 1;           // G and Y: row block (steps i)
+  const int cb = w & 1;            // G: column block (steps j); Y: column block (channels p)
+  const int pb = w >> 1;           // state: row block (channels p)
+  const int lr = l & 31, lk = (l >> 5) * 8;
+
+  struct Bank {
+    u32x4_t c[NV], bb[NV], x[2], z[2];
+    uint32_t dt;
+  };
+  Bank bank;
+  auto issue = [&](int64_t t0, int nt) SSM_INLINE {
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      const int v = tid + 256 * r;
+      const int row = min(v / (N / 8), nt - 1);
+      const int c8 = v % (N / 8);
+      bank.c[r] = *reinterpret_cast<const u32x4_t*>(Cb + (t0 + row) * bcrow + c8 * 8);
+      bank.bb[r] = *reinterpret_cast<const u32x4_t*>(Bb + (t0 + row) * bcrow + c8 * 8);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int v = tid + 256 * r;
+      const int row = min(v >> 3, nt - 1);
+      const int c8 = v & 7;
+      bank.x[r] = *reinterpret_cast<const u32x4_t*>(xb + (t0 + row) * xrow + c8 * 8);
+      if (has_z) bank.z[r] = *reinterpret_cast<const u32x4_t*>(zb + (t0 + row) * xrow + c8 * 8);
+    }
+    if (tid < kQ) bank.dt = dtb[(t0 + min(tid, nt - 1)) * H];
+  };
+
+  // Stage the banked chunk into LDS (rows past nt carry x = 0 and dt = 0, so
+  // they change nothing) and form the step sizes and cumulative decay.
+  auto stage = [&](int nt) SSM_INLINE {
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      const int v = tid + 256 * r;
+      const int row = v / (N / 8);
+      const int c8 = v % (N / 8);
+      *reinterpret_cast<u32x4_t*>(&sC[row * SN + c8 * 8]) = bank.c[r];
+      *reinterpret_cast<u32x4_t*>(&sB[row * SN + c8 * 8]) = bank.bb[r];
+      const u32x4_t wv = bank.bb[r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sBt[(c8 * 8 + 2 * e) * SQ + row] = (uint16_t)(wv[e] & 0xffffu);
+        sBt[(c8 * 8 + 2 * e + 1) * SQ + row] = (uint16_t)(wv[e] >> 16);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int v = tid + 256 * r;
+      const int row = v >> 3;
+      const int c8 = v & 7;
+      const bool live = row < nt;
+      const u32x4_t wv = bank.x[r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sXt[(c8 * 8 + 2 * e) * SQ + row] = live ? (uint16_t)(wv[e] & 0xffffu) : (uint16_t)0;
+        sXt[(c8 * 8 + 2 * e + 1) * SQ + row] = live ? (uint16_t)(wv[e] >> 16) : (uint16_t)0;
+      }
+      if (has_z) *reinterpret_cast<u32x4_t*>(&sZ[row * SP + c8 * 8]) = bank.z[r];
+    }
+    if (w == 0) {
+      float d = 0.0f;
+      if (l < nt) {
+        const float u = bf16_to_f32(bank.dt) + bias;
+        d = softplus ? softplus_f(u) : u;
+      }
+      float one = 1.0f, c = d * A2;
+      affine_wave_scan(one, c);  // (1, c) pairs compose to prefix sums of c
+      s_dt[l] = d;
+      s_cum[l] = c;
+    }
+  };
+
+  // state accumulators and the initial state
+  f32x16_t accS[NT];
+#pragma unroll
+  for (int s = 0; s < NT; ++s) {
+    const int nb = cb * NT + s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int p = pb * 32 + frag_row(r, l), n = nb * 32 + lr;
+      accS[s][r] = a.h0 ? a.h0[(((int64_t)b * H + h) * kP + p) * N + n] : 0.0f;
+    }
+  }
+  bool has_state = a.h0 != nullptr;
+  auto write_state = [&]() SSM_INLINE {
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+      const int nb = cb * NT + s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = pb * 32 + frag_row(r, l), n = nb * 32 + lr;
+        uint16_t hi, lo;
+        split_bf16(accS[s][r], hi, lo);
+        sH[0][p * SN + n] = hi;
+        sH[1][p * SN + n] = lo;
+      }
+    }
+  };
+  if (has_state) write_state();
+
+  const int64_t nchunks = (L + kQ - 1) / kQ;
+  issue(0, (int)min((int64_t)kQ, L));
+  for (int64_t ch = 0; ch < nchunks; ++ch) {
+    const int64_t t0 = ch * kQ;
+    const int nt = (int)min((int64_t)kQ, L - t0);
+    stage(nt);
+    if (ch + 1 < nchunks) issue(t0 + kQ, (int)min((int64_t)kQ, L - t0 - kQ));
+    block_sync();
+
+    // Phase 1: W = (C B^T) o decay mask, and the decayed, dt-weighted x.
+    const float c_end = s_cum[kQ - 1];
+    if (cb <= ib) {
+      f32x16_t acc = {};
+#pragma unroll
+      for (int k = 0; k < N / 16; ++k)
+        acc = mfma(ld_op(&sC[(ib * 32 + lr) * SN + 16 * k + lk]), ld_op(&sB[(cb * 32 + lr) * SN + 16 * k + lk]), acc);
+      const int j = cb * 32 + lr;
+      const float cj = s_cum[j], dj = s_dt[j];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = ib * 32 + frag_row(r, l);
+        const float v = j <= i ? acc[r] * __builtin_amdgcn_exp2f(s_cum[i] - cj) * dj : 0.0f;
+        uint16_t hi, lo;
+        split_bf16(v, hi, lo);
+        sW[0][i * SQ + j] = hi;
+        sW[1][i * SQ + j] = lo;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int v = tid + 256 * r;
+      const int p = v >> 3;
+      const int j0 = (v & 7) * 8;
+      const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(&sXt[p * SQ + j0]);
+      u32x4_t hv, lv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint16_t h0, l0, h1, l1;
+        const int j = j0 + 2 * e;
+        split_bf16(bf16_to_f32(wv[e] & 0xffffu) * __builtin_amdgcn_exp2f(c_end - s_cum[j]) * s_dt[j], h0, l0);
+        split_bf16(__uint_as_float(wv[e] & 0xffff0000u) * __builtin_amdgcn_exp2f(c_end - s_cum[j + 1]) * s_dt[j + 1],
+                   h1, l1);
+        hv[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lv[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      *reinterpret_cast<u32x4_t*>(&sXs[0][p * SQ + j0]) = hv;
+      *reinterpret_cast<u32x4_t*>(&sXs[1][p * SQ + j0]) = lv;
+    }
+    block_sync();
+
+    // Phase 2: Y = diag(exp(c_i)) C S^T + W X, then D skip, gate and store;
+    // the state moves to the end of the chunk.
+    {
+      f32x16_t acc = {};
+      if (has_state) {
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k) {
+          const bf16x8_t ca = ld_op(&sC[(ib * 32 + lr) * SN + 16 * k + lk]);
+          acc = mfma(ca, ld_op(&sH[0][(cb * 32 + lr) * SN + 16 * k + lk]), acc);
+          acc = mfma(ca, ld_op(&sH[1][(cb * 32 + lr) * SN + 16 * k + lk]), acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] *= __builtin_amdgcn_exp2f(s_cum[ib * 32 + frag_row(r, l)]);
+      }
+      // W is zero above the diagonal: row block ib needs column blocks 0..ib
+      for (int k = 0; k < 2 * (ib + 1); ++k) {
+        const bf16x8_t xo = ld_op(&sXt[(cb * 32 + lr) * SQ + 16 * k + lk]);
+        acc = mfma(ld_op(&sW[0][(ib * 32 + lr) * SQ + 16 * k + lk]), xo, acc);
+        acc = mfma(ld_op(&sW[1][(ib * 32 + lr) * SQ + 16 * k + lk]), xo, acc);
+      }
+      const int p = cb * 32 + lr;
+      const float Dp = Dh ? Dh[p] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = ib * 32 + frag_row(r, l);
+        float y = acc[r];
+        if (Dh) y = __builtin_fmaf(Dp, bf16_to_f32(sXt[p * SQ + i]), y);
+        if (has_z) y = y * silu_f(bf16_to_f32(sZ[i * SP + p]));
+        if (i < nt) Io<Tout>::store(ob, (t0 + i) * xrow + p, y);
+      }
+    }
+    {
+      const float e_end = __builtin_amdgcn_exp2f(c_end);
+#pragma unroll
+      for (int s = 0; s < NT; ++s) {
+        const int nb = cb * NT + s;
+        f32x16_t acc = accS[s];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] *= e_end;
+#pragma unroll
+        for (int k = 0; k < kQ / 16; ++k) {
+          const bf16x8_t bo = ld_op(&sBt[(nb * 32 + lr) * SQ + 16 * k + lk]);
+          acc = mfma(ld_op(&sXs[0][(pb * 32 + lr) * SQ + 16 * k + lk]), bo, acc);
+          acc = mfma(ld_op(&sXs[1][(pb * 32 + lr) * SQ + 16 * k + lk]), bo, acc);
+        }
+        accS[s] = acc;
+      }
+    }
+    has_state = true;
+    block_sync();
+    if (ch + 1 < nchunks) write_state();
+  }
+
+  if (a.state != nullptr) {
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+      const int nb = cb * NT + s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = pb * 32 + frag_row(r, l), n = nb * 32 + lr;
+        a.state[(((int64_t)b * H + h) * kP + p) * N + n] = accS[s][r];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ decode step
+//
+// One step for every (b, h, p): the state row [N] is read and written once
+// (16 bytes per lane, N / 4 lanes per row), the readout is reduced across
+// those lanes with butterfly shuffles, and the row's first lane finishes y.
+template <typename Tin, typename Tout, int N>
+__global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a, int64_t rows) {
+  constexpr int LPR = N / 4;   // lanes per state row
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / LPR;          // (b * H + h) * P + p
+  const int q = (int)(gid % LPR);
+  if (row >= rows) return;                // whole rows leave together
+  const int P = a.headdim, H = a.nheads, G = a.ngroups;
+  const int64_t bh = row / P;
+  const int p = (int)(row % P);
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const int g = h / (H / G);
+  const float u = ld_in(static_cast<const Tin*>(a.dt) + bh) + (a.bias ? a.bias[h] : 0.0f);
+  const float dt = a.softplus ? softplus_f(u) : u;
+  const float ar = __builtin_amdgcn_exp2f(dt * a.A[h] * kLog2e);
+  const float x = ld_in(static_cast<const Tin*>(a.x) + row);
+  const float dtx = dt * x;
+  float* st = a.state + row * N + 4 * q;
+  float4 s4 = *reinterpret_cast<const float4*>(st);
+  float hs[4] = {s4.x, s4.y, s4.z, s4.w};
+  const int64_t bc = (b * G + g) * N + 4 * q;
+  float y = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float Bv = ld_in(static_cast<const Tin*>(a.B) + bc + i);
+    const float Cv = ld_in(static_cast<const Tin*>(a.C) + bc + i);
+    hs[i] = __builtin_fmaf(ar, hs[i], dtx * Bv);
+    y = __builtin_fmaf(Cv, hs[i], y);
+  }
+  *reinterpret_cast<float4*>(st) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) y += __shfl_xor(y, m, LPR);
+  if (q == 0) {
+    if (a.D) y = __builtin_fmaf(a.D[(int64_t)h * P + p], x, y);
+    if (a.z) y = y * silu_f(ld_in(static_cast<const Tin*>(a.z) + row));
+    Io<Tout>::store(a.out, row, y);
+  }
+}
+
+template <int N>
+void launch_ssd_n(const SsdArgs& a, DT out, hipStream_t s) {
+  const dim3 grid((unsigned)a.nheads, (unsigned)a.batch);
+  if (out == DT::F32) hipLaunchKernelGGL((ssd_chunk_kernel<N, float>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ssd_chunk_kernel<N, uint16_t>), grid, dim3(256), 0, s, a);
+}
+
+template <typename Tin, typename Tout>
+void launch_ssd_update_t(const SsdArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.batch * a.nheads * a.headdim;
+  const int64_t threads = rows * (a.d_state / 4);
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  if (a.d_state == 64) hipLaunchKernelGGL((ssd_update_kernel<Tin, Tout, 64>), dim3(grid), dim3(256), 0, s, a, rows);
+  else hipLaunchKernelGGL((ssd_update_kernel<Tin, Tout, 128>), dim3(grid), dim3(256), 0, s, a, rows);
+}
+
+}  // namespace
+
+hipError_t launch_ssd(const SsdArgs& a, DT out, hipStream_t s) {
+  if (a.d_state == 64) launch_ssd_n<64>(a, out, s);
+  else launch_ssd_n<128>(a, out, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_ssd_update(const SsdArgs& a, DT in, DT out, hipStream_t s) {
+  if (in == DT::F32 && out == DT::F32) launch_ssd_update_t<float, float>(a, s);
+  else if (in == DT::F32 && out == DT::BF16) launch_ssd_update_t<float, uint16_t>(a, s);
+  else if (in == DT::BF16 && out == DT::F32) launch_ssd_update_t<uint16_t, float>(a, s);
+  else launch_ssd_update_t<uint16_t, uint16_t>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -22,13 +22,13 @@ def test_every_declared_function_is_exported():
     names = header_functions()
     assert {"ssm_scan_fwd", "ssm_state_update", "ssm_scan_plan", "ssm_scan_fwd_plan", "ssm_scan_fwd_from",
             "ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_affine_exclusive_scan", "ssm_status_string",
-            "ssm_last_error", "ssm_abi_version"} <= set(names)
+            "ssm_last_error", "ssm_abi_version", "ssm_scan_bwd", "ssm_ssd_fwd", "ssm_ssd_state_update"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssmscan.h but not exported"
 
 
 def test_version_and_strings():
-    assert ssm.ssm_abi_version() == 4
+    assert ssm.ssm_abi_version() == 5
     for code, name in ssm.STATUS_NAMES.items():
         assert ssm.ssm_status_string(code).startswith(name)
     assert "unknown" in ssm.ssm_status_string(99)
@@ -258,3 +258,45 @@ def test_step_flags():
         assert scan(softplus=good, batch=0) == ssm.SSM_OK, good
         assert lib.ssm_state_update(P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, P + 0x5000000,
                                     None, None, None, good, P + 0x6000000, 0, 64, 16, F32, F32, None) == ssm.SSM_OK
+
+
+def test_ssd_rejections():
+    """Host-side checks of the Mamba-2 calls (nothing is enqueued on these paths)."""
+    lib = ssm.library()
+
+    def ssd(**kw):
+        a = dict(x=P, dt=P + 0x1000000, A=P + 0x2000000, B=P + 0x3000000, C=P + 0x4000000, D=None, z=None, bias=None,
+                 flags=1, h0=None, out=P + 0x5000000, last=None, batch=2, seqlen=8, nheads=4, headdim=64, ngroups=2,
+                 d_state=128, ind=BF16, outd=F32)
+        a.update(kw)
+        return lib.ssm_ssd_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["flags"], a["h0"],
+                               a["out"], a["last"], a["batch"], a["seqlen"], a["nheads"], a["headdim"], a["ngroups"],
+                               a["d_state"], a["ind"], a["outd"], None)
+    for k in ("x", "dt", "A", "B", "C", "out"):
+        assert ssd(**{k: None}) == ssm.SSM_ERR_NULL_ARG, k
+    assert ssd(ind=F32) == ssm.SSM_ERR_UNSUPPORTED and "bf16" in ssm.ssm_last_error()
+    assert ssd(headdim=32) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd(d_state=16) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd(ngroups=3) == ssm.SSM_ERR_UNSUPPORTED                         # 4 heads in 3 groups
+    assert ssd(ngroups=0) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd(flags=ssm.SSM_ZOH) == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd(seqlen=-1) == ssm.SSM_ERR_BAD_SHAPE
+    assert ssd(x=P + 8) == ssm.SSM_ERR_UNSUPPORTED and "aligned" in ssm.ssm_last_error()
+    assert ssd(dt=P + 0x1000000 + 1) == ssm.SSM_ERR_UNSUPPORTED               # dt: element alignment
+    assert ssd(dt=P + 0x1000000 + 2, batch=0) == ssm.SSM_OK
+    assert ssd(out=P + 0x1000000) == ssm.SSM_ERR_UNSUPPORTED                 # out on dt
+    assert ssd(last=P + 0x6000000, h0=P + 0x6000000 + 256) == ssm.SSM_ERR_UNSUPPORTED  # partial overlap
+    assert ssd(last=P + 0x6000000, h0=P + 0x6000000, batch=0) == ssm.SSM_OK     # in place is allowed
+    assert ssd(batch=0) == ssm.SSM_OK
+
+    def upd(**kw):
+        a = dict(state=P, x=P + 0x1000000, dt=P + 0x2000000, A=P + 0x3000000, B=P + 0x4000000, C=P + 0x5000000,
+                 out=P + 0x6000000, batch=2, nheads=4, headdim=48, ngroups=1, d_state=64, ind=F32)
+        a.update(kw)
+        return lib.ssm_ssd_state_update(a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"], None, None, None, 1,
+                                        a["out"], a["batch"], a["nheads"], a["headdim"], a["ngroups"], a["d_state"],
+                                        a["ind"], F32, None)
+    assert upd(state=None) == ssm.SSM_ERR_NULL_ARG
+    assert upd(d_state=32) == ssm.SSM_ERR_UNSUPPORTED
+    assert upd(out=P + 64) == ssm.SSM_ERR_UNSUPPORTED                        # out inside the state
+    assert upd(batch=0) == ssm.SSM_OK

@@ -41,10 +41,12 @@ __all__ = [
     "ScanConfig", "DecodeConfig", "SCAN_CONFIGS", "DECODE_CONFIG",
     "scan_inputs", "decode_inputs", "round_to_bf16", "bf16_bits",
     "scan_algorithmic_bytes", "decode_algorithmic_bytes",
+    "SsdConfig", "SSD_CONFIGS", "ssd_inputs", "ssd_initial_state", "ssd_algorithmic_bytes",
 ]
 
 # Tensor ids used as the first spawn key (stable; never renumber).
-_T_BIAS, _T_X, _T_DT, _T_Z, _T_B, _T_C, _T_W, _T_TOK, _T_BETA, _T_A, _T_D, _T_CW, _T_CB, _T_CS, _T_H0 = range(15)
+(_T_BIAS, _T_X, _T_DT, _T_Z, _T_B, _T_C, _T_W, _T_TOK, _T_BETA, _T_A, _T_D, _T_CW, _T_CB, _T_CS, _T_H0,
+ _T_SA, _T_SD) = range(17)
 _BLOCK_ELEMS = 1 << 20
 
 
@@ -85,6 +87,30 @@ SCAN_CONFIGS = {
     "long_dna": ScanConfig("long_dna", 1, 2048, 16, 262144, "bf16", dmin=1e-4, x_kind="dna",
                            description="long-sequence DNA/audio-like scan"),
 }
+
+
+@dataclasses.dataclass(frozen=True)
+class SsdConfig:
+    """A Mamba-2 (SSD) layer: channels = nheads x headdim, B/C in ngroups groups."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    d_state: int
+    dtype: str = "bf16"
+    dmin: float = 1e-3
+    dmax: float = 0.1
+    description: str = ""
+
+
+SSD_CONFIGS = {
+    "mamba2_2p7b": SsdConfig("mamba2_2p7b", 8, 2048, 80, 64, 1, 128,
+                             description="Mamba-2-2.7B-like SSD layer: 5120 channels as 80 heads x 64, "
+                                         "d_state 128, one B/C group"),
+}
+
 DECODE_CONFIG = DecodeConfig("decode_b256", 256, 8192, 16, 512, "bf16",
                              description="decode state update, 512 steps at batch 256")
 
@@ -297,3 +323,47 @@ def conv_algorithmic_bytes(batch, seqlen, d_inner, d_conv, in_dtype, out_dtype) 
     """Bytes a convolution prefill must move: x read once, out written once (the
     filter, bias and caches, a few KiB per channel group, are excluded)."""
     return batch * seqlen * d_inner * (_esize(in_dtype) + _esize(out_dtype))
+
+
+def ssd_inputs(cfg: SsdConfig, seed: int = 0, batch: int | None = None, seqlen: int | None = None,
+               nheads: int | None = None, ngroups: int | None = None):
+    """Inputs for ``ssm_ssd_fwd`` under ``cfg`` (sizes may be overridden).
+
+    Recipe: A[h] = -exp(U(0, log 16)) per head (decay rates 1..16, fp32); D ~ U(0.5, 1.5)
+    per channel; the step drawn as for the Mamba-1 scan but per (b, t, head), with a
+    per-head bias, so softplus(dt + bias) is log-uniform in [dmin, dmax]; x, z ~ N(0, 1)
+    [batch, L, nheads, headdim]; B, C ~ N(0, 1) [batch, L, ngroups, d_state]; all but A,
+    D and the bias rounded to the input dtype.
+    """
+    bsz = cfg.batch if batch is None else batch
+    L = cfg.seqlen if seqlen is None else seqlen
+    H = cfg.nheads if nheads is None else nheads
+    G = cfg.ngroups if ngroups is None else ngroups
+    P, N, dt = cfg.headdim, cfg.d_state, cfg.dtype
+    A = (-np.exp(_gen(seed, _T_SA, 0).uniform(0.0, math.log(16.0), size=H))).astype(np.float32)
+    D = _gen(seed, _T_SD, 0).uniform(0.5, 1.5, size=H * P).astype(np.float32)
+    beta = _log_uniform64(_gen(seed, _T_BETA, 0), H, cfg.dmin, cfg.dmax)
+    bias = np.log(np.expm1(beta)).astype(np.float32)
+    shape = (bsz, L, H, P)
+    return {
+        "x": _to_dtype(_normal(shape, seed, _T_X), dt),
+        "dt": _to_dtype(_delta((bsz, L, H), bias, cfg.dmin, cfg.dmax, seed, _T_DT), dt),
+        "z": _to_dtype(_normal(shape, seed, _T_Z), dt),
+        "B": _to_dtype(_normal((bsz, L, G, N), seed, _T_B), dt),
+        "C": _to_dtype(_normal((bsz, L, G, N), seed, _T_C), dt),
+        "A": A, "D": D, "dt_bias": bias, "dtype": dt,
+    }
+
+
+def ssd_initial_state(batch: int, nheads: int, headdim: int, d_state: int, seed: int = 0) -> np.ndarray:
+    """A stored Mamba-2 state [batch, nheads, headdim, d_state] ~ N(0, 1), fp32."""
+    return _normal((batch, nheads, headdim, d_state), seed, _T_H0)
+
+
+def ssd_algorithmic_bytes(batch, seqlen, nheads, headdim, ngroups, d_state, in_dtype, out_dtype,
+                          with_z=True) -> int:
+    """Bytes a Mamba-2 scan must move at minimum: x, (z), dt, B, C read once, out written once."""
+    si, so = _esize(in_dtype), _esize(out_dtype)
+    e = batch * seqlen * nheads * headdim
+    nread = 2 if with_z else 1
+    return e * (nread * si + so) + batch * seqlen * (nheads + 2 * ngroups * d_state) * si
