@@ -71,12 +71,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba2p8b",
-                    choices=["mamba2p8b", "mamba130m", "long_dna", "tiny_fp32", "decode", "copy"])
+                    choices=["mamba2p8b", "mamba130m", "long_dna", "tiny_fp32", "decode", "copy", "ssd"])
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true")
+    ap.add_argument("--no-zoh", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--plan", default=None, help="states_per_wave,chunk_len (tuning only)")
     return ap.parse_args()
@@ -281,6 +283,83 @@ def backward_case(cfg, steps=5):
             "alu_frac": round(floor_us / (ms * 1e3), 4)}
 
 
+def zoh_case(cfg, run_dt_ms, reps=20):
+    """The scan with the exact zero-order-hold input coefficient (SSM_ZOH) on the
+    layer's shape, timed as back-to-back calls, beside the dt coefficient's time."""
+    import torch
+
+    import sequence_scan_amd as ssm
+    import workloads
+
+    inp = workloads.scan_inputs(cfg, seed=0)
+    t = {k: (torch.from_numpy(v).to(torch.bfloat16) if k in ("x", "delta", "z", "B", "C") else torch.from_numpy(v)).cuda()
+         for k, v in inp.items() if k != "dtype"}
+    del inp
+    out = torch.empty(t["x"].shape, dtype=torch.float32, device="cuda")
+    run = lambda: ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                                   out=out, zoh=True)
+    ms, _ = time_steps(run, reps, 3)
+    return {"workload": f"{cfg.name} scan with SSM_ZOH (exact zero-order-hold input coefficient)",
+            "us_per_call": round(ms * 1e3, 1), "dt_coefficient_us_per_call": round(run_dt_ms * 1e3, 1),
+            "ratio": round(ms / run_dt_ms, 3)}
+
+
+def ssd_case(reps=20, decode_steps=64):
+    """The Mamba-2 (SSD) scan on its layer's shape (bf16 in, fp32 out, softplus,
+    D, z), timed as back-to-back calls, against the HBM roofline (algorithmic
+    bytes) with the matrix-core work beside it; and its decode step at batch 64."""
+    import torch
+
+    import sequence_scan_amd as ssm
+    import workloads
+
+    cfg = workloads.SSD_CONFIGS["mamba2_2p7b"]
+    inp = workloads.ssd_inputs(cfg, seed=0)
+    t = {k: (torch.from_numpy(v).to(torch.bfloat16) if k in ("x", "dt", "z", "B", "C") else torch.from_numpy(v)).cuda()
+         for k, v in inp.items() if k != "dtype"}
+    del inp
+    out = torch.empty(t["x"].shape, dtype=torch.float32, device="cuda")
+    run = lambda: ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["z"], t["dt_bias"], out=out)
+    ms, _ = time_steps(run, reps, 3)
+    B_, L_, H_, P_, G_, N_ = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.d_state
+    nbytes = workloads.ssd_algorithmic_bytes(B_, L_, H_, P_, G_, N_, "bf16", "f32")
+    # algorithmic multiply-adds of the chunked form per (batch row, head, 64-step
+    # chunk): C B^T (Q Q N), W X (Q Q P), C S^T (Q N P), the state update (Q P N)
+    Q = 64
+    macs = B_ * H_ * ((L_ + Q - 1) // Q) * (Q * Q * N_ + Q * Q * P_ + 2 * Q * N_ * P_)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    tflops = 2 * macs / (ms / 1e3) / 1e12
+    del t, out
+    # decode step at batch 64
+    dcfg = workloads.SsdConfig("mamba2_2p7b_decode", 64, decode_steps, H_, P_, G_, N_)
+    dinp = workloads.ssd_inputs(dcfg, seed=1)
+    dv = {k: (torch.from_numpy(v).to(torch.bfloat16) if k in ("x", "dt", "z", "B", "C") else torch.from_numpy(v)).cuda()
+          for k, v in dinp.items() if k != "dtype"}
+    del dinp
+    steps = [{k: (v[:, s].contiguous() if k in ("x", "dt", "z", "B", "C") else v) for k, v in dv.items()}
+             for s in range(decode_steps)]
+    state = torch.zeros((64, H_, P_, N_), device="cuda")
+    dout = torch.empty((64, H_, P_), dtype=torch.float32, device="cuda")
+
+    def run_decode():
+        for sv in steps:
+            ssm.ssm_ssd_state_update(state, sv["x"], sv["dt"], sv["A"], sv["B"], sv["C"], sv["D"], sv["z"],
+                                     sv["dt_bias"], out=dout)
+    dms, _ = time_steps(run_decode, 2, 1)
+    step_ms = dms / decode_steps
+    step_bytes = 64 * H_ * P_ * (2 * 4 * N_ + 2 * 2 + 4) + 64 * (H_ * 2 + 2 * G_ * N_ * 2)
+    return {"workload": f"ssm_ssd_fwd {cfg.name}: {cfg.description}; batch {B_}, seqlen {L_}, bf16 in, fp32 out, "
+                        "softplus, D, z",
+            "us_per_call": round(ms * 1e3, 1), "bytes_per_call": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "mfma": {"algorithmic_tflops": round(tflops, 1), "peak_bf16_tflops": 2500.0,
+                     "frac": round(tflops / 2500.0, 4), "macs_per_call": macs},
+            "decode_step": {"workload": f"ssm_ssd_state_update batch 64, {H_} heads x {P_}, d_state {N_}, bf16 in",
+                            "us_per_step": round(step_ms * 1e3, 2), "bytes_per_step": step_bytes,
+                            "GBps": round(step_bytes / (step_ms / 1e3) / 1e9, 1)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -302,6 +381,12 @@ def main():
         nbytes = 2 * n * 4
         print(json.dumps({"metric": "device copy bandwidth (read + write)", "value": round(nbytes / (ms / 1e3) / 1e9, 1),
                           "unit": "GB/s", "bytes_per_copy": nbytes, "ms_per_copy": round(ms, 4), "n_gpus": 1}), flush=True)
+        return
+
+    if args.workload == "ssd":
+        d = ssd_case(args.steps)
+        print(json.dumps({"metric": "Mamba-2 SSD scan GB/s", "value": d["roofline"]["achieved"], "unit": "GB/s",
+                          "n_gpus": 1, "higher_is_better": True, "ssd": d}), flush=True)
         return
 
     if args.workload == "decode":
@@ -378,6 +463,10 @@ def main():
         line["conv1d"] = conv_case(cfg.batch, cfg.seqlen, cfg.d_inner)
     if not args.no_backward and args.workload == "mamba2p8b":
         line["backward"] = backward_case(cfg)
+    if not args.no_zoh and args.workload == "mamba2p8b":
+        line["zoh"] = zoh_case(cfg, ms)
+    if not args.no_ssd and args.workload == "mamba2p8b":
+        line["ssd"] = ssd_case()
     print(json.dumps(line), flush=True)
 
 

@@ -13,48 +13,60 @@
 //     s[p,n] <- a s[p,n] + dt B[b,t,g,n] x[b,t,h,p]
 //     out[b,t,h,p] = (sum_n C[b,t,g,n] s[p,n] + D[h P + p] x) * silu(z)
 //
-// Chunked form used here, per (batch row, head) and chunk of Q = 64 steps with
+// Chunked form used here, per (batch row, head) and chunk of Q = 32 steps with
 // cumulative log-decay c_i = sum_{r<=i} dt_r A (log2 units, from the chunk start):
-//   G   = C B^T                                   (Q x Q, over d_state)
-//   W   = G o [j <= i] exp(c_i - c_j) dt_j          (causal decay mask)
-//   Y   = diag(exp(c_i)) C S^T + W X              (S: state entering the chunk)
-//   S  <- exp(c_end) S + (X o exp(c_end - c_j) dt_j)^T B
-// Every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  B, C
-// and X are bf16 inputs, exact as operands.  W, the scaled X and the state are
-// computed in fp32 and enter as two bf16 operands, hi = bf16(v) and
+//   G    = C B^T                                  (Q x Q, over d_state)
+//   W    = G o [j <= i] exp(c_i - c_j) dt_j         (causal decay mask)
+//   Y    = diag(exp(c_i)) C S^T + W X             (S: state entering the chunk)
+//   S^T <- exp(c_end) S^T + B^T (X o exp(c_end - c_j) dt_j)
+// Every product runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  B,
+// C and X are bf16 inputs, exact as operands.  W, the scaled X and the state
+// are computed in fp32 and enter as two bf16 operands, hi = bf16(v) and
 // lo = bf16(v - hi), whose products are summed: about 16 significant bits.
 //
 // Work decomposition (MI355X-first): a workgroup of four wavefronts owns one
-// (batch row, head) and walks its chunks in order, so the state never leaves
-// the chip: it lives in MFMA accumulators (the P x N tile split over the four
-// waves) and is copied to LDS as bf16 hi/lo once per chunk, as an operand of
-// the next chunk's readout.  Each wave owns one 32 x 32 tile of G and of Y and
-// N/64 32 x 32 tiles of the state.  The HBM reads of the next chunk are issued
-// before the current chunk's arithmetic.
+// (batch row, head) and walks its chunks in order; wave w owns channels
+// p in [16w, 16w + 16).  The state is held transposed, S^T [d_state x 16] per
+// wave, in MFMA accumulators for the whole sequence.  Its accumulator layout
+// (lane = channel, four consecutive n per lane and tile) is, up to a fixed
+// permutation of n, the operand layout the readout C S^T needs; since that
+// product sums over n, the C operand is read with the same permutation (two
+// 8-byte LDS reads) and the state feeds the matrix cores straight from
+// registers, never through LDS.  G is shared by the four waves (three 16 x 16
+// tiles, one per wave) and reaches the W X product through LDS.  Inputs whose
+// contraction runs over time (B for the state update, x for both products)
+// are staged transposed; their global loads map lanes to steps, so the
+// transposing LDS writes of a wave land on consecutive addresses.  About 52
+// KiB of LDS per workgroup: three workgroups per CU.  The HBM reads of the
+// next chunk are issued before the current chunk's arithmetic.
 #include "device.h"
 
 namespace ssm {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // 16 bytes as a native vector (HIP's uint4 is a struct, whose copies the
-// compiler routes through private memory here)
+// compiler routes through private memory)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kQ = 64;    // steps per chunk
+constexpr int kQ = 32;    // steps per chunk
 constexpr int kP = 64;    // channels per head (headdim)
 constexpr int kPad = 8;   // bf16 row padding: 16 bytes
-
-// Row of accumulator register r of lane l in a 32 x 32 MFMA tile (the column
-// is l % 32).
-__device__ __forceinline__ int frag_row(int r, int l) { return (r >> 2) * 8 + (l >> 5) * 4 + (r & 3); }
 
 // Eight consecutive bf16 of a k-contiguous LDS row: one MFMA operand.
 __device__ __forceinline__ bf16x8_t ld_op(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
-__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// Two runs of four bf16 (8 bytes each) joined into one operand.
+__device__ __forceinline__ bf16x8_t ld_op2(const uint16_t* p0, const uint16_t* p1) {
+  const bf16x4_t a = *reinterpret_cast<const bf16x4_t*>(p0);
+  const bf16x4_t b = *reinterpret_cast<const bf16x4_t*>(p1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // v as a pair of bf16 whose sum carries about 16 significant bits.
@@ -64,9 +76,9 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
 }
 
 template <int N, typename Tout>
-__global__ void __launch_bounds__(256) ssd_chunk_kernel(SsdArgs a) {
-  constexpr int NV = N / 32;          // 16-byte vectors of a B or C chunk per thread
-  constexpr int NT = N / 64;          // state tiles per wave
+__global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
+  constexpr int NT = N / 16;          // 16 x 16 state tiles per wave
+  constexpr int NR = N / 64;          // 16-byte B/C vectors per thread and chunk
   constexpr int SN = N + kPad;        // row strides (elements)
   constexpr int SQ = kQ + kPad;
   constexpr int SP = kP + kPad;
@@ -76,7 +88,6 @@ __global__ void __launch_bounds__(256) ssd_chunk_kernel(SsdArgs a) {
   __shared__ uint16_t sXt[kP * SQ] __attribute__((aligned(16)));     // x[j][p] at [p][j]
   __shared__ uint16_t sXs[2][kP * SQ] __attribute__((aligned(16)));  // scaled x, hi/lo, [p][j]
   __shared__ uint16_t sW[2][kQ * SQ] __attribute__((aligned(16)));   // W[i][j], hi/lo
-  __shared__ uint16_t sH[2][kP * SN] __attribute__((aligned(16)));   // state S[p][n], hi/lo
   __shared__ uint16_t sZ[kQ * SP] __attribute__((aligned(16)));      // z[i][p]
   __shared__ float s_dt[kQ];                                          // step sizes
   __shared__ float s_cum[kQ];                                         // cumulative log2 decay
@@ -84,6 +95,7 @@ __global__ void __launch_bounds__(256) ssd_chunk_kernel(SsdArgs a) {
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = l & 15, q = l >> 4;      // 16 x 16 tile: column / quarter of the lane
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int H = a.nheads;
@@ -102,70 +114,57 @@ __global__ void __launch_bounds__(256) ssd_chunk_kernel(SsdArgs a) {
   const float bias = a.bias ? a.bias[h] : 0.0f;
   const bool softplus = a.softplus != 0;
   const bool has_z = zb != nullptr;
-  const float* Dh = a.D ? a.D + (int64_t)h * kP : nullptr;
+  const int p = 16 * w + lr;              // this lane's channel in the readout and the state
+  const float Dp = a.D ? a.D[(int64_t)h * kP + p] : 0.0f;
 
-  // tiles of this wave
-  const int ib = w >> 1;           // G and Y: row block (steps i)
-  const int cb = w & 1;            // G: column block (steps j); Y: column block (channels p)
-  const int pb = w >> 1;           // state: row block (channels p)
-  const int lr = l & 31, lk = (l >> 5) * 8;
-
+  // Global-to-LDS mappings.  C and z: row-major (16-byte vectors along a row).
+  // B and x: lane = step j (l % 32), so the transposed LDS writes of a wave are
+  // consecutive; the column vector c8 comes from the wave and the lane half.
+  const int jl = l & 31;
   struct Bank {
-    u32x4_t c[NV], bb[NV], x[2], z[2];
+    u32x4_t c[NR], bb[NR], x, z;
     uint32_t dt;
   };
   Bank bank;
   auto issue = [&](int64_t t0, int nt) SSM_INLINE {
 #pragma unroll
-    for (int r = 0; r < NV; ++r) {
+    for (int r = 0; r < NR; ++r) {
       const int v = tid + 256 * r;
       const int row = min(v / (N / 8), nt - 1);
-      const int c8 = v % (N / 8);
-      bank.c[r] = *reinterpret_cast<const u32x4_t*>(Cb + (t0 + row) * bcrow + c8 * 8);
-      bank.bb[r] = *reinterpret_cast<const u32x4_t*>(Bb + (t0 + row) * bcrow + c8 * 8);
+      bank.c[r] = *reinterpret_cast<const u32x4_t*>(Cb + (t0 + row) * bcrow + (v % (N / 8)) * 8);
+      const int c8 = ((w * NR + r) << 1) + (l >> 5);
+      bank.bb[r] = *reinterpret_cast<const u32x4_t*>(Bb + (t0 + min(jl, nt - 1)) * bcrow + c8 * 8);
     }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int v = tid + 256 * r;
-      const int row = min(v >> 3, nt - 1);
-      const int c8 = v & 7;
-      bank.x[r] = *reinterpret_cast<const u32x4_t*>(xb + (t0 + row) * xrow + c8 * 8);
-      if (has_z) bank.z[r] = *reinterpret_cast<const u32x4_t*>(zb + (t0 + row) * xrow + c8 * 8);
-    }
+    bank.x = *reinterpret_cast<const u32x4_t*>(xb + (t0 + min(jl, nt - 1)) * xrow + ((w << 1) + (l >> 5)) * 8);
+    if (has_z) bank.z = *reinterpret_cast<const u32x4_t*>(zb + (t0 + min(tid >> 3, nt - 1)) * xrow + (tid & 7) * 8);
     if (tid < kQ) bank.dt = dtb[(t0 + min(tid, nt - 1)) * H];
   };
 
-  // Stage the banked chunk into LDS (rows past nt carry x = 0 and dt = 0, so
+  // Stage the banked chunk into LDS (steps past nt carry x = 0 and dt = 0, so
   // they change nothing) and form the step sizes and cumulative decay.
   auto stage = [&](int nt) SSM_INLINE {
 #pragma unroll
-    for (int r = 0; r < NV; ++r) {
+    for (int r = 0; r < NR; ++r) {
       const int v = tid + 256 * r;
-      const int row = v / (N / 8);
-      const int c8 = v % (N / 8);
-      *reinterpret_cast<u32x4_t*>(&sC[row * SN + c8 * 8]) = bank.c[r];
-      *reinterpret_cast<u32x4_t*>(&sB[row * SN + c8 * 8]) = bank.bb[r];
-      const u32x4_t wv = bank.bb[r];
+      *reinterpret_cast<u32x4_t*>(&sC[(v / (N / 8)) * SN + (v % (N / 8)) * 8]) = bank.c[r];
+      const int c8 = ((w * NR + r) << 1) + (l >> 5);
+      *reinterpret_cast<u32x4_t*>(&sB[jl * SN + c8 * 8]) = bank.bb[r];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sBt[(c8 * 8 + 2 * e) * SQ + row] = (uint16_t)(wv[e] & 0xffffu);
-        sBt[(c8 * 8 + 2 * e + 1) * SQ + row] = (uint16_t)(wv[e] >> 16);
+        sBt[(c8 * 8 + 2 * e) * SQ + jl] = (uint16_t)(bank.bb[r][e] & 0xffffu);
+        sBt[(c8 * 8 + 2 * e + 1) * SQ + jl] = (uint16_t)(bank.bb[r][e] >> 16);
       }
     }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int v = tid + 256 * r;
-      const int row = v >> 3;
-      const int c8 = v & 7;
-      const bool live = row < nt;
-      const u32x4_t wv = bank.x[r];
+    {
+      const int c8 = (w << 1) + (l >> 5);
+      const bool live = jl < nt;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sXt[(c8 * 8 + 2 * e) * SQ + row] = live ? (uint16_t)(wv[e] & 0xffffu) : (uint16_t)0;
-        sXt[(c8 * 8 + 2 * e + 1) * SQ + row] = live ? (uint16_t)(wv[e] >> 16) : (uint16_t)0;
+        sXt[(c8 * 8 + 2 * e) * SQ + jl] = live ? (uint16_t)(bank.x[e] & 0xffffu) : (uint16_t)0;
+        sXt[(c8 * 8 + 2 * e + 1) * SQ + jl] = live ? (uint16_t)(bank.x[e] >> 16) : (uint16_t)0;
       }
-      if (has_z) *reinterpret_cast<u32x4_t*>(&sZ[row * SP + c8 * 8]) = bank.z[r];
     }
+    if (has_z) *reinterpret_cast<u32x4_t*>(&sZ[(tid >> 3) * SP + (tid & 7) * 8]) = bank.z;
     if (w == 0) {
       float d = 0.0f;
       if (l < nt) {
@@ -174,38 +173,33 @@ __global__ void __launch_bounds__(256) ssd_chunk_kernel(SsdArgs a) {
       }
       float one = 1.0f, c = d * A2;
       affine_wave_scan(one, c);  // (1, c) pairs compose to prefix sums of c
-      s_dt[l] = d;
-      s_cum[l] = c;
-    }
-  };
-
-  // state accumulators and the initial state
-  f32x16_t accS[NT];
-#pragma unroll
-  for (int s = 0; s < NT; ++s) {
-    const int nb = cb * NT + s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int p = pb * 32 + frag_row(r, l), n = nb * 32 + lr;
-      accS[s][r] = a.h0 ? a.h0[(((int64_t)b * H + h) * kP + p) * N + n] : 0.0f;
-    }
-  }
-  bool has_state = a.h0 != nullptr;
-  auto write_state = [&]() SSM_INLINE {
-#pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      const int nb = cb * NT + s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = pb * 32 + frag_row(r, l), n = nb * 32 + lr;
-        uint16_t hi, lo;
-        split_bf16(accS[s][r], hi, lo);
-        sH[0][p * SN + n] = hi;
-        sH[1][p * SN + n] = lo;
+      if (l < kQ) {
+        s_dt[l] = d;
+        s_cum[l] = c;
       }
     }
   };
-  if (has_state) write_state();
+
+  // The state S^T: tile t holds n in [16t, 16t + 16) x this wave's 16 channels;
+  // register r of lane l is S^T[16t + 4(l/16) + r][p].
+  f32x4_t accS[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (a.h0 != nullptr) {
+      const float4 v = *reinterpret_cast<const float4*>(a.h0 + (((int64_t)b * H + h) * kP + p) * N + 16 * t + 4 * q);
+      accS[t] = f32x4_t{v.x, v.y, v.z, v.w};
+    } else {
+      accS[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
+  bool has_state = a.h0 != nullptr;
+
+  // W is zero above the diagonal: its block (rows 0..15, columns 16..31) is
+  // never written by the chunks, so clear it once.
+  for (int e = tid; e < 2 * 16 * 16; e += 256) {
+    const int k = e >> 8, i = (e >> 4) & 15, j = 16 + (e & 15);
+    sW[k][i * SQ + j] = 0;
+  }
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
   issue(0, (int)min((int64_t)kQ, L));
@@ -216,18 +210,20 @@ __global__ void __launch_bounds__(256) ssd_chunk_kernel(SsdArgs a) {
     if (ch + 1 < nchunks) issue(t0 + kQ, (int)min((int64_t)kQ, L - t0 - kQ));
     block_sync();
 
-    // Phase 1: W = (C B^T) o decay mask, and the decayed, dt-weighted x.
+    // Phase 1.  Waves 0..2: one 16 x 16 tile of G each, masked and decayed into W.
     const float c_end = s_cum[kQ - 1];
-    if (cb <= ib) {
-      f32x16_t acc = {};
+    if (w < 3) {
+      const int ib = w == 0 ? 0 : 1, jb = w == 2 ? 1 : 0;
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k = 0; k < N / 16; ++k)
-        acc = mfma(ld_op(&sC[(ib * 32 + lr) * SN + 16 * k + lk]), ld_op(&sB[(cb * 32 + lr) * SN + 16 * k + lk]), acc);
-      const int j = cb * 32 + lr;
+      for (int m = 0; m < N / 32; ++m)
+        acc = mfma(ld_op(&sC[(16 * ib + lr) * SN + 32 * m + 8 * q]), ld_op(&sB[(16 * jb + lr) * SN + 32 * m + 8 * q]),
+                   acc);
+      const int j = 16 * jb + lr;
       const float cj = s_cum[j], dj = s_dt[j];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = ib * 32 + frag_row(r, l);
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ib + 4 * q + r;
         const float v = j <= i ? acc[r] * __builtin_amdgcn_exp2f(s_cum[i] - cj) * dj : 0.0f;
         uint16_t hi, lo;
         split_bf16(v, hi, lo);
@@ -235,91 +231,101 @@ __global__ void __launch_bounds__(256) ssd_chunk_kernel(SsdArgs a) {
         sW[1][i * SQ + j] = lo;
       }
     }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int v = tid + 256 * r;
-      const int p = v >> 3;
-      const int j0 = (v & 7) * 8;
-      const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(&sXt[p * SQ + j0]);
+    // The decayed, dt-weighted x of the state update, [p][j] as hi/lo.
+    {
+      const int pp = tid >> 2, j0 = (tid & 3) * 8;
+      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(&sXt[pp * SQ + j0]);
       u32x4_t hv, lv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        uint16_t h0, l0, h1, l1;
         const int j = j0 + 2 * e;
-        split_bf16(bf16_to_f32(wv[e] & 0xffffu) * __builtin_amdgcn_exp2f(c_end - s_cum[j]) * s_dt[j], h0, l0);
-        split_bf16(__uint_as_float(wv[e] & 0xffff0000u) * __builtin_amdgcn_exp2f(c_end - s_cum[j + 1]) * s_dt[j + 1],
+        uint16_t h0, l0, h1, l1;
+        split_bf16(bf16_to_f32(xv[e] & 0xffffu) * __builtin_amdgcn_exp2f(c_end - s_cum[j]) * s_dt[j], h0, l0);
+        split_bf16(__uint_as_float(xv[e] & 0xffff0000u) * __builtin_amdgcn_exp2f(c_end - s_cum[j + 1]) * s_dt[j + 1],
                    h1, l1);
         hv[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         lv[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
       }
-      *reinterpret_cast<u32x4_t*>(&sXs[0][p * SQ + j0]) = hv;
-      *reinterpret_cast<u32x4_t*>(&sXs[1][p * SQ + j0]) = lv;
+      *reinterpret_cast<u32x4_t*>(&sXs[0][pp * SQ + j0]) = hv;
+      *reinterpret_cast<u32x4_t*>(&sXs[1][pp * SQ + j0]) = lv;
+    }
+    // The readout of the incoming state, Y = diag(exp(c_i)) C S^T, from the
+    // state registers: tiles 2m and 2m + 1 give the eight k slots of product m
+    // (n = 32m + 4q + 0..3 and 32m + 16 + 4q + 0..3), and C is read with the
+    // same n order.
+    f32x4_t accY[2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) accY[ib] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (has_state) {
+#pragma unroll
+      for (int m = 0; m < N / 32; ++m) {
+        bf16x8_t shi, slo;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float v = r < 4 ? accS[2 * m][r] : accS[2 * m + 1][r - 4];
+          const __bf16 hv = (__bf16)v;
+          shi[r] = hv;
+          slo[r] = (__bf16)(v - (float)hv);
+        }
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const uint16_t* crow = &sC[(16 * ib + lr) * SN + 32 * m + 4 * q];
+          const bf16x8_t ca = ld_op2(crow, crow + 16);
+          accY[ib] = mfma(ca, shi, accY[ib]);
+          accY[ib] = mfma(ca, slo, accY[ib]);
+        }
+      }
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accY[ib][r] *= __builtin_amdgcn_exp2f(s_cum[16 * ib + 4 * q + r]);
     }
     block_sync();
 
-    // Phase 2: Y = diag(exp(c_i)) C S^T + W X, then D skip, gate and store;
-    // the state moves to the end of the chunk.
+    // Phase 2.  Y += W X; D skip, gate and store; the state moves to the end
+    // of the chunk.
     {
-      f32x16_t acc = {};
-      if (has_state) {
+      const bf16x8_t xo = ld_op(&sXt[p * SQ + 8 * q]);
 #pragma unroll
-        for (int k = 0; k < N / 16; ++k) {
-          const bf16x8_t ca = ld_op(&sC[(ib * 32 + lr) * SN + 16 * k + lk]);
-          acc = mfma(ca, ld_op(&sH[0][(cb * 32 + lr) * SN + 16 * k + lk]), acc);
-          acc = mfma(ca, ld_op(&sH[1][(cb * 32 + lr) * SN + 16 * k + lk]), acc);
+      for (int ib = 0; ib < 2; ++ib) {
+        accY[ib] = mfma(ld_op(&sW[0][(16 * ib + lr) * SQ + 8 * q]), xo, accY[ib]);
+        accY[ib] = mfma(ld_op(&sW[1][(16 * ib + lr) * SQ + 8 * q]), xo, accY[ib]);
+      }
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ib + 4 * q + r;
+          float y = accY[ib][r];
+          if (a.D) y = __builtin_fmaf(Dp, bf16_to_f32(sXt[p * SQ + i]), y);
+          if (has_z) y = y * silu_f(bf16_to_f32(sZ[i * SP + p]));
+          if (i < nt) Io<Tout>::store(ob, (t0 + i) * xrow + p, y);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] *= __builtin_amdgcn_exp2f(s_cum[ib * 32 + frag_row(r, l)]);
-      }
-      // W is zero above the diagonal: row block ib needs column blocks 0..ib
-      for (int k = 0; k < 2 * (ib + 1); ++k) {
-        const bf16x8_t xo = ld_op(&sXt[(cb * 32 + lr) * SQ + 16 * k + lk]);
-        acc = mfma(ld_op(&sW[0][(ib * 32 + lr) * SQ + 16 * k + lk]), xo, acc);
-        acc = mfma(ld_op(&sW[1][(ib * 32 + lr) * SQ + 16 * k + lk]), xo, acc);
-      }
-      const int p = cb * 32 + lr;
-      const float Dp = Dh ? Dh[p] : 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = ib * 32 + frag_row(r, l);
-        float y = acc[r];
-        if (Dh) y = __builtin_fmaf(Dp, bf16_to_f32(sXt[p * SQ + i]), y);
-        if (has_z) y = y * silu_f(bf16_to_f32(sZ[i * SP + p]));
-        if (i < nt) Io<Tout>::store(ob, (t0 + i) * xrow + p, y);
-      }
     }
     {
       const float e_end = __builtin_amdgcn_exp2f(c_end);
+      const bf16x8_t xh = ld_op(&sXs[0][p * SQ + 8 * q]);
+      const bf16x8_t xl = ld_op(&sXs[1][p * SQ + 8 * q]);
 #pragma unroll
-      for (int s = 0; s < NT; ++s) {
-        const int nb = cb * NT + s;
-        f32x16_t acc = accS[s];
+      for (int t = 0; t < NT; ++t) {
+        f32x4_t acc = accS[t];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] *= e_end;
-#pragma unroll
-        for (int k = 0; k < kQ / 16; ++k) {
-          const bf16x8_t bo = ld_op(&sBt[(nb * 32 + lr) * SQ + 16 * k + lk]);
-          acc = mfma(ld_op(&sXs[0][(pb * 32 + lr) * SQ + 16 * k + lk]), bo, acc);
-          acc = mfma(ld_op(&sXs[1][(pb * 32 + lr) * SQ + 16 * k + lk]), bo, acc);
-        }
-        accS[s] = acc;
+        for (int r = 0; r < 4; ++r) acc[r] *= e_end;
+        const bf16x8_t bt = ld_op(&sBt[(16 * t + lr) * SQ + 8 * q]);
+        acc = mfma(bt, xh, acc);
+        acc = mfma(bt, xl, acc);
+        accS[t] = acc;
       }
     }
     has_state = true;
     block_sync();
-    if (ch + 1 < nchunks) write_state();
   }
 
   if (a.state != nullptr) {
 #pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      const int nb = cb * NT + s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = pb * 32 + frag_row(r, l), n = nb * 32 + lr;
-        a.state[(((int64_t)b * H + h) * kP + p) * N + n] = accS[s][r];
-      }
-    }
+    for (int t = 0; t < NT; ++t)
+      *reinterpret_cast<float4*>(a.state + (((int64_t)b * H + h) * kP + p) * N + 16 * t + 4 * q) =
+          make_float4(accS[t][0], accS[t][1], accS[t][2], accS[t][3]);
   }
 }
 
