@@ -33,12 +33,16 @@
 // product sums over n, the C operand is read with the same permutation (two
 // 8-byte LDS reads) and the state feeds the matrix cores straight from
 // registers, never through LDS.  G is shared by the four waves (three 16 x 16
-// tiles, one per wave) and reaches the W X product through LDS.  Inputs whose
-// contraction runs over time (B for the state update, x for both products)
-// are staged transposed; their global loads map lanes to steps, so the
-// transposing LDS writes of a wave land on consecutive addresses.  About 52
-// KiB of LDS per workgroup: three workgroups per CU.  The HBM reads of the
-// next chunk are issued before the current chunk's arithmetic.
+// tiles, one per wave) and reaches the W X product through LDS.  Every input
+// is staged in LDS in its HBM layout (rows = steps) with 16-byte writes;
+// operands whose contraction runs over time (B for the state update, x for
+// both products) and the epilogue's x and z are read with gfx950's
+// transposing LDS read, ds_read_b64_tr_b16: within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+// 4e + i / 4 (e = 0..3), so lanes that address four rows of a row-major tile
+// four columns apart receive its columns.  About 42 KiB of LDS per
+// workgroup: three workgroups per CU.  The HBM reads of the next chunk are
+// issued before the current chunk's arithmetic.
 #include "device.h"
 
 namespace ssm {
@@ -46,6 +50,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // 16 bytes as a native vector (HIP's uint4 is a struct, whose copies the
 // compiler routes through private memory)
@@ -53,7 +58,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 32;    // steps per chunk
 constexpr int kP = 64;    // channels per head (headdim)
-constexpr int kPad = 8;   // bf16 row padding: 16 bytes
 
 // Eight consecutive bf16 of a k-contiguous LDS row: one MFMA operand.
 __device__ __forceinline__ bf16x8_t ld_op(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
@@ -65,32 +69,55 @@ __device__ __forceinline__ bf16x8_t ld_op2(const uint16_t* p0, const uint16_t* p
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Transposing read of 4 x 16-bit values (see the decomposition notes above).
+__device__ __forceinline__ i16x4_t ld_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+}
+
+// A column operand from a row-major tile: lane c of each 16-lane group gets
+// rows r0 .. r0 + 7 of column c0 + c.  `tile` is the tile's first element,
+// `stride` its row stride; lane l addresses row r0 + 4 half + (l % 16) / 4 and
+// columns c0 + 4 (l % 4) .. + 3.
+__device__ __forceinline__ bf16x8_t ld_col8(const uint16_t* tile, int stride, int r0, int c0, int l) {
+  const int k = l & 15;
+  const uint16_t* a0 = tile + (r0 + (k >> 2)) * stride + c0 + 4 * (k & 3);
+  const i16x4_t lo = ld_tr(a0);
+  const i16x4_t hi = ld_tr(a0 + 4 * stride);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// v as a pair of bf16 whose sum carries about 16 significant bits.
-__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-  hi = f32_to_bf16_rne(v);
-  lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
+// Two values as pairs of bf16 (hi = bf16(v), lo = bf16(v - hi)), packed with
+// the first value in the low half: one conversion instruction per pair.
+struct Split2 {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Split2 split_bf16x2(float v0, float v1) {
+  const uint32_t hi = pack_bf16x2(v0, v1);
+  return {hi, pack_bf16x2(v0 - __uint_as_float(hi << 16), v1 - __uint_as_float(hi & 0xffff0000u))};
 }
 
 template <int N, typename Tout>
 __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
   constexpr int NT = N / 16;          // 16 x 16 state tiles per wave
   constexpr int NR = N / 64;          // 16-byte B/C vectors per thread and chunk
-  constexpr int SN = N + kPad;        // row strides (elements)
-  constexpr int SQ = kQ + kPad;
-  constexpr int SP = kP + kPad;
-  __shared__ uint16_t sC[kQ * SN] __attribute__((aligned(16)));      // C[i][n]
-  __shared__ uint16_t sB[kQ * SN] __attribute__((aligned(16)));      // B[j][n]
-  __shared__ uint16_t sBt[N * SQ] __attribute__((aligned(16)));      // B[j][n] at [n][j]
-  __shared__ uint16_t sXt[kP * SQ] __attribute__((aligned(16)));     // x[j][p] at [p][j]
-  __shared__ uint16_t sXs[2][kP * SQ] __attribute__((aligned(16)));  // scaled x, hi/lo, [p][j]
-  __shared__ uint16_t sW[2][kQ * SQ] __attribute__((aligned(16)));   // W[i][j], hi/lo
+  constexpr int SC = N + 8;           // row strides (elements)
+  constexpr int SB = N + 16;
+  constexpr int SP = kP + 8;
+  constexpr int SW = kQ + 8;
+  __shared__ uint16_t sC[kQ * SC] __attribute__((aligned(16)));      // C[i][n]
+  __shared__ uint16_t sB[kQ * SB] __attribute__((aligned(16)));      // B[j][n]
+  __shared__ uint16_t sX[kQ * SP] __attribute__((aligned(16)));      // x[j][p]
   __shared__ uint16_t sZ[kQ * SP] __attribute__((aligned(16)));      // z[i][p]
-  __shared__ float s_dt[kQ];                                          // step sizes
-  __shared__ float s_cum[kQ];                                         // cumulative log2 decay
+  __shared__ uint16_t sXs[2][kQ * SP] __attribute__((aligned(16)));  // scaled x[j][p], hi/lo
+  __shared__ uint16_t sW[2][kQ * SW] __attribute__((aligned(16)));   // W[i][j], hi/lo
+  __shared__ float s_dt[kQ];                                          // step sizes dt_j
+  __shared__ float s_cum[kQ];                                         // cumulative log2 decay c_j
+  __shared__ float s_xs[kQ];                                          // exp(c_end - c_j) dt_j
+  __shared__ float s_ec[kQ + 1];                                      // exp(c_i); [kQ]: exp(c_end)
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -114,13 +141,14 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
   const float bias = a.bias ? a.bias[h] : 0.0f;
   const bool softplus = a.softplus != 0;
   const bool has_z = zb != nullptr;
+  const bool has_D = a.D != nullptr;
   const int p = 16 * w + lr;              // this lane's channel in the readout and the state
-  const float Dp = a.D ? a.D[(int64_t)h * kP + p] : 0.0f;
+  const float Dp = has_D ? a.D[(int64_t)h * kP + p] : 0.0f;
 
-  // Global-to-LDS mappings.  C and z: row-major (16-byte vectors along a row).
-  // B and x: lane = step j (l % 32), so the transposed LDS writes of a wave are
-  // consecutive; the column vector c8 comes from the wave and the lane half.
-  const int jl = l & 31;
+  // Global loads and LDS staging: row-major 16-byte vectors (thread v covers
+  // row v / (width / 8), vector v % (width / 8)); rows past the chunk's last
+  // step re-read that step.
+  const int xrow_i = tid >> 3, xc8 = tid & 7;
   struct Bank {
     u32x4_t c[NR], bb[NR], x, z;
     uint32_t dt;
@@ -130,41 +158,29 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int v = tid + 256 * r;
-      const int row = min(v / (N / 8), nt - 1);
-      bank.c[r] = *reinterpret_cast<const u32x4_t*>(Cb + (t0 + row) * bcrow + (v % (N / 8)) * 8);
-      const int c8 = ((w * NR + r) << 1) + (l >> 5);
-      bank.bb[r] = *reinterpret_cast<const u32x4_t*>(Bb + (t0 + min(jl, nt - 1)) * bcrow + c8 * 8);
+      const int64_t off = (t0 + min(v / (N / 8), nt - 1)) * bcrow + (v % (N / 8)) * 8;
+      bank.c[r] = *reinterpret_cast<const u32x4_t*>(Cb + off);
+      bank.bb[r] = *reinterpret_cast<const u32x4_t*>(Bb + off);
     }
-    bank.x = *reinterpret_cast<const u32x4_t*>(xb + (t0 + min(jl, nt - 1)) * xrow + ((w << 1) + (l >> 5)) * 8);
-    if (has_z) bank.z = *reinterpret_cast<const u32x4_t*>(zb + (t0 + min(tid >> 3, nt - 1)) * xrow + (tid & 7) * 8);
+    const int64_t xoff = (t0 + min(xrow_i, nt - 1)) * xrow + xc8 * 8;
+    bank.x = *reinterpret_cast<const u32x4_t*>(xb + xoff);
+    if (has_z) bank.z = *reinterpret_cast<const u32x4_t*>(zb + xoff);
     if (tid < kQ) bank.dt = dtb[(t0 + min(tid, nt - 1)) * H];
   };
 
-  // Stage the banked chunk into LDS (steps past nt carry x = 0 and dt = 0, so
-  // they change nothing) and form the step sizes and cumulative decay.
+  // Stage the banked chunk (steps past nt carry x = 0 and dt = 0, so they
+  // change nothing) and form the step sizes and per-step decay factors.
   auto stage = [&](int nt) SSM_INLINE {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int v = tid + 256 * r;
-      *reinterpret_cast<u32x4_t*>(&sC[(v / (N / 8)) * SN + (v % (N / 8)) * 8]) = bank.c[r];
-      const int c8 = ((w * NR + r) << 1) + (l >> 5);
-      *reinterpret_cast<u32x4_t*>(&sB[jl * SN + c8 * 8]) = bank.bb[r];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sBt[(c8 * 8 + 2 * e) * SQ + jl] = (uint16_t)(bank.bb[r][e] & 0xffffu);
-        sBt[(c8 * 8 + 2 * e + 1) * SQ + jl] = (uint16_t)(bank.bb[r][e] >> 16);
-      }
+      const int row = v / (N / 8), c8 = v % (N / 8);
+      *reinterpret_cast<u32x4_t*>(&sC[row * SC + c8 * 8]) = bank.c[r];
+      *reinterpret_cast<u32x4_t*>(&sB[row * SB + c8 * 8]) = bank.bb[r];
     }
-    {
-      const int c8 = (w << 1) + (l >> 5);
-      const bool live = jl < nt;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sXt[(c8 * 8 + 2 * e) * SQ + jl] = live ? (uint16_t)(bank.x[e] & 0xffffu) : (uint16_t)0;
-        sXt[(c8 * 8 + 2 * e + 1) * SQ + jl] = live ? (uint16_t)(bank.x[e] >> 16) : (uint16_t)0;
-      }
-    }
-    if (has_z) *reinterpret_cast<u32x4_t*>(&sZ[(tid >> 3) * SP + (tid & 7) * 8]) = bank.z;
+    if (xrow_i >= nt) bank.x = u32x4_t{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t*>(&sX[xrow_i * SP + xc8 * 8]) = bank.x;
+    if (has_z) *reinterpret_cast<u32x4_t*>(&sZ[xrow_i * SP + xc8 * 8]) = bank.z;
     if (w == 0) {
       float d = 0.0f;
       if (l < nt) {
@@ -173,10 +189,15 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
       }
       float one = 1.0f, c = d * A2;
       affine_wave_scan(one, c);  // (1, c) pairs compose to prefix sums of c
+      // steps past nt add nothing, so the prefix at the last step is c_end
+      const float c_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), kQ - 1));
       if (l < kQ) {
         s_dt[l] = d;
         s_cum[l] = c;
+        s_xs[l] = __builtin_amdgcn_exp2f(c_end - c) * d;
+        s_ec[l] = __builtin_amdgcn_exp2f(c);
       }
+      if (l == kQ) s_ec[kQ] = __builtin_amdgcn_exp2f(c_end);
     }
   };
 
@@ -198,8 +219,43 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
   // never written by the chunks, so clear it once.
   for (int e = tid; e < 2 * 16 * 16; e += 256) {
     const int k = e >> 8, i = (e >> 4) & 15, j = 16 + (e & 15);
-    sW[k][i * SQ + j] = 0;
+    sW[k][i * SW + j] = 0;
   }
+
+  // D skip, gate and store of this lane's eight outputs (steps 16 ib + 4q + r
+  // of channel p); the D and z switches are uniform and taken once per chunk,
+  // and only a ragged last chunk checks its steps.
+  auto finish = [&](const f32x4_t* accY, auto d_c, auto z_c, int nt, int64_t t0) SSM_INLINE {
+    float y[2][4];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      // rows 16 ib + 4q .. + 3 of column p: one transposing read each
+      const int k = l & 15;
+      const int off = (16 * ib + 4 * q + (k >> 2)) * SP + 16 * w + 4 * (k & 3);
+      i16x4_t xv = {0, 0, 0, 0}, zv = {0, 0, 0, 0};
+      if (decltype(d_c)::value) xv = ld_tr(&sX[off]);
+      if (decltype(z_c)::value) zv = ld_tr(&sZ[off]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = accY[ib][r];
+        if (decltype(d_c)::value) v = __builtin_fmaf(Dp, bf16_to_f32((uint16_t)xv[r]), v);
+        if (decltype(z_c)::value) v = v * silu_f(bf16_to_f32((uint16_t)zv[r]));
+        y[ib][r] = v;
+      }
+    }
+    if (nt == kQ) {
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Io<Tout>::store(ob, (t0 + 16 * ib + 4 * q + r) * xrow + p, y[ib][r]);
+    } else {
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * ib + 4 * q + r < nt) Io<Tout>::store(ob, (t0 + 16 * ib + 4 * q + r) * xrow + p, y[ib][r]);
+    }
+  };
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
   issue(0, (int)min((int64_t)kQ, L));
@@ -207,47 +263,49 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
     const int64_t t0 = ch * kQ;
     const int nt = (int)min((int64_t)kQ, L - t0);
     stage(nt);
+    const u32x4_t xreg = bank.x;        // this thread's staged x vector, for the scaled copy
     if (ch + 1 < nchunks) issue(t0 + kQ, (int)min((int64_t)kQ, L - t0 - kQ));
     block_sync();
 
     // Phase 1.  Waves 0..2: one 16 x 16 tile of G each, masked and decayed into W.
-    const float c_end = s_cum[kQ - 1];
     if (w < 3) {
       const int ib = w == 0 ? 0 : 1, jb = w == 2 ? 1 : 0;
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int m = 0; m < N / 32; ++m)
-        acc = mfma(ld_op(&sC[(16 * ib + lr) * SN + 32 * m + 8 * q]), ld_op(&sB[(16 * jb + lr) * SN + 32 * m + 8 * q]),
+        acc = mfma(ld_op(&sC[(16 * ib + lr) * SC + 32 * m + 8 * q]), ld_op(&sB[(16 * jb + lr) * SB + 32 * m + 8 * q]),
                    acc);
       const int j = 16 * jb + lr;
       const float cj = s_cum[j], dj = s_dt[j];
+      float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ib + 4 * q + r;
-        const float v = j <= i ? acc[r] * __builtin_amdgcn_exp2f(s_cum[i] - cj) * dj : 0.0f;
-        uint16_t hi, lo;
-        split_bf16(v, hi, lo);
-        sW[0][i * SQ + j] = hi;
-        sW[1][i * SQ + j] = lo;
+        v[r] = j <= i ? acc[r] * __builtin_amdgcn_exp2f(s_cum[i] - cj) * dj : 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const int i = 16 * ib + 4 * q + r;
+        const Split2 sp = split_bf16x2(v[r], v[r + 1]);
+        sW[0][i * SW + j] = (uint16_t)(sp.hi & 0xffffu);
+        sW[0][(i + 1) * SW + j] = (uint16_t)(sp.hi >> 16);
+        sW[1][i * SW + j] = (uint16_t)(sp.lo & 0xffffu);
+        sW[1][(i + 1) * SW + j] = (uint16_t)(sp.lo >> 16);
       }
     }
-    // The decayed, dt-weighted x of the state update, [p][j] as hi/lo.
+    // The decayed, dt-weighted x of the state update, from this thread's own
+    // staged vector: row j = xrow_i, channels 8 xc8 .. + 7, as hi/lo.
     {
-      const int pp = tid >> 2, j0 = (tid & 3) * 8;
-      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(&sXt[pp * SQ + j0]);
+      const float sc = s_xs[xrow_i];
       u32x4_t hv, lv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 2 * e;
-        uint16_t h0, l0, h1, l1;
-        split_bf16(bf16_to_f32(xv[e] & 0xffffu) * __builtin_amdgcn_exp2f(c_end - s_cum[j]) * s_dt[j], h0, l0);
-        split_bf16(__uint_as_float(xv[e] & 0xffff0000u) * __builtin_amdgcn_exp2f(c_end - s_cum[j + 1]) * s_dt[j + 1],
-                   h1, l1);
-        hv[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lv[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        const Split2 sp = split_bf16x2(bf16_to_f32(xreg[e] & 0xffffu) * sc, __uint_as_float(xreg[e] & 0xffff0000u) * sc);
+        hv[e] = sp.hi;
+        lv[e] = sp.lo;
       }
-      *reinterpret_cast<u32x4_t*>(&sXs[0][pp * SQ + j0]) = hv;
-      *reinterpret_cast<u32x4_t*>(&sXs[1][pp * SQ + j0]) = lv;
+      *reinterpret_cast<u32x4_t*>(&sXs[0][xrow_i * SP + xc8 * 8]) = hv;
+      *reinterpret_cast<u32x4_t*>(&sXs[1][xrow_i * SP + xc8 * 8]) = lv;
     }
     // The readout of the incoming state, Y = diag(exp(c_i)) C S^T, from the
     // state registers: tiles 2m and 2m + 1 give the eight k slots of product m
@@ -259,17 +317,21 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
     if (has_state) {
 #pragma unroll
       for (int m = 0; m < N / 32; ++m) {
-        bf16x8_t shi, slo;
+        u32x4_t hw, lw;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float v = r < 4 ? accS[2 * m][r] : accS[2 * m + 1][r - 4];
-          const __bf16 hv = (__bf16)v;
-          shi[r] = hv;
-          slo[r] = (__bf16)(v - (float)hv);
+        for (int r = 0; r < 4; r += 2) {
+          const Split2 s0 = split_bf16x2(accS[2 * m][r], accS[2 * m][r + 1]);
+          const Split2 s1 = split_bf16x2(accS[2 * m + 1][r], accS[2 * m + 1][r + 1]);
+          hw[r / 2] = s0.hi;
+          lw[r / 2] = s0.lo;
+          hw[2 + r / 2] = s1.hi;
+          lw[2 + r / 2] = s1.lo;
         }
+        const bf16x8_t shi = __builtin_bit_cast(bf16x8_t, hw);
+        const bf16x8_t slo = __builtin_bit_cast(bf16x8_t, lw);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
-          const uint16_t* crow = &sC[(16 * ib + lr) * SN + 32 * m + 4 * q];
+          const uint16_t* crow = &sC[(16 * ib + lr) * SC + 32 * m + 4 * q];
           const bf16x8_t ca = ld_op2(crow, crow + 16);
           accY[ib] = mfma(ca, shi, accY[ib]);
           accY[ib] = mfma(ca, slo, accY[ib]);
@@ -278,40 +340,34 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accY[ib][r] *= __builtin_amdgcn_exp2f(s_cum[16 * ib + 4 * q + r]);
+        for (int r = 0; r < 4; ++r) accY[ib][r] *= s_ec[16 * ib + 4 * q + r];
     }
     block_sync();
 
     // Phase 2.  Y += W X; D skip, gate and store; the state moves to the end
     // of the chunk.
     {
-      const bf16x8_t xo = ld_op(&sXt[p * SQ + 8 * q]);
+      const bf16x8_t xo = ld_col8(sX, SP, 8 * q, 16 * w, l);   // x[8q .. 8q + 7][p]
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
-        accY[ib] = mfma(ld_op(&sW[0][(16 * ib + lr) * SQ + 8 * q]), xo, accY[ib]);
-        accY[ib] = mfma(ld_op(&sW[1][(16 * ib + lr) * SQ + 8 * q]), xo, accY[ib]);
+        accY[ib] = mfma(ld_op(&sW[0][(16 * ib + lr) * SW + 8 * q]), xo, accY[ib]);
+        accY[ib] = mfma(ld_op(&sW[1][(16 * ib + lr) * SW + 8 * q]), xo, accY[ib]);
       }
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * ib + 4 * q + r;
-          float y = accY[ib][r];
-          if (a.D) y = __builtin_fmaf(Dp, bf16_to_f32(sXt[p * SQ + i]), y);
-          if (has_z) y = y * silu_f(bf16_to_f32(sZ[i * SP + p]));
-          if (i < nt) Io<Tout>::store(ob, (t0 + i) * xrow + p, y);
-        }
+      if (has_D && has_z) finish(accY, std::true_type(), std::true_type(), nt, t0);
+      else if (has_D) finish(accY, std::true_type(), std::false_type(), nt, t0);
+      else if (has_z) finish(accY, std::false_type(), std::true_type(), nt, t0);
+      else finish(accY, std::false_type(), std::false_type(), nt, t0);
     }
     {
-      const float e_end = __builtin_amdgcn_exp2f(c_end);
-      const bf16x8_t xh = ld_op(&sXs[0][p * SQ + 8 * q]);
-      const bf16x8_t xl = ld_op(&sXs[1][p * SQ + 8 * q]);
+      const float e_end = s_ec[kQ];
+      const bf16x8_t xh = ld_col8(sXs[0], SP, 8 * q, 16 * w, l);   // scaled x[8q .. 8q + 7][p]
+      const bf16x8_t xl = ld_col8(sXs[1], SP, 8 * q, 16 * w, l);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         f32x4_t acc = accS[t];
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] *= e_end;
-        const bf16x8_t bt = ld_op(&sBt[(16 * t + lr) * SQ + 8 * q]);
+        const bf16x8_t bt = ld_col8(sB, SB, 8 * q, 16 * t, l);     // B[8q .. 8q + 7][16t + lr]
         acc = mfma(bt, xh, acc);
         acc = mfma(bt, xl, acc);
         accS[t] = acc;
