@@ -352,7 +352,7 @@ def ssd_case(reps=20, decode_steps=64):
                         "softplus, D, z",
             "us_per_call": round(ms * 1e3, 1), "bytes_per_call": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("ssd_mamba2_2p7b")},
             "mfma": {"algorithmic_tflops": round(tflops, 1), "peak_bf16_tflops": 2500.0,
                      "frac": round(tflops / 2500.0, 4), "macs_per_call": macs},
             "decode_step": {"workload": f"ssm_ssd_state_update batch 64, {H_} heads x {P_}, d_state {N_}, bf16 in",
