@@ -28,14 +28,17 @@ namespace {
 // fixed-order reduction kernel: the result does not depend on timing.
 
 template <typename Tin, typename Tg, bool HAS_Z, int CW>
-__global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
   constexpr int NS = 4, G = 4, T = kBwdTile, NTHR = 256;
   constexpr int CPR = kWave / CW;
   constexpr int IPT = T * CPR / NTHR;
   static_assert(IPT >= 1 && IPT * NTHR == T * CPR, "tile does not split evenly");
   using R = Raw<Tin, CW>;
   using RG = Raw<Tg, CW>;
-  constexpr int RS = kWave + 4;  // staging row stride (16-byte aligned rows)
+  // B and C staging: one value per thread and tile (256 threads = T rows x 16
+  // states x {B, C} for 8-step tiles; both per thread for 16-step tiles)
+  constexpr bool kSplitBC = T * kDState * 2 <= NTHR;
+  static_assert(T * kDState * (kSplitBC ? 2 : 1) == NTHR, "B/C staging does not cover the tile");
 
   __shared__ float2 sh_dtu[T][kWave + 1];      // (dt2, u2)
   __shared__ float sh_dy[T][kWave + 1];
@@ -65,7 +68,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
   for (int i = 0; i < NS; ++i) Ad[i] = a.A[dl * kDState + g * NS + i];
 
   int irow[IPT], icol[IPT];
-  float ibias[IPT][CW], ibias2[IPT][CW], iD[IPT][CW];
+  float ibias[IPT][CW], iD[IPT][CW];
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
     const int idx = tid + it * NTHR;
@@ -75,7 +78,6 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
     for (int q = 0; q < CW; ++q) {
       const int64_t dq = d0 + min(icol[it] + q, nvalid - 1);
       ibias[it][q] = a.bias != nullptr ? a.bias[dq] : 0.0f;
-      ibias2[it][q] = ibias[it][q] * kLog2e;
       iD[it][q] = a.D != nullptr ? a.D[dq] : 0.0f;
     }
   }
@@ -109,14 +111,28 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
         if (HAS_Z) bk.rz[it].load(zb + off);
       }
     }
-    const int64_t t = t0 + min(tid / kDState, nt - 1);
-    bk.bv = ld_in(Bb + t * kDState + tid % kDState);
-    if (full) bk.cv = ld_in(Cb + t * kDState + tid % kDState);
+    if constexpr (kSplitBC) {
+      // waves 0..1 take B, waves 2..3 take C (uniform per wave)
+      const int64_t t = t0 + min((tid / kDState) % T, nt - 1);
+      if (tid < T * kDState) bk.bv = ld_in(Bb + t * kDState + tid % kDState);
+      else if (full) bk.bv = ld_in(Cb + t * kDState + tid % kDState);
+    } else {
+      const int64_t t = t0 + min(tid / kDState, nt - 1);
+      bk.bv = ld_in(Bb + t * kDState + tid % kDState);
+      if (full) bk.cv = ld_in(Cb + t * kDState + tid % kDState);
+    }
   };
   auto stage_bc = [&](const Bank& bk, bool with_c) SSM_INLINE {
-    const int r = tid / kDState, n = tid % kDState;
-    sh_B[r][n] = bk.bv * kLn2;
-    if (with_c) sh_C[r][n] = bk.cv;
+    const int n = tid % kDState;
+    if constexpr (kSplitBC) {
+      const int r = (tid / kDState) % T;
+      if (tid < T * kDState) sh_B[r][n] = bk.bv * kLn2;
+      else if (with_c) sh_C[r][n] = bk.bv;
+    } else {
+      const int r = tid / kDState;
+      sh_B[r][n] = bk.bv * kLn2;
+      if (with_c) sh_C[r][n] = bk.cv;
+    }
   };
 
   // ---- phase 1: forward, storing the state entering each tile
@@ -132,7 +148,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
     for (int it = 0; it < IPT; ++it) {
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
-        const float u2 = __builtin_fmaf(cur.rd[it].get(q), kLog2e, ibias2[it][q]);
+        const float u2 = (cur.rd[it].get(q) + ibias[it][q]) * kLog2e;
         const float dt2 = softplus ? softplus2_f(u2) : u2;
         sh_dtu[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * cur.rx[it].get(q));
       }
@@ -168,27 +184,21 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
   for (int64_t k = ntiles - 1; k >= 0; --k) {
     const int64_t t0 = k * T;
     const int nt = tile_rows(k);
-    float xv[IPT][CW], dyv[IPT][CW], dt2v[IPT][CW], sgv[IPT][CW], gv[IPT][CW], zv[IPT][CW];
+    // the tile's per-element values, from the raw inputs (which stay live for
+    // the tile; the finish below derives them again instead of keeping them)
+    auto elem = [&](int it, int q, float& x, float& dt2, float& dy) SSM_INLINE {
+      x = cur.rx[it].get(q);
+      const float u2 = (cur.rd[it].get(q) + ibias[it][q]) * kLog2e;
+      dt2 = softplus ? softplus2_f(u2) : u2;
+      dy = cur.rg[it].get(q);
+      if (HAS_Z) dy = dy * silu_f(cur.rz[it].get(q));
+    };
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
-        const float x = cur.rx[it].get(q);
-        const float u = cur.rd[it].get(q) + ibias[it][q];
-        const float u2 = __builtin_fmaf(cur.rd[it].get(q), kLog2e, ibias2[it][q]);
-        const float dt2 = softplus ? softplus2_f(u2) : u2;
-        const float gg = cur.rg[it].get(q);
-        float dy = gg;
-        if (HAS_Z) {
-          const float z = cur.rz[it].get(q);
-          zv[it][q] = z;
-          dy = gg * silu_f(z);
-        }
-        xv[it][q] = x;
-        gv[it][q] = gg;
-        dyv[it][q] = dy;
-        dt2v[it][q] = dt2;
-        sgv[it][q] = softplus ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u * kLog2e)) : 1.0f;
+        float x, dt2, dy;
+        elem(it, q, x, dt2, dy);
         sh_dtu[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * x);
         sh_dy[irow[it]][icol[it] + q] = dy;
       }
@@ -289,16 +299,19 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(BwdArgs a) {
             S2 += sh_s2[r][gg * kWave + col];
             if (HAS_Z) y += sh_y[r][gg * kWave + col];
           }
+          float xq, dt2q, dyq;
+          elem(it, q, xq, dt2q, dyq);
           if (HAS_Z) {
-            y = __builtin_fmaf(iD[it][q], xv[it][q], y);
-            const float z = zv[it][q];
+            y = __builtin_fmaf(iD[it][q], xq, y);
+            const float z = cur.rz[it].get(q);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
-            oz[q] = gv[it][q] * y * (sg * __builtin_fmaf(z, 1.0f - sg, 1.0f));
+            oz[q] = cur.rg[it].get(q) * y * (sg * __builtin_fmaf(z, 1.0f - sg, 1.0f));
           }
-          ox[q] = __builtin_fmaf(dyv[it][q], iD[it][q], dt2v[it][q] * S1);
-          const float ddt = __builtin_fmaf(xv[it][q] * kLog2e, S1, S2);
-          od[q] = ddt * sgv[it][q];
-          dDacc[it][q] = __builtin_fmaf(dyv[it][q], xv[it][q], dDacc[it][q]);
+          ox[q] = __builtin_fmaf(dyq, iD[it][q], dt2q * S1);
+          const float ddt = __builtin_fmaf(xq * kLog2e, S1, S2);
+          const float u = cur.rd[it].get(q) + ibias[it][q];
+          od[q] = softplus ? ddt * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u * kLog2e)) : ddt;
+          dDacc[it][q] = __builtin_fmaf(dyq, xq, dDacc[it][q]);
           dBacc[it][q] += od[q];
         }
         const int64_t off = (t0 + r) * Dn + icol[it];
@@ -391,9 +404,10 @@ template <typename Tin, typename Tg>
 void launch_scan_bwd_t(const BwdArgs& a, float* dA, void* dB, void* dC, float* dD, float* dbias, hipStream_t s) {
   const dim3 grid((unsigned)a.nblk, (unsigned)a.batch);
   if (a.seqlen > 0) {
-    if (a.d_inner % 4 == 0) {
-      if (a.z != nullptr) hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, true, 4>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, false, 4>), grid, dim3(256), 0, s, a);
+    // channels per element item: 8-step tiles x 64 channels = 256 threads x 2
+    if (a.d_inner % 2 == 0) {
+      if (a.z != nullptr) hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, true, 2>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, false, 2>), grid, dim3(256), 0, s, a);
     } else {
       if (a.z != nullptr) hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, true, 1>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, false, 1>), grid, dim3(256), 0, s, a);

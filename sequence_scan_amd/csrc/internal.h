@@ -119,7 +119,7 @@ struct BwdArgs {
   int32_t nblk;           // ceil(d_inner / 64)
 };
 
-constexpr int kBwdTile = 16;  // steps per backward tile (and per checkpoint)
+constexpr int kBwdTile = 8;  // steps per backward tile (and per checkpoint)
 
 // Launchers; each returns the hipGetLastError() of its launches.
 hipError_t launch_scan(const ScanArgs& a, DT in, DT out, int states_per_wave, hipStream_t s);
