@@ -231,6 +231,7 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
   a.zoh = (softplus & SSM_ZOH) ? 1 : 0;
   a.batch = (int32_t)batch;
+  a.cus = device_simds() / 4;
 
   void* ws = nullptr;
   hipError_t e = hipSuccess;

@@ -157,6 +157,20 @@ __device__ __forceinline__ float silu_f(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// The wavefronts that share a SIMD are issued oldest first.  When every
+// workgroup of a grid is resident at once, the workgroups placed last on a CU
+// therefore fall behind and finish alone, with one wavefront per SIMD.
+// Lowering a wavefront's issue priority as it progresses (four levels, one per
+// quarter of its work) hands issue slots to the wavefronts that lag, so the
+// workgroups of a CU finish together.  done / total is uniform in the wave.
+__device__ __forceinline__ void yield_by_progress(int64_t done, int64_t total) {
+  const int q = (int)((done * 4) / total);
+  if (q <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // ------------------------------------------------ wavefront affine-pair scan
 
 #define SSM_DPP(old, src, ctrl, rmask)                                                    \

@@ -33,6 +33,8 @@ struct ScanArgs {
   int32_t softplus;
   int32_t batch;
   int32_t zoh;            // exact zero-order-hold input coefficient
+  int32_t cus;            // compute units of the device
+  int32_t fair;           // set by the launcher: the whole grid is co-resident
 };
 
 struct DecodeArgs {

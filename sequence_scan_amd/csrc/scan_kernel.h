@@ -321,6 +321,7 @@ scan_chunk_kernel(ScanArgs a) {
     int64_t f = 1;
     for (; f + 1 < nfull; f += 2) {
       const int64_t t0 = tail + f * T;
+      if (a.fair) yield_by_progress(f, nfull);
       full_tile(bk0, t0, min(t0 + 2 * T, last_full), std::true_type(), t0 - T);
       full_tile(bk1, t0 + T, min(t0 + 3 * T, last_full), std::true_type(), t0);
     }
@@ -341,21 +342,43 @@ scan_chunk_kernel(ScanArgs a) {
 }
 
 
+// Workgroups of `kern` that one CU holds at once (0 if the query fails).
+template <typename K>
+int resident_per_cu(K kern, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess) n = 0;
+  return n;
+}
+
+// Launch one pass; the progress-priority scheme (yield_by_progress) is turned
+// on when the device holds the whole grid at once.
+template <typename K>
+void launch_pass(K kern, int per_cu, dim3 grid, int threads, const ScanArgs& a, hipStream_t s) {
+  ScanArgs b = a;
+  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+  b.fair = (per_cu > 0 && a.cus > 0 && wgs <= (int64_t)per_cu * a.cus) ? 1 : 0;
+  hipLaunchKernelGGL(kern, grid, dim3(threads), 0, s, b);
+}
+
 template <typename Tin, typename Tout, int NS, bool WIDE, bool ZOH>
 hipError_t launch_scan_w(const ScanArgs& a, hipStream_t s) {
   constexpr int G = kDState / NS;
+  constexpr int NTHR = kWave * G;
+  const auto kA = scan_chunk_kernel<Tin, Tout, NS, true, false, WIDE, ZOH>;
+  const auto kBz = scan_chunk_kernel<Tin, Tout, NS, false, true, WIDE, ZOH>;
+  const auto kB = scan_chunk_kernel<Tin, Tout, NS, false, false, WIDE, ZOH>;
+  static const int occA = resident_per_cu(kA, NTHR);
+  static const int occBz = resident_per_cu(kBz, NTHR);
+  static const int occB = resident_per_cu(kB, NTHR);
   const unsigned nblk = (unsigned)((a.d_inner + kWave - 1) / kWave);
   if (a.n_chunks > 1) {
-    dim3 gridA(nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch);
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, true, false, WIDE, ZOH>), gridA, dim3(kWave * G), 0, s, a);
+    launch_pass(kA, occA, dim3(nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch), NTHR, a, s);
     const hipError_t e = launch_carry(a, s);
     if (e != hipSuccess) return e;
   }
-  dim3 gridB(nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
-  if (a.z != nullptr)
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, true, WIDE, ZOH>), gridB, dim3(kWave * G), 0, s, a);
-  else
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, NS, false, false, WIDE, ZOH>), gridB, dim3(kWave * G), 0, s, a);
+  const dim3 gridB(nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
+  if (a.z != nullptr) launch_pass(kBz, occBz, gridB, NTHR, a, s);
+  else launch_pass(kB, occB, gridB, NTHR, a, s);
   return hipGetLastError();
 }
 
