@@ -40,6 +40,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Streaming (non-temporal) 16-byte access to four floats, for data that a
+// kernel touches once: the decode kernels' states, which one step reads and
+// writes and the next step reads again after every other state has passed
+// through the caches.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream4(float* p, float4 v) {
+  const f32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t*>(p));
+}
+
 template <typename T>
 struct Io;
 

@@ -409,7 +409,7 @@ __global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a, int64_t rows
   const float x = ld_in(static_cast<const Tin*>(a.x) + row);
   const float dtx = dt * x;
   float* st = a.state + row * N + 4 * q;
-  float4 s4 = *reinterpret_cast<const float4*>(st);
+  float4 s4 = load_stream4(st);  // the state streams, as in the Mamba-1 decode
   float hs[4] = {s4.x, s4.y, s4.z, s4.w};
   const int64_t bc = (b * G + g) * N + 4 * q;
   float y = 0.0f;
@@ -420,7 +420,7 @@ __global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a, int64_t rows
     hs[i] = __builtin_fmaf(ar, hs[i], dtx * Bv);
     y = __builtin_fmaf(Cv, hs[i], y);
   }
-  *reinterpret_cast<float4*>(st) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+  store_stream4(st, make_float4(hs[0], hs[1], hs[2], hs[3]));
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) y += __shfl_xor(y, m, LPR);
   if (q == 0) {
