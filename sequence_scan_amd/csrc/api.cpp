@@ -498,6 +498,7 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
   a.batch = (int32_t)batch;
   a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
   a.nblk = (int32_t)nblk;
+  a.cus = device_simds() / 4;
   e = ssm::launch_scan_bwd(a, to_dt(in_dtype), to_dt(grad_dtype), dA, dB, dC, dD, ddelta_bias, s);
   hipError_t e2 = hipFreeAsync(ws, s);
   if (e == hipSuccess) e = e2;
@@ -669,6 +670,7 @@ ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void
   a.ngroups = (int32_t)ngroups;
   a.d_state = (int32_t)d_state;
   a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
+  a.cus = device_simds() / 4;
   hipError_t e = ssm::launch_ssd(a, to_dt(out_dtype), s);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();

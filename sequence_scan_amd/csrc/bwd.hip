@@ -139,9 +139,13 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
   float h[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) h[i] = a.h0 != nullptr ? a.h0[(b * Dn + dl) * kDState + g * NS + i] : 0.0f;
+  // Progress weights for ProgressPriority: a phase-1 tile counts 2, a
+  // phase-2 tile (about 4.5 times the work) 9.
+  const ProgressPriority prio(11 * ntiles);
   Bank cur, nxt;
   load(cur, 0, false);
   for (int64_t k = 0; k < ntiles; ++k) {
+    if (a.fair) prio.at(2 * k);
     const int nt = tile_rows(k);
     *reinterpret_cast<float4*>(ck + (k * kWave + lane) * kDState + g * NS) = make_float4(h[0], h[1], h[2], h[3]);
 #pragma unroll
@@ -182,6 +186,7 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
   load(cur, ntiles - 1, true);
   float4 hc = *reinterpret_cast<const float4*>(ck + ((ntiles - 1) * kWave + lane) * kDState + g * NS);
   for (int64_t k = ntiles - 1; k >= 0; --k) {
+    if (a.fair) prio.at(2 * ntiles + 9 * (ntiles - 1 - k));
     const int64_t t0 = k * T;
     const int nt = tile_rows(k);
     // the tile's per-element values, from the raw inputs (which stay live for
@@ -400,17 +405,26 @@ __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(const float* ws_
 
 namespace {
 
+// One launch of a backward kernel instance, with the progress-priority scheme
+// (ProgressPriority) on when the device holds the whole grid at once.
+template <typename K>
+void launch_bwd_pass(K kern, dim3 grid, const BwdArgs& a, hipStream_t s) {
+  BwdArgs b = a;
+  b.fair = grid_coresident(resident_per_cu(kern, 256), a.cus, grid) ? 1 : 0;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, b);
+}
+
 template <typename Tin, typename Tg>
 void launch_scan_bwd_t(const BwdArgs& a, float* dA, void* dB, void* dC, float* dD, float* dbias, hipStream_t s) {
   const dim3 grid((unsigned)a.nblk, (unsigned)a.batch);
   if (a.seqlen > 0) {
     // channels per element item: 8-step tiles x 64 channels = 256 threads x 2
     if (a.d_inner % 2 == 0) {
-      if (a.z != nullptr) hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, true, 2>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, false, 2>), grid, dim3(256), 0, s, a);
+      if (a.z != nullptr) launch_bwd_pass(scan_bwd_kernel<Tin, Tg, true, 2>, grid, a, s);
+      else launch_bwd_pass(scan_bwd_kernel<Tin, Tg, false, 2>, grid, a, s);
     } else {
-      if (a.z != nullptr) hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, true, 1>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, false, 1>), grid, dim3(256), 0, s, a);
+      if (a.z != nullptr) launch_bwd_pass(scan_bwd_kernel<Tin, Tg, true, 1>, grid, a, s);
+      else launch_bwd_pass(scan_bwd_kernel<Tin, Tg, false, 1>, grid, a, s);
     }
     const int64_t rows = (int64_t)a.batch * a.seqlen;
     const int64_t n = rows * 2 * kDState;

@@ -178,13 +178,32 @@ __device__ __forceinline__ float silu_f(float z) {
 // therefore fall behind and finish alone, with one wavefront per SIMD.
 // Lowering a wavefront's issue priority as it progresses (four levels, one per
 // quarter of its work) hands issue slots to the wavefronts that lag, so the
-// workgroups of a CU finish together.  done / total is uniform in the wave.
-__device__ __forceinline__ void yield_by_progress(int64_t done, int64_t total) {
-  const int q = (int)((done * 4) / total);
-  if (q <= 0) __builtin_amdgcn_s_setprio(3);
-  else if (q == 1) __builtin_amdgcn_s_setprio(2);
-  else if (q == 2) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
+// workgroups of a CU finish together.  Work counts are uniform in the wave.
+struct ProgressPriority {
+  int64_t q1, q2, q3;  // first item of the second, third and fourth quarter
+  __device__ explicit ProgressPriority(int64_t total)
+      : q1((total + 3) / 4), q2((2 * total + 3) / 4), q3((3 * total + 3) / 4) {}
+  __device__ __forceinline__ void at(int64_t done) const {
+    if (done < q1) __builtin_amdgcn_s_setprio(3);
+    else if (done < q2) __builtin_amdgcn_s_setprio(2);
+    else if (done < q3) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
+};
+
+// Host side: workgroups of `kern` that one CU holds at once (0 if the query
+// fails), and whether a grid of that kernel is resident all at once on a
+// device of `cus` CUs.
+template <typename K>
+inline int resident_per_cu(K kern, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess) n = 0;
+  return n;
+}
+
+inline bool grid_coresident(int per_cu, int cus, dim3 grid) {
+  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+  return per_cu > 0 && cus > 0 && wgs <= (int64_t)per_cu * cus;
 }
 
 // ------------------------------------------------ wavefront affine-pair scan

@@ -91,6 +91,8 @@ struct SsdArgs {
   int32_t ngroups;
   int32_t d_state;
   int32_t softplus;
+  int32_t cus;            // compute units of the device
+  int32_t fair;           // set by the launcher: the whole grid is co-resident
 };
 
 // Backward of the scan.  Elementwise gradients and dout share one dtype.
@@ -119,6 +121,8 @@ struct BwdArgs {
   int32_t batch;
   int32_t softplus;
   int32_t nblk;           // ceil(d_inner / 64)
+  int32_t cus;            // compute units of the device
+  int32_t fair;           // set by the launcher: the whole grid is co-resident
 };
 
 constexpr int kBwdTile = 8;  // steps per backward tile (and per checkpoint)

@@ -318,10 +318,11 @@ scan_chunk_kernel(ScanArgs a) {
   // stores the outputs of tile f - 1
   if (nfull > 0) {
     full_tile(bk1, tail, min(tail + 2 * T, last_full), std::false_type(), 0);
+    const ProgressPriority prio(nfull);
     int64_t f = 1;
     for (; f + 1 < nfull; f += 2) {
       const int64_t t0 = tail + f * T;
-      if (a.fair) yield_by_progress(f, nfull);
+      if (a.fair) prio.at(f);
       full_tile(bk0, t0, min(t0 + 2 * T, last_full), std::true_type(), t0 - T);
       full_tile(bk1, t0 + T, min(t0 + 3 * T, last_full), std::true_type(), t0);
     }
@@ -342,21 +343,12 @@ scan_chunk_kernel(ScanArgs a) {
 }
 
 
-// Workgroups of `kern` that one CU holds at once (0 if the query fails).
-template <typename K>
-int resident_per_cu(K kern, int threads) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess) n = 0;
-  return n;
-}
-
-// Launch one pass; the progress-priority scheme (yield_by_progress) is turned
+// Launch one pass; the progress-priority scheme (ProgressPriority) is turned
 // on when the device holds the whole grid at once.
 template <typename K>
 void launch_pass(K kern, int per_cu, dim3 grid, int threads, const ScanArgs& a, hipStream_t s) {
   ScanArgs b = a;
-  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
-  b.fair = (per_cu > 0 && a.cus > 0 && wgs <= (int64_t)per_cu * a.cus) ? 1 : 0;
+  b.fair = grid_coresident(per_cu, a.cus, grid) ? 1 : 0;
   hipLaunchKernelGGL(kern, grid, dim3(threads), 0, s, b);
 }
 

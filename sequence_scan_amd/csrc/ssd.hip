@@ -258,8 +258,10 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
   };
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
+  const ProgressPriority prio(nchunks);
   issue(0, (int)min((int64_t)kQ, L));
   for (int64_t ch = 0; ch < nchunks; ++ch) {
+    if (a.fair) prio.at(ch);
     const int64_t t0 = ch * kQ;
     const int nt = (int)min((int64_t)kQ, L - t0);
     stage(nt);
@@ -430,11 +432,19 @@ __global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a, int64_t rows
   }
 }
 
+template <int N, typename Tout>
+void launch_ssd_nt(const SsdArgs& a, hipStream_t s) {
+  static const int per_cu = resident_per_cu(ssd_chunk_kernel<N, Tout>, 256);
+  const dim3 grid((unsigned)a.nheads, (unsigned)a.batch);
+  SsdArgs b = a;
+  b.fair = grid_coresident(per_cu, a.cus, grid) ? 1 : 0;  // see ProgressPriority
+  hipLaunchKernelGGL((ssd_chunk_kernel<N, Tout>), grid, dim3(256), 0, s, b);
+}
+
 template <int N>
 void launch_ssd_n(const SsdArgs& a, DT out, hipStream_t s) {
-  const dim3 grid((unsigned)a.nheads, (unsigned)a.batch);
-  if (out == DT::F32) hipLaunchKernelGGL((ssd_chunk_kernel<N, float>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ssd_chunk_kernel<N, uint16_t>), grid, dim3(256), 0, s, a);
+  if (out == DT::F32) launch_ssd_nt<N, float>(a, s);
+  else launch_ssd_nt<N, uint16_t>(a, s);
 }
 
 template <typename Tin, typename Tout>
