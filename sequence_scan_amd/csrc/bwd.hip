@@ -216,17 +216,26 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
     }
     block_sync();
 
-    // forward within the tile: each step's incoming state, and readout partials
-    float hp[T][NS];
+    // forward within the tile: each step's incoming state, and readout
+    // partials; steps past a ragged tile's end keep the final state, so
+    // hp[s + 1] (or h after the last step) is the state after step s
+    // With two channels per item the transitions a of the tile also stay in
+    // registers for the reverse walk (32 VGPRs, 163 in all: still three
+    // workgroups per CU); the one-channel variant recomputes them, which
+    // keeps it from spilling.
+    constexpr bool kKeepA = CW == 2;
+    float hp[T][NS], ap[T][NS];
 #pragma unroll
     for (int s = 0; s < T; ++s) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) hp[s][i] = h[i];
       if (s < nt) {
         const float2 v = sh_dtu[s][loff];
         float y = 0.0f;
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-          hp[s][i] = h[i];
-          h[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(v.x * Ad[i]), h[i], v.y * sh_B[s][g * NS + i]);
+          ap[s][i] = __builtin_amdgcn_exp2f(v.x * Ad[i]);
+          h[i] = __builtin_fmaf(ap[s][i], h[i], v.y * sh_B[s][g * NS + i]);
           y = __builtin_fmaf(sh_C[s][g * NS + i], h[i], y);
         }
         sh_y[s][g * kWave + lane] = y;
@@ -242,10 +251,10 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
         float s1 = 0.0f, s2 = 0.0f, cb[NS], cc[NS];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-          const float aa = __builtin_amdgcn_exp2f(v.x * Ad[i]);
+          const float aa = kKeepA ? ap[s][i] : __builtin_amdgcn_exp2f(v.x * Ad[i]);
           const float Bs = sh_B[s][g * NS + i];
           const float dh = __builtin_fmaf(dy, sh_C[s][g * NS + i], carry[i]);
-          const float hs = __builtin_fmaf(aa, hp[s][i], v.y * Bs);
+          const float hs = s + 1 < T ? hp[s + 1][i] : h[i];  // the state after step s
           cc[i] = dy * hs;
           cb[i] = dh * v.y;
           s1 = __builtin_fmaf(dh, Bs, s1);
