@@ -21,7 +21,8 @@ namespace {
 // lane, as in the forward).  Phase 1 runs the forward and stores the state
 // entering every tile of kBwdTile steps.  Phase 2 walks the tiles backwards:
 // it recomputes the tile's forward from its checkpoint (keeping each step's
-// incoming state in registers), then runs the reverse recurrence.  Sums over a
+// incoming state, and with two-channel items each transition, in registers),
+// then runs the reverse recurrence on those values.  Sums over a
 // channel's 16 states go through LDS partials, summed in a fixed order; dB and
 // dC are reduced over the wavefront's 64 channels through a wave-local LDS
 // transpose and 3 DPP steps, and stored per channel block for a second,
@@ -95,7 +96,7 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
   struct Bank {
     R rx[IPT], rd[IPT], rz[IPT];
     RG rg[IPT];
-    float bv, cv;   // this thread's B, C element (256 threads = 16 rows x 16 states)
+    float bv, cv;   // this thread's staged B or C element (cv only when one thread stages both)
   };
   auto tile_rows = [&](int64_t k) SSM_INLINE { return (int)min((int64_t)T, L - k * T); };
   auto load = [&](Bank& bk, int64_t k, bool full) SSM_INLINE {

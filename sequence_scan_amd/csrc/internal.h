@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host layer (api.cpp) and the gfx950
-// kernels (kernels.hip).  Not installed; not part of the ABI.
+// kernel units (scan_inst.hip, scan.hip, conv.hip, bwd.hip, ssd.hip).  Not
+// installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,7 +8,7 @@
 
 namespace ssm {
 
-constexpr int kDState = 16;   // the one d_state this build supports
+constexpr int kDState = 16;   // the Mamba-1 scan's d_state (the SSD kernels take 64 or 128)
 constexpr int kWave = 64;     // gfx950 wavefront size
 
 enum class DT : int { F32 = 0, BF16 = 1 };
