@@ -40,6 +40,11 @@
  * asynchronous on `stream` (a hipStream_t; NULL is the null stream): faults
  * during execution surface at the caller's next synchronisation.  Results
  * are bitwise reproducible for identical inputs and plan (no atomics).
+ *
+ * Graph capture: a call enqueues only kernels on `stream` (zero fills and
+ * state copies are kernels, not memset or memcpy nodes), plus the
+ * stream-ordered workspace allocation above, so it may be captured in a HIP
+ * graph and replayed; the host checks run at capture time.
  */
 #ifndef SSMSCAN_H
 #define SSMSCAN_H
