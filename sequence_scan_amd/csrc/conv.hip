@@ -26,8 +26,13 @@ namespace {
 // Grid: x = blocks of 64 channel groups (one wavefront), y = runs (strided),
 // z = batch row, so the run (and with it every load and store condition) is
 // uniform across the wavefront.
+// With write_cache, the thread that runs a channel group's last run also
+// stores the outgoing cache from its final window (the last K inputs, oldest
+// first); the host asks for this only when the outgoing cache is not the
+// incoming one, which other runs may still be reading.
 template <typename Tin, typename Tout, int K, int CW, bool SILU>
-__global__ void __launch_bounds__(64) conv1d_kernel(ConvArgs a, int64_t groups, int64_t runs, int run_len) {
+__global__ void __launch_bounds__(64) conv1d_kernel(ConvArgs a, int64_t groups, int64_t runs, int run_len,
+                                                    int write_cache) {
   using R = Raw<Tin, CW>;
   const int64_t cg = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (cg >= groups) return;
@@ -108,6 +113,22 @@ __global__ void __launch_bounds__(64) conv1d_kernel(ConvArgs a, int64_t groups, 
         float y[CW];
         step(win, xr, y);
         store_row<Tout, CW>(ob + (t0 + j) * Dn, y);
+      }
+    }
+    if (write_cache && r == runs - 1) {
+      // exact: every window value came from a Tin
+      Tin* cache = static_cast<Tin*>(a.state_out) + (b * Dn + d0) * K;
+      constexpr int kCacheBytes = CW * K * (int)sizeof(Tin);
+      float cv[CW * K];
+#pragma unroll
+      for (int q = 0; q < CW; ++q)
+#pragma unroll
+        for (int k = 0; k < K; ++k) cv[q * K + k] = win[k][q];
+      if constexpr (kCacheBytes == 4 || kCacheBytes == 8 || kCacheBytes % 16 == 0) {
+        store_row<Tin, CW * K>(cache, cv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < CW * K; ++j) st_in(cache + j, cv[j]);
       }
     }
   }
@@ -191,11 +212,21 @@ __global__ void __launch_bounds__(256) conv1d_update_kernel(ConvArgs a, int64_t 
 namespace {
 
 // Run length: 32 steps, doubled while the grid would need more than about
-// three wavefronts per SIMD (the kernel's occupancy), so that one round of
-// resident wavefronts covers the whole sequence.
+// six wavefronts per SIMD, so that few rounds of wavefronts cover the whole
+// sequence and each run's K - 1 re-read steps stay a small share.  (On
+// MI355X: 32 steps for the Mamba-2.8B-like layer ran 80.5 us against 84.5 us
+// at 64; 16 steps slowed narrow layers; the 2^18-step sequence runs 256 at
+// copy speed.)
+// The prefill kernel stores the outgoing cache itself unless it is the
+// incoming one (updated in place): then a separate kernel, launched after the
+// prefill, reads each channel's inputs before writing them.
+bool conv_cache_fused(const ConvArgs& a) {
+  return a.state_out != nullptr && a.state_out != a.state_in && a.seqlen > 0;
+}
+
 int conv_run_len(int64_t waves_per_step_row, int64_t batch, int64_t seqlen) {
   int run = 32;
-  while (run < 256 && waves_per_step_row * batch * ((seqlen + run - 1) / run) > 3 * 1024) run *= 2;
+  while (run < 256 && waves_per_step_row * batch * ((seqlen + run - 1) / run) > 6 * 1024) run *= 2;
   return run;
 }
 
@@ -206,10 +237,11 @@ void launch_conv1d_cw(const ConvArgs& a, hipStream_t s) {
   const int run = conv_run_len(gblocks, a.batch, a.seqlen);
   const int64_t runs = (a.seqlen + run - 1) / run;
   const dim3 grid((unsigned)gblocks, (unsigned)min(runs, (int64_t)65535), (unsigned)a.batch);
+  const int wc = conv_cache_fused(a) ? 1 : 0;
   if (a.silu)
-    hipLaunchKernelGGL((conv1d_kernel<Tin, Tout, K, CW, true>), grid, dim3(64), 0, s, a, groups, runs, run);
+    hipLaunchKernelGGL((conv1d_kernel<Tin, Tout, K, CW, true>), grid, dim3(64), 0, s, a, groups, runs, run, wc);
   else
-    hipLaunchKernelGGL((conv1d_kernel<Tin, Tout, K, CW, false>), grid, dim3(64), 0, s, a, groups, runs, run);
+    hipLaunchKernelGGL((conv1d_kernel<Tin, Tout, K, CW, false>), grid, dim3(64), 0, s, a, groups, runs, run, wc);
 }
 
 template <typename Tin, typename Tout, int K>
@@ -219,7 +251,7 @@ hipError_t launch_conv1d_k(const ConvArgs& a, hipStream_t s) {
     if (a.d_inner % CWV == 0) launch_conv1d_cw<Tin, Tout, K, CWV>(a, s);
     else launch_conv1d_cw<Tin, Tout, K, 1>(a, s);
   }
-  if (a.state_out != nullptr && a.batch > 0 && a.d_inner > 0) {
+  if (a.state_out != nullptr && a.batch > 0 && a.d_inner > 0 && !conv_cache_fused(a)) {
     const int64_t blocks = ((int64_t)a.batch * a.d_inner + 255) / 256;
     hipLaunchKernelGGL((conv1d_state_kernel<Tin, K>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   }
