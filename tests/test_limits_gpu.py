@@ -1,0 +1,128 @@
+"""GPU parity at the limits of the C ABI: the largest batch (65535, one grid
+dimension) and tensors of more than 2^31 elements, whose offsets need 64-bit
+arithmetic.  Inputs are drawn on the GPU from a seeded generator (the sizes are
+too large to draw on the host); the oracle runs on the channels and rows
+sampled from the same values."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import rowinf, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+ssm = pytest.importorskip("sequence_scan_amd")
+
+TOL_BF16 = 2e-3
+N = 16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    ssm.library()
+
+
+def _normal_bf16(shape, gen):
+    out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    flat = out.view(-1)
+    step = 1 << 28  # draw in pieces to bound the fp32 temporary
+    for i in range(0, flat.numel(), step):
+        n = min(step, flat.numel() - i)
+        flat[i:i + n] = torch.randn(n, generator=gen, device="cuda").to(torch.bfloat16)
+    return out
+
+
+def _delta_bf16(shape, gen):
+    # softplus^-1 of steps log-uniform in [1e-3, 0.1] lies in [-6.907, -2.252]
+    out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    flat = out.view(-1)
+    step = 1 << 28
+    for i in range(0, flat.numel(), step):
+        n = min(step, flat.numel() - i)
+        flat[i:i + n] = (torch.rand(n, generator=gen, device="cuda") * 4.655 - 6.907).to(torch.bfloat16)
+    return out
+
+
+def _params(d_inner):
+    A = (-torch.arange(1, N + 1, dtype=torch.float32)).repeat(d_inner, 1).contiguous()
+    return A.cuda(), torch.ones(d_inner, device="cuda"), torch.zeros(d_inner, device="cuda")
+
+
+def _np(t):
+    return t.float().cpu().numpy()
+
+
+def test_max_batch_scan_and_decode():
+    batch, L, Dn = 65535, 3, 8
+    say(f"limits: batch {batch} (the maximum), seqlen {L}, d_inner {Dn}: scan, then one decode step")
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    x, z = _normal_bf16((batch, L, Dn), gen), _normal_bf16((batch, L, Dn), gen)
+    dl = _delta_bf16((batch, L, Dn), gen)
+    B, C = _normal_bf16((batch, L, N), gen), _normal_bf16((batch, L, N), gen)
+    A, D, bias = _params(Dn)
+    last = torch.empty((batch, Dn, N), device="cuda")
+    out = ssm.ssm_scan_fwd(x, dl, A, B, C, D, z, bias, out_dtype=torch.float32, last_state=last)
+    # one more step from the final state
+    xs, ds, zs = x[:, 0].contiguous(), dl[:, 0].contiguous(), z[:, 0].contiguous()
+    Bs, Cs = B[:, 0].contiguous(), C[:, 0].contiguous()
+    st = last.clone()
+    yd = ssm.ssm_state_update(st, xs, ds, A, Bs, Cs, D, zs, bias, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    An, Dnp, bn = _np(A), _np(D), _np(bias)
+    ref, ref_last = oracle.scan_fwd(_np(x), _np(dl), An, _np(B), _np(C), Dnp, _np(z), bn)
+    assert rowinf(_np(out), ref, 1) <= TOL_BF16
+    assert rowinf(_np(last), ref_last, 2) <= TOL_BF16
+    ref_y, ref_st = oracle.state_update(ref_last, _np(xs), _np(ds), An, _np(Bs), _np(Cs), Dnp, _np(zs), bn)
+    assert rowinf(_np(yd), ref_y, 1) <= TOL_BF16  # one step: rows are batch items over channels
+    assert rowinf(_np(st), ref_st, 2) <= TOL_BF16
+
+
+def test_scan_over_2g_elements_sampled():
+    batch, L, Dn = 1, (1 << 19) + 5, 4160  # 2.18e9 elements; 65 channel blocks; a ragged tail
+    plan = ssm.ssm_scan_plan(batch, L, Dn)
+    say(f"limits: scan over {batch * L * Dn / 1e9:.2f}e9 elements (batch {batch}, seqlen {L}, d_inner {Dn}), "
+        f"plan {plan}")
+    assert batch * L * Dn > 2 ** 31
+    gen = torch.Generator(device="cuda").manual_seed(32)
+    x, z = _normal_bf16((batch, L, Dn), gen), _normal_bf16((batch, L, Dn), gen)
+    dl = _delta_bf16((batch, L, Dn), gen)
+    B, C = _normal_bf16((batch, L, N), gen), _normal_bf16((batch, L, N), gen)
+    A, D, bias = _params(Dn)
+    last = torch.empty((batch, Dn, N), device="cuda")
+    out = ssm.ssm_scan_fwd(x, dl, A, B, C, D, z, bias, out_dtype=torch.float32, last_state=last)
+    torch.cuda.synchronize()
+    sel = [0, 2111, Dn - 1]  # first block, a middle one, the last channel
+    ref, ref_last = oracle.scan_fwd(_np(x[:, :, sel]), _np(dl[:, :, sel]), _np(A[sel]), _np(B), _np(C),
+                                    _np(D[sel]), _np(z[:, :, sel]), _np(bias[sel]))
+    got = _np(out[:, :, sel])
+    assert np.all(np.isfinite(got))
+    assert rowinf(got, ref, 1) <= TOL_BF16
+    assert rowinf(_np(last[:, sel]), ref_last, 2) <= TOL_BF16
+    # the last steps of the last channel, where a 32-bit offset would first wrap
+    assert rowinf(got[:, -4096:, -1:], ref[:, -4096:, -1:], 1) <= TOL_BF16
+
+
+def test_decode_over_2g_state_values_sampled():
+    batch, Dn = 65535, 2112  # state: 2.21e9 fp32 values
+    say(f"limits: decode step with a {batch * Dn * N / 1e9:.2f}e9-value state (batch {batch}, d_inner {Dn})")
+    assert batch * Dn * N > 2 ** 31
+    gen = torch.Generator(device="cuda").manual_seed(33)
+    st = torch.empty((batch, Dn, N), device="cuda")
+    flat = st.view(-1)
+    for i in range(0, flat.numel(), 1 << 28):
+        n = min(1 << 28, flat.numel() - i)
+        flat[i:i + n] = torch.randn(n, generator=gen, device="cuda")
+    x, z = _normal_bf16((batch, Dn), gen), _normal_bf16((batch, Dn), gen)
+    dl = _delta_bf16((batch, Dn), gen)
+    B, C = _normal_bf16((batch, N), gen), _normal_bf16((batch, N), gen)
+    A, D, bias = _params(Dn)
+    rows = [0, 1, 40000, batch - 1]
+    st0 = _np(st[rows])
+    y = ssm.ssm_state_update(st, x, dl, A, B, C, D, z, bias, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_y, ref_st = oracle.state_update(st0, _np(x[rows]), _np(dl[rows]), _np(A), _np(B[rows]), _np(C[rows]),
+                                        _np(D), _np(z[rows]), _np(bias))
+    assert rowinf(_np(y[rows]), ref_y, 1) <= TOL_BF16  # one step: rows are batch items over channels
+    assert rowinf(_np(st[rows]), ref_st, 2) <= TOL_BF16
