@@ -126,3 +126,49 @@ def test_decode_over_2g_state_values_sampled():
                                         _np(D), _np(z[rows]), _np(bias))
     assert rowinf(_np(y[rows]), ref_y, 1) <= TOL_BF16  # one step: rows are batch items over channels
     assert rowinf(_np(st[rows]), ref_st, 2) <= TOL_BF16
+
+
+def test_conv1d_over_2g_elements_sampled():
+    batch, L, Dn, K = 1, (1 << 19) + 5, 4160, 4  # 2.18e9 elements
+    say(f"limits: conv1d over {batch * L * Dn / 1e9:.2f}e9 elements (batch {batch}, seqlen {L}, d_inner {Dn})")
+    assert batch * L * Dn > 2 ** 31
+    gen = torch.Generator(device="cuda").manual_seed(34)
+    x = _normal_bf16((batch, L, Dn), gen)
+    cache_in = _normal_bf16((batch, Dn, K), gen)
+    w = torch.randn((Dn, K), generator=gen, device="cuda") * 0.5
+    b = torch.randn((Dn,), generator=gen, device="cuda") * 0.1
+    cache_out = torch.empty_like(cache_in)
+    out = ssm.ssm_conv1d_fwd(x, w, b, conv_state_in=cache_in, conv_state_out=cache_out, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    sel = [0, 2111, Dn - 1]
+    ref, ref_st = oracle.conv1d_fwd(_np(x[:, :, sel]), _np(w[sel]), _np(b[sel]), conv_state=_np(cache_in[:, sel]))
+    got = _np(out[:, :, sel])
+    assert rowinf(got, ref, 1) <= 1e-5
+    np.testing.assert_array_equal(_np(cache_out[:, sel]), ref_st)
+
+
+def test_ssd_over_2g_elements_sampled():
+    batch, L, H, P, N2 = 1, (1 << 19) + 37, 64, 64, 128  # 2.15e9 elements; a ragged last chunk
+    say(f"limits: Mamba-2 scan over {batch * L * H * P / 1e9:.2f}e9 elements (batch {batch}, seqlen {L}, "
+        f"{H} heads x {P}, d_state {N2})")
+    assert batch * L * H * P > 2 ** 31
+    gen = torch.Generator(device="cuda").manual_seed(35)
+    x, z = _normal_bf16((batch, L, H, P), gen), _normal_bf16((batch, L, H, P), gen)
+    dt = _delta_bf16((batch, L, H), gen)
+    B, C = _normal_bf16((batch, L, 1, N2), gen), _normal_bf16((batch, L, 1, N2), gen)
+    A = -(torch.rand(H, generator=gen, device="cuda") * 2.0 + 0.5)
+    D = torch.rand(H * P, generator=gen, device="cuda") + 0.5
+    bias = torch.zeros(H, device="cuda")
+    last = torch.empty((batch, H, P, N2), device="cuda")
+    out = ssm.ssm_ssd_fwd(x, dt, A, B, C, D, z, bias, out=torch.empty((batch, L, H, P), device="cuda"),
+                          last_state=last)
+    torch.cuda.synchronize()
+    psel = [0, 17, P - 1]
+    for h in (0, H - 1):
+        ref, ref_last = oracle.ssd_fwd(_np(x[:, :, h:h + 1, psel]), _np(dt[:, :, h:h + 1]), _np(A[h:h + 1]),
+                                       _np(B), _np(C), _np(D[[h * P + p for p in psel]]),
+                                       _np(z[:, :, h:h + 1, psel]), _np(bias[h:h + 1]))
+        got = _np(out[:, :, h:h + 1, psel])
+        assert rowinf(got.reshape(batch, L, -1), ref.reshape(batch, L, -1), 1) <= TOL_BF16
+        assert rowinf(_np(last[:, h:h + 1, psel]).reshape(batch, len(psel), N2),
+                      ref_last.reshape(batch, len(psel), N2), 2) <= TOL_BF16
