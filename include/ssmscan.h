@@ -293,7 +293,7 @@ ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void
  * (pages as above; "Модуль 8", section 7: decode is the recurrent step with a
  * fixed-size state).  x, z, out: [batch, nheads, headdim]; dt: [batch, nheads];
  * B, C: [batch, ngroups, d_state].  in_dtype fp32 or bf16; any headdim >= 1;
- * d_state 64 or 128; other rules as for ssm_ssd_fwd.
+ * nheads <= 65535; d_state 64 or 128; other rules as for ssm_ssd_fwd.
  */
 ssm_status ssm_ssd_state_update(float* state, const void* x, const void* dt, const float* A, const void* B,
                                 const void* C, const float* D, const void* z, const float* dt_bias, int softplus,

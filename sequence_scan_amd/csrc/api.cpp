@@ -297,6 +297,8 @@ ssm_status ssd_check(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
       !mul_ok(t2, headdim * d_state, &sz->state) || !mul_ok(sz->state, 8, &t3))
     return fail(SSM_ERR_BAD_SHAPE, "element count overflows int64");
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch=%lld exceeds 65535", (long long)batch);
+  if (!scan && nheads > 65535)  // the decode grid has one workgroup row per head
+    return fail(SSM_ERR_UNSUPPORTED, "nheads=%lld exceeds 65535 for the decode step", (long long)nheads);
   if (nheads > INT32_MAX || headdim > INT32_MAX || ngroups > INT32_MAX)
     return fail(SSM_ERR_UNSUPPORTED, "nheads, headdim and ngroups must fit in 32 bits");
   return SSM_OK;

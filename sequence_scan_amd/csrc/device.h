@@ -56,6 +56,22 @@ __device__ __forceinline__ void store_stream4(float* p, float4 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t*>(p));
 }
 
+// Four consecutive input elements (fp32, or bf16 bit patterns) as floats; the
+// address is 16-byte (fp32) or 8-byte (bf16) aligned.
+template <typename Tin>
+__device__ __forceinline__ void load4(const void* p, int64_t i, float* o) {
+  if constexpr (sizeof(Tin) == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+}
+
 template <typename T>
 struct Io;
 

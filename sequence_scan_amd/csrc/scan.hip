@@ -147,28 +147,15 @@ __device__ __forceinline__ float nt_load(const void* p, int64_t i) {
   }
 }
 
-template <typename Tin>
-__device__ __forceinline__ void load4(const void* p, int64_t i, float* o) {
-  if constexpr (sizeof(Tin) == 4) {
-    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
-    o[0] = __uint_as_float(v.x << 16);
-    o[1] = __uint_as_float(v.x & 0xffff0000u);
-    o[2] = __uint_as_float(v.y << 16);
-    o[3] = __uint_as_float(v.y & 0xffff0000u);
-  }
-}
 
 template <typename Tin, typename Tout, bool ZOH>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t e = gid >> 2;
+  // grid: x = blocks of 64 channels, y = batch row (no division by runtime sizes)
+  const int64_t d = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
   const int q = threadIdx.x & 3;
-  if (e >= a.pairs) return;  // whole quads leave together
-  const int64_t d = e % a.d_inner;
-  const int64_t b = e / a.d_inner;
+  if (d >= a.d_inner) return;  // whole quads leave together
+  const int64_t b = blockIdx.y;
+  const int64_t e = b * a.d_inner + d;
 
   float4 hs = load_stream4(a.state + e * kDState + 4 * q);
   const float4 av = *reinterpret_cast<const float4*>(a.A + d * kDState + 4 * q);
@@ -239,8 +226,7 @@ namespace {
 
 template <bool ZOH>
 void launch_decode_z(const DecodeArgs& a, DT in, DT out, hipStream_t s) {
-  const int64_t threads = a.pairs * 4;
-  const unsigned grid = (unsigned)((threads + 255) / 256);
+  const dim3 grid((unsigned)((a.d_inner + 63) / 64), (unsigned)(a.pairs / a.d_inner));
   if (in == DT::F32 && out == DT::F32)
     hipLaunchKernelGGL((decode_kernel<float, float, ZOH>), dim3(grid), dim3(256), 0, s, a);
   else if (in == DT::F32 && out == DT::BF16)

@@ -393,18 +393,19 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
 // (16 bytes per lane, N / 4 lanes per row), the readout is reduced across
 // those lanes with butterfly shuffles, and the row's first lane finishes y.
 template <typename Tin, typename Tout, int N>
-__global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a, int64_t rows) {
+__global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a) {
   constexpr int LPR = N / 4;   // lanes per state row
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / LPR;          // (b * H + h) * P + p
-  const int q = (int)(gid % LPR);
-  if (row >= rows) return;                // whole rows leave together
+  // grid: x = blocks of 256 / LPR channels of one head, y = head, z = batch row
+  // (the indices come from the grid, with no division by runtime sizes)
+  const int p = (int)(blockIdx.x * (256 / LPR) + threadIdx.x / LPR);
+  const int q = (int)(threadIdx.x % LPR);
   const int P = a.headdim, H = a.nheads, G = a.ngroups;
-  const int64_t bh = row / P;
-  const int p = (int)(row % P);
-  const int h = (int)(bh % H);
-  const int64_t b = bh / H;
-  const int g = h / (H / G);
+  if (p >= P) return;                     // whole rows leave together
+  const int h = (int)blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int64_t bh = b * H + h;
+  const int64_t row = bh * P + p;         // (b * H + h) * P + p
+  const int g = h / (H / G);              // uniform in the workgroup
   const float u = ld_in(static_cast<const Tin*>(a.dt) + bh) + (a.bias ? a.bias[h] : 0.0f);
   const float dt = a.softplus ? softplus_f(u) : u;
   const float ar = __builtin_amdgcn_exp2f(dt * a.A[h] * kLog2e);
@@ -414,13 +415,14 @@ __global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a, int64_t rows
   float4 s4 = load_stream4(st);  // the state streams, as in the Mamba-1 decode
   float hs[4] = {s4.x, s4.y, s4.z, s4.w};
   const int64_t bc = (b * G + g) * N + 4 * q;
+  float Bv[4], Cv[4];
+  load4<Tin>(a.B, bc, Bv);
+  load4<Tin>(a.C, bc, Cv);
   float y = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float Bv = ld_in(static_cast<const Tin*>(a.B) + bc + i);
-    const float Cv = ld_in(static_cast<const Tin*>(a.C) + bc + i);
-    hs[i] = __builtin_fmaf(ar, hs[i], dtx * Bv);
-    y = __builtin_fmaf(Cv, hs[i], y);
+    hs[i] = __builtin_fmaf(ar, hs[i], dtx * Bv[i]);
+    y = __builtin_fmaf(Cv[i], hs[i], y);
   }
   store_stream4(st, make_float4(hs[0], hs[1], hs[2], hs[3]));
 #pragma unroll
@@ -449,11 +451,11 @@ void launch_ssd_n(const SsdArgs& a, DT out, hipStream_t s) {
 
 template <typename Tin, typename Tout>
 void launch_ssd_update_t(const SsdArgs& a, hipStream_t s) {
-  const int64_t rows = (int64_t)a.batch * a.nheads * a.headdim;
-  const int64_t threads = rows * (a.d_state / 4);
-  const unsigned grid = (unsigned)((threads + 255) / 256);
-  if (a.d_state == 64) hipLaunchKernelGGL((ssd_update_kernel<Tin, Tout, 64>), dim3(grid), dim3(256), 0, s, a, rows);
-  else hipLaunchKernelGGL((ssd_update_kernel<Tin, Tout, 128>), dim3(grid), dim3(256), 0, s, a, rows);
+  const int rows_per_block = 256 / (a.d_state / 4);
+  const dim3 grid((unsigned)((a.headdim + rows_per_block - 1) / rows_per_block), (unsigned)a.nheads,
+                  (unsigned)a.batch);
+  if (a.d_state == 64) hipLaunchKernelGGL((ssd_update_kernel<Tin, Tout, 64>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ssd_update_kernel<Tin, Tout, 128>), grid, dim3(256), 0, s, a);
 }
 
 }  // namespace

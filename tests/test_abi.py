@@ -299,4 +299,5 @@ def test_ssd_rejections():
     assert upd(state=None) == ssm.SSM_ERR_NULL_ARG
     assert upd(d_state=32) == ssm.SSM_ERR_UNSUPPORTED
     assert upd(out=P + 64) == ssm.SSM_ERR_UNSUPPORTED                        # out inside the state
+    assert upd(nheads=65536, ngroups=1) == ssm.SSM_ERR_UNSUPPORTED and "65535" in ssm.ssm_last_error()
     assert upd(batch=0) == ssm.SSM_OK
