@@ -425,9 +425,18 @@ __global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a) {
     y = __builtin_fmaf(Cv[i], hs[i], y);
   }
   store_stream4(st, make_float4(hs[0], hs[1], hs[2], hs[3]));
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) y += __shfl_xor(y, m, LPR);
-  if (q == 0) {
+  // The row's readout over its LPR lanes (16 or 32, aligned to the 16-lane
+  // DPP rows): quad permutes, then the 8- and 16-lane mirrors leave each
+  // 16-lane row's sum in all its lanes; with 32 lanes, row_bcast:15 adds the
+  // first half's sum into the second, whose first lane then holds the total.
+  y += SSM_DPP(0.0f, y, 0xB1, 0xf);   // quad_perm [1,0,3,2]
+  y += SSM_DPP(0.0f, y, 0x4E, 0xf);   // quad_perm [2,3,0,1]
+  y += SSM_DPP(0.0f, y, 0x141, 0xf);  // row_half_mirror
+  y += SSM_DPP(0.0f, y, 0x140, 0xf);  // row_mirror
+  if constexpr (LPR == 32) y += SSM_DPP(0.0f, y, 0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+  static_assert(LPR == 16 || LPR == 32, "the readout sum assumes 16 or 32 lanes per row");
+  constexpr int kOut = LPR == 32 ? 16 : 0;  // the lane that holds the row's total
+  if (q == kOut) {
     if (a.D) y = __builtin_fmaf(a.D[(int64_t)h * P + p], x, y);
     if (a.z) y = y * silu_f(ld_in(static_cast<const Tin*>(a.z) + row));
     Io<Tout>::store(a.out, row, y);
