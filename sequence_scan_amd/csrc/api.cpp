@@ -76,17 +76,25 @@ int device_simds() {
 
 // The plan (from measurements on MI355X): 4 states per wave (a workgroup of
 // 4 wavefronts per 64 channels) is the fastest split on every workload
-// measured, down to 0.75 wavefronts per SIMD.  When the channel blocks give
-// fewer than half a wavefront per SIMD, the sequence is also cut into chunks
-// until there are about 12 wavefronts per SIMD, with chunks of at least 1024
-// steps: the extra reduction pass costs less than idle SIMDs.
+// measured.  When the channel blocks give fewer than half a wavefront per
+// SIMD, the sequence is also cut into chunks until there are about 12
+// wavefronts per SIMD, with chunks of at least 1024 steps: the extra
+// reduction pass costs less than idle SIMDs.  With more blocks than that but
+// fewer than one per CU, some CUs would idle: the sequence is cut so that the
+// grid holds about three workgroups per CU (the kernel's occupancy), with
+// chunks of at least 512 steps.  (The Mamba-130M-like layer, 192 blocks: 4
+// chunks, 203 us against 218 us in one chunk; 2, 3 or 5 chunks were slower.)
 void choose_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_plan* p) {
   const int64_t blocks = batch * ((d_inner + 63) / 64);
   const int64_t waves = std::max<int64_t>(1, blocks * 4);
+  const int64_t cus = std::max(1, simds / 4);
   int64_t chunks = 1;
   if (waves < simds / 2) {
     chunks = (12 * (int64_t)simds + waves - 1) / waves;
     chunks = std::min(chunks, std::max<int64_t>(1, seqlen / 1024));
+  } else if (blocks < cus) {
+    chunks = (3 * cus + blocks - 1) / blocks;
+    chunks = std::min(chunks, std::max<int64_t>(1, seqlen / 512));
   }
   int64_t chunk_len = seqlen > 0 ? (seqlen + chunks - 1) / chunks : 1;
   if (chunk_len < 1) chunk_len = 1;

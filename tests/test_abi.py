@@ -139,6 +139,10 @@ def test_plan_choices():
     assert p["n_chunks"] == 1 and p["states_per_wave"] == 4
     p = ssm.ssm_scan_plan(1, 262144, 2048)
     assert p["n_chunks"] > 1 and p["chunk_len"] * p["n_chunks"] >= 262144
+    p = ssm.ssm_scan_plan(8, 2048, 1536)   # 192 blocks for 256 CUs: about three workgroups per CU
+    assert p["n_chunks"] == 4 and p["chunk_len"] == 512
+    p = ssm.ssm_scan_plan(8, 700, 1536)    # too short to cut into chunks of 512
+    assert p["n_chunks"] == 1
     p = ssm.ssm_scan_plan(1, 0, 64)
     assert p["n_chunks"] == 0
     with pytest.raises(ssm.SSMError):
