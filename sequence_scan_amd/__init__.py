@@ -122,6 +122,27 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
+def _expect(like, **tensors):
+    """Check each named tensor against (shape, dtype) before its pointer reaches the
+    C ABI, which trusts the sizes it is given: a mismatch would make the kernels read
+    or write past a tensor.  dtype None accepts float32 or bfloat16; every tensor
+    must be on ``like``'s device.  None tensors (optional inputs) are skipped."""
+    import torch
+    for name, spec in tensors.items():
+        t, shape, dtype = spec
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if dtype is None:
+            if t.dtype not in (torch.float32, torch.bfloat16):
+                raise TypeError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+        elif t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.device != like.device:
+            raise ValueError(f"{name} is on {t.device}, expected {like.device}")
+
+
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
@@ -173,7 +194,13 @@ def ssm_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: b
     if x.dim() != 3:
         raise ValueError("x must be [batch, seqlen, d_inner]")
     batch, seqlen, d_inner = x.shape
-    d_state = A.shape[-1] if A.dim() == 2 else -1
+    if A.dim() != 2:
+        raise ValueError("A must be [d_inner, d_state]")
+    d_state = A.shape[1]
+    f32, xs, bcs, st = torch.float32, (batch, seqlen, d_inner), (batch, seqlen, d_state), (batch, d_inner, d_state)
+    _expect(x, x=(x, xs, None), delta=(delta, xs, x.dtype), z=(z, xs, x.dtype), B=(B, bcs, x.dtype),
+            C=(C, bcs, x.dtype), A=(A, (d_inner, d_state), f32), D=(D, (d_inner,), f32),
+            delta_bias=(delta_bias, (d_inner,), f32), out=(out, xs, None), last_state=(last_state, st, f32))
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     lib = _load()
@@ -213,7 +240,14 @@ def ssm_scan_fwd_from(x, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
     if x.dim() != 3:
         raise ValueError("x must be [batch, seqlen, d_inner]")
     batch, seqlen, d_inner = x.shape
-    d_state = A.shape[-1] if A.dim() == 2 else -1
+    if A.dim() != 2:
+        raise ValueError("A must be [d_inner, d_state]")
+    d_state = A.shape[1]
+    f32, xs, bcs, st = torch.float32, (batch, seqlen, d_inner), (batch, seqlen, d_state), (batch, d_inner, d_state)
+    _expect(x, x=(x, xs, None), delta=(delta, xs, x.dtype), z=(z, xs, x.dtype), B=(B, bcs, x.dtype),
+            C=(C, bcs, x.dtype), A=(A, (d_inner, d_state), f32), D=(D, (d_inner,), f32),
+            delta_bias=(delta_bias, (d_inner,), f32), out=(out, xs, None), last_state=(last_state, st, f32),
+            initial_state=(initial_state, st, f32))
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     _check(_load().ssm_scan_fwd_from(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -234,10 +268,17 @@ def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: b
     if x.dim() != 3 or dout is None:
         raise ValueError("x must be [batch, seqlen, d_inner] and dout given")
     batch, seqlen, d_inner = x.shape
-    d_state = A.shape[-1] if A.dim() == 2 else -1
+    if A.dim() != 2:
+        raise ValueError("A must be [d_inner, d_state]")
+    d_state = A.shape[1]
     gdt = grad_dtype or dout.dtype
     if dout.dtype != gdt:
         raise TypeError("dout must have the gradient dtype")
+    f32, xs, bcs, st = torch.float32, (batch, seqlen, d_inner), (batch, seqlen, d_state), (batch, d_inner, d_state)
+    _expect(x, x=(x, xs, None), delta=(delta, xs, x.dtype), z=(z, xs, x.dtype), B=(B, bcs, x.dtype),
+            C=(C, bcs, x.dtype), A=(A, (d_inner, d_state), f32), D=(D, (d_inner,), f32),
+            delta_bias=(delta_bias, (d_inner,), f32), initial_state=(initial_state, st, f32),
+            dout=(dout, xs, None), dlast_state=(dlast_state, st, f32))
     dev = x.device
     g = {"dx": torch.empty(x.shape, dtype=gdt, device=dev), "ddelta": torch.empty(x.shape, dtype=gdt, device=dev),
          "dA": torch.empty(A.shape, dtype=torch.float32, device=dev),
@@ -268,11 +309,13 @@ def ssm_conv1d_fwd(x, weight, bias=None, silu: bool = True, conv_state_in=None, 
     if x.dim() != 3 or weight.dim() != 2:
         raise ValueError("x must be [batch, seqlen, d_inner] and weight [d_inner, d_conv]")
     batch, seqlen, d_inner = x.shape
+    K = weight.shape[1]
+    f32, xs, cs = torch.float32, (batch, seqlen, d_inner), (batch, d_inner, K)
+    _expect(x, x=(x, xs, None), weight=(weight, (d_inner, K), f32), bias=(bias, (d_inner,), f32),
+            conv_state_in=(conv_state_in, cs, x.dtype), conv_state_out=(conv_state_out, cs, x.dtype),
+            out=(out, xs, None))
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    for c in (conv_state_in, conv_state_out):
-        if c is not None and c.dtype != x.dtype:
-            raise TypeError("conv caches must have x's dtype")
     _check(_load().ssm_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), int(bool(silu)), _ptr(conv_state_in),
                                   _ptr(out), _ptr(conv_state_out), batch, seqlen, d_inner, weight.shape[1],
                                   _dtype_code(x), _dtype_code(out), _stream(stream)))
@@ -286,9 +329,11 @@ def ssm_conv1d_update(conv_state, x, weight, bias=None, silu: bool = True, out=N
     import torch
     if x.dim() != 2 or weight.dim() != 2:
         raise ValueError("x must be [batch, d_inner] and weight [d_inner, d_conv]")
-    if conv_state.dtype != x.dtype:
-        raise TypeError("conv_state must have x's dtype")
     batch, d_inner = x.shape
+    K = weight.shape[1]
+    _expect(x, x=(x, (batch, d_inner), None), conv_state=(conv_state, (batch, d_inner, K), x.dtype),
+            weight=(weight, (d_inner, K), torch.float32), bias=(bias, (d_inner,), torch.float32),
+            out=(out, (batch, d_inner), None))
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     _check(_load().ssm_conv1d_update(_ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias), int(bool(silu)),
@@ -305,7 +350,13 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, 
     if x.dim() != 2:
         raise ValueError("x must be [batch, d_inner]")
     batch, d_inner = x.shape
-    d_state = state.shape[-1] if state.dim() == 3 else -1
+    if state.dim() != 3:
+        raise ValueError("state must be [batch, d_inner, d_state]")
+    d_state = state.shape[2]
+    f32, xs, bcs = torch.float32, (batch, d_inner), (batch, d_state)
+    _expect(x, state=(state, (batch, d_inner, d_state), f32), x=(x, xs, None), delta=(delta, xs, x.dtype),
+            z=(z, xs, x.dtype), B=(B, bcs, x.dtype), C=(C, bcs, x.dtype), A=(A, (d_inner, d_state), f32),
+            D=(D, (d_inner,), f32), delta_bias=(delta_bias, (d_inner,), f32), out=(out, xs, None))
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     _check(_load().ssm_state_update(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
@@ -318,6 +369,8 @@ def ssm_affine_exclusive_scan(a, b, out_a=None, out_b=None, stream=None):
     """Exclusive scan of affine pairs (a[k], b[k]) in time order on the GPU (float32)."""
     import torch
     n = a.numel()
+    _expect(a, a=(a, (n,), torch.float32), b=(b, (n,), torch.float32), out_a=(out_a, (n,), torch.float32),
+            out_b=(out_b, (n,), torch.float32))
     out_a = torch.empty_like(a) if out_a is None else out_a
     out_b = torch.empty_like(b) if out_b is None else out_b
     _check(_load().ssm_affine_exclusive_scan(_ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b), n, _stream(stream)))
@@ -335,6 +388,11 @@ def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = T
         raise ValueError("x must be [batch, seqlen, nheads, headdim] and B [batch, seqlen, ngroups, d_state]")
     batch, seqlen, nheads, headdim = x.shape
     ngroups, d_state = B.shape[2], B.shape[3]
+    f32, xs, bcs, st = torch.float32, tuple(x.shape), (batch, seqlen, ngroups, d_state), (batch, nheads, headdim, d_state)
+    _expect(x, x=(x, xs, None), dt=(dt, (batch, seqlen, nheads), x.dtype), z=(z, xs, x.dtype), B=(B, bcs, x.dtype),
+            C=(C, bcs, x.dtype), A=(A, (nheads,), f32), D=(D, (nheads * headdim,), f32),
+            dt_bias=(dt_bias, (nheads,), f32), initial_state=(initial_state, st, f32), out=(out, xs, None),
+            last_state=(last_state, st, f32))
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     _check(_load().ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
@@ -354,6 +412,11 @@ def ssm_ssd_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, so
         raise ValueError("x must be [batch, nheads, headdim] and B [batch, ngroups, d_state]")
     batch, nheads, headdim = x.shape
     ngroups, d_state = B.shape[1], B.shape[2]
+    f32, xs, bcs = torch.float32, tuple(x.shape), (batch, ngroups, d_state)
+    _expect(x, state=(state, (batch, nheads, headdim, d_state), f32), x=(x, xs, None),
+            dt=(dt, (batch, nheads), x.dtype), z=(z, xs, x.dtype), B=(B, bcs, x.dtype), C=(C, bcs, x.dtype),
+            A=(A, (nheads,), f32), D=(D, (nheads * headdim,), f32), dt_bias=(dt_bias, (nheads,), f32),
+            out=(out, xs, None))
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     _check(_load().ssm_ssd_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),

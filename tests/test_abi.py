@@ -305,3 +305,45 @@ def test_ssd_rejections():
     assert upd(out=P + 64) == ssm.SSM_ERR_UNSUPPORTED                        # out inside the state
     assert upd(nheads=65536, ngroups=1) == ssm.SSM_ERR_UNSUPPORTED and "65535" in ssm.ssm_last_error()
     assert upd(batch=0) == ssm.SSM_OK
+
+
+def test_binding_checks_tensor_shapes_and_dtypes():
+    """The binding checks every tensor against the sizes it passes to the C ABI (which
+    trusts them) before anything is launched; CPU tensors reach the device check last."""
+    torch = pytest.importorskip("torch")
+    f32, bf = torch.float32, torch.bfloat16
+    x, A, B = torch.zeros(2, 5, 8), torch.zeros(8, 16), torch.zeros(2, 5, 16)
+    with pytest.raises(ValueError, match="delta"):
+        ssm.ssm_scan_fwd(x, torch.zeros(2, 5, 7), A, B, B)
+    with pytest.raises(TypeError, match="delta"):
+        ssm.ssm_scan_fwd(x, torch.zeros(2, 5, 8, dtype=bf), A, B, B)
+    with pytest.raises(ValueError, match="B"):
+        ssm.ssm_scan_fwd(x, x, A, torch.zeros(2, 5, 8), B)
+    with pytest.raises(ValueError, match="last_state"):
+        ssm.ssm_scan_fwd(x, x, A, B, B, last_state=torch.zeros(2, 8, 8))
+    with pytest.raises(TypeError, match="D"):
+        ssm.ssm_scan_fwd(x, x, A, B, B, D=torch.zeros(8, dtype=bf))
+    with pytest.raises(ValueError, match="initial_state"):
+        ssm.ssm_scan_fwd_from(x, x, A, B, B, initial_state=torch.zeros(2, 8))
+    with pytest.raises(ValueError, match="dout"):
+        ssm.ssm_scan_bwd(x, x, A, B, B, dout=torch.zeros(2, 4, 8))
+    with pytest.raises(ValueError, match="B"):
+        ssm.ssm_state_update(torch.zeros(2, 8, 16), x[:, 0], x[:, 0], A, torch.zeros(2, 8), torch.zeros(2, 16))
+    with pytest.raises(ValueError, match="conv_state_in"):
+        ssm.ssm_conv1d_fwd(x, torch.zeros(8, 4), conv_state_in=torch.zeros(2, 8, 3))
+    with pytest.raises(TypeError, match="conv_state"):
+        ssm.ssm_conv1d_update(torch.zeros(2, 8, 4, dtype=bf), x[:, 0], torch.zeros(8, 4))
+    xs = torch.zeros(2, 5, 4, 64, dtype=bf)
+    Bs = torch.zeros(2, 5, 2, 128, dtype=bf)
+    with pytest.raises(ValueError, match="dt"):
+        ssm.ssm_ssd_fwd(xs, torch.zeros(2, 5, 3, dtype=bf), torch.zeros(4), Bs, Bs)
+    with pytest.raises(ValueError, match="D"):
+        ssm.ssm_ssd_fwd(xs, torch.zeros(2, 5, 4, dtype=bf), torch.zeros(4), Bs, Bs, D=torch.zeros(4))
+    with pytest.raises(ValueError, match="state"):
+        ssm.ssm_ssd_state_update(torch.zeros(2, 4, 64, 64), xs[:, 0], torch.zeros(2, 4, dtype=bf), torch.zeros(4),
+                                 Bs[:, 0], Bs[:, 0])
+    with pytest.raises(ValueError, match="b"):
+        ssm.ssm_affine_exclusive_scan(torch.zeros(5), torch.zeros(4))
+    # consistent tensors pass the checks; these CPU tensors then fail the device check
+    with pytest.raises(ValueError, match="GPU"):
+        ssm.ssm_scan_fwd(x, x, A, B, B, D=torch.zeros(8, dtype=f32))
