@@ -174,6 +174,18 @@ def per_launch_ms(run, reps, flush_bytes=0):
     return sum(times) / len(times), times[len(times) // 2], times[0]
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (None where it is not readable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, inp):
     import oracle
     nthreads = oracle.default_threads()
@@ -479,7 +491,7 @@ def main():
         log("timing the fp64 oracle on the host cores")
         secs, cores = cpu_baseline(cfg, inp)
         line["cpu_baseline"] = {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": cores,
-                                "kind": "oracle", "seconds": round(secs, 2),
+                                "kind": "oracle", "seconds": round(secs, 2), "cpu": cpu_model(),
                                 "sample": f"the full {cfg.name} workload (every row and step), fp64"}
     del inp
     if not args.no_decode and args.workload == "mamba2p8b":
