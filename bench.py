@@ -14,6 +14,10 @@ the whole batch with inputs resident in HBM.  Prints ONE JSON line:
   cpu_baseline the fp64 oracle on the host cores over the same workload;
   decode      512 consecutive ssm_state_update steps at batch 256, d_inner 8192:
               tokens/s (the second half of the metric).
+  conv1d, backward, zoh, ssd
+              the other operations on the layer's shape, each timed on its own
+              (the backward also on the long single-row sequence, in the
+              planner's time chunks and in one chunk).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--out-dtype f32|bf16] [--no-cpu-baseline] [--no-decode]
@@ -337,10 +341,50 @@ def backward_case(cfg, steps=5):
     cyc = 20 + 24 + 52 + 12
     updates = cfg.batch * cfg.seqlen * cfg.d_inner * cfg.d_state
     floor_us = updates / 64 * cyc / (SIMDS * CLOCK_HZ) * 1e6
+    del t, dout
     return {"workload": f"ssm_scan_bwd {cfg.name}: batch {cfg.batch}, seqlen {cfg.seqlen}, d_inner {cfg.d_inner}, "
                         "bf16 inputs and gradients, softplus, D, z",
             "us_per_call": round(ms * 1e3, 1), "alu_floor_us": round(floor_us, 1),
-            "alu_frac": round(floor_us / (ms * 1e3), 4)}
+            "alu_frac": round(floor_us / (ms * 1e3), 4), "long_sequence": backward_long_case()}
+
+
+def backward_long_case():
+    """ssm_scan_bwd on the long single-row workload (batch 1, 32 channel blocks): the
+    planner's time chunks against one chunk.  Inputs are drawn on the GPU (seeded)."""
+    import torch
+
+    import sequence_scan_amd as ssm
+    import workloads
+
+    cfg = workloads.SCAN_CONFIGS["long_dna"]
+    sh = (cfg.batch, cfg.seqlen, cfg.d_inner)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+
+    def draw(shape, scale=1.0, shift=0.0, uniform=False):
+        out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        flat = out.view(-1)
+        for i in range(0, flat.numel(), 1 << 28):
+            n = min(1 << 28, flat.numel() - i)
+            r = torch.rand(n, generator=gen, device="cuda") if uniform else torch.randn(n, generator=gen, device="cuda")
+            flat[i:i + n] = (r * scale + shift).to(torch.bfloat16)
+        return out
+
+    x, z, dout = draw(sh), draw(sh), draw(sh)
+    dl = draw(sh, 4.605, -6.907, uniform=True)   # softplus^-1 of steps in [1e-3, 0.1]
+    B, C = draw((cfg.batch, cfg.seqlen, cfg.d_state)), draw((cfg.batch, cfg.seqlen, cfg.d_state))
+    A = (-torch.arange(1, cfg.d_state + 1, dtype=torch.float32, device="cuda")).repeat(cfg.d_inner, 1).contiguous()
+    D = torch.ones(cfg.d_inner, device="cuda")
+    bias = torch.zeros(cfg.d_inner, device="cuda")
+    plan = ssm.ssm_scan_bwd_plan_query(*sh)
+    res = {"workload": f"ssm_scan_bwd {cfg.name}: batch {cfg.batch}, seqlen {cfg.seqlen}, d_inner {cfg.d_inner}, "
+                       "bf16 inputs and gradients, softplus, D, z", "plan": plan}
+    for key, p in (("us_per_call", None), ("one_chunk_us_per_call",
+                                           {"states_per_wave": 4, "chunk_len": cfg.seqlen})):
+        run = lambda: ssm.ssm_scan_bwd(x, dl, A, B, C, D, z, bias, softplus=True, dout=dout, plan=p)
+        settle(run, 0.1)
+        ms, _ = time_steps(run, 3, 1)
+        res[key] = round(ms * 1e3, 1)
+    return res
 
 
 def zoh_case(cfg, run_dt_ms, reps=20):

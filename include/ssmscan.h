@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 /*
  * Bits of the step-flags argument (named `softplus` in the calls below):
@@ -192,11 +192,13 @@ ssm_status ssm_scan_fwd_from(const void* x, const void* delta, const float* A, c
  *   dinitial_state: [batch, d_inner, d_state] fp32 or NULL (not computed)
  * Every gradient is overwritten (not accumulated).  Reductions (dB, dC over
  * channels; dA, dD, ddelta_bias over rows) run in a fixed order: results are
- * bitwise reproducible.  A workspace of about batch * seqlen * d_inner * 4 +
- * batch * seqlen * ceil(d_inner / 64) * 128 bytes is taken with hipMallocAsync
- * on `stream` and released with hipFreeAsync.  Outputs must not overlap any
- * input or each other.  Sizes, dtypes, alignment and errors as for
- * ssm_scan_fwd (grad_dtype in place of out_dtype).
+ * bitwise reproducible for a given plan (below).  A workspace of about
+ * batch * seqlen * d_inner * 8 + batch * seqlen * ceil(d_inner / 64) * 128
+ * bytes (the states entering every 8-step tile, and per-block dB, dC) is taken
+ * with hipMallocAsync on `stream` and released with hipFreeAsync.  With few
+ * channel blocks the sequence is cut into time chunks (ssm_scan_bwd_plan).
+ * Outputs must not overlap any input or each other.  Sizes, dtypes, alignment
+ * and errors as for ssm_scan_fwd (grad_dtype in place of out_dtype).
  */
 ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B,
                         const void* C, const float* D, const void* z, const float* delta_bias,
@@ -205,6 +207,35 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
                         void* dC, float* dD, void* dz, float* ddelta_bias, float* dinitial_state,
                         int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                         ssm_dtype in_dtype, ssm_dtype grad_dtype, void* stream);
+
+/*
+ * Plans of the backward.  With fewer 64-channel blocks (batch *
+ * ceil(d_inner / 64)) than compute units, ssm_scan_bwd cuts the sequence into
+ * time chunks that run in parallel: each chunk's entering state comes from the
+ * forward's chunk carry (vladkulikov.com, "Модуль 8. Альтернативы
+ * Transformer", section 7: the affine pairs (exp(A S), end state) composed in
+ * time order), and the gradient arriving at its end from the same pair
+ * operator composed in reverse order (the reverse recurrence over a chunk is
+ * affine in the gradient that arrives at its end, with the same decay
+ * exp(A S)).  ssm_scan_bwd_plan_query reports the plan ssm_scan_bwd picks;
+ * ssm_scan_bwd_plan runs with a given one (tests and tuning).
+ * plan->states_per_wave must be 4; plan->chunk_len >= 1, and a multiple of 8
+ * whenever it is below seqlen; at most 65535 chunks.  Any valid plan computes
+ * the same gradients up to rounding order.  A chunked run takes
+ * batch * n_chunks * d_inner * (3 * d_state + 2) * 4 more bytes of workspace.
+ * Otherwise as for ssm_scan_bwd.
+ */
+ssm_status ssm_scan_bwd_plan_query(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                   ssm_plan* plan);
+
+ssm_status ssm_scan_bwd_plan(const void* x, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z,
+                             const float* delta_bias, int softplus, const float* initial_state,
+                             const void* dout, const float* dlast_state, void* dx, void* ddelta,
+                             float* dA, void* dB, void* dC, float* dD, void* dz,
+                             float* ddelta_bias, float* dinitial_state, int64_t batch,
+                             int64_t seqlen, int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
+                             ssm_dtype grad_dtype, void* stream, const ssm_plan* plan);
 
 /*
  * The block's short causal depthwise convolution that feeds the scan (page

@@ -8,7 +8,8 @@ loaded, every call raises.
 
 Functions carry the C names: ``ssm_scan_fwd``, ``ssm_state_update``,
 ``ssm_scan_fwd_plan``, ``ssm_scan_fwd_from``, ``ssm_scan_plan``,
-``ssm_scan_bwd``, ``ssm_conv1d_fwd``, ``ssm_conv1d_update``, ``ssm_affine_exclusive_scan``,
+``ssm_scan_bwd``, ``ssm_scan_bwd_plan``, ``ssm_scan_bwd_plan_query``, ``ssm_conv1d_fwd``,
+``ssm_conv1d_update``, ``ssm_ssd_fwd``, ``ssm_ssd_state_update``, ``ssm_affine_exclusive_scan``,
 ``ssm_status_string``, ``ssm_last_error``, ``ssm_abi_version``.
 """
 from __future__ import annotations
@@ -69,6 +70,10 @@ def _load():
     lib.ssm_scan_fwd_from.restype = ctypes.c_int
     lib.ssm_scan_bwd.argtypes = [_vp] * 8 + [ctypes.c_int] + [_vp] * 12 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int, _vp]
     lib.ssm_scan_bwd.restype = ctypes.c_int
+    lib.ssm_scan_bwd_plan.argtypes = lib.ssm_scan_bwd.argtypes + [ctypes.POINTER(ssm_plan)]
+    lib.ssm_scan_bwd_plan.restype = ctypes.c_int
+    lib.ssm_scan_bwd_plan_query.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(ssm_plan)]
+    lib.ssm_scan_bwd_plan_query.restype = ctypes.c_int
     lib.ssm_conv1d_fwd.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                    ctypes.c_int, ctypes.c_int, _vp]
     lib.ssm_conv1d_fwd.restype = ctypes.c_int
@@ -257,13 +262,26 @@ def ssm_scan_fwd_from(x, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
     return out
 
 
+def ssm_scan_bwd_plan(*args, plan: dict, **kw):
+    return ssm_scan_bwd(*args, plan=plan, **kw)
+
+
+def ssm_scan_bwd_plan_query(batch: int, seqlen: int, d_inner: int, d_state: int = D_STATE) -> dict:
+    """The plan ``ssm_scan_bwd`` picks for these sizes (its time chunks)."""
+    p = ssm_plan()
+    _check(_load().ssm_scan_bwd_plan_query(batch, seqlen, d_inner, d_state, ctypes.byref(p)))
+    return {"states_per_wave": p.states_per_wave, "chunk_len": p.chunk_len, "n_chunks": p.n_chunks}
+
+
 def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, initial_state=None,
-                 dout=None, dlast_state=None, want_dinitial_state: bool = False, grad_dtype=None, stream=None):
+                 dout=None, dlast_state=None, want_dinitial_state: bool = False, grad_dtype=None, stream=None,
+                 plan: Optional[dict] = None):
     """Gradients of the scan (see include/ssmscan.h).  Forward inputs as for
     ``ssm_scan_fwd_from``; ``dout`` [batch, seqlen, d_inner] (its dtype is the gradient
     dtype unless ``grad_dtype`` is given); ``dlast_state`` optional.  Returns a dict with
     dx, ddelta, dA, dB, dC and, for the inputs given, dD, dz, ddelta_bias, and
-    dinitial_state when ``want_dinitial_state``."""
+    dinitial_state when ``want_dinitial_state``.  ``plan`` = {"states_per_wave": 4,
+    "chunk_len": ..} forces the time chunks (``ssm_scan_bwd_plan``)."""
     import torch
     if x.dim() != 3 or dout is None:
         raise ValueError("x must be [batch, seqlen, d_inner] and dout given")
@@ -291,12 +309,16 @@ def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: b
         g["ddelta_bias"] = torch.empty(delta_bias.shape, dtype=torch.float32, device=dev)
     if want_dinitial_state:
         g["dinitial_state"] = torch.empty((batch, d_inner, d_state), dtype=torch.float32, device=dev)
-    _check(_load().ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(dout),
-                                _ptr(dlast_state), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
-                                _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
-                                _ptr(g.get("dinitial_state")), batch, seqlen, d_inner, d_state, _dtype_code(x),
-                                _dtype_code(g["dx"]), _stream(stream)))
+    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(softplus)), _ptr(initial_state), _ptr(dout), _ptr(dlast_state), _ptr(g["dx"]),
+            _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")), _ptr(g.get("dz")),
+            _ptr(g.get("ddelta_bias")), _ptr(g.get("dinitial_state")), batch, seqlen, d_inner, d_state,
+            _dtype_code(x), _dtype_code(g["dx"]), _stream(stream))
+    lib = _load()
+    if plan is None:
+        _check(lib.ssm_scan_bwd(*args))
+    else:
+        _check(lib.ssm_scan_bwd_plan(*args, _plan_struct(plan)))
     return g
 
 

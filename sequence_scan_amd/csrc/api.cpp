@@ -105,6 +105,30 @@ void choose_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_
   for (auto& r : p->reserved) r = 0;
 }
 
+// The backward's plan.  Its workgroup holds 64 channels of one batch row for
+// a whole chunk; with fewer channel blocks than CUs the sequence is cut into
+// chunks (a multiple of the 8-step tile, at least 512 steps) until there are
+// about three workgroups per CU, the kernel's occupancy.  Each cut costs a
+// forward pass A and a reverse pass A over the chunks, about half the
+// backward's own work per step, which idle CUs more than pay for.
+void choose_bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_plan* p) {
+  const int64_t blocks = std::max<int64_t>(1, batch * ((d_inner + 63) / 64));
+  const int64_t cus = std::max(1, simds / 4);
+  int64_t chunks = 1;
+  if (blocks < cus) {
+    chunks = (3 * cus + blocks - 1) / blocks;
+    chunks = std::min(chunks, std::max<int64_t>(1, seqlen / 512));
+  }
+  int64_t chunk_len = seqlen > 0 ? (seqlen + chunks - 1) / chunks : 1;
+  if (chunks > 1) chunk_len = (chunk_len + ssm::kBwdTile - 1) / ssm::kBwdTile * ssm::kBwdTile;
+  if (chunk_len < 1) chunk_len = 1;
+  p->states_per_wave = 4;
+  p->reserved0 = 0;
+  p->chunk_len = chunk_len;
+  p->n_chunks = seqlen > 0 ? (seqlen + chunk_len - 1) / chunk_len : 0;
+  for (auto& r : p->reserved) r = 0;
+}
+
 struct Sizes {
   int64_t elems;      // batch * seqlen * d_inner
   int64_t bc;         // batch * seqlen * d_state
@@ -405,12 +429,12 @@ ssm_status ssm_state_update(float* state, const void* x, const void* delta, cons
   return ok();
 }
 
-ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
-                        const float* D, const void* z, const float* delta_bias, int softplus,
-                        const float* initial_state, const void* dout, const float* dlast_state, void* dx,
-                        void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
-                        float* dinitial_state, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                        ssm_dtype in_dtype, ssm_dtype grad_dtype, void* stream) {
+static ssm_status bwd_impl(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, int softplus,
+                           const float* initial_state, const void* dout, const float* dlast_state, void* dx,
+                           void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                           float* dinitial_state, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                           ssm_dtype in_dtype, ssm_dtype grad_dtype, void* stream, const ssm_plan* plan_in) {
   Sizes sz;
   ssm_status st = check_common(batch, seqlen, d_inner, d_state, in_dtype, grad_dtype, &sz);
   if (st != SSM_OK) return st;
@@ -457,6 +481,23 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
       if (overlaps(outs[i], outs[j]))
         return fail(SSM_ERR_UNSUPPORTED, "%s overlaps %s", outs[i].name, outs[j].name);
   }
+  ssm_plan plan;
+  if (plan_in) {
+    plan = *plan_in;
+    if (plan.states_per_wave != 4)
+      return fail(SSM_ERR_UNSUPPORTED, "plan.states_per_wave=%d: the backward carries 4 states per wavefront",
+                  plan.states_per_wave);
+    if (plan.chunk_len < 1) return fail(SSM_ERR_UNSUPPORTED, "plan.chunk_len must be >= 1");
+    plan.n_chunks = seqlen > 0 ? (seqlen + plan.chunk_len - 1) / plan.chunk_len : 0;
+    if (plan.n_chunks > 1 && plan.chunk_len % ssm::kBwdTile != 0)
+      return fail(SSM_ERR_UNSUPPORTED, "plan.chunk_len=%lld must be a multiple of %d when it cuts the sequence",
+                  (long long)plan.chunk_len, ssm::kBwdTile);
+    if (plan.n_chunks > 65535) return fail(SSM_ERR_UNSUPPORTED, "plan gives more than 65535 chunks");
+  } else {
+    choose_bwd_plan(batch, seqlen, d_inner, device_simds(), &plan);
+  }
+  const int64_t K = std::max<int64_t>(1, plan.n_chunks);
+
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (d_inner == 0) return ok();
@@ -474,10 +515,13 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
   }
   const int64_t nblk = (d_inner + 63) / 64;
   const int64_t ntiles = (seqlen + ssm::kBwdTile - 1) / ssm::kBwdTile;
-  int64_t n_ck, n_bc, n_a, n_dd, bytes;
+  // per (row, chunk): dA partials, dD / dbias partials; chunked runs also
+  // keep each chunk's entering state, arriving gradient and reverse pair
+  int64_t n_ck, n_bc, n_a, n_dd, n_cs, n_cd, bytes;
   if (!mul_ok(batch * nblk, ntiles * 64 * d_state, &n_ck) || !mul_ok(sz.bc / d_state, nblk * 2 * d_state, &n_bc) ||
-      !mul_ok(sz.state, 1, &n_a) || !mul_ok(batch * d_inner, 2, &n_dd) ||
-      !mul_ok(n_ck + n_bc + n_a + n_dd, 4, &bytes))
+      !mul_ok(sz.state, K, &n_a) || !mul_ok(batch * d_inner, 2 * K, &n_dd) ||
+      !mul_ok(sz.state, K > 1 ? K : 0, &n_cs) || !mul_ok(batch * d_inner, K > 1 ? K : 0, &n_cd) ||
+      !mul_ok(n_ck + n_bc + n_a + n_dd + 3 * n_cs + 2 * n_cd, 4, &bytes))
     return fail(SSM_ERR_BAD_SHAPE, "workspace size overflows int64");
   void* ws = nullptr;
   e = hipMallocAsync(&ws, (size_t)bytes, s);
@@ -502,9 +546,18 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
   a.ws_bc = a.ws_ckpt + n_ck;
   a.ws_a = a.ws_bc + n_bc;
   a.ws_dd = a.ws_a + n_a;
+  if (K > 1) {
+    a.ws_hin = a.ws_dd + n_dd;
+    a.ws_rev = a.ws_hin + n_cs;
+    a.ws_dl = a.ws_rev + n_cs;
+    a.ws_fsum = a.ws_dl + n_cs;
+    a.ws_rsum = a.ws_fsum + n_cd;
+  }
   a.dh0 = dinitial_state;
   a.seqlen = seqlen;
   a.d_inner = d_inner;
+  a.chunk_len = K > 1 ? plan.chunk_len : seqlen;
+  a.n_chunks = (int32_t)K;
   a.batch = (int32_t)batch;
   a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
   a.nblk = (int32_t)nblk;
@@ -514,6 +567,40 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
   if (e == hipSuccess) e = e2;
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                        const float* D, const void* z, const float* delta_bias, int softplus,
+                        const float* initial_state, const void* dout, const float* dlast_state, void* dx,
+                        void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                        float* dinitial_state, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                        ssm_dtype in_dtype, ssm_dtype grad_dtype, void* stream) {
+  return bwd_impl(x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, dout, dlast_state, dx, ddelta, dA,
+                  dB, dC, dD, dz, ddelta_bias, dinitial_state, batch, seqlen, d_inner, d_state, in_dtype, grad_dtype,
+                  stream, nullptr);
+}
+
+ssm_status ssm_scan_bwd_plan(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int softplus,
+                             const float* initial_state, const void* dout, const float* dlast_state, void* dx,
+                             void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                             float* ddelta_bias, float* dinitial_state, int64_t batch, int64_t seqlen,
+                             int64_t d_inner, int64_t d_state, ssm_dtype in_dtype, ssm_dtype grad_dtype,
+                             void* stream, const ssm_plan* plan) {
+  if (!plan) return fail(SSM_ERR_NULL_ARG, "plan is NULL");
+  return bwd_impl(x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, dout, dlast_state, dx, ddelta, dA,
+                  dB, dC, dD, dz, ddelta_bias, dinitial_state, batch, seqlen, d_inner, d_state, in_dtype, grad_dtype,
+                  stream, plan);
+}
+
+ssm_status ssm_scan_bwd_plan_query(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                   ssm_plan* plan) {
+  if (!plan) return fail(SSM_ERR_NULL_ARG, "plan is NULL");
+  Sizes sz;
+  ssm_status st = check_common(batch, seqlen, d_inner, d_state, SSM_F32, SSM_F32, &sz);
+  if (st != SSM_OK) return st;
+  choose_bwd_plan(batch, seqlen, d_inner, device_simds(), plan);
+  return SSM_OK;
 }
 
 ssm_status ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, int silu,

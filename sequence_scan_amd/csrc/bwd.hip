@@ -27,6 +27,15 @@ namespace {
 // dC are reduced over the wavefront's 64 channels through a wave-local LDS
 // transpose and 3 DPP steps, and stored per channel block for a second,
 // fixed-order reduction kernel: the result does not depend on timing.
+//
+// A long sequence with few channel blocks is cut into time chunks, one
+// workgroup per (chunk, batch row, block).  Chunk k then starts its forward
+// from the state entering it (slot k - 1 of ws_hin, from the forward's pass A
+// and carry; the caller's initial state for k = 0) and its reverse walk from
+// the gradient arriving at its end (slot k of ws_dl, from the reverse pass A
+// and carry below; the caller's dlast for the last chunk).  The chunk length
+// is a multiple of the tile, so the chunk's tiles are tiles of the whole
+// sequence and share its checkpoint layout.
 
 template <typename Tin, typename Tg, bool HAS_Z, int CW>
 __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
@@ -54,7 +63,9 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int64_t b = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int kc = blockIdx.y;   // time chunk
+  const int K = a.n_chunks;
   const int blk = blockIdx.x;
   const int64_t Dn = a.d_inner, L = a.seqlen;
   const int64_t d0 = (int64_t)blk * kWave;
@@ -62,7 +73,10 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
   const int loff = min(lane, nvalid - 1);
   const int64_t dl = d0 + loff;
   const bool softplus = a.softplus != 0;
-  const int64_t ntiles = (L + T - 1) / T;
+  const int64_t t_begin = (int64_t)kc * a.chunk_len;
+  const int64_t Lc = min(a.chunk_len, L - t_begin);   // steps of this chunk
+  const int64_t ntiles = (Lc + T - 1) / T;
+  const int64_t row = b * K + kc;                      // per-(row, chunk) partial sums
 
   float Ad[NS];
 #pragma unroll
@@ -82,14 +96,15 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
       iD[it][q] = a.D != nullptr ? a.D[dq] : 0.0f;
     }
   }
-  const int64_t row0 = b * L * Dn + d0;
+  const int64_t row0 = (b * L + t_begin) * Dn + d0;
   const Tin* xb = static_cast<const Tin*>(a.x) + row0;
   const Tin* db = static_cast<const Tin*>(a.delta) + row0;
   const Tin* zb = HAS_Z ? static_cast<const Tin*>(a.z) + row0 : nullptr;
   const Tg* gb = static_cast<const Tg*>(a.dout) + row0;
-  const Tin* Bb = static_cast<const Tin*>(a.B) + b * L * kDState;
-  const Tin* Cb = static_cast<const Tin*>(a.C) + b * L * kDState;
-  float* ck = a.ws_ckpt + ((b * a.nblk + blk) * ntiles) * (int64_t)(kWave * kDState);
+  const Tin* Bb = static_cast<const Tin*>(a.B) + (b * L + t_begin) * kDState;
+  const Tin* Cb = static_cast<const Tin*>(a.C) + (b * L + t_begin) * kDState;
+  const int64_t ntiles_all = (L + T - 1) / T;
+  float* ck = a.ws_ckpt + ((b * a.nblk + blk) * ntiles_all + t_begin / T) * (int64_t)(kWave * kDState);
 
   // Raw inputs of one tile, loaded one tile ahead of their use (rows past
   // the tile's end repeat its last row, so every load is unconditional).
@@ -98,7 +113,7 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
     RG rg[IPT];
     float bv, cv;   // this thread's staged B or C element (cv only when one thread stages both)
   };
-  auto tile_rows = [&](int64_t k) SSM_INLINE { return (int)min((int64_t)T, L - k * T); };
+  auto tile_rows = [&](int64_t k) SSM_INLINE { return (int)min((int64_t)T, Lc - k * T); };
   auto load = [&](Bank& bk, int64_t k, bool full) SSM_INLINE {
     const int64_t t0 = k * T;
     const int nt = tile_rows(k);
@@ -138,8 +153,10 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
 
   // ---- phase 1: forward, storing the state entering each tile
   float h[NS];
+  const float* hsrc = kc > 0 ? a.ws_hin + ((row - 1) * Dn + dl) * kDState
+                      : a.h0 != nullptr ? a.h0 + (b * Dn + dl) * kDState : nullptr;
 #pragma unroll
-  for (int i = 0; i < NS; ++i) h[i] = a.h0 != nullptr ? a.h0[(b * Dn + dl) * kDState + g * NS + i] : 0.0f;
+  for (int i = 0; i < NS; ++i) h[i] = hsrc != nullptr ? hsrc[g * NS + i] : 0.0f;
   // Progress weights for ProgressPriority: a phase-1 tile counts 2, a
   // phase-2 tile (about 4.5 times the work) 9.
   const ProgressPriority prio(11 * ntiles);
@@ -173,9 +190,11 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
 
   // ---- phase 2: the tiles in reverse
   float carry[NS], dAacc[NS];
+  const float* gsrc = kc + 1 < K ? a.ws_dl + (row * Dn + dl) * kDState
+                      : a.dlast != nullptr ? a.dlast + (b * Dn + dl) * kDState : nullptr;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    carry[i] = a.dlast != nullptr ? a.dlast[(b * Dn + dl) * kDState + g * NS + i] : 0.0f;
+    carry[i] = gsrc != nullptr ? gsrc[g * NS + i] : 0.0f;
     dAacc[i] = 0.0f;
   }
   float dDacc[IPT][CW], dBacc[IPT][CW];
@@ -338,17 +357,17 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
     // this tile's dB', dC of the block
     for (int i = tid; i < nt * 2 * kDState; i += NTHR) {
       const int s = i / (2 * kDState), w = i % (2 * kDState);
-      a.ws_bc[((b * L + t0 + s) * a.nblk + blk) * (2 * kDState) + w] = (&sh_bc[s][0][0])[w];
+      a.ws_bc[((b * L + t_begin + t0 + s) * a.nblk + blk) * (2 * kDState) + w] = (&sh_bc[s][0][0])[w];
     }
     block_sync();
     cur = nxt;
   }
 
-  // per-row parameter gradients and the initial state's gradient
+  // per-(row, chunk) parameter gradients and the initial state's gradient
   if (lane < nvalid) {
-    *reinterpret_cast<float4*>(a.ws_a + (b * Dn + dl) * kDState + g * NS) =
+    *reinterpret_cast<float4*>(a.ws_a + (row * Dn + dl) * kDState + g * NS) =
         make_float4(dAacc[0] * kLn2, dAacc[1] * kLn2, dAacc[2] * kLn2, dAacc[3] * kLn2);
-    if (a.dh0 != nullptr)
+    if (kc == 0 && a.dh0 != nullptr)
       *reinterpret_cast<float4*>(a.dh0 + (b * Dn + dl) * kDState + g * NS) =
           make_float4(carry[0], carry[1], carry[2], carry[3]);
   }
@@ -368,8 +387,156 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
       sD += sred[r * kWave + tid];
       sB += sred[T * kWave + r * kWave + tid];
     }
-    a.ws_dd[(b * Dn + d0 + tid) * 2] = sD;
-    a.ws_dd[(b * Dn + d0 + tid) * 2 + 1] = sB;
+    a.ws_dd[(row * Dn + d0 + tid) * 2] = sD;
+    a.ws_dd[(row * Dn + d0 + tid) * 2 + 1] = sB;
+  }
+}
+
+// ------------------------------------------------- chunked backward carries
+//
+// The gradient arriving at the end of chunk k depends on chunks k+1 .. K-1
+// only through an affine map: with g the gradient with respect to the state
+// after chunk k+1's last step, the reverse recurrence over chunk k+1 yields
+//   dL/d(state entering chunk k+1) = r_{k+1} + exp2(A S_{k+1}) g,
+// where r_{k+1} is that walk started from g = 0 and S_{k+1} the chunk's
+// step-size sum (log2 units).  That is the pair operator of the forward's
+// chunk carry, applied in reverse time order.
+//
+// bwd_rev_kernel: r_k and S_k for chunks k = 1 .. K-1, one workgroup per
+// (chunk, batch row, 64-channel block), lane = channel and 4 states per lane
+// as in the backward kernel.  Tiles of kBwdTile steps are walked from the
+// chunk's end; each stages (dt2, dy) and C in LDS and runs
+//   g <- exp2(dt2 A) (dy C + g)
+// over its steps in reverse.  The next tile's raw inputs load behind it.
+template <typename Tin, typename Tg, bool HAS_Z, int CW>
+__global__ void __launch_bounds__(256) bwd_rev_kernel(BwdArgs a) {
+  constexpr int NS = 4, T = kBwdTile, NTHR = 256;
+  constexpr int CPR = kWave / CW;
+  constexpr int IPT = T * CPR / NTHR;
+  static_assert(IPT >= 1 && IPT * NTHR == T * CPR, "tile does not split evenly");
+  static_assert(T * kDState <= NTHR, "C staging takes one element per thread");
+  using R = Raw<Tin, CW>;
+  using RG = Raw<Tg, CW>;
+  __shared__ float2 sh_dty[T][kWave + 1];   // (dt2, dy)
+  __shared__ float sh_C[T][kDState];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int64_t b = blockIdx.z;
+  const int kc = blockIdx.y + 1;
+  const int blk = blockIdx.x;
+  const int64_t Dn = a.d_inner, L = a.seqlen;
+  const int64_t d0 = (int64_t)blk * kWave;
+  const int nvalid = (int)min((int64_t)kWave, Dn - d0);
+  const int loff = min(lane, nvalid - 1);
+  const int64_t dl = d0 + loff;
+  const bool softplus = a.softplus != 0;
+  const int64_t t_begin = (int64_t)kc * a.chunk_len;
+  const int64_t Lc = min(a.chunk_len, L - t_begin);
+  const int64_t ntiles = (Lc + T - 1) / T;
+
+  float Ad[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) Ad[i] = a.A[dl * kDState + g * NS + i];
+  int irow[IPT], icol[IPT];
+  float ibias[IPT][CW];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int idx = tid + it * NTHR;
+    irow[it] = idx / CPR;
+    icol[it] = min(idx % CPR, (nvalid + CW - 1) / CW - 1) * CW;
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+      const int64_t dq = d0 + min(icol[it] + q, nvalid - 1);
+      ibias[it][q] = a.bias != nullptr ? a.bias[dq] : 0.0f;
+    }
+  }
+  const int64_t row0 = (b * L + t_begin) * Dn + d0;
+  const Tin* db = static_cast<const Tin*>(a.delta) + row0;
+  const Tin* zb = HAS_Z ? static_cast<const Tin*>(a.z) + row0 : nullptr;
+  const Tg* gb = static_cast<const Tg*>(a.dout) + row0;
+  const Tin* Cb = static_cast<const Tin*>(a.C) + (b * L + t_begin) * kDState;
+
+  struct Bank {
+    R rd[IPT], rz[IPT];
+    RG rg[IPT];
+    float cv;
+  };
+  auto load = [&](Bank& bk, int64_t k) SSM_INLINE {
+    const int64_t t0 = k * T;
+    const int nt = (int)min((int64_t)T, Lc - t0);
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int64_t off = (t0 + min(irow[it], nt - 1)) * Dn + icol[it];
+      bk.rd[it].load(db + off);
+      bk.rg[it].load(gb + off);
+      if (HAS_Z) bk.rz[it].load(zb + off);
+    }
+    if (tid < T * kDState) bk.cv = ld_in(Cb + (t0 + min(tid / kDState, nt - 1)) * kDState + tid % kDState);
+  };
+
+  float gacc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) gacc[i] = 0.0f;
+  float dtsum = 0.0f;
+  Bank cur, nxt;
+  load(cur, ntiles - 1);
+  for (int64_t k = ntiles - 1; k >= 0; --k) {
+    const int nt = (int)min((int64_t)T, Lc - k * T);
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        const float u2 = (cur.rd[it].get(q) + ibias[it][q]) * kLog2e;
+        const float dt2 = softplus ? softplus2_f(u2) : u2;
+        float dy = cur.rg[it].get(q);
+        if (HAS_Z) dy = dy * silu_f(cur.rz[it].get(q));
+        sh_dty[irow[it]][icol[it] + q] = make_float2(dt2, dy);
+      }
+    }
+    if (tid < T * kDState) sh_C[tid / kDState][tid % kDState] = cur.cv;
+    if (k > 0) load(nxt, k - 1);
+    block_sync();
+#pragma unroll
+    for (int s = T - 1; s >= 0; --s) {
+      if (s < nt) {
+        const float2 v = sh_dty[s][loff];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const float dh = __builtin_fmaf(v.y, sh_C[s][g * NS + i], gacc[i]);
+          gacc[i] = __builtin_amdgcn_exp2f(v.x * Ad[i]) * dh;
+        }
+        dtsum += v.x;
+      }
+    }
+    block_sync();
+    cur = nxt;
+  }
+  if (lane < nvalid) {
+    const int64_t slot = (b * a.n_chunks + kc) * Dn + dl;
+    *reinterpret_cast<float4*>(a.ws_rev + slot * kDState + g * NS) = make_float4(gacc[0], gacc[1], gacc[2], gacc[3]);
+    if (g == 0) a.ws_rsum[slot] = dtsum;
+  }
+}
+
+// bwd_rev_carry_kernel: the gradient arriving at the end of every chunk but
+// the last, composing the chunks' pairs from the sequence's end (where the
+// caller's dlast, or zero, arrives) in reverse order.  One thread per
+// (batch row, channel, state), sequential over chunks.
+__global__ void __launch_bounds__(256) bwd_rev_carry_kernel(BwdArgs a) {
+  const int64_t ncol = a.d_inner * kDState;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = blockIdx.y;
+  if (i >= ncol) return;
+  const int K = a.n_chunks;
+  const float a2 = a.A[i];
+  float gv = a.dlast != nullptr ? a.dlast[b * ncol + i] : 0.0f;
+  for (int k = K - 1; k >= 1; --k) {
+    const int64_t p = b * K + k;
+    gv = __builtin_fmaf(__builtin_amdgcn_exp2f(a2 * a.ws_rsum[p * a.d_inner + (i >> 4)]), gv,
+                        a.ws_rev[p * ncol + i]);
+    a.ws_dl[(p - 1) * ncol + i] = gv;
   }
 }
 
@@ -390,7 +557,8 @@ __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(const float* ws_bc, 
   else dst[o] = f32_to_bf16_rne(v);
 }
 
-// dA, dD, dbias: sum the per-row partials over the batch in row order.
+// dA, dD, dbias: sum the per-(row, chunk) partials in order (`batch` counts
+// rows times chunks).
 __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(const float* ws_a, const float* ws_dd, float* dA,
                                                                 float* dD, float* dbias, int64_t batch,
                                                                 int64_t Dn) {
@@ -424,15 +592,57 @@ void launch_bwd_pass(K kern, dim3 grid, const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, b);
 }
 
+// The chunked backward's carries: each chunk's entering state (the forward's
+// pass A and carry, run by the forward scan's own launcher), then each
+// chunk's arriving gradient (reverse pass A, reverse carry).
+template <typename Tin, typename Tg, int CW>
+hipError_t launch_bwd_carries(const BwdArgs& a, DT in, hipStream_t s) {
+  ScanArgs f{};
+  f.x = a.x;
+  f.delta = a.delta;
+  f.B = a.B;
+  f.C = a.C;
+  f.A = a.A;
+  f.bias = a.bias;
+  f.h0 = a.h0;
+  f.ws_state = a.ws_hin;
+  f.ws_dtsum = a.ws_fsum;
+  f.seqlen = a.seqlen;
+  f.d_inner = a.d_inner;
+  f.chunk_len = a.chunk_len;
+  f.n_chunks = a.n_chunks;
+  f.softplus = a.softplus;
+  f.batch = a.batch;
+  f.cus = a.cus;
+  f.states_only = 1;
+  hipError_t e = launch_scan(f, in, DT::F32, 4, s);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)a.nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch);
+  if (a.z != nullptr) hipLaunchKernelGGL((bwd_rev_kernel<Tin, Tg, true, CW>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((bwd_rev_kernel<Tin, Tg, false, CW>), grid, dim3(256), 0, s, a);
+  const unsigned ncolblk = (unsigned)((a.d_inner * kDState + 255) / 256);
+  hipLaunchKernelGGL(bwd_rev_carry_kernel, dim3(ncolblk, (unsigned)a.batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename Tin, typename Tg>
-void launch_scan_bwd_t(const BwdArgs& a, float* dA, void* dB, void* dC, float* dD, float* dbias, hipStream_t s) {
-  const dim3 grid((unsigned)a.nblk, (unsigned)a.batch);
+hipError_t launch_scan_bwd_t(const BwdArgs& a, DT in, float* dA, void* dB, void* dC, float* dD, float* dbias,
+                             hipStream_t s) {
+  const dim3 grid((unsigned)a.nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
   if (a.seqlen > 0) {
     // channels per element item: 8-step tiles x 64 channels = 256 threads x 2
     if (a.d_inner % 2 == 0) {
+      if (a.n_chunks > 1) {
+        const hipError_t e = launch_bwd_carries<Tin, Tg, 2>(a, in, s);
+        if (e != hipSuccess) return e;
+      }
       if (a.z != nullptr) launch_bwd_pass(scan_bwd_kernel<Tin, Tg, true, 2>, grid, a, s);
       else launch_bwd_pass(scan_bwd_kernel<Tin, Tg, false, 2>, grid, a, s);
     } else {
+      if (a.n_chunks > 1) {
+        const hipError_t e = launch_bwd_carries<Tin, Tg, 1>(a, in, s);
+        if (e != hipSuccess) return e;
+      }
       if (a.z != nullptr) launch_bwd_pass(scan_bwd_kernel<Tin, Tg, true, 1>, grid, a, s);
       else launch_bwd_pass(scan_bwd_kernel<Tin, Tg, false, 1>, grid, a, s);
     }
@@ -443,18 +653,18 @@ void launch_scan_bwd_t(const BwdArgs& a, float* dA, void* dB, void* dC, float* d
   }
   const int64_t np = a.d_inner * kDState;
   hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s, a.ws_a, a.ws_dd,
-                     dA, dD, dbias, (int64_t)a.batch, a.d_inner);
+                     dA, dD, dbias, (int64_t)a.batch * a.n_chunks, a.d_inner);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_scan_bwd(const BwdArgs& a, DT in, DT grad, float* dA, void* dB, void* dC, float* dD,
                            float* dbias, hipStream_t s) {
-  if (in == DT::F32 && grad == DT::F32) launch_scan_bwd_t<float, float>(a, dA, dB, dC, dD, dbias, s);
-  else if (in == DT::F32 && grad == DT::BF16) launch_scan_bwd_t<float, uint16_t>(a, dA, dB, dC, dD, dbias, s);
-  else if (in == DT::BF16 && grad == DT::F32) launch_scan_bwd_t<uint16_t, float>(a, dA, dB, dC, dD, dbias, s);
-  else launch_scan_bwd_t<uint16_t, uint16_t>(a, dA, dB, dC, dD, dbias, s);
-  return hipGetLastError();
+  if (in == DT::F32 && grad == DT::F32) return launch_scan_bwd_t<float, float>(a, in, dA, dB, dC, dD, dbias, s);
+  if (in == DT::F32 && grad == DT::BF16) return launch_scan_bwd_t<float, uint16_t>(a, in, dA, dB, dC, dD, dbias, s);
+  if (in == DT::BF16 && grad == DT::F32) return launch_scan_bwd_t<uint16_t, float>(a, in, dA, dB, dC, dD, dbias, s);
+  return launch_scan_bwd_t<uint16_t, uint16_t>(a, in, dA, dB, dC, dD, dbias, s);
 }
 
 }  // namespace ssm

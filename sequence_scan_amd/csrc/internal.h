@@ -36,6 +36,8 @@ struct ScanArgs {
   int32_t zoh;            // exact zero-order-hold input coefficient
   int32_t cus;            // compute units of the device
   int32_t fair;           // set by the launcher: the whole grid is co-resident
+  int32_t states_only;    // chunked runs: stop after the carry pass (ws_state then holds
+                          // the state entering chunk k + 1 in slot k); no out is written
 };
 
 struct DecodeArgs {
@@ -117,8 +119,16 @@ struct BwdArgs {
   float* ws_a;            // [batch, d_inner, 16] per-row dA
   float* ws_dd;           // [batch, d_inner, 2] per-row dD, dbias
   float* dh0;             // nullable: [batch, d_inner, 16]
+  // Chunked runs (n_chunks > 1) only, each [batch, n_chunks, d_inner, ...]:
+  float* ws_hin;          // [.., 16] slot k: the state entering chunk k + 1 (forward pass A + carry)
+  float* ws_fsum;         // [..] forward pass A's step-size sums
+  float* ws_rev;          // [.., 16] slot k: dL/d(state entering chunk k) when none arrives at its end
+  float* ws_rsum;         // [..] slot k: chunk k's step-size sum (log2 units)
+  float* ws_dl;           // [.., 16] slot k: dL/d(state after chunk k), k < n_chunks - 1
   int64_t seqlen;
   int64_t d_inner;
+  int64_t chunk_len;      // steps per chunk: a multiple of kBwdTile unless n_chunks == 1
+  int32_t n_chunks;
   int32_t batch;
   int32_t softplus;
   int32_t nblk;           // ceil(d_inner / 64)
@@ -150,7 +160,10 @@ hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t 
 hipError_t launch_conv1d(const ConvArgs& a, DT in, DT out, int K, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvArgs& a, DT in, DT out, int K, hipStream_t s);
 // Backward: the per-block kernel, then the fixed-order reductions into dA, dB,
-// dC, dD and dbias (dD / dbias may be NULL when the forward had none).
+// dC, dD and dbias (dD / dbias may be NULL when the forward had none).  With
+// n_chunks > 1 it first runs the forward's pass A and carry (launch_scan with
+// states_only) for each chunk's entering state, and the reverse pass A and
+// reverse carry for the gradient arriving at each chunk's end.
 hipError_t launch_scan_bwd(const BwdArgs& a, DT in, DT grad, float* dA, void* dB, void* dC, float* dD,
                            float* dbias, hipStream_t s);
 // The SSD scan (bf16 inputs, headdim 64, d_state 64 or 128) and decode step.

@@ -368,6 +368,7 @@ hipError_t launch_scan_w(const ScanArgs& a, hipStream_t s) {
     const hipError_t e = launch_carry(a, s);
     if (e != hipSuccess) return e;
   }
+  if (a.states_only) return hipGetLastError();
   const dim3 gridB(nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
   if (a.z != nullptr) launch_pass(kBz, occBz, gridB, NTHR, a, s);
   else launch_pass(kB, occB, gridB, NTHR, a, s);

@@ -22,13 +22,14 @@ def test_every_declared_function_is_exported():
     names = header_functions()
     assert {"ssm_scan_fwd", "ssm_state_update", "ssm_scan_plan", "ssm_scan_fwd_plan", "ssm_scan_fwd_from",
             "ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_affine_exclusive_scan", "ssm_status_string",
-            "ssm_last_error", "ssm_abi_version", "ssm_scan_bwd", "ssm_ssd_fwd", "ssm_ssd_state_update"} <= set(names)
+            "ssm_last_error", "ssm_abi_version", "ssm_scan_bwd", "ssm_scan_bwd_plan", "ssm_scan_bwd_plan_query",
+            "ssm_ssd_fwd", "ssm_ssd_state_update"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssmscan.h but not exported"
 
 
 def test_version_and_strings():
-    assert ssm.ssm_abi_version() == 5
+    assert ssm.ssm_abi_version() == 6
     for code, name in ssm.STATUS_NAMES.items():
         assert ssm.ssm_status_string(code).startswith(name)
     assert "unknown" in ssm.ssm_status_string(99)
@@ -246,6 +247,42 @@ def test_scan_bwd_rejections():
         assert bwd(flags=flags) == ssm.SSM_ERR_UNSUPPORTED
         assert "SSM_ZOH" in ssm.ssm_last_error()
     assert bwd(flags=4) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_bwd_plan_choices():
+    # MI355X: 256 CUs.  The layer has 640 blocks: one chunk.
+    p = ssm.ssm_scan_bwd_plan_query(8, 2048, 5120)
+    assert p["n_chunks"] == 1 and p["states_per_wave"] == 4
+    p = ssm.ssm_scan_bwd_plan_query(8, 2048, 1536)    # 192 blocks: about three workgroups per CU
+    assert p["n_chunks"] == 4 and p["chunk_len"] == 512
+    p = ssm.ssm_scan_bwd_plan_query(1, 262144, 2048)  # 32 blocks
+    assert p["n_chunks"] == 24 and p["chunk_len"] % 8 == 0 and p["chunk_len"] * p["n_chunks"] >= 262144
+    assert p["chunk_len"] * (p["n_chunks"] - 1) < 262144
+    p = ssm.ssm_scan_bwd_plan_query(2, 300, 200)      # too short to cut
+    assert p["n_chunks"] == 1
+    p = ssm.ssm_scan_bwd_plan_query(1, 0, 64)
+    assert p["n_chunks"] == 0
+    with pytest.raises(ssm.SSMError):
+        ssm.ssm_scan_bwd_plan_query(1, 10, 64, 12)
+
+
+def test_bwd_bad_plan_rejected_before_launch():
+    lib = ssm.library()
+
+    def bwd(spw, chunk, seqlen=100, plan=True):
+        p = ssm.ssm_plan()
+        p.states_per_wave = spw
+        p.chunk_len = chunk
+        return lib.ssm_scan_bwd_plan(P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, None, None, None, 1,
+                                     None, P + 0x5000000, None, P + 0x6000000, P + 0x7000000, P + 0x8000000,
+                                     P + 0x9000000, P + 0xa000000, None, None, None, None, 1, seqlen, 64, 16, F32, F32,
+                                     None, ctypes.byref(p) if plan else None)
+    for spw, chunk, seqlen in ((2, 16, 100), (8, 16, 100), (4, 0, 100), (4, -8, 100),
+                               (4, 12, 100),       # cuts the sequence at a step that is not a tile boundary
+                               (4, 8, 600000)):    # more than 65535 chunks
+        assert bwd(spw, chunk, seqlen) == ssm.SSM_ERR_UNSUPPORTED, (spw, chunk, seqlen)
+    assert "multiple of 8" in (bwd(4, 12) and ssm.ssm_last_error())
+    assert bwd(4, 16, plan=False) == ssm.SSM_ERR_NULL_ARG
 
 
 def test_step_flags():

@@ -44,14 +44,15 @@ def _case(batch, L, Dn, dtype="f32", seed=3, softplus=True):
     return inp, g, gl, h0
 
 
-def _run(inp, g, gl, h0, softplus=True, use=("D", "z", "delta_bias"), grad_dtype=torch.float32):
+def _run(inp, g, gl, h0, softplus=True, use=("D", "z", "delta_bias"), grad_dtype=torch.float32, chunk_len=None):
     t = to_dev(inp)
     dout = torch.from_numpy(g).to(grad_dtype).cuda()
     res = ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"] if "D" in use else None,
                            t["z"] if "z" in use else None, t["delta_bias"] if "delta_bias" in use else None,
                            softplus=softplus, initial_state=torch.from_numpy(h0).cuda() if h0 is not None else None,
                            dout=dout, dlast_state=torch.from_numpy(gl).cuda() if gl is not None else None,
-                           want_dinitial_state=True)
+                           want_dinitial_state=True,
+                           plan={"states_per_wave": 4, "chunk_len": chunk_len} if chunk_len else None)
     torch.cuda.synchronize()
     return {k: v.float().cpu().numpy() for k, v in res.items()}
 
@@ -120,6 +121,7 @@ def test_bwd_deterministic_and_empty():
 
 
 def test_bwd_layer_shape():
+    # batch 1 has 80 channel blocks, which the planner cuts into time chunks; batch 8 runs in one chunk
     say("backward, Mamba-2.8B-like layer at batch 1 (all channels: dB, dC) and batch 8 (sampled channels)")
     cfg = workloads.SCAN_CONFIGS["mamba2p8b"]
     inp = workloads.scan_inputs(cfg, seed=0, batch=1)
@@ -140,3 +142,103 @@ def test_bwd_layer_shape():
     for k in ("dD", "ddelta_bias"):
         err = float(np.max(np.abs(got8[k][sel] - ref8[k])) / np.max(np.abs(ref8[k])))
         assert err <= TOL, k
+
+
+# ---- time-chunked backward (ssm_scan_bwd_plan): each chunk starts from the state
+# the forward carry gives it and from the gradient the reverse carry gives it
+
+@pytest.mark.parametrize("batch,L,Dn,chunk", [(1, 100, 64, 16), (2, 203, 70, 24), (1, 77, 65, 8), (2, 300, 200, 64),
+                                              (1, 1000, 128, 104)])
+def test_bwd_chunked_vs_oracle(batch, L, Dn, chunk):
+    # ragged last chunks and tiles; an odd d_inner (one-channel items); chunks of one tile
+    say(f"chunked backward batch {batch} seqlen {L} d_inner {Dn} chunk_len {chunk}")
+    inp, g, gl, h0 = _case(batch, L, Dn, seed=13)
+    _compare(_run(inp, g, gl, h0, chunk_len=chunk), _ref(inp, g, gl, h0))
+
+
+@pytest.mark.parametrize("softplus,use", [(False, ("D", "z", "delta_bias")), (True, ()), (True, ("z",))])
+def test_bwd_chunked_options(softplus, use):
+    say(f"chunked backward options softplus={softplus} inputs={use}")
+    inp, g, gl, h0 = _case(2, 150, 96, softplus=softplus, seed=17)
+    _compare(_run(inp, g, None, None, softplus=softplus, use=use, chunk_len=32),
+             _ref(inp, g, None, None, softplus=softplus, use=use))
+    _compare(_run(inp, g, gl, h0, softplus=softplus, use=use, chunk_len=40),
+             _ref(inp, g, gl, h0, softplus=softplus, use=use))
+
+
+def test_bwd_chunked_bf16_and_deterministic():
+    say("chunked backward with bf16 inputs: fp32 gradients vs the oracle, bf16 = RNE of fp32, repeat is bitwise equal")
+    inp, g, gl, h0 = _case(2, 200, 128, dtype="bf16", seed=19)
+    g32 = _run(inp, g, gl, h0, chunk_len=48)
+    _compare(g32, _ref(inp, g, gl, h0))
+    again = _run(inp, g, gl, h0, chunk_len=48)
+    for k in g32:
+        assert np.array_equal(g32[k], again[k]), k
+    g16 = _run(inp, g, gl, h0, grad_dtype=torch.bfloat16, chunk_len=48)
+    for k in ("dx", "ddelta", "dz", "dB", "dC"):
+        np.testing.assert_array_equal(g16[k], rne_bf16_of(torch.from_numpy(g32[k])), err_msg=k)
+
+
+def test_bwd_planner_chunks_a_long_sequence():
+    L, Dn = 16384, 256  # 4 channel blocks: the planner cuts the sequence
+    plan = ssm.ssm_scan_bwd_plan_query(1, L, Dn)
+    say(f"backward, batch 1 seqlen {L} d_inner {Dn} bf16, planner's plan {plan}")
+    assert plan["n_chunks"] > 1
+    inp, g, gl, h0 = _case(1, L, Dn, dtype="bf16", seed=21)
+    _compare(_run(inp, g, gl, h0), _ref(inp, g, gl, h0))
+
+
+def test_bwd_long_dna_sampled():
+    """The long single-row workload (batch 1, seqlen 262144, d_inner 2048) on the
+    planner's chunks, inputs drawn on the GPU.  Per-channel gradients are checked on
+    sampled channels over the whole sequence (a channel's gradients depend on no
+    other channel).  dB and dC sum over all channels: dB of the last steps depends
+    only on those steps (the reverse walk starts at the end, with no dlast), and dC
+    of the first steps only on the first steps (the forward starts from zero), so
+    both are checked there against the oracle run on those steps alone."""
+    cfg = workloads.SCAN_CONFIGS["long_dna"]
+    batch, L, Dn = cfg.batch, cfg.seqlen, cfg.d_inner
+    plan = ssm.ssm_scan_bwd_plan_query(batch, L, Dn)
+    say(f"backward, long_dna batch {batch} seqlen {L} d_inner {Dn}, planner's plan {plan}")
+    assert plan["n_chunks"] > 1
+    gen = torch.Generator(device="cuda").manual_seed(41)
+
+    def bf16(shape, scale=1.0, shift=0.0, uniform=False):
+        out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        flat = out.view(-1)
+        for i in range(0, flat.numel(), 1 << 28):
+            n = min(1 << 28, flat.numel() - i)
+            r = torch.rand(n, generator=gen, device="cuda") if uniform else torch.randn(n, generator=gen, device="cuda")
+            flat[i:i + n] = (r * scale + shift).to(torch.bfloat16)
+        return out
+
+    sh = (batch, L, Dn)
+    x, z = bf16(sh), bf16(sh)
+    dl = bf16(sh, 6.907 - 2.302, -6.907, uniform=True)  # softplus^-1 of steps in [1e-3, 0.1]
+    dout = bf16(sh).float()                            # fp32 gradients of bf16-exact values
+    B, C = bf16((batch, L, 16)), bf16((batch, L, 16))
+    A = -(torch.rand((Dn, 16), generator=gen, device="cuda") * 15.0 + 0.5)
+    D = torch.rand(Dn, generator=gen, device="cuda") + 0.5
+    bias = torch.rand(Dn, generator=gen, device="cuda") * 0.1
+    res = ssm.ssm_scan_bwd(x, dl, A, B, C, D, z, bias, softplus=True, dout=dout)
+    torch.cuda.synchronize()
+
+    def np_(t):
+        return t.float().cpu().numpy()
+
+    sel = [0, 1023, Dn - 1]
+    ref = oracle.scan_bwd(np_(x[..., sel]), np_(dl[..., sel]), np_(A[sel]), np_(B), np_(C), np_(D[sel]),
+                          np_(z[..., sel]), np_(bias[sel]), softplus=True, dout=np_(dout[..., sel]))
+    for k in ("dx", "ddelta", "dz"):
+        assert rowinf(np_(res[k][..., sel]), ref[k], 1) <= TOL, k
+    assert rowinf(np_(res["dA"][sel]), ref["dA"], 1) <= TOL
+    for k in ("dD", "ddelta_bias"):
+        got = np_(res[k][sel])
+        assert float(np.max(np.abs(got - ref[k])) / np.max(np.abs(ref[k]))) <= TOL, k
+    m = 64
+    tail = oracle.scan_bwd(np_(x[:, -m:]), np_(dl[:, -m:]), np_(A), np_(B[:, -m:]), np_(C[:, -m:]), np_(D),
+                           np_(z[:, -m:]), np_(bias), softplus=True, dout=np_(dout[:, -m:]))
+    assert rowinf(np_(res["dB"][:, -m:]), tail["dB"], 1) <= TOL
+    head = oracle.scan_bwd(np_(x[:, :m]), np_(dl[:, :m]), np_(A), np_(B[:, :m]), np_(C[:, :m]), np_(D),
+                           np_(z[:, :m]), np_(bias), softplus=True, dout=np_(dout[:, :m]))
+    assert rowinf(np_(res["dC"][:, :m]), head["dC"], 1) <= TOL
