@@ -170,3 +170,36 @@ def test_ssd_graph():
         assert torch.equal(torch.cat([out.flatten(), yd.flatten()]), want[0]), f"replay {r}: outputs differ"
         assert torch.equal(last, want[1]), f"replay {r}: state differs"
     assert np.isfinite(want[0].cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("chunk_len", [None, 32])
+def test_backward_graph(chunk_len):
+    """The backward, whose workspace comes from hipMallocAsync on the stream (a
+    graph allocation node), one chunk and time chunks (forward and reverse carries)."""
+    L = 150
+    say(f"graph: backward batch 2 L {L} d_inner 96 bf16, chunk_len {chunk_len}")
+    cfg = workloads.ScanConfig("g", 2, 96, 16, L, "bf16")
+    t = to_dev(workloads.scan_inputs(cfg, seed=25, random_params=True))
+    gen = torch.Generator().manual_seed(6)
+    dout = torch.randn((2, L, 96), generator=gen).cuda()
+    dlast = torch.randn((2, 96, 16), generator=gen).cuda()
+    h0 = torch.randn((2, 96, 16), generator=gen).cuda()
+    plan = {"states_per_wave": 4, "chunk_len": chunk_len} if chunk_len else None
+    outs = {}
+
+    def call():
+        outs.update(ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                                     softplus=True, initial_state=h0, dout=dout, dlast_state=dlast,
+                                     want_dinitial_state=True, plan=plan))
+
+    call()
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in outs.items()}
+    g = _capture(call)  # the capture's call allocated the gradients that replays write
+    for r in range(REPLAYS):
+        _poison(*outs.values())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v, want[k]), f"replay {r}: {k} differs from the eager result"

@@ -2,6 +2,8 @@
 every entry point is called through the C ABI with real device buffers and one
 invalid argument at a time; its outputs, filled with a sentinel beforehand, must
 keep it after a device synchronisation."""
+import ctypes
+
 import pytest
 
 from gpu_util import say
@@ -61,6 +63,14 @@ def test_scan_rejections_write_nothing():
     rc = lib.ssm_scan_bwd(_p(x), _p(dl), _p(A), _p(B), _p(C), _p(D), _p(z), _p(bias), ssm.SSM_ZOH, None, _p(x), None,
                           *[_p(t) for t in g], None, b, L, d, n, F32, F32, None)
     assert rc != ssm.SSM_OK
+    _untouched(*g)
+    # a backward plan that cuts the sequence off a tile boundary
+    plan = ssm.ssm_plan()
+    plan.states_per_wave, plan.chunk_len = 4, 12
+    say("rejection: ssm_scan_bwd_plan with chunk_len 12")
+    rc = lib.ssm_scan_bwd_plan(_p(x), _p(dl), _p(A), _p(B), _p(C), _p(D), _p(z), _p(bias), 1, None, _p(x), None,
+                               *[_p(t) for t in g], None, b, L, d, n, F32, F32, None, ctypes.byref(plan))
+    assert rc == ssm.SSM_ERR_UNSUPPORTED
     _untouched(*g)
 
 
