@@ -105,18 +105,24 @@ void choose_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_
   for (auto& r : p->reserved) r = 0;
 }
 
-// The backward's plan.  Its workgroup holds 64 channels of one batch row for
-// a whole chunk; with fewer channel blocks than CUs the sequence is cut into
-// chunks (a multiple of the 8-step tile, at least 512 steps) until there are
-// about three workgroups per CU, the kernel's occupancy.  Each cut costs a
-// forward pass A and a reverse pass A over the chunks, about half the
-// backward's own work per step, which idle CUs more than pay for.
+// The backward's plan (from measurements on MI355X).  Its workgroup holds 64
+// channels of one batch row for a whole chunk, three workgroups per CU.  With
+// at most 1.75 channel blocks per CU the sequence is cut into chunks (a
+// multiple of the 8-step tile, at least 512 steps) until there are about 24
+// workgroups per CU.  Cutting at all costs a forward pass A and a reverse pass
+// A over the sequence, about 45 % of the backward's own work, whatever the
+// number of chunks; more, shorter chunks then only balance the CUs better.
+// Measured against one chunk: 448 blocks 1.67 against 1.74 ms, 320 blocks
+// 1.22 against 1.70 ms, the Mamba-130M-like layer (192 blocks) 0.75 against
+// 1.51 ms, the long single-row sequence (32 blocks, 262144 steps) 13.5 ms in
+// chunks of 1024 steps against 14.6 ms in chunks of 10928 and 184 ms in one.
+// At 512 blocks two chunks were slower (2.00 against 1.77 ms).
 void choose_bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_plan* p) {
   const int64_t blocks = std::max<int64_t>(1, batch * ((d_inner + 63) / 64));
   const int64_t cus = std::max(1, simds / 4);
   int64_t chunks = 1;
-  if (blocks < cus) {
-    chunks = (3 * cus + blocks - 1) / blocks;
+  if (4 * blocks <= 7 * cus) {
+    chunks = (24 * cus + blocks - 1) / blocks;
     chunks = std::min(chunks, std::max<int64_t>(1, seqlen / 512));
   }
   int64_t chunk_len = seqlen > 0 ? (seqlen + chunks - 1) / chunks : 1;

@@ -404,17 +404,23 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
 //
 // bwd_rev_kernel: r_k and S_k for chunks k = 1 .. K-1, one workgroup per
 // (chunk, batch row, 64-channel block), lane = channel and 4 states per lane
-// as in the backward kernel.  Tiles of kBwdTile steps are walked from the
-// chunk's end; each stages (dt2, dy) and C in LDS and runs
+// as in the backward kernel.  Tiles of 32 steps are walked from the chunk's
+// end (its ragged tile first); each stages (dt2, dy) and C in LDS and runs
 //   g <- exp2(dt2 A) (dy C + g)
-// over its steps in reverse.  The next tile's raw inputs load behind it.
-template <typename Tin, typename Tg, bool HAS_Z, int CW>
+// over its steps in reverse.  As in the forward scan, a thread item is 8
+// consecutive channels of one step (16-byte loads) when d_inner is a multiple
+// of 8, else one channel; the next tile's raw inputs load behind the current
+// tile's arithmetic.
+template <typename Tin, typename Tg, bool HAS_Z, bool WIDE>
 __global__ void __launch_bounds__(256) bwd_rev_kernel(BwdArgs a) {
-  constexpr int NS = 4, T = kBwdTile, NTHR = 256;
+  constexpr int NS = 4, T = 32, NTHR = 256;
+  constexpr int CW = WIDE ? 8 : 1;
   constexpr int CPR = kWave / CW;
   constexpr int IPT = T * CPR / NTHR;
   static_assert(IPT >= 1 && IPT * NTHR == T * CPR, "tile does not split evenly");
-  static_assert(T * kDState <= NTHR, "C staging takes one element per thread");
+  constexpr int EPV = Vec16<Tin>::kElems;   // C elements per 16-byte vector
+  constexpr int CVECS = T * kDState / EPV;  // 16-byte vectors of a tile's C rows
+  static_assert(CVECS <= NTHR, "C staging takes at most one vector per thread");
   using R = Raw<Tin, CW>;
   using RG = Raw<Tg, CW>;
   __shared__ float2 sh_dty[T][kWave + 1];   // (dt2, dy)
@@ -461,8 +467,9 @@ __global__ void __launch_bounds__(256) bwd_rev_kernel(BwdArgs a) {
   struct Bank {
     R rd[IPT], rz[IPT];
     RG rg[IPT];
-    float cv;
+    uint4 cv;
   };
+  // rows past the tile's end repeat its last row, so every load is unconditional
   auto load = [&](Bank& bk, int64_t k) SSM_INLINE {
     const int64_t t0 = k * T;
     const int nt = (int)min((int64_t)T, Lc - t0);
@@ -473,42 +480,56 @@ __global__ void __launch_bounds__(256) bwd_rev_kernel(BwdArgs a) {
       bk.rg[it].load(gb + off);
       if (HAS_Z) bk.rz[it].load(zb + off);
     }
-    if (tid < T * kDState) bk.cv = ld_in(Cb + (t0 + min(tid / kDState, nt - 1)) * kDState + tid % kDState);
+    const int v = tid % CVECS;
+    const int64_t t = t0 + min(v / (kDState / EPV), nt - 1);
+    bk.cv = *reinterpret_cast<const uint4*>(Cb + t * kDState + (v % (kDState / EPV)) * EPV);
+  };
+  auto stage = [&](const Bank& bk) SSM_INLINE {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        const float u2 = (bk.rd[it].get(q) + ibias[it][q]) * kLog2e;
+        const float dt2 = softplus ? softplus2_f(u2) : u2;
+        float dy = bk.rg[it].get(q);
+        if (HAS_Z) dy = dy * silu_f(bk.rz[it].get(q));
+        sh_dty[irow[it]][icol[it] + q] = make_float2(dt2, dy);
+      }
+    }
+    if (tid < CVECS) {
+      float f[EPV];
+      Vec16<Tin>::unpack(bk.cv, f);
+      float* dst = &sh_C[tid / (kDState / EPV)][(tid % (kDState / EPV)) * EPV];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) dst[e] = f[e];
+    }
   };
 
   float gacc[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) gacc[i] = 0.0f;
   float dtsum = 0.0f;
+  auto step = [&](int s) SSM_INLINE {
+    const float2 v = sh_dty[s][loff];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const float dh = __builtin_fmaf(v.y, sh_C[s][g * NS + i], gacc[i]);
+      gacc[i] = __builtin_amdgcn_exp2f(v.x * Ad[i]) * dh;
+    }
+    dtsum += v.x;
+  };
   Bank cur, nxt;
   load(cur, ntiles - 1);
   for (int64_t k = ntiles - 1; k >= 0; --k) {
     const int nt = (int)min((int64_t)T, Lc - k * T);
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-#pragma unroll
-      for (int q = 0; q < CW; ++q) {
-        const float u2 = (cur.rd[it].get(q) + ibias[it][q]) * kLog2e;
-        const float dt2 = softplus ? softplus2_f(u2) : u2;
-        float dy = cur.rg[it].get(q);
-        if (HAS_Z) dy = dy * silu_f(cur.rz[it].get(q));
-        sh_dty[irow[it]][icol[it] + q] = make_float2(dt2, dy);
-      }
-    }
-    if (tid < T * kDState) sh_C[tid / kDState][tid % kDState] = cur.cv;
+    stage(cur);
     if (k > 0) load(nxt, k - 1);
     block_sync();
+    if (nt == T) {   // every tile but possibly the chunk's last, which is walked first
 #pragma unroll
-    for (int s = T - 1; s >= 0; --s) {
-      if (s < nt) {
-        const float2 v = sh_dty[s][loff];
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          const float dh = __builtin_fmaf(v.y, sh_C[s][g * NS + i], gacc[i]);
-          gacc[i] = __builtin_amdgcn_exp2f(v.x * Ad[i]) * dh;
-        }
-        dtsum += v.x;
-      }
+      for (int s = T - 1; s >= 0; --s) step(s);
+    } else {
+      for (int s = nt - 1; s >= 0; --s) step(s);
     }
     block_sync();
     cur = nxt;
@@ -595,7 +616,7 @@ void launch_bwd_pass(K kern, dim3 grid, const BwdArgs& a, hipStream_t s) {
 // The chunked backward's carries: each chunk's entering state (the forward's
 // pass A and carry, run by the forward scan's own launcher), then each
 // chunk's arriving gradient (reverse pass A, reverse carry).
-template <typename Tin, typename Tg, int CW>
+template <typename Tin, typename Tg>
 hipError_t launch_bwd_carries(const BwdArgs& a, DT in, hipStream_t s) {
   ScanArgs f{};
   f.x = a.x;
@@ -618,8 +639,15 @@ hipError_t launch_bwd_carries(const BwdArgs& a, DT in, hipStream_t s) {
   hipError_t e = launch_scan(f, in, DT::F32, 4, s);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)a.nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch);
-  if (a.z != nullptr) hipLaunchKernelGGL((bwd_rev_kernel<Tin, Tg, true, CW>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((bwd_rev_kernel<Tin, Tg, false, CW>), grid, dim3(256), 0, s, a);
+  // the wide items need rows that split into aligned groups of 8
+  const bool wide = a.d_inner % 8 == 0;
+  if (a.z != nullptr) {
+    if (wide) hipLaunchKernelGGL((bwd_rev_kernel<Tin, Tg, true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bwd_rev_kernel<Tin, Tg, true, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (wide) hipLaunchKernelGGL((bwd_rev_kernel<Tin, Tg, false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bwd_rev_kernel<Tin, Tg, false, false>), grid, dim3(256), 0, s, a);
+  }
   const unsigned ncolblk = (unsigned)((a.d_inner * kDState + 255) / 256);
   hipLaunchKernelGGL(bwd_rev_carry_kernel, dim3(ncolblk, (unsigned)a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -633,14 +661,14 @@ hipError_t launch_scan_bwd_t(const BwdArgs& a, DT in, float* dA, void* dB, void*
     // channels per element item: 8-step tiles x 64 channels = 256 threads x 2
     if (a.d_inner % 2 == 0) {
       if (a.n_chunks > 1) {
-        const hipError_t e = launch_bwd_carries<Tin, Tg, 2>(a, in, s);
+        const hipError_t e = launch_bwd_carries<Tin, Tg>(a, in, s);
         if (e != hipSuccess) return e;
       }
       if (a.z != nullptr) launch_bwd_pass(scan_bwd_kernel<Tin, Tg, true, 2>, grid, a, s);
       else launch_bwd_pass(scan_bwd_kernel<Tin, Tg, false, 2>, grid, a, s);
     } else {
       if (a.n_chunks > 1) {
-        const hipError_t e = launch_bwd_carries<Tin, Tg, 1>(a, in, s);
+        const hipError_t e = launch_bwd_carries<Tin, Tg>(a, in, s);
         if (e != hipSuccess) return e;
       }
       if (a.z != nullptr) launch_bwd_pass(scan_bwd_kernel<Tin, Tg, true, 1>, grid, a, s);

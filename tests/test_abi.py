@@ -253,10 +253,14 @@ def test_bwd_plan_choices():
     # MI355X: 256 CUs.  The layer has 640 blocks: one chunk.
     p = ssm.ssm_scan_bwd_plan_query(8, 2048, 5120)
     assert p["n_chunks"] == 1 and p["states_per_wave"] == 4
-    p = ssm.ssm_scan_bwd_plan_query(8, 2048, 1536)    # 192 blocks: about three workgroups per CU
+    p = ssm.ssm_scan_bwd_plan_query(8, 2048, 1536)    # 192 blocks: chunks of the 512-step minimum
     assert p["n_chunks"] == 4 and p["chunk_len"] == 512
-    p = ssm.ssm_scan_bwd_plan_query(1, 262144, 2048)  # 32 blocks
-    assert p["n_chunks"] == 24 and p["chunk_len"] % 8 == 0 and p["chunk_len"] * p["n_chunks"] >= 262144
+    p = ssm.ssm_scan_bwd_plan_query(7, 2048, 4096)    # 448 blocks = 1.75 per CU: still cut
+    assert p["n_chunks"] == 4
+    p = ssm.ssm_scan_bwd_plan_query(8, 2048, 4096)    # 512 blocks: one chunk
+    assert p["n_chunks"] == 1
+    p = ssm.ssm_scan_bwd_plan_query(1, 262144, 2048)  # 32 blocks: about 24 workgroups per CU
+    assert p["n_chunks"] == 192 and p["chunk_len"] % 8 == 0 and p["chunk_len"] * p["n_chunks"] >= 262144
     assert p["chunk_len"] * (p["n_chunks"] - 1) < 262144
     p = ssm.ssm_scan_bwd_plan_query(2, 300, 200)      # too short to cut
     assert p["n_chunks"] == 1
