@@ -1,12 +1,13 @@
 """GPU parity at the limits of the C ABI: the largest batch (65535, one grid
-dimension) and tensors of more than 2^31 elements, whose offsets need 64-bit
-arithmetic.  Inputs are drawn on the GPU from a seeded generator (the sizes are
+dimension), the largest number of time chunks (65535, another), and tensors of
+more than 2^31 elements, whose offsets need 64-bit arithmetic.  Inputs are drawn on the GPU from a seeded generator (the sizes are
 too large to draw on the host); the oracle runs on the channels and rows
 sampled from the same values."""
 import numpy as np
 import pytest
 
 import oracle
+import workloads
 from gpu_util import rowinf, say
 
 pytestmark = pytest.mark.gpu
@@ -172,3 +173,71 @@ def test_ssd_over_2g_elements_sampled():
         assert rowinf(got.reshape(batch, L, -1), ref.reshape(batch, L, -1), 1) <= TOL_BF16
         assert rowinf(_np(last[:, h:h + 1, psel]).reshape(batch, len(psel), N2),
                       ref_last.reshape(batch, len(psel), N2), 2) <= TOL_BF16
+
+
+def _host_case(batch, L, Dn, seed):
+    cfg = workloads.ScanConfig("limit", batch, Dn, N, L, "bf16")
+    inp = workloads.scan_inputs(cfg, seed=seed, random_params=True)
+    rng = np.random.default_rng(seed)
+    g = workloads.round_to_bf16(rng.standard_normal((batch, L, Dn)).astype(np.float32))
+    return inp, g
+
+
+def _dev(inp):
+    return {k: (torch.from_numpy(v).to(torch.bfloat16) if k in ("x", "delta", "z", "B", "C") else torch.from_numpy(v)).cuda()
+            for k, v in inp.items() if k != "dtype"}
+
+
+def _bwd_errs(got, ref, per_item=False):
+    """Row-relative errors of the backward's gradients: rows over t as in the
+    backward's parity tests, or (per_item) whole batch items, for sequences too
+    short for a row over t to have a meaningful scale."""
+    errs = {}
+    for k in ("dx", "ddelta", "dz", "dB", "dC"):
+        gk, rk = got[k].float().cpu().numpy(), ref[k]
+        if per_item:
+            gk, rk = gk.reshape(gk.shape[0], -1), rk.reshape(rk.shape[0], -1)
+        errs[k] = rowinf(gk, rk, 1)
+    errs["dA"] = rowinf(got["dA"].float().cpu().numpy(), ref["dA"], 1)
+    for k in ("dD", "ddelta_bias"):
+        r = ref[k]
+        errs[k] = float(np.max(np.abs(got[k].float().cpu().numpy() - r)) / np.max(np.abs(r)))
+    return errs
+
+
+def test_max_chunks_scan_and_backward():
+    L, Dn = 65535 * 8, 8   # 8-step chunks: 65535 of them, the largest plan
+    say(f"limits: forward and backward in 65535 time chunks of 8 steps (batch 1, seqlen {L}, d_inner {Dn})")
+    inp, g = _host_case(1, L, Dn, seed=36)
+    t = _dev(inp)
+    plan = {"states_per_wave": 4, "chunk_len": 8}
+    last = torch.empty((1, Dn, N), device="cuda")
+    out = ssm.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                           out_dtype=torch.float32, last_state=last, plan=plan)
+    res = ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                           dout=torch.from_numpy(g).cuda(), plan=plan)
+    torch.cuda.synchronize()
+    ref, ref_last = oracle.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                    inp["delta_bias"])
+    assert rowinf(_np(out), ref, 1) <= TOL_BF16
+    assert rowinf(_np(last), ref_last, 2) <= TOL_BF16
+    refg = oracle.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                           inp["delta_bias"], softplus=True, dout=g)
+    for k, e in _bwd_errs(res, refg).items():
+        assert e <= 1e-4, f"{k}: {e:.3e}"
+
+
+def test_max_batch_backward():
+    batch, L, Dn = 65535, 3, 8
+    say(f"limits: backward at batch {batch} (the maximum), seqlen {L}, d_inner {Dn}")
+    inp, g = _host_case(batch, L, Dn, seed=37)
+    t = _dev(inp)
+    res = ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                           dout=torch.from_numpy(g).cuda())
+    torch.cuda.synchronize()
+    refg = oracle.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                           inp["delta_bias"], softplus=True, dout=g)
+    errs = _bwd_errs(res, refg, per_item=True)  # three steps: rows are batch items
+    say("errors: " + " ".join(f"{k}={e:.1e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= 1e-4, f"{k}: {e:.3e}"
