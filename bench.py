@@ -16,8 +16,8 @@ the whole batch with inputs resident in HBM.  Prints ONE JSON line:
               tokens/s (the second half of the metric).
   conv1d, backward, zoh, ssd
               the other operations on the layer's shape, each timed on its own
-              (the backward also on the long single-row sequence, in the
-              planner's time chunks and in one chunk).
+              (the backward and the Mamba-2 scan also on a long single-row
+              sequence, in the planner's time chunks and in one chunk).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--out-dtype f32|bf16] [--no-cpu-baseline] [--no-decode]
@@ -464,7 +464,47 @@ def ssd_case(reps=20, decode_steps=64):
                      "frac": round(tflops / 2500.0, 4), "macs_per_call": macs},
             "decode_step": {"workload": f"ssm_ssd_state_update batch 64, {H_} heads x {P_}, d_state {N_}, bf16 in",
                             "us_per_step": round(step_ms * 1e3, 2), "bytes_per_step": step_bytes,
-                            "GBps": round(step_bytes / (step_ms / 1e3) / 1e9, 1)}}
+                            "GBps": round(step_bytes / (step_ms / 1e3) / 1e9, 1)},
+            "long_sequence": ssd_long_case()}
+
+
+def ssd_long_case():
+    """ssm_ssd_fwd on one long row: the long workload's length and 2048 channels as 32
+    Mamba-2 heads of 64 (d_state 128, one B/C group), in the planner's time chunks and
+    in one chunk.  Inputs are drawn on the GPU (seeded)."""
+    import torch
+
+    import sequence_scan_amd as ssm
+    import workloads
+
+    L, H, P, N = workloads.SCAN_CONFIGS["long_dna"].seqlen, 32, 64, 128
+    gen = torch.Generator(device="cuda").manual_seed(8)
+
+    def draw(shape, scale=1.0, shift=0.0, uniform=False):
+        out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        flat = out.view(-1)
+        for i in range(0, flat.numel(), 1 << 28):
+            n = min(1 << 28, flat.numel() - i)
+            r = torch.rand(n, generator=gen, device="cuda") if uniform else torch.randn(n, generator=gen, device="cuda")
+            flat[i:i + n] = (r * scale + shift).to(torch.bfloat16)
+        return out
+
+    x, z = draw((1, L, H, P)), draw((1, L, H, P))
+    dt = draw((1, L, H), 4.605, -6.907, uniform=True)   # softplus^-1 of steps in [1e-3, 0.1]
+    B, C = draw((1, L, 1, N)), draw((1, L, 1, N))
+    A = -(torch.rand(H, generator=gen, device="cuda") * 2.0 + 0.5)
+    D = torch.ones(H * P, device="cuda")
+    bias = torch.zeros(H, device="cuda")
+    out = torch.empty((1, L, H, P), device="cuda")
+    plan = ssm.ssm_ssd_plan_query(1, L, H, P, 1, N)
+    res = {"workload": f"ssm_ssd_fwd: batch 1, seqlen {L}, {H} heads x {P}, d_state {N}, one B/C group, bf16 in, "
+                       "fp32 out, softplus, D, z", "plan": plan}
+    for key, p in (("us_per_call", None), ("one_chunk_us_per_call", {"chunk_len": L})):
+        run = lambda: ssm.ssm_ssd_fwd(x, dt, A, B, C, D, z, bias, out=out, plan=p)
+        settle(run, 0.1)
+        ms, _ = time_steps(run, 3, 1)
+        res[key] = round(ms * 1e3, 1)
+    return res
 
 
 def main():

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 
 /*
  * Bits of the step-flags argument (named `softplus` in the calls below):
@@ -317,6 +317,33 @@ ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void
                        const float* initial_state, void* out, float* last_state, int64_t batch, int64_t seqlen,
                        int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state, ssm_dtype in_dtype,
                        ssm_dtype out_dtype, void* stream);
+
+/*
+ * Plans of the Mamba-2 scan.  A workgroup walks one (batch row, head) through
+ * the sequence; with at most 1.75 of them per compute unit, ssm_ssd_fwd cuts
+ * the sequence into time chunks that run in parallel.  A head's decay over a
+ * chunk is the scalar exp(A * sum of dt), so each chunk reduces to the pair
+ * (decay, end state from zero), and the pairs compose in time order into each
+ * chunk's entering state (vladkulikov.com, "Модуль 8. Альтернативы
+ * Transformer", section 7: the affine pair operator of the chunked scan).
+ * ssm_ssd_plan_query reports the plan ssm_ssd_fwd picks; ssm_ssd_fwd_plan
+ * runs with a given one (tests and tuning): plan->chunk_len >= 1, and a
+ * multiple of 32 whenever it is below seqlen; at most 65535 chunks;
+ * states_per_wave is ignored.  A chunked run takes
+ * batch * n_chunks * nheads * (headdim * d_state + 1) * 4 bytes of workspace
+ * (plus a copy of an in-place initial state) with hipMallocAsync on `stream`.
+ * Any valid plan computes the same function up to rounding order.  Otherwise
+ * as for ssm_ssd_fwd.
+ */
+ssm_status ssm_ssd_plan_query(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                              int64_t ngroups, int64_t d_state, ssm_plan* plan);
+
+ssm_status ssm_ssd_fwd_plan(const void* x, const void* dt, const float* A, const void* B,
+                            const void* C, const float* D, const void* z, const float* dt_bias,
+                            int softplus, const float* initial_state, void* out, float* last_state,
+                            int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                            int64_t ngroups, int64_t d_state, ssm_dtype in_dtype,
+                            ssm_dtype out_dtype, void* stream, const ssm_plan* plan);
 
 /*
  * One Mamba-2 decode step for every (b, h, p), continuing from `state`

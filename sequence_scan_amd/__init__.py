@@ -9,7 +9,8 @@ loaded, every call raises.
 Functions carry the C names: ``ssm_scan_fwd``, ``ssm_state_update``,
 ``ssm_scan_fwd_plan``, ``ssm_scan_fwd_from``, ``ssm_scan_plan``,
 ``ssm_scan_bwd``, ``ssm_scan_bwd_plan``, ``ssm_scan_bwd_plan_query``, ``ssm_conv1d_fwd``,
-``ssm_conv1d_update``, ``ssm_ssd_fwd``, ``ssm_ssd_state_update``, ``ssm_affine_exclusive_scan``,
+``ssm_conv1d_update``, ``ssm_ssd_fwd``, ``ssm_ssd_fwd_plan``, ``ssm_ssd_plan_query``, ``ssm_ssd_state_update``,
+``ssm_affine_exclusive_scan``,
 ``ssm_status_string``, ``ssm_last_error``, ``ssm_abi_version``.
 """
 from __future__ import annotations
@@ -86,6 +87,10 @@ def _load():
     lib.ssm_ssd_fwd.argtypes = [_vp] * 8 + [ctypes.c_int, _vp, _vp, _vp] + [_i64] * 6 + [ctypes.c_int, ctypes.c_int,
                                                                                          _vp]
     lib.ssm_ssd_fwd.restype = ctypes.c_int
+    lib.ssm_ssd_fwd_plan.argtypes = lib.ssm_ssd_fwd.argtypes + [ctypes.POINTER(ssm_plan)]
+    lib.ssm_ssd_fwd_plan.restype = ctypes.c_int
+    lib.ssm_ssd_plan_query.argtypes = [_i64] * 6 + [ctypes.POINTER(ssm_plan)]
+    lib.ssm_ssd_plan_query.restype = ctypes.c_int
     lib.ssm_ssd_state_update.argtypes = [_vp] * 9 + [ctypes.c_int, _vp] + [_i64] * 5 + [ctypes.c_int, ctypes.c_int,
                                                                                       _vp]
     lib.ssm_ssd_state_update.restype = ctypes.c_int
@@ -399,12 +404,21 @@ def ssm_affine_exclusive_scan(a, b, out_a=None, out_b=None, stream=None):
     return out_a, out_b
 
 
+def ssm_ssd_plan_query(batch: int, seqlen: int, nheads: int, headdim: int = 64, ngroups: int = 1,
+                       d_state: int = 128) -> dict:
+    """The time chunks ``ssm_ssd_fwd`` picks for these sizes."""
+    p = ssm_plan()
+    _check(_load().ssm_ssd_plan_query(batch, seqlen, nheads, headdim, ngroups, d_state, ctypes.byref(p)))
+    return {"chunk_len": p.chunk_len, "n_chunks": p.n_chunks}
+
+
 def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True, initial_state=None,
-                out=None, last_state=None, out_dtype=None, stream=None):
+                out=None, last_state=None, out_dtype=None, stream=None, plan: Optional[dict] = None):
     """Mamba-2 (SSD) scan (see include/ssmscan.h).  x, z: [batch, seqlen, nheads, headdim]
     (bfloat16); dt: [batch, seqlen, nheads]; B, C: [batch, seqlen, ngroups, d_state]; A,
     dt_bias: [nheads] and D: [nheads * headdim] (float32); states [batch, nheads, headdim,
-    d_state] float32.  Returns out (allocated if None, dtype ``out_dtype`` or x's)."""
+    d_state] float32.  Returns out (allocated if None, dtype ``out_dtype`` or x's).
+    ``plan`` = {"chunk_len": ..} forces the time chunks (``ssm_ssd_fwd_plan``)."""
     import torch
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x must be [batch, seqlen, nheads, headdim] and B [batch, seqlen, ngroups, d_state]")
@@ -417,10 +431,15 @@ def ssm_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = T
             last_state=(last_state, st, f32))
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    _check(_load().ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
-                               _flags(softplus, False), _ptr(initial_state), _ptr(out), _ptr(last_state), batch,
-                               seqlen, nheads, headdim, ngroups, d_state, _dtype_code(x), _dtype_code(out),
-                               _stream(stream)))
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _flags(softplus, False),
+            _ptr(initial_state), _ptr(out), _ptr(last_state), batch, seqlen, nheads, headdim, ngroups, d_state,
+            _dtype_code(x), _dtype_code(out), _stream(stream))
+    if plan is None:
+        _check(_load().ssm_ssd_fwd(*args))
+    else:
+        p = ssm_plan()
+        p.chunk_len = int(plan["chunk_len"])
+        _check(_load().ssm_ssd_fwd_plan(*args, ctypes.byref(p)))
     return out
 
 

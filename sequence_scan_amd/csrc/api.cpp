@@ -135,6 +135,30 @@ void choose_bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, 
   for (auto& r : p->reserved) r = 0;
 }
 
+// The Mamba-2 scan's plan.  Its workgroup walks one (batch row, head) through
+// the sequence; with at most 1.75 such workgroups per CU the sequence is cut
+// into time chunks (a multiple of the 32-step matrix chunk, at least 1024
+// steps) until there are about 12 workgroups per CU.  Each cut costs a pass A
+// (the chunk's state update alone, about half the scan's work per step) and
+// a carry over the chunks.
+void choose_ssd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int simds, ssm_plan* p) {
+  const int64_t wgs = std::max<int64_t>(1, batch * nheads);
+  const int64_t cus = std::max(1, simds / 4);
+  int64_t chunks = 1;
+  if (4 * wgs <= 7 * cus) {
+    chunks = (12 * cus + wgs - 1) / wgs;
+    chunks = std::min(chunks, std::max<int64_t>(1, seqlen / 1024));
+  }
+  int64_t chunk_len = seqlen > 0 ? (seqlen + chunks - 1) / chunks : 1;
+  if (chunks > 1) chunk_len = (chunk_len + 31) / 32 * 32;
+  if (chunk_len < 1) chunk_len = 1;
+  p->states_per_wave = 0;
+  p->reserved0 = 0;
+  p->chunk_len = chunk_len;
+  p->n_chunks = seqlen > 0 ? (seqlen + chunk_len - 1) / chunk_len : 0;
+  for (auto& r : p->reserved) r = 0;
+}
+
 struct Sizes {
   int64_t elems;      // batch * seqlen * d_inner
   int64_t bc;         // batch * seqlen * d_state
@@ -702,11 +726,11 @@ ssm_status ssm_affine_exclusive_scan(const float* a, const float* b, float* out_
   return ok();
 }
 
-ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
-                       const float* D, const void* z, const float* dt_bias, int softplus,
-                       const float* initial_state, void* out, float* last_state, int64_t batch, int64_t seqlen,
-                       int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state, ssm_dtype in_dtype,
-                       ssm_dtype out_dtype, void* stream) {
+static ssm_status ssd_impl(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* dt_bias, int softplus,
+                           const float* initial_state, void* out, float* last_state, int64_t batch,
+                           int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state,
+                           ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream, const ssm_plan* plan_in) {
   SsdSizes sz;
   ssm_status st = ssd_check(batch, seqlen, nheads, headdim, ngroups, d_state, in_dtype, out_dtype, softplus, true,
                             &sz);
@@ -743,6 +767,19 @@ ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void
   const bool in_place = initial_state != nullptr &&
                         static_cast<const void*>(initial_state) == static_cast<const void*>(last_state);
   if (!in_place && overlaps(rl, rh)) return fail(SSM_ERR_UNSUPPORTED, "last_state partly overlaps initial_state");
+  ssm_plan plan;
+  if (plan_in) {
+    plan = *plan_in;
+    if (plan.chunk_len < 1) return fail(SSM_ERR_UNSUPPORTED, "plan.chunk_len must be >= 1");
+    plan.n_chunks = seqlen > 0 ? (seqlen + plan.chunk_len - 1) / plan.chunk_len : 0;
+    if (plan.n_chunks > 1 && plan.chunk_len % 32 != 0)
+      return fail(SSM_ERR_UNSUPPORTED, "plan.chunk_len=%lld must be a multiple of 32 when it cuts the sequence",
+                  (long long)plan.chunk_len);
+    if (plan.n_chunks > 65535) return fail(SSM_ERR_UNSUPPORTED, "plan gives more than 65535 chunks");
+  } else {
+    choose_ssd_plan(batch, seqlen, nheads, device_simds(), &plan);
+  }
+  const int64_t K = std::max<int64_t>(1, plan.n_chunks);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch == 0) return ok();
@@ -767,6 +804,8 @@ ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void
   a.out = out;
   a.state = last_state;
   a.seqlen = seqlen;
+  a.chunk_len = K > 1 ? plan.chunk_len : seqlen;
+  a.n_chunks = (int32_t)K;
   a.batch = (int32_t)batch;
   a.nheads = (int32_t)nheads;
   a.headdim = (int32_t)headdim;
@@ -774,9 +813,64 @@ ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void
   a.d_state = (int32_t)d_state;
   a.softplus = (softplus & SSM_SOFTPLUS) ? 1 : 0;
   a.cus = device_simds() / 4;
-  hipError_t e = ssm::launch_ssd(a, to_dt(out_dtype), s);
+  void* ws = nullptr;
+  hipError_t e = hipSuccess;
+  if (K > 1) {
+    // With several chunks, the workgroups that read the initial state are not
+    // the ones that write the final state: an in-place initial state is read
+    // from a copy in the workspace.
+    const int64_t n_h0 = in_place ? sz.state : 0;
+    int64_t n_state, n_decay, bytes;
+    if (!mul_ok(sz.state, K, &n_state) || !mul_ok(batch * nheads, K, &n_decay) ||
+        !mul_ok(n_state + n_decay + n_h0, 4, &bytes))
+      return fail(SSM_ERR_BAD_SHAPE, "workspace size overflows int64");
+    e = hipMallocAsync(&ws, (size_t)bytes, s);
+    if (e != hipSuccess || ws == nullptr)
+      return fail(SSM_ERR_HIP, "hipMallocAsync(%lld bytes) failed: %s", (long long)bytes, hipGetErrorString(e));
+    a.ws_state = static_cast<float*>(ws);
+    a.ws_decay = a.ws_state + n_state;
+    if (n_h0 > 0) {
+      float* copy = a.ws_decay + n_decay;
+      e = ssm::launch_copy_f32(copy, initial_state, n_h0, s);
+      a.h0 = copy;
+    }
+  }
+  if (e == hipSuccess) e = ssm::launch_ssd(a, to_dt(out_dtype), s);
+  if (ws) {
+    hipError_t e2 = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = e2;
+  }
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias, int softplus,
+                       const float* initial_state, void* out, float* last_state, int64_t batch, int64_t seqlen,
+                       int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state, ssm_dtype in_dtype,
+                       ssm_dtype out_dtype, void* stream) {
+  return ssd_impl(x, dt, A, B, C, D, z, dt_bias, softplus, initial_state, out, last_state, batch, seqlen, nheads,
+                  headdim, ngroups, d_state, in_dtype, out_dtype, stream, nullptr);
+}
+
+ssm_status ssm_ssd_fwd_plan(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                            const float* D, const void* z, const float* dt_bias, int softplus,
+                            const float* initial_state, void* out, float* last_state, int64_t batch,
+                            int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state,
+                            ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream, const ssm_plan* plan) {
+  if (!plan) return fail(SSM_ERR_NULL_ARG, "plan is NULL");
+  return ssd_impl(x, dt, A, B, C, D, z, dt_bias, softplus, initial_state, out, last_state, batch, seqlen, nheads,
+                  headdim, ngroups, d_state, in_dtype, out_dtype, stream, plan);
+}
+
+ssm_status ssm_ssd_plan_query(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                              int64_t d_state, ssm_plan* plan) {
+  if (!plan) return fail(SSM_ERR_NULL_ARG, "plan is NULL");
+  SsdSizes sz;
+  ssm_status st = ssd_check(batch, seqlen, nheads, headdim, ngroups, d_state, SSM_BF16, SSM_F32, 0, true, &sz);
+  if (st != SSM_OK) return st;
+  choose_ssd_plan(batch, seqlen, nheads, device_simds(), plan);
+  return SSM_OK;
 }
 
 ssm_status ssm_ssd_state_update(float* state, const void* x, const void* dt, const float* A, const void* B,

@@ -87,7 +87,13 @@ struct SsdArgs {
   const float* h0;        // nullable (scan only)
   void* out;
   float* state;           // scan: last_state (nullable); decode: the state, in place
+  // Scans cut into time chunks (n_chunks > 1) only:
+  float* ws_state;        // [batch, n_chunks, nheads, headdim, d_state]: pass A's end states; after the
+                          // carry, slot k holds the state entering chunk k + 1
+  float* ws_decay;        // [batch, n_chunks, nheads]: a chunk's summed log2 decay, sum of dt A log2(e)
   int64_t seqlen;
+  int64_t chunk_len;      // steps per time chunk: a multiple of 32 unless n_chunks == 1
+  int32_t n_chunks;
   int32_t batch;
   int32_t nheads;
   int32_t headdim;

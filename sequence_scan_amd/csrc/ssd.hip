@@ -100,7 +100,12 @@ __device__ __forceinline__ Split2 split_bf16x2(float v0, float v1) {
   return {hi, pack_bf16x2(v0 - __uint_as_float(hi << 16), v1 - __uint_as_float(hi & 0xffff0000u))};
 }
 
-template <int N, typename Tout>
+// STATE_ONLY is pass A of a scan cut into time chunks: the chunk's end state
+// from zero (chunk 0: from the initial state) and its summed log2 decay, with
+// no readout and no output.  Otherwise time chunk blockIdx.z starts from the
+// state the carry gives it (chunk 0: the initial state); with one chunk that
+// is the whole sequence.
+template <int N, typename Tout, bool STATE_ONLY>
 __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
   constexpr int NT = N / 16;          // 16 x 16 state tiles per wave
   constexpr int NR = N / 64;          // 16-byte B/C vectors per thread and chunk
@@ -125,22 +130,27 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
   const int lr = l & 15, q = l >> 4;      // 16 x 16 tile: column / quarter of the lane
   const int h = blockIdx.x;
   const int b = blockIdx.y;
+  const int kt = blockIdx.z;                // time chunk
+  const int K = a.n_chunks;
   const int H = a.nheads;
   const int G = a.ngroups;
   const int g = h / (H / G);
-  const int64_t L = a.seqlen;
+  const int64_t t_begin = (int64_t)kt * a.chunk_len;
+  const int64_t L = min(a.chunk_len, a.seqlen - t_begin);   // steps of this time chunk
+  const int64_t row0 = (int64_t)b * a.seqlen + t_begin;      // its first step, as a row of the batch
   const int64_t xrow = (int64_t)H * kP;     // elements between consecutive steps of x, z, out
   const int64_t bcrow = (int64_t)G * N;     // ... of B and C
-  const uint16_t* xb = static_cast<const uint16_t*>(a.x) + (int64_t)b * L * xrow + (int64_t)h * kP;
-  const uint16_t* zb = a.z ? static_cast<const uint16_t*>(a.z) + (int64_t)b * L * xrow + (int64_t)h * kP : nullptr;
-  const uint16_t* dtb = static_cast<const uint16_t*>(a.dt) + (int64_t)b * L * H + h;
-  const uint16_t* Bb = static_cast<const uint16_t*>(a.B) + (int64_t)b * L * bcrow + (int64_t)g * N;
-  const uint16_t* Cb = static_cast<const uint16_t*>(a.C) + (int64_t)b * L * bcrow + (int64_t)g * N;
-  Tout* ob = static_cast<Tout*>(a.out) + (int64_t)b * L * xrow + (int64_t)h * kP;
+  const uint16_t* xb = static_cast<const uint16_t*>(a.x) + row0 * xrow + (int64_t)h * kP;
+  const uint16_t* zb = a.z ? static_cast<const uint16_t*>(a.z) + row0 * xrow + (int64_t)h * kP : nullptr;
+  const uint16_t* dtb = static_cast<const uint16_t*>(a.dt) + row0 * H + h;
+  const uint16_t* Bb = static_cast<const uint16_t*>(a.B) + row0 * bcrow + (int64_t)g * N;
+  const uint16_t* Cb = static_cast<const uint16_t*>(a.C) + row0 * bcrow + (int64_t)g * N;
+  Tout* ob = static_cast<Tout*>(a.out) + row0 * xrow + (int64_t)h * kP;
+  const int64_t head_state = (int64_t)kP * N;   // state elements of one head
   const float A2 = a.A[h] * kLog2e;
   const float bias = a.bias ? a.bias[h] : 0.0f;
   const bool softplus = a.softplus != 0;
-  const bool has_z = zb != nullptr;
+  const bool has_z = !STATE_ONLY && zb != nullptr;   // pass A reads neither z nor C
   const bool has_D = a.D != nullptr;
   const int p = 16 * w + lr;              // this lane's channel in the readout and the state
   const float Dp = has_D ? a.D[(int64_t)h * kP + p] : 0.0f;
@@ -159,7 +169,7 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
     for (int r = 0; r < NR; ++r) {
       const int v = tid + 256 * r;
       const int64_t off = (t0 + min(v / (N / 8), nt - 1)) * bcrow + (v % (N / 8)) * 8;
-      bank.c[r] = *reinterpret_cast<const u32x4_t*>(Cb + off);
+      if (!STATE_ONLY) bank.c[r] = *reinterpret_cast<const u32x4_t*>(Cb + off);
       bank.bb[r] = *reinterpret_cast<const u32x4_t*>(Bb + off);
     }
     const int64_t xoff = (t0 + min(xrow_i, nt - 1)) * xrow + xc8 * 8;
@@ -170,12 +180,13 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
 
   // Stage the banked chunk (steps past nt carry x = 0 and dt = 0, so they
   // change nothing) and form the step sizes and per-step decay factors.
+  float csum = 0.0f;   // wave 0: the summed log2 decay of the chunks so far
   auto stage = [&](int nt) SSM_INLINE {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int v = tid + 256 * r;
       const int row = v / (N / 8), c8 = v % (N / 8);
-      *reinterpret_cast<u32x4_t*>(&sC[row * SC + c8 * 8]) = bank.c[r];
+      if (!STATE_ONLY) *reinterpret_cast<u32x4_t*>(&sC[row * SC + c8 * 8]) = bank.c[r];
       *reinterpret_cast<u32x4_t*>(&sB[row * SB + c8 * 8]) = bank.bb[r];
     }
     if (xrow_i >= nt) bank.x = u32x4_t{0u, 0u, 0u, 0u};
@@ -191,6 +202,7 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
       affine_wave_scan(one, c);  // (1, c) pairs compose to prefix sums of c
       // steps past nt add nothing, so the prefix at the last step is c_end
       const float c_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), kQ - 1));
+      csum += c_end;
       if (l < kQ) {
         s_dt[l] = d;
         s_cum[l] = c;
@@ -203,17 +215,20 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
 
   // The state S^T: tile t holds n in [16t, 16t + 16) x this wave's 16 channels;
   // register r of lane l is S^T[16t + 4(l/16) + r][p].
+  const float* hsrc = kt == 0 ? (a.h0 != nullptr ? a.h0 + ((int64_t)b * H + h) * head_state : nullptr)
+                     : STATE_ONLY ? nullptr
+                     : a.ws_state + ((int64_t)(b * K + kt - 1) * H + h) * head_state;
   f32x4_t accS[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    if (a.h0 != nullptr) {
-      const float4 v = *reinterpret_cast<const float4*>(a.h0 + (((int64_t)b * H + h) * kP + p) * N + 16 * t + 4 * q);
+    if (hsrc != nullptr) {
+      const float4 v = *reinterpret_cast<const float4*>(hsrc + (int64_t)p * N + 16 * t + 4 * q);
       accS[t] = f32x4_t{v.x, v.y, v.z, v.w};
     } else {
       accS[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
-  bool has_state = a.h0 != nullptr;
+  bool has_state = hsrc != nullptr;
 
   // W is zero above the diagonal: its block (rows 0..15, columns 16..31) is
   // never written by the chunks, so clear it once.
@@ -270,7 +285,7 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
     block_sync();
 
     // Phase 1.  Waves 0..2: one 16 x 16 tile of G each, masked and decayed into W.
-    if (w < 3) {
+    if (!STATE_ONLY && w < 3) {
       const int ib = w == 0 ? 0 : 1, jb = w == 2 ? 1 : 0;
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -316,7 +331,7 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
     f32x4_t accY[2];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) accY[ib] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    if (has_state) {
+    if (!STATE_ONLY && has_state) {
 #pragma unroll
       for (int m = 0; m < N / 32; ++m) {
         u32x4_t hw, lw;
@@ -348,7 +363,7 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
 
     // Phase 2.  Y += W X; D skip, gate and store; the state moves to the end
     // of the chunk.
-    {
+    if constexpr (!STATE_ONLY) {
       const bf16x8_t xo = ld_col8(sX, SP, 8 * q, 16 * w, l);   // x[8q .. 8q + 7][p]
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
@@ -379,11 +394,35 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
     block_sync();
   }
 
-  if (a.state != nullptr) {
+  float* sdst = STATE_ONLY ? a.ws_state + ((int64_t)(b * K + kt) * H + h) * head_state
+               : kt == K - 1 && a.state != nullptr ? a.state + ((int64_t)b * H + h) * head_state : nullptr;
+  if (sdst != nullptr) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      *reinterpret_cast<float4*>(a.state + (((int64_t)b * H + h) * kP + p) * N + 16 * t + 4 * q) =
+      *reinterpret_cast<float4*>(sdst + (int64_t)p * N + 16 * t + 4 * q) =
           make_float4(accS[t][0], accS[t][1], accS[t][2], accS[t][3]);
+  }
+  if (STATE_ONLY && tid == 0) a.ws_decay[(int64_t)(b * K + kt) * H + h] = csum;
+}
+
+// The carry of a scan cut into time chunks.  A head's decay over a chunk is
+// the scalar exp2(summed log2 decay), so the pair (decay, end state) of every
+// chunk composes in time order into the state entering the next chunk:
+// S <- exp2(decay_k) S + end_k, from S = 0 (chunk 0's pair already carries the
+// initial state).  One thread per (batch row, head, state element),
+// sequential over chunks; slot k is replaced by the state entering chunk k + 1.
+__global__ void __launch_bounds__(256) ssd_carry_kernel(SsdArgs a) {
+  const int64_t per = (int64_t)a.headdim * a.d_state;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int h = (int)blockIdx.y;
+  const int64_t b = blockIdx.z;
+  if (e >= per) return;
+  const int K = a.n_chunks, H = a.nheads;
+  float S = 0.0f;
+  for (int k = 0; k + 1 < K; ++k) {
+    const int64_t slot = (b * K + k) * H + h;
+    S = __builtin_fmaf(__builtin_amdgcn_exp2f(a.ws_decay[slot]), S, a.ws_state[slot * per + e]);
+    a.ws_state[slot * per + e] = S;
   }
 }
 
@@ -443,13 +482,27 @@ __global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a) {
   }
 }
 
+// One launch of a chunk-kernel instance, with the progress-priority scheme
+// (ProgressPriority) on when the device holds the whole grid at once.
+template <typename Kern>
+void launch_ssd_pass(Kern kern, int per_cu, dim3 grid, const SsdArgs& a, hipStream_t s) {
+  SsdArgs b = a;
+  b.fair = grid_coresident(per_cu, a.cus, grid) ? 1 : 0;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, b);
+}
+
 template <int N, typename Tout>
 void launch_ssd_nt(const SsdArgs& a, hipStream_t s) {
-  static const int per_cu = resident_per_cu(ssd_chunk_kernel<N, Tout>, 256);
-  const dim3 grid((unsigned)a.nheads, (unsigned)a.batch);
-  SsdArgs b = a;
-  b.fair = grid_coresident(per_cu, a.cus, grid) ? 1 : 0;  // see ProgressPriority
-  hipLaunchKernelGGL((ssd_chunk_kernel<N, Tout>), grid, dim3(256), 0, s, b);
+  static const int per_cu = resident_per_cu(ssd_chunk_kernel<N, Tout, false>, 256);
+  static const int per_cu_a = resident_per_cu(ssd_chunk_kernel<N, float, true>, 256);
+  if (a.n_chunks > 1) {
+    launch_ssd_pass(ssd_chunk_kernel<N, float, true>, per_cu_a,
+                    dim3((unsigned)a.nheads, (unsigned)a.batch, (unsigned)(a.n_chunks - 1)), a, s);
+    const unsigned blocks = (unsigned)(((int64_t)a.headdim * a.d_state + 255) / 256);
+    hipLaunchKernelGGL(ssd_carry_kernel, dim3(blocks, (unsigned)a.nheads, (unsigned)a.batch), dim3(256), 0, s, a);
+  }
+  launch_ssd_pass(ssd_chunk_kernel<N, Tout, false>, per_cu,
+                  dim3((unsigned)a.nheads, (unsigned)a.batch, (unsigned)a.n_chunks), a, s);
 }
 
 template <int N>

@@ -23,13 +23,13 @@ def test_every_declared_function_is_exported():
     assert {"ssm_scan_fwd", "ssm_state_update", "ssm_scan_plan", "ssm_scan_fwd_plan", "ssm_scan_fwd_from",
             "ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_affine_exclusive_scan", "ssm_status_string",
             "ssm_last_error", "ssm_abi_version", "ssm_scan_bwd", "ssm_scan_bwd_plan", "ssm_scan_bwd_plan_query",
-            "ssm_ssd_fwd", "ssm_ssd_state_update"} <= set(names)
+            "ssm_ssd_fwd", "ssm_ssd_fwd_plan", "ssm_ssd_plan_query", "ssm_ssd_state_update"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssmscan.h but not exported"
 
 
 def test_version_and_strings():
-    assert ssm.ssm_abi_version() == 6
+    assert ssm.ssm_abi_version() == 7
     for code, name in ssm.STATUS_NAMES.items():
         assert ssm.ssm_status_string(code).startswith(name)
     assert "unknown" in ssm.ssm_status_string(99)

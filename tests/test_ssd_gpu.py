@@ -48,7 +48,8 @@ def _case(batch, L, H, G, N, seed, dtype="bf16"):
     return workloads.ssd_inputs(cfg, seed=seed)
 
 
-def _run(inp, use=("D", "z", "dt_bias"), softplus=True, h0=None, out_dtype=torch.float32, in_place=False):
+def _run(inp, use=("D", "z", "dt_bias"), softplus=True, h0=None, out_dtype=torch.float32, in_place=False,
+         chunk_len=None):
     t = _dev(inp)
     batch, L, H, P = inp["x"].shape
     N = inp["B"].shape[3]
@@ -56,7 +57,8 @@ def _run(inp, use=("D", "z", "dt_bias"), softplus=True, h0=None, out_dtype=torch
     last = h if in_place else torch.full((batch, H, P, N), float("nan"), device="cuda")
     out = ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"] if "D" in use else None,
                           t["z"] if "z" in use else None, t["dt_bias"] if "dt_bias" in use else None,
-                          softplus=softplus, initial_state=h, last_state=last, out_dtype=out_dtype)
+                          softplus=softplus, initial_state=h, last_state=last, out_dtype=out_dtype,
+                          plan={"chunk_len": chunk_len} if chunk_len else None)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), last.cpu().numpy()
 
@@ -162,3 +164,46 @@ def test_ssd_layer_shape_sampled():
     sub["D"] = np.ascontiguousarray(inp["D"].reshape(80, 64)[sel].reshape(-1))
     ref, ref_last = _ref(sub)
     _check(out[:, :, sel], last[:, sel], ref, ref_last)
+
+
+# ---- time chunks (ssm_ssd_fwd_plan): pass A's end states and per-head decays,
+# composed by the carry into each chunk's entering state
+
+@pytest.mark.parametrize("batch,L,H,G,N,chunk", [(1, 200, 2, 1, 64, 32), (2, 300, 3, 1, 128, 64),
+                                                 (1, 1000, 2, 2, 128, 96), (2, 257, 4, 2, 64, 128),
+                                                 (1, 65, 1, 1, 128, 32)])
+def test_ssd_time_chunks_vs_oracle(batch, L, H, G, N, chunk):
+    # ragged last time chunks and matrix chunks; chunks of one 32-step matrix chunk
+    say(f"SSD in time chunks: batch {batch} seqlen {L} nheads {H} ngroups {G} d_state {N} chunk_len {chunk}")
+    inp = _case(batch, L, H, G, N, seed=L + 7 * H)
+    h0 = workloads.ssd_initial_state(batch, H, 64, N, seed=L)
+    out, last = _run(inp, h0=h0, chunk_len=chunk)
+    _check(out, last, *_ref(inp, h0=h0))
+    out0, last0 = _run(inp, chunk_len=chunk)
+    _check(out0, last0, *_ref(inp))
+
+
+@pytest.mark.parametrize("softplus,use,in_place", [(False, ("D", "z", "dt_bias"), False), (True, (), True),
+                                                   (True, ("z",), True)])
+def test_ssd_time_chunks_options(softplus, use, in_place):
+    say(f"SSD in time chunks: options softplus={softplus} inputs={use} in place {in_place}; bf16 out = RNE of fp32")
+    inp = _case(2, 230, 3, 1, 128, seed=87)
+    if not softplus:
+        rng = np.random.default_rng(88)
+        inp["dt"] = workloads.round_to_bf16(np.exp(rng.uniform(np.log(1e-3), np.log(0.1), inp["dt"].shape)))
+        inp["dt_bias"] = np.zeros_like(inp["dt_bias"])
+    h0 = workloads.ssd_initial_state(2, 3, 64, 128, seed=89)
+    out, last = _run(inp, use=use, softplus=softplus, h0=h0, in_place=in_place, chunk_len=64)
+    _check(out, last, *_ref(inp, use=use, softplus=softplus, h0=h0))
+    o16, _ = _run(inp, use=use, softplus=softplus, h0=h0, out_dtype=torch.bfloat16, chunk_len=64)
+    np.testing.assert_array_equal(o16, rne_bf16_of(torch.from_numpy(out)))
+
+
+def test_ssd_planner_chunks_a_long_sequence():
+    L, H = 8192, 2   # 2 workgroups: the planner cuts the sequence
+    plan = ssm.ssm_ssd_plan_query(1, L, H, 64, 1, 128)
+    say(f"SSD batch 1 seqlen {L} nheads {H} d_state 128, planner's plan {plan}")
+    assert plan["n_chunks"] > 1
+    inp = _case(1, L, H, 1, 128, seed=91)
+    out, last = _run(inp)
+    _check(out, last, *_ref(inp))
