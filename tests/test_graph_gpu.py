@@ -140,8 +140,9 @@ def test_conv1d_graph():
         assert torch.equal(cache, want[1]), f"replay {r}: cache differs"
 
 
-def test_ssd_graph():
-    say("graph: Mamba-2 SSD batch 2 L 100 heads 4 x 64 d_state 64 bf16, then 3 decode steps")
+@pytest.mark.parametrize("chunk_len", [None, 32])
+def test_ssd_graph(chunk_len):
+    say(f"graph: Mamba-2 SSD batch 2 L 100 heads 4 x 64 d_state 64 bf16 (chunk_len {chunk_len}), then 3 decode steps")
     cfg = workloads.SsdConfig("g", 2, 100, 4, 64, 1, 64)
     t = {k: (torch.from_numpy(v).to(torch.bfloat16) if k in ("x", "dt", "z", "B", "C") else torch.from_numpy(v)).cuda()
          for k, v in workloads.ssd_inputs(cfg, seed=24).items() if k != "dtype"}
@@ -153,7 +154,7 @@ def test_ssd_graph():
 
     def call():
         ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["z"], t["dt_bias"],
-                        out=out, last_state=last)
+                        out=out, last_state=last, plan={"chunk_len": chunk_len} if chunk_len else None)
         for s, d in enumerate(dec):
             ssm.ssm_ssd_state_update(last, d["x"], d["dt"], t["A"], d["B"], d["C"], t["D"], d["z"], t["dt_bias"],
                                      softplus=True, out=yd[s])
