@@ -305,6 +305,30 @@ def test_step_flags():
                                     None, None, None, good, P + 0x6000000, 0, 64, 16, F32, F32, None) == ssm.SSM_OK
 
 
+def test_ssd_plan_choices_and_rejections():
+    # MI355X: 256 CUs.  The Mamba-2-2.7B-like layer (640 workgroups) runs in one chunk; one long row is cut.
+    p = ssm.ssm_ssd_plan_query(8, 2048, 80, 64, 1, 128)
+    assert p["n_chunks"] == 1
+    p = ssm.ssm_ssd_plan_query(1, 262144, 32, 64, 1, 128)
+    assert p["n_chunks"] > 1 and p["chunk_len"] % 32 == 0 and p["chunk_len"] >= 1024
+    assert p["chunk_len"] * p["n_chunks"] >= 262144 > p["chunk_len"] * (p["n_chunks"] - 1)
+    assert ssm.ssm_ssd_plan_query(1, 1000, 2, 64, 1, 128)["n_chunks"] == 1     # too short to cut
+    with pytest.raises(ssm.SSMError):
+        ssm.ssm_ssd_plan_query(1, 10, 4, 32, 1, 128)                            # headdim 32
+    lib = ssm.library()
+
+    def ssd(chunk, seqlen=100, plan=True):
+        pl = ssm.ssm_plan()
+        pl.chunk_len = chunk
+        return lib.ssm_ssd_fwd_plan(P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, None, None, None, 1,
+                                    None, P + 0x5000000, None, 1, seqlen, 4, 64, 1, 128, BF16, F32, None,
+                                    ctypes.byref(pl) if plan else None)
+    for chunk, seqlen in ((0, 100), (-32, 100), (48, 100), (32, 65536 * 32)):
+        assert ssd(chunk, seqlen) == ssm.SSM_ERR_UNSUPPORTED, (chunk, seqlen)
+    assert "multiple of 32" in (ssd(48) and ssm.ssm_last_error())
+    assert ssd(32, plan=False) == ssm.SSM_ERR_NULL_ARG
+
+
 def test_ssd_rejections():
     """Host-side checks of the Mamba-2 calls (nothing is enqueued on these paths)."""
     lib = ssm.library()
