@@ -780,6 +780,9 @@ static ssm_status ssd_impl(const void* x, const void* dt, const float* A, const 
     choose_ssd_plan(batch, seqlen, nheads, device_simds(), &plan);
   }
   const int64_t K = std::max<int64_t>(1, plan.n_chunks);
+  // the carry between time chunks has one workgroup row per head
+  if (K > 1 && nheads > 65535)
+    return fail(SSM_ERR_UNSUPPORTED, "nheads=%lld exceeds 65535 for a scan cut into time chunks", (long long)nheads);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch == 0) return ok();

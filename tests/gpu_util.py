@@ -64,3 +64,70 @@ def rne_bf16_of(t):
     """Round a float32 torch tensor to bfloat16 (nearest even), returned as float32 on the CPU."""
     from workloads import round_to_bf16
     return round_to_bf16(t.float().cpu().numpy())
+
+
+def _max(a: float, b: float) -> float:
+    """max that keeps a NaN (Python's max drops one in the second place)."""
+    return a if (a != a or a >= b) else b
+
+
+class Parity:
+    """Errors of a GPU result against the oracle, accumulated over blocks that each
+    hold whole rows (a row is the reduced axis: (b, d) over t for a scan's out,
+    over steps for decode, over n for a state).
+
+      row_inf    max over rows of max|y - ref| / max|ref| (the gated metric);
+      elem_rms   max over elements of |y - ref| / max(|ref|, rms of the row);
+      elem_rms3  the same with the floor 1e-3 * rms of the row;
+      whole_inf  max|y - ref| / max|ref| over the whole tensor.
+    NaN anywhere in the error makes every metric NaN, so a bar check fails."""
+
+    def __init__(self, name: str):
+        self.name = name
+        self.row_inf = 0.0
+        self.elem_rms = 0.0
+        self.elem_rms3 = 0.0
+        self.max_err = 0.0
+        self.max_ref = 0.0
+        self.count = 0
+
+    def add(self, y, ref, axis):
+        y = np.asarray(y, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert y.shape == ref.shape, (y.shape, ref.shape)
+        if y.size == 0:
+            return self
+        err = np.abs(y - ref)
+        aref = np.abs(ref)
+        den = np.max(aref, axis=axis, keepdims=True)
+        self.row_inf = _max(self.row_inf, float(np.max(np.max(err, axis=axis, keepdims=True) /
+                                                       np.where(den > 0, den, 1.0))))
+        rms = np.sqrt(np.mean(ref * ref, axis=axis, keepdims=True))
+        for attr, floor in (("elem_rms", rms), ("elem_rms3", 1e-3 * rms)):
+            f = np.maximum(aref, floor)
+            setattr(self, attr, _max(getattr(self, attr), float(np.max(err / np.where(f > 0, f, 1.0)))))
+        self.max_err = _max(self.max_err, float(np.max(err)))
+        self.max_ref = _max(self.max_ref, float(np.max(aref)))
+        self.count += y.size
+        return self
+
+    @property
+    def whole_inf(self) -> float:
+        return self.max_err / self.max_ref if self.max_ref > 0 else self.max_err
+
+    def report(self) -> str:
+        return (f"{self.name}: {self.count} values, row_inf {self.row_inf:.3e}, elem_rms {self.elem_rms:.3e}, "
+                f"elem_rms3 {self.elem_rms3:.3e}, whole_inf {self.whole_inf:.3e}")
+
+    def check(self, gate: float, tight: float | None = None, tight_rms3: float | None = None):
+        """Gate: row_inf and elem_rms <= gate.  tight: every metric but elem_rms3 <= tight
+        (inputs are identical on both sides, so only fp32 rounding differs); tight_rms3:
+        elem_rms3 <= tight_rms3."""
+        print(f"[parity] {self.report()}", flush=True)
+        assert self.count > 0, self.name
+        assert self.row_inf <= gate, self.report()
+        assert self.elem_rms <= gate, self.report()
+        if tight is not None:
+            assert max(self.row_inf, self.elem_rms, self.whole_inf) <= tight, self.report()
+        if tight_rms3 is not None:
+            assert self.elem_rms3 <= tight_rms3, self.report()
