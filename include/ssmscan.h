@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 7
+#define SSM_ABI_VERSION 8
 
 /*
  * Bits of the step-flags argument (named `softplus` in the calls below):
@@ -171,6 +171,30 @@ ssm_status ssm_scan_fwd_from(const void* x, const void* delta, const float* A, c
                              void* out, float* last_state, int64_t batch, int64_t seqlen,
                              int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
                              ssm_dtype out_dtype, void* stream, const ssm_plan* plan);
+
+/*
+ * ssm_scan_fwd_from for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and checks as ssm_scan_fwd_from, and
+ * the same kernels; it calls no hipMalloc, hipMallocAsync or hipFree.  A plan
+ * with more than one time chunk keeps its carry workspace (about
+ * batch * n_chunks * d_inner * 68 bytes, plus the state when initial_state
+ * is last_state) in a fixed array of SSM_NOALLOC_SCRATCH_BYTES bytes that
+ * every GPU the library runs on holds from the first use until the process
+ * ends.  A plan that needs more returns SSM_ERR_UNSUPPORTED (nothing
+ * enqueued); ssm_scan_plan gives the planner's chunks.  All calls on one GPU
+ * share that GPU's array and leave their contents in it: calls that overlap
+ * in time on one GPU (different streams, or different host threads without
+ * ordering) race and give wrong results.  The first call on a device looks
+ * up the array's address (no allocation).
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+ssm_status ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B,
+                                const void* C, const float* D, const void* z,
+                                const float* delta_bias, int softplus, const float* initial_state,
+                                void* out, float* last_state, int64_t batch, int64_t seqlen,
+                                int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
+                                ssm_dtype out_dtype, void* stream, const ssm_plan* plan);
 
 /*
  * Backward of the scan: the gradients of a loss L with respect to every input

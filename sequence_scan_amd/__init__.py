@@ -69,6 +69,8 @@ def _load():
                                       _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp,
                                       ctypes.POINTER(ssm_plan)]
     lib.ssm_scan_fwd_from.restype = ctypes.c_int
+    lib.ssm_scan_fwd_noalloc.argtypes = lib.ssm_scan_fwd_from.argtypes
+    lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssm_scan_bwd.argtypes = [_vp] * 8 + [ctypes.c_int] + [_vp] * 12 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int, _vp]
     lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_scan_bwd_plan.argtypes = lib.ssm_scan_bwd.argtypes + [ctypes.POINTER(ssm_plan)]
@@ -246,6 +248,22 @@ def ssm_scan_fwd_from(x, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
     """Forward scan continuing from ``initial_state`` [batch, d_inner, d_state] float32
     (None: zero); ``last_state`` may be the same tensor (replaced in place).  Other
     arguments as for ``ssm_scan_fwd``.  Returns out."""
+    return _scan_from("ssm_scan_fwd_from", x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, out,
+                      last_state, out_dtype, stream, plan, zoh)
+
+
+def ssm_scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                         initial_state=None, out=None, last_state=None, out_dtype=None, stream=None,
+                         plan: Optional[dict] = None, zoh: bool = False):
+    """``ssm_scan_fwd_from`` whose carry workspace is the library's fixed per-device
+    scratch (SSM_NOALLOC_SCRATCH_BYTES) instead of a stream-ordered allocation.  The C
+    call allocates nothing; pass ``out`` to keep this wrapper from allocating it."""
+    return _scan_from("ssm_scan_fwd_noalloc", x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, out,
+                      last_state, out_dtype, stream, plan, zoh)
+
+
+def _scan_from(fn, x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, out, last_state, out_dtype,
+               stream, plan, zoh):
     import torch
     if x.dim() != 3:
         raise ValueError("x must be [batch, seqlen, d_inner]")
@@ -260,10 +278,10 @@ def ssm_scan_fwd_from(x, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
             initial_state=(initial_state, st, f32))
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    _check(_load().ssm_scan_fwd_from(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                     _ptr(delta_bias), _flags(softplus, zoh), _ptr(initial_state), _ptr(out),
-                                     _ptr(last_state), batch, seqlen, d_inner, d_state, _dtype_code(x),
-                                     _dtype_code(out), _stream(stream), _plan_struct(plan)))
+    _check(getattr(_load(), fn)(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(delta_bias), _flags(softplus, zoh), _ptr(initial_state), _ptr(out),
+                                _ptr(last_state), batch, seqlen, d_inner, d_state, _dtype_code(x),
+                                _dtype_code(out), _stream(stream), _plan_struct(plan)))
     return out
 
 

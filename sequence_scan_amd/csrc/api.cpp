@@ -213,7 +213,7 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
                      const float* D, const void* z, const float* delta_bias, int softplus, const float* h0,
                      void* out, float* last_state, int64_t batch, int64_t seqlen, int64_t d_inner,
                      int64_t d_state, ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream,
-                     const ssm_plan* plan_in) {
+                     const ssm_plan* plan_in, bool fixed_scratch = false) {
   Sizes sz;
   ssm_status st = check_common(batch, seqlen, d_inner, d_state, in_dtype, out_dtype, &sz);
   if (st != SSM_OK) return st;
@@ -295,7 +295,7 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   a.batch = (int32_t)batch;
   a.cus = device_simds() / 4;
 
-  void* ws = nullptr;
+  void* ws = nullptr;       // a stream-ordered allocation, freed below
   hipError_t e = hipSuccess;
   if (plan.n_chunks > 1) {
     // With several chunks, the workgroups that read the initial state are not
@@ -306,10 +306,23 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
     if (!mul_ok(batch * plan.n_chunks, d_inner * d_state, &n_state) ||
         !mul_ok(batch * plan.n_chunks, d_inner, &n_sum) || !mul_ok(n_state + n_sum + n_h0, 4, &bytes))
       return fail(SSM_ERR_BAD_SHAPE, "workspace size overflows int64");
-    e = hipMallocAsync(&ws, (size_t)bytes, s);
-    if (e != hipSuccess || ws == nullptr)
-      return fail(SSM_ERR_HIP, "hipMallocAsync(%lld bytes) failed: %s", (long long)bytes, hipGetErrorString(e));
-    a.ws_state = static_cast<float*>(ws);
+    float* base = nullptr;
+    if (fixed_scratch) {
+      // Every slot the passes read is written first in stream order (pass A,
+      // the carry, the initial-state copy), so the array needs no clearing.
+      if (bytes > ssm::kScratchBytes)
+        return fail(SSM_ERR_UNSUPPORTED, "the plan's carry workspace needs %lld bytes; the fixed scratch holds %lld",
+                    (long long)bytes, (long long)ssm::kScratchBytes);
+      e = ssm::scratch_address(&base);
+      if (e != hipSuccess)
+        return fail(SSM_ERR_HIP, "looking up the fixed scratch failed: %s", hipGetErrorString(e));
+    } else {
+      e = hipMallocAsync(&ws, (size_t)bytes, s);
+      if (e != hipSuccess || ws == nullptr)
+        return fail(SSM_ERR_HIP, "hipMallocAsync(%lld bytes) failed: %s", (long long)bytes, hipGetErrorString(e));
+      base = static_cast<float*>(ws);
+    }
+    a.ws_state = base;
     a.ws_dtsum = a.ws_state + n_state;
     if (n_h0 > 0) {
       float* copy = a.ws_dtsum + n_sum;
@@ -395,6 +408,17 @@ ssm_status ssm_scan_fwd_from(const void* x, const void* delta, const float* A, c
                              ssm_dtype out_dtype, void* stream, const ssm_plan* plan) {
   return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, out, last_state, batch, seqlen,
                    d_inner, d_state, in_dtype, out_dtype, stream, plan);
+}
+
+static_assert(ssm::kScratchBytes == SSM_NOALLOC_SCRATCH_BYTES, "the header states the fixed scratch size");
+
+ssm_status ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                                const float* D, const void* z, const float* delta_bias, int softplus,
+                                const float* initial_state, void* out, float* last_state, int64_t batch,
+                                int64_t seqlen, int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
+                                ssm_dtype out_dtype, void* stream, const ssm_plan* plan) {
+  return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, out, last_state, batch, seqlen,
+                   d_inner, d_state, in_dtype, out_dtype, stream, plan, true);
 }
 
 ssm_status ssm_scan_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, ssm_plan* plan) {

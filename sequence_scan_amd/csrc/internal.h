@@ -144,6 +144,10 @@ struct BwdArgs {
 
 constexpr int kBwdTile = 8;  // steps per backward tile (and per checkpoint)
 
+// Size of the fixed per-device scratch array that ssm_scan_fwd_noalloc uses
+// in place of a stream-ordered workspace (scan.hip).
+constexpr int64_t kScratchBytes = 32ll << 20;
+
 // Launchers; each returns the hipGetLastError() of its launches.
 hipError_t launch_scan(const ScanArgs& a, DT in, DT out, int states_per_wave, hipStream_t s);
 // What launch_scan dispatches to: the kernel instances of one (input dtype,
@@ -161,6 +165,9 @@ hipError_t launch_carry(const ScanArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, DT in, DT out, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+// The device address of the current device's copy of the fixed scratch array
+// (kScratchBytes), looked up once per device.
+hipError_t scratch_address(float** out);
 // K is the filter width (2, 3 or 4).  The forward launch writes out, then
 // (stream-ordered) the new cache; the update reads and rewrites the cache.
 hipError_t launch_conv1d(const ConvArgs& a, DT in, DT out, int K, hipStream_t s);

@@ -28,6 +28,8 @@
 //    the step-size sum S (the chunk's decay is exp(A S)).  The carry kernel
 //    scans the pairs in time order with a wavefront DPP scan (lane = chunk).
 //    Pass B re-runs each chunk from its incoming state with the full readout.
+#include <mutex>
+
 #include "device.h"
 
 namespace ssm {
@@ -266,5 +268,34 @@ hipError_t launch_affine_exclusive_scan(const float* a, const float* b, float* o
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ fixed scratch
+//
+// The carry workspace of ssm_scan_fwd_noalloc, for callers that cannot
+// allocate device memory.  Every GPU the library runs on holds its own copy of
+// this array until the process ends.  In host code the name `scratch` is a
+// host-side stand-in, not a device address: each device's address is looked
+// up once with hipGetSymbolAddress while that device is current, and only that
+// address is ever handed to kernels.
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+hipError_t scratch_address(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 }  // namespace ssm

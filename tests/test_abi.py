@@ -23,13 +23,14 @@ def test_every_declared_function_is_exported():
     assert {"ssm_scan_fwd", "ssm_state_update", "ssm_scan_plan", "ssm_scan_fwd_plan", "ssm_scan_fwd_from",
             "ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_affine_exclusive_scan", "ssm_status_string",
             "ssm_last_error", "ssm_abi_version", "ssm_scan_bwd", "ssm_scan_bwd_plan", "ssm_scan_bwd_plan_query",
-            "ssm_ssd_fwd", "ssm_ssd_fwd_plan", "ssm_ssd_plan_query", "ssm_ssd_state_update"} <= set(names)
+            "ssm_ssd_fwd", "ssm_ssd_fwd_plan", "ssm_ssd_plan_query", "ssm_ssd_state_update",
+            "ssm_scan_fwd_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssmscan.h but not exported"
 
 
 def test_version_and_strings():
-    assert ssm.ssm_abi_version() == 7
+    assert ssm.ssm_abi_version() == 8
     for code, name in ssm.STATUS_NAMES.items():
         assert ssm.ssm_status_string(code).startswith(name)
     assert "unknown" in ssm.ssm_status_string(99)
@@ -183,6 +184,31 @@ def test_scan_from_state_rejections():
     bad.states_per_wave, bad.chunk_len = 3, 8
     assert lib.ssm_scan_fwd_from(P, P, P, P, P, None, None, None, 1, None, P + 0x5000000, None, 1, 8, 64, 16,
                                  F32, F32, None, ctypes.byref(bad)) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejections():
+    """The entry point that allocates nothing checks what ssm_scan_fwd_from checks, and
+    rejects a plan whose carry workspace exceeds its fixed scratch, before any HIP call."""
+    lib = ssm.library()
+    G = 0x10000000000  # 1 TiB apart: the fake tensors never overlap
+
+    def run(batch, seqlen, d_inner, chunk, x=P, h0=None, last=None):
+        pl = ssm.ssm_plan()
+        pl.states_per_wave, pl.chunk_len = 4, chunk
+        return lib.ssm_scan_fwd_noalloc(x, P + G, P + 2 * G, P + 3 * G, P + 4 * G, None, None, None, 1, h0,
+                                        P + 5 * G, last, batch, seqlen, d_inner, 16, BF16, F32, None,
+                                        ctypes.byref(pl))
+    # batch 8 x 5120 channels in 16 chunks: 8 * 16 * 5120 * 17 * 4 bytes = 44.6 MB > 32 MiB
+    assert run(8, 2048, 5120, 128) == ssm.SSM_ERR_UNSUPPORTED
+    msg = ssm.ssm_last_error()
+    assert "scratch" in msg and str(32 * 1024 * 1024) in msg
+    assert run(8, 2048, 5120, 512, h0=P + 6 * G, last=P + 6 * G + 16) == ssm.SSM_ERR_UNSUPPORTED  # partial overlap
+    assert "initial_state" in ssm.ssm_last_error()
+    assert run(8, 2048, 5120, 128, x=None) == ssm.SSM_ERR_NULL_ARG
+    assert run(8, 2048, 5120, 128, x=P + 4) == ssm.SSM_ERR_UNSUPPORTED and "aligned" in ssm.ssm_last_error()
+    assert run(0, 2048, 5120, 128) == ssm.SSM_OK          # empty: nothing to do, nothing looked up
+    assert lib.ssm_scan_fwd_noalloc(P, P + G, P + 2 * G, P + 3 * G, P + 4 * G, None, None, None, 4, None,
+                                    P + 5 * G, None, 1, 8, 64, 16, F32, F32, None, None) == ssm.SSM_ERR_UNSUPPORTED
 
 
 def test_conv1d_rejections():
