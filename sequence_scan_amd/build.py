@@ -43,6 +43,10 @@ SOURCES = sorted({u[0] for u in DEVICE_UNITS + HOST_UNITS})
 HEADERS = [os.path.join(CSRC, f) for f in ("internal.h", "device.h", "scan_kernel.h")] + [
     os.path.join(os.path.dirname(HERE), "include", "ssmscan.h")]
 LIB = os.path.join(HERE, "libssmscan.so")
+# The benchmark's VALU issue-rate probe: a separate small library, not part of
+# the scan library's ABI.
+PROBE_SRC = os.path.join(CSRC, "valu_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libssmprobe.so")
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -93,8 +97,11 @@ def build(verbose: bool = False) -> str:
         comp = [f for f in FLAGS if f != "-shared"]
         _run_all([["hipcc", *comp, *defs, "-c", src, "-o", obj] for (src, defs, _), obj in zip(units, objs)], verbose)
         # -z defs: a launcher declared but built in no unit fails here, not at load time
-        _run_all([["hipcc", *FLAGS, "-Wl,-z,defs", *objs, "-o", tmp]], verbose)
+        ptmp = PROBE_LIB + f".tmp{os.getpid()}"
+        _run_all([["hipcc", *FLAGS, "-Wl,-z,defs", *objs, "-o", tmp],
+                  ["hipcc", *FLAGS, "-Wl,-z,defs", PROBE_SRC, "-o", ptmp]], verbose)
     os.replace(tmp, LIB)
+    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 

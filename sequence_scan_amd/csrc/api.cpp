@@ -30,6 +30,16 @@ ssm_status ok() {
   return SSM_OK;
 }
 
+// A failed HIP runtime call also records its error as the calling thread's
+// last error, which the launchers read back after their launches.  Once a
+// call has reported such a failure itself, it clears that record, so the
+// failure is not reported a second time by a later, valid call.
+ssm_status fail_hip(const char* what, long long bytes, hipError_t e) {
+  (void)hipGetLastError();
+  if (bytes >= 0) return fail(SSM_ERR_HIP, "%s(%lld bytes) failed: %s", what, bytes, hipGetErrorString(e));
+  return fail(SSM_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
 struct Range {
   const char* name;
   uintptr_t lo;
@@ -68,9 +78,13 @@ ssm_status check_align(const char* name, const void* p, uintptr_t bytes = 16) {
 int device_simds() {
   int dev = 0;
   int cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 1024;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+  // without a device the planner assumes MI355X's 256 CUs; the failed query's
+  // error record is cleared (see fail_hip)
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
     return 1024;
+  }
   return cus * 4;
 }
 
@@ -314,12 +328,11 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
         return fail(SSM_ERR_UNSUPPORTED, "the plan's carry workspace needs %lld bytes; the fixed scratch holds %lld",
                     (long long)bytes, (long long)ssm::kScratchBytes);
       e = ssm::scratch_address(&base);
-      if (e != hipSuccess)
-        return fail(SSM_ERR_HIP, "looking up the fixed scratch failed: %s", hipGetErrorString(e));
+      if (e != hipSuccess) return fail_hip("looking up the fixed scratch", -1, e);
     } else {
       e = hipMallocAsync(&ws, (size_t)bytes, s);
       if (e != hipSuccess || ws == nullptr)
-        return fail(SSM_ERR_HIP, "hipMallocAsync(%lld bytes) failed: %s", (long long)bytes, hipGetErrorString(e));
+        return fail_hip("hipMallocAsync", (long long)bytes, e);
       base = static_cast<float*>(ws);
     }
     a.ws_state = base;
@@ -580,7 +593,7 @@ static ssm_status bwd_impl(const void* x, const void* delta, const float* A, con
   void* ws = nullptr;
   e = hipMallocAsync(&ws, (size_t)bytes, s);
   if (e != hipSuccess || ws == nullptr)
-    return fail(SSM_ERR_HIP, "hipMallocAsync(%lld bytes) failed: %s", (long long)bytes, hipGetErrorString(e));
+    return fail_hip("hipMallocAsync", (long long)bytes, e);
   ssm::BwdArgs a{};
   a.x = x;
   a.delta = delta;
@@ -853,7 +866,7 @@ static ssm_status ssd_impl(const void* x, const void* dt, const float* A, const 
       return fail(SSM_ERR_BAD_SHAPE, "workspace size overflows int64");
     e = hipMallocAsync(&ws, (size_t)bytes, s);
     if (e != hipSuccess || ws == nullptr)
-      return fail(SSM_ERR_HIP, "hipMallocAsync(%lld bytes) failed: %s", (long long)bytes, hipGetErrorString(e));
+      return fail_hip("hipMallocAsync", (long long)bytes, e);
     a.ws_state = static_cast<float*>(ws);
     a.ws_decay = a.ws_state + n_state;
     if (n_h0 > 0) {

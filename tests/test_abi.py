@@ -211,6 +211,21 @@ def test_noalloc_rejections():
                                     P + 5 * G, None, 1, 8, 64, 16, F32, F32, None, None) == ssm.SSM_ERR_UNSUPPORTED
 
 
+def test_failed_workspace_allocation_is_reported():
+    """Without a usable device a chunked plan's hipMallocAsync fails: the call returns
+    SSM_ERR_HIP naming the allocation.  (That a later valid call is not handed the same
+    error again is checked on the GPU, where the failure is forced by size.)"""
+    lib = ssm.library()
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("needs a host without a GPU (the GPU suite forces the failure by size)")
+    pl = ssm.ssm_plan()
+    pl.states_per_wave, pl.chunk_len = 4, 4
+    st = lib.ssm_scan_fwd_plan(P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, None, None, None, 1,
+                               P + 0x5000000, None, 2, 8, 64, 16, F32, F32, None, ctypes.byref(pl))
+    assert st == ssm.SSM_ERR_HIP and "hipMallocAsync" in ssm.ssm_last_error()
+
+
 def test_conv1d_rejections():
     lib = ssm.library()
 

@@ -113,3 +113,31 @@ def test_decode_conv_and_ssd_rejections_write_nothing():
     assert lib.ssm_ssd_fwd(_p(xs), _p(dts), _p(As), _p(Bs), _p(Bs), None, None, None, 1, None, _p(sout), _p(slast),
                            b, L, H, P, 1, N2, F32, F32, None) != ssm.SSM_OK
     _untouched(sout, slast)
+
+
+def test_workspace_allocation_failure_writes_nothing():
+    """A chunked plan whose carry workspace (65535 rows x 2 chunks x 65536 channels x
+    68 bytes, about 584 GB) exceeds the device's memory: hipMallocAsync fails, the call
+    returns SSM_ERR_HIP before enqueuing anything, and the next valid call succeeds (the
+    failure is not reported a second time).  The tensors are never touched on this path,
+    so only `out` is a real buffer (a sentinel far smaller than its nominal size); the
+    inputs are distinct addresses 1 TiB apart."""
+    lib = ssm.library()
+    out = torch.full((4096,), SENTINEL, device="cuda")
+    base, G = out.data_ptr(), 1 << 40
+    batch, L, Dn = 65535, 2, 65536
+    plan = ssm.ssm_plan()
+    plan.states_per_wave, plan.chunk_len = 4, 1
+    say("scan whose carry workspace cannot be allocated")
+    st = lib.ssm_scan_fwd_plan(base + G, base + 2 * G, base + 3 * G, base + 4 * G, base + 5 * G, None, None, None, 1,
+                               base, None, batch, L, Dn, 16, BF16, F32, None, ctypes.byref(plan))
+    assert st == ssm.SSM_ERR_HIP, (st, ssm.ssm_last_error())
+    assert "hipMallocAsync" in ssm.ssm_last_error()
+    _untouched(out)
+    say("a valid chunked scan right after the failed one")
+    x = torch.randn(1, 64, 64, device="cuda")
+    B, C = torch.randn(1, 64, 16, device="cuda"), torch.randn(1, 64, 16, device="cuda")
+    A = -torch.rand(64, 16, device="cuda") - 0.5
+    y = ssm.ssm_scan_fwd(x, torch.randn(1, 64, 64, device="cuda"), A, B, C, plan={"states_per_wave": 4, "chunk_len": 8})
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(y))
