@@ -34,6 +34,19 @@ namespace {
 // ZOH selects the exact zero-order-hold input coefficient: per state the
 // update adds zoh_ratio(a) * (dt2 x) * B with a = exp2(dt2 A), which is
 // (e^{dt A} - 1) / A * x * B (B is then staged without the ln 2 factor).
+//
+// Transitions from powers (NS == 4, dt coefficient).  Where every channel of
+// the block has A[d, n] = (n + 1) * A[d, 0] -- the standard initialisation
+// A = -exp(log(n + 1)) -- the transitions of one step are powers of one
+// number: exp(dt A[d, n]) = e^(n + 1) with e = exp2(dt2 A[d, 0]).  Phase 1
+// then stages e in place of dt2 (one exponential per (step, channel)), and
+// the recurrence forms e^(n + 1) by multiplication: its instruction stream
+// holds no transcendental, so gfx950 issues its fp32 VALU work at about twice
+// the rate it manages beside v_exp_f32 (about 2.2 against 4 SIMD-cycles per
+// wave64 instruction, measured).  A workgroup checks this structure of A
+// exactly, once, and otherwise runs the exponentials.  With NS == 4, wave g
+// carries the states n = g + 4 i (i < 4), so its transitions are
+// e^(g+1) * (e^4)^i; B and C rows are staged in that order.
 template <typename Tin, typename Tout, int NS, bool PASS_A, bool HAS_Z, bool WIDE, bool ZOH>
 __global__ void __launch_bounds__(kWave * (kDState / NS))
 scan_chunk_kernel(ScanArgs a) {
@@ -49,6 +62,9 @@ scan_chunk_kernel(ScanArgs a) {
   constexpr int BC_VECS = (PASS_A ? 1 : 2) * T * VPR;
   constexpr int BC_R = (BC_VECS + NTHR - 1) / NTHR;
   constexpr bool kZ = HAS_Z && !PASS_A;
+  // states of wave g: g + 4 i (interleaved) with NS == 4, else g * NS + i
+  constexpr bool kPerm = NS == 4;
+  constexpr bool kPow = kPerm && !ZOH;
   using R = Raw<Tin, CW>;
 
   // Rows are padded by one element: the prologue/epilogue items (CW
@@ -58,6 +74,7 @@ scan_chunk_kernel(ScanArgs a) {
   __shared__ float sh_B[T][kDState];
   __shared__ float sh_C[PASS_A ? 1 : T][kDState];
   __shared__ float sh_y[PASS_A ? 1 : T][G * kWave + 1];  // partial readouts, [row][wave][channel]
+  __shared__ float sh_dt2[PASS_A && kPow ? T : 1][kWave + 1];  // pass A with powers: dt2 for the step-size sum
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -78,13 +95,37 @@ scan_chunk_kernel(ScanArgs a) {
   const bool softplus = a.softplus != 0;
   const bool has_D = a.D != nullptr;
 
+  // the state held in slot i of this wave
+  auto st_of = [&](int i) SSM_INLINE { return kPerm ? g + 4 * i : g * NS + i; };
   float Ad[NS];  // this lane's A[d, n]; step sizes are in log2 units (dt2)
 #pragma unroll
-  for (int i = 0; i < NS; ++i) Ad[i] = a.A[dl * kDState + g * NS + i];
+  for (int i = 0; i < NS; ++i) Ad[i] = a.A[dl * kDState + st_of(i)];
+  // Transitions from powers when every channel's A row is (n + 1) * A[d, 0]
+  // (the check is exact; every wave covers the same channels, so all waves of
+  // the workgroup reach the same answer).
+  bool pow_mode = false;
+  float pf1 = 0.0f, pn1 = 1.0f, pf2 = 0.0f, pn2 = 1.0f;  // selects e^(g+1) = e * e^(g&1) * (e^2)^(g>>1)
+  if constexpr (kPow) {
+    const float* Ar = a.A + dl * kDState;
+    bool ok = true;
+#pragma unroll
+    for (int n = 1; n < kDState; ++n) ok = ok && (Ar[n] == (float)(n + 1) * Ar[0]);
+    pow_mode = __all(ok);
+    // per-wave constants, kept in VGPRs (computed from the thread index): an SGPR
+    // operand would slow the VALU instructions that read it
+    const int gv = (int)(threadIdx.x >> 6);
+    pf1 = (float)(gv & 1);
+    pn1 = 1.0f - pf1;
+    pf2 = (float)((gv >> 1) & 1);
+    pn2 = 1.0f - pf2;
+  }
 
-  // phases 1 and 3: this thread's items (row, first channel), fixed for the kernel
+  // phases 1 and 3: this thread's items (row, first channel), fixed for the kernel.
+  // (Their per-channel parameters stay in registers: LDS tables for them would
+  // take the workgroup past the LDS share that lets three share a CU.)
   int irow[IPT], icol[IPT];
   float ibias[IPT][CW], iD[IPT][CW];  // bias in log2 units, D
+  float iA0[kPow ? IPT : 1][kPow ? CW : 1];  // A[d, 0] of the items (transitions from powers)
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
     const int idx = tid + it * NTHR;
@@ -95,18 +136,19 @@ scan_chunk_kernel(ScanArgs a) {
       const int64_t dq = d0 + min(icol[it] + q, nvalid - 1);
       ibias[it][q] = a.bias != nullptr ? a.bias[dq] * kLog2e : 0.0f;
       iD[it][q] = has_D ? a.D[dq] : 0.0f;
+      if constexpr (kPow) iA0[it][q] = a.A[dq * kDState];
     }
   }
 
   float h[NS];
   if (!PASS_A && k > 0) {
-    const float* src = a.ws_state + (((int64_t)b * K + (k - 1)) * Dn + dl) * kDState + g * NS;
+    const float* src = a.ws_state + (((int64_t)b * K + (k - 1)) * Dn + dl) * kDState;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) h[i] = src[i];
+    for (int i = 0; i < NS; ++i) h[i] = src[st_of(i)];
   } else if (k == 0 && a.h0 != nullptr) {  // continuing from a stored state
-    const float* src = a.h0 + ((int64_t)b * Dn + dl) * kDState + g * NS;
+    const float* src = a.h0 + ((int64_t)b * Dn + dl) * kDState;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) h[i] = src[i];
+    for (int i = 0; i < NS; ++i) h[i] = src[st_of(i)];
   } else {
 #pragma unroll
     for (int i = 0; i < NS; ++i) h[i] = 0.0f;
@@ -157,7 +199,8 @@ scan_chunk_kernel(ScanArgs a) {
   // dt2 * x carries is folded into the staged B rows); stage B/C rows as
   // fp32.  The softplus switch is taken once per tile (a uniform branch
   // around the whole item loop), never per element.
-  auto discretise = [&](Bank& bk, auto sp_c) SSM_INLINE {
+  // With transitions from powers, (e, dt2 * x) is staged, e = exp2(dt2 A[d, 0]).
+  auto discretise = [&](Bank& bk, auto sp_c, auto pow_c) SSM_INLINE {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
 #pragma unroll
@@ -165,14 +208,29 @@ scan_chunk_kernel(ScanArgs a) {
         const float x = bk.rx[it].get(q);
         const float u2 = __builtin_fmaf(bk.rdt[it].get(q), kLog2e, ibias[it][q]);
         const float dt2 = decltype(sp_c)::value ? softplus2_f(u2) : u2;
-        sh_dtv[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * x);
+        if constexpr (decltype(pow_c)::value) {
+          sh_dtv[irow[it]][icol[it] + q] = make_float2(__builtin_amdgcn_exp2f(dt2 * iA0[it][q]), dt2 * x);
+          if constexpr (PASS_A) sh_dt2[irow[it]][icol[it] + q] = dt2;
+        } else {
+          sh_dtv[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * x);
+        }
         xs[it][q] = x;
       }
     }
   };
   auto commit = [&](Bank& bk) SSM_INLINE {
-    if (softplus) discretise(bk, std::true_type());
-    else discretise(bk, std::false_type());
+    if constexpr (kPow) {
+      if (pow_mode) {
+        if (softplus) discretise(bk, std::true_type(), std::true_type());
+        else discretise(bk, std::false_type(), std::true_type());
+      } else {
+        if (softplus) discretise(bk, std::true_type(), std::false_type());
+        else discretise(bk, std::false_type(), std::false_type());
+      }
+    } else {
+      if (softplus) discretise(bk, std::true_type(), std::false_type());
+      else discretise(bk, std::false_type(), std::false_type());
+    }
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       if (kZ) zs[it] = bk.rz[it];
@@ -186,11 +244,16 @@ scan_chunk_kernel(ScanArgs a) {
       const int part = w % VPR;
       float f[EPV];
       Vec16<Tin>::unpack(bk.rbc[r], f);
-      float* dst = which ? &sh_C[PASS_A ? 0 : row][part * EPV] : &sh_B[row][part * EPV];
+      float* dst = which ? &sh_C[PASS_A ? 0 : row][0] : &sh_B[row][0];
       // B carries the ln 2 of dt2 * x; with ZOH, zoh_ratio carries it
       const float scale = (which || ZOH) ? 1.0f : kLn2;
 #pragma unroll
-      for (int i = 0; i < EPV; ++i) dst[i] = f[i] * scale;
+      for (int i = 0; i < EPV; ++i) {
+        // state n goes to the slot that the wave holding it reads: slot g * NS + i
+        // holds state g + 4 i when the states are interleaved
+        const int n = part * EPV + i;
+        dst[kPerm ? (n & 3) * 4 + (n >> 2) : n] = f[i] * scale;
+      }
     }
   };
 
@@ -200,7 +263,88 @@ scan_chunk_kernel(ScanArgs a) {
   // computed while step s updates it, which keeps each exp's latency off the
   // h dependency chain.
   constexpr int NR = ZOH ? NS : 1;
+  // The recurrence with transitions from powers: slot i holds state g + 4 i,
+  // whose transition is e^(g+1) * (e^4)^i; e^(g+1) = e * e^(g&1) * (e^2)^(g>>1)
+  // is selected by per-wave 0/1 constants (fma(f, v, 1 - f) is v or exactly 1).
+  // No transcendental: eight multiplies, two selects and the update's three
+  // instructions per state.
+  auto run_steps_pow_plain = [&](int n) SSM_INLINE {  // the peeled ragged tile
+    for (int s = 0; s < n; ++s) {
+      const float2 v = sh_dtv[s][loff];
+      const float e = v.x;
+      const float e2 = e * e;
+      const float e4 = e2 * e2;
+      float ap = (e * __builtin_fmaf(pf1, e, pn1)) * __builtin_fmaf(pf2, e2, pn2);
+      float y = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if (i > 0) ap = ap * e4;
+        h[i] = __builtin_fmaf(ap, h[i], v.y * sh_B[s][g * NS + i]);
+        if (!PASS_A) y = __builtin_fmaf(sh_C[PASS_A ? 0 : s][g * NS + i], h[i], y);
+      }
+      if (PASS_A) {
+        dtsum += sh_dt2[PASS_A ? s : 0][loff];
+      } else {
+        sh_y[PASS_A ? 0 : s][(PASS_A ? 0 : g) * kWave + lane] = y;
+      }
+    }
+  };
+  auto run_steps_pow_piped = [&](auto n_c) SSM_INLINE {  // full tiles (n is a constant)
+    constexpr int n = decltype(n_c)::value;
+    // Software-pipelined by two steps: a step's LDS operands -- (e, dt2 x) of the
+    // lane's channel and the wave's four B and C values -- are read two steps
+    // before they are used.  Without the exponentials a step is only about
+    // twenty VALU instructions, too short to cover an LDS read's latency.
+    constexpr int PD = 2;
+    float2 rv[PD + 1];
+    float4 rb[PD + 1], rc[PD + 1];
+    auto fetch = [&](int s, int slot) SSM_INLINE {
+      rv[slot] = sh_dtv[s][loff];
+      rb[slot] = *reinterpret_cast<const float4*>(&sh_B[s][g * NS]);
+      if (!PASS_A) rc[slot] = *reinterpret_cast<const float4*>(&sh_C[PASS_A ? 0 : s][g * NS]);
+    };
+#pragma unroll
+    for (int p = 0; p < PD; ++p)
+      if (p < n) fetch(p, p);
+#pragma unroll
+    for (int s = 0; s < n; ++s) {
+      if (s + PD < n) fetch(s + PD, (s + PD) % (PD + 1));
+      const int cur = s % (PD + 1);
+      const float2 v = rv[cur];
+      const float bv[4] = {rb[cur].x, rb[cur].y, rb[cur].z, rb[cur].w};
+      const float cv[4] = {rc[cur].x, rc[cur].y, rc[cur].z, rc[cur].w};
+      const float e = v.x;
+      const float e2 = e * e;
+      const float e4 = e2 * e2;
+      float ap = (e * __builtin_fmaf(pf1, e, pn1)) * __builtin_fmaf(pf2, e2, pn2);
+      float y = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if (i > 0) ap = ap * e4;
+        h[i] = __builtin_fmaf(ap, h[i], v.y * bv[i]);
+        if (!PASS_A) y = __builtin_fmaf(cv[i], h[i], y);
+      }
+      if (PASS_A) {
+        dtsum += sh_dt2[PASS_A ? s : 0][loff];
+      } else {
+        sh_y[PASS_A ? 0 : s][(PASS_A ? 0 : g) * kWave + lane] = y;
+      }
+      // keep the prefetch distance: the scheduler would otherwise sink the
+      // reads of step s + PD next to their use
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto run_steps_pow = [&](auto n_c) SSM_INLINE {
+    if constexpr (std::is_same_v<decltype(n_c), int>) run_steps_pow_plain(n_c);
+    else run_steps_pow_piped(n_c);
+  };
   auto run_steps = [&](auto n_c) SSM_INLINE {
+    if constexpr (kPow) {
+      if (pow_mode) {
+        run_steps_pow(n_c);
+        return;
+      }
+    }
     const int n = n_c;
     float2 v = sh_dtv[0][loff];
     float ar[NS], rr[NR];
@@ -331,14 +475,14 @@ scan_chunk_kernel(ScanArgs a) {
   }
 
   if (PASS_A) {
-    float* dst = a.ws_state + (((int64_t)b * K + k) * Dn + dl) * kDState + g * NS;
+    float* dst = a.ws_state + (((int64_t)b * K + k) * Dn + dl) * kDState;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) dst[i] = h[i];
+    for (int i = 0; i < NS; ++i) dst[st_of(i)] = h[i];
     if (g == 0) a.ws_dtsum[((int64_t)b * K + k) * Dn + dl] = dtsum;
   } else if (k == K - 1 && a.last_state != nullptr) {
-    float* dst = a.last_state + ((int64_t)b * Dn + dl) * kDState + g * NS;
+    float* dst = a.last_state + ((int64_t)b * Dn + dl) * kDState;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) dst[i] = h[i];
+    for (int i = 0; i < NS; ++i) dst[st_of(i)] = h[i];
   }
 }
 
