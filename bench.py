@@ -53,6 +53,9 @@ FLOPS_PER_STATE_UPDATE = 7       # mul (dt*A), exp, mul (dt*x*B), FMA (update, 2
 # per-instruction costs of the ISA's issue model) is used only when no record
 # exists.
 MODEL_CYCLES_PER_WAVE_UPDATE = 24.0
+# transitions as powers of one exponential: 21 VALU instructions per 4 updates
+# at ~2.2 cycles each, no transcendental
+MODEL_POWERS_CYCLES_PER_WAVE_UPDATE = 21 / 4 * 2.2
 
 
 def log(msg):
@@ -89,13 +92,17 @@ def measured_traffic(key):
     return None if rec is None else rec["hbm_bytes"]
 
 
-def mix_ceiling():
+def mix_ceiling(powers=False):
     """(cycles per wavefront state update, where it comes from) for the scan's
-    instruction mix: the VALU probe's record in profiles/, else the issue model."""
+    instruction mix: the VALU probe's record in profiles/, else the issue model.
+    `powers`: the mix of the transitions formed as powers of one exponential,
+    which the kernel runs where A[d, n] = (n + 1) A[d, 0] (every stated workload)."""
     rec = read_record("valu-record")
-    if rec is not None:
-        return float(rec["scan_mix_cycles_per_wave_update"]), "measured (profiles/ valu-record)"
-    return MODEL_CYCLES_PER_WAVE_UPDATE, "issue model (no valu-record in profiles/)"
+    key = "scan_powers_cycles_per_wave_update" if powers else "scan_mix_cycles_per_wave_update"
+    if rec is not None and key in rec:
+        return float(rec[key]), f"measured (profiles/ valu-record, {key})"
+    return (MODEL_POWERS_CYCLES_PER_WAVE_UPDATE if powers else MODEL_CYCLES_PER_WAVE_UPDATE,
+            "issue model (no valu-record in profiles/)")
 
 
 def alu_floor_us(updates, cycles):
@@ -587,10 +594,11 @@ def valu_probe_case(total_iters=16384):
     lib.ssm_probe_ops_per_iter.argtypes = [ctypes.c_int]
     lib.ssm_probe_ops_per_iter.restype = ctypes.c_int
     names = {0: "v_mul_f32", 1: "v_fma_f32", 2: "v_exp_f32", 4: "v_log_f32", 5: "v_rcp_f32", 3: "scan_update",
-             6: "scan_update_without_exp", 7: "v_mul_f32_sgpr_operand", 8: "exp_waves_beside_fma_waves"}
+             6: "scan_update_without_exp", 7: "v_mul_f32_sgpr_operand", 8: "exp_waves_beside_fma_waves",
+             9: "scan_update_powers"}
     stream = torch.cuda.current_stream().cuda_stream
     res = {}
-    for kind in (0, 1, 2, 4, 5, 3, 6, 7, 8):
+    for kind in (0, 1, 2, 4, 5, 3, 6, 7, 8, 9):
         per = {}
         for wps in (1, 2, 3, 4, 8):
             blocks = 256 * wps            # workgroups of 4 wavefronts (one per SIMD)
@@ -611,12 +619,22 @@ def valu_probe_case(total_iters=16384):
                              "ms": round(ms, 4)}
         res[names[kind]] = per
     best = min(v["cycles"] for k, v in res["scan_update"].items() if int(k) >= 2)
-    return {"unit": "SIMD-cycles per wave64 instruction (scan_update: per state update)",
+    best_pow = min(v["cycles"] for k, v in res["scan_update_powers"].items() if int(k) >= 2)
+    return {"unit": "SIMD-cycles per wave64 instruction (scan_update*: per state update)",
             "method": "launch duration x measured shader clock / instructions issued per SIMD",
-            "rates": res, "scan_mix_cycles_per_wave_update": best}
+            "rates": res, "scan_mix_cycles_per_wave_update": best,
+            "scan_powers_cycles_per_wave_update": best_pow}
 
 
-def gpu_scan_inputs(cfg, seed=7):
+def a_is_powers(A) -> bool:
+    """Whether every row of A is (n + 1) * A[d, 0] exactly: the kernel then forms the
+    transitions as powers of one exponential (the same check it makes per block)."""
+    import numpy as np
+    A = np.asarray(A, dtype=np.float32)
+    return bool(np.all(A == np.arange(1, A.shape[1] + 1, dtype=np.float32)[None, :] * A[:, :1]))
+
+
+def gpu_scan_inputs(cfg, seed=7, general_a=False):
     """Inputs of the same shape and distributions as workloads.scan_inputs, drawn on
     the GPU with torch's seeded generator (for timing only; parity tests use the
     workloads generator).  Step sizes: Delta* log-uniform in [dmin, dmax] per element
@@ -656,30 +674,37 @@ def gpu_scan_inputs(cfg, seed=7):
             xflat[r:r + n] = (W[tok] + 0.1 * torch.randn((n, cfg.d_inner), generator=gen, device="cuda")).to(tdt)
     else:
         x = normal(shape)
-    A = (-torch.arange(1, cfg.d_state + 1, dtype=torch.float32, device="cuda")).repeat(cfg.d_inner, 1).contiguous()
+    if general_a:   # a general A < 0 per (channel, state), as a trained layer holds
+        A = -torch.exp(torch.rand((cfg.d_inner, cfg.d_state), generator=gen, device="cuda") * 4.0 - 1.0)
+    else:
+        A = (-torch.arange(1, cfg.d_state + 1, dtype=torch.float32, device="cuda")).repeat(cfg.d_inner, 1).contiguous()
     return {"x": x, "delta": delta, "z": normal(shape), "B": normal((cfg.batch, cfg.seqlen, cfg.d_state)),
             "C": normal((cfg.batch, cfg.seqlen, cfg.d_state)), "A": A,
             "D": torch.ones(cfg.d_inner, device="cuda"), "delta_bias": bias}
 
 
-def scan_leg(name, out_dtype, cyc, reps=20, gpu_inputs=False):
+def scan_leg(name, out_dtype, reps=20, gpu_inputs=False, general_a=False):
     """ssm_scan_fwd on workload `name` (default plan; softplus, D and z on), timed as
     back-to-back calls at the sustained clock, against the HBM roofline and the
-    instruction-mix ceiling.  The tiny workload is launch-bound: its calls are also
-    captured in a HIP graph and replayed, which gives the GPU's own time per call."""
+    instruction-mix ceiling of the path the kernel takes.  `general_a` replaces the
+    workload's A = -(n + 1) by a general A (the exponential path).  The tiny workload
+    is launch-bound: its calls are also captured in a HIP graph and replayed, which
+    gives the GPU's own time per call."""
     import torch
 
     import sequence_scan_amd as ssm
     import workloads
     cfg = workloads.SCAN_CONFIGS[name]
-    if gpu_inputs:
-        dev = gpu_scan_inputs(cfg)
+    if gpu_inputs or general_a:
+        dev = gpu_scan_inputs(cfg, general_a=general_a)
     else:
         inp = workloads.scan_inputs(cfg, seed=0)
         tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         dev = {k: (torch.from_numpy(v).to(tdt) if k in ("x", "delta", "z", "B", "C") else torch.from_numpy(v)).cuda()
                for k, v in inp.items() if k != "dtype"}
         del inp
+    powers = a_is_powers(dev["A"].cpu().numpy())
+    cyc, cyc_src = mix_ceiling(powers)
     odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
     out = torch.empty((cfg.batch, cfg.seqlen, cfg.d_inner), dtype=odt, device="cuda")
     last = torch.empty((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32, device="cuda")
@@ -690,8 +715,12 @@ def scan_leg(name, out_dtype, cyc, reps=20, gpu_inputs=False):
     nbytes = workloads.scan_algorithmic_bytes(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dtype, out_dtype)
     updates = cfg.batch * cfg.seqlen * cfg.d_inner * cfg.d_state
     res = {"workload": f"{name}: {cfg.description}; batch {cfg.batch}, seqlen {cfg.seqlen}, d_inner {cfg.d_inner}, "
-                       f"{cfg.dtype} in, {out_dtype} out, softplus, D, z",
-           "inputs": "drawn on the GPU (same distributions)" if gpu_inputs else "workloads generator, seed 0",
+                       f"{cfg.dtype} in, {out_dtype} out, softplus, D, z" + (", general A" if general_a else ""),
+           "inputs": ("drawn on the GPU (same distributions" + (", A = -exp(U(-1, 3)) per (d, n))" if general_a
+                                                                 else ")")) if (gpu_inputs or general_a)
+                     else "workloads generator, seed 0",
+           "transitions": "powers of one exponential" if powers else "one exponential per state",
+           "alu_cycles_per_wave_update": cyc, "alu_cycles_source": cyc_src,
            "plan": ssm.ssm_scan_plan(cfg.batch, cfg.seqlen, cfg.d_inner), "bytes_per_call": nbytes}
     if name == "tiny_fp32":
         eager = ms
@@ -773,8 +802,9 @@ def main():
                           "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "decode": d}), flush=True)
         return
 
-    cyc, cyc_src = mix_ceiling()
     cfg, inp, run, nbytes, plan = scan_case(args.workload, args.out_dtype, args.plan)
+    powers = a_is_powers(inp["A"])
+    cyc, cyc_src = mix_ceiling(powers)
     plan_used = plan or ssm.ssm_scan_plan(cfg.batch, cfg.seqlen, cfg.d_inner)
     log(f"plan {plan_used}; algorithmic bytes {nbytes}")
     # The shader clock needs tens of milliseconds of sustained load to reach its
@@ -818,11 +848,13 @@ def main():
         "frac_of_measured_copy": (round(k_gbs / copy_rec["GBps"], 4) if copy_rec else None),
         "cold_cache_us": {k: round(v * 1e3, 2) for k, v in cw.items()},
         "cold_cache_timing": "single synchronised calls, cold (after a 1 GiB read) and warm interleaved",
-        # The ceiling that binds this kernel is the VALU issue rate for its
-        # instruction mix (one v_exp_f32 and four fp32 VALU instructions per
-        # state update), not HBM: its traffic is ~1.02x the algorithmic bytes.
+        # The ceiling beside HBM is the VALU issue rate of the state update's
+        # instruction mix: with the workload's A = -(n + 1) the kernel forms the
+        # transitions as powers of one exponential (21 VALU instructions per 4
+        # updates), with a general A one v_exp_f32 and four VALU per update.  The
+        # kernel's traffic is ~1.02x the algorithmic bytes.
         "alu": {
-            "binding": True,
+            "transitions": "powers of one exponential" if powers else "one exponential per state",
             "cycles_per_wave_update": cyc,
             "cycles_source": cyc_src,
             "floor_us": round(floor_us, 2),
@@ -831,6 +863,7 @@ def main():
             "mix_peak_tflops": round(mix_peak, 2),
             "flops_per_state_update": FLOPS_PER_STATE_UPDATE,
             "peak_basis": f"1024 SIMDs x 2.4 GHz x 64 lanes / {cyc} cycles per wavefront state update",
+            "cycles_per_wave_update_with_exponentials": mix_ceiling(False)[0],
             "fp32_peak_tflops": FP32_PEAK_TFLOPS,
             "fp32_peak_frac": round(tflops / FP32_PEAK_TFLOPS, 4),
             "fp32_unpacked_fma_peak_tflops": round(FMA_PEAK_TFLOPS, 2),
@@ -871,10 +904,11 @@ def main():
     if full and not args.no_legs:
         log("legs: the other scan workloads, VALU probe")
         line["legs"] = {
-            "mamba2p8b_bf16_out": scan_leg("mamba2p8b", "bf16", cyc),
-            "mamba130m": scan_leg("mamba130m", "f32", cyc),
-            "tiny_fp32": scan_leg("tiny_fp32", "f32", cyc),
-            "long_dna": scan_leg("long_dna", "f32", cyc, reps=5, gpu_inputs=True),
+            "mamba2p8b_bf16_out": scan_leg("mamba2p8b", "bf16"),
+            "mamba2p8b_general_A": scan_leg("mamba2p8b", "f32", general_a=True),
+            "mamba130m": scan_leg("mamba130m", "f32"),
+            "tiny_fp32": scan_leg("tiny_fp32", "f32"),
+            "long_dna": scan_leg("long_dna", "f32", reps=5, gpu_inputs=True),
         }
         line["valu_probe"] = valu_probe_case()
     if not args.no_decode and full:

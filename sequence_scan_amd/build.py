@@ -56,15 +56,42 @@ FLAGS = [
 ]
 
 
+def _code_tokens(text: str) -> bytes:
+    """The source with its comments removed and each run of whitespace made one
+    space: an edit of a comment leaves the code, and so its hash, unchanged.
+    String and character literals are kept whole."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split()).encode()
+
+
 def kernel_source_sha256() -> str:
-    """One hash over every device source and header (in a fixed order): the
-    identity of the kernels that a profile was taken of."""
+    """One hash over the code of every device source and header (in a fixed
+    order, comments and layout left out): the identity of the kernels that a
+    profile was taken of."""
     import hashlib
     h = hashlib.sha256()
     for path in sorted({u[0] for u in DEVICE_UNITS} | set(HEADERS)):
         h.update(os.path.basename(path).encode() + b"\0")
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, "r", encoding="utf-8") as f:
+            h.update(_code_tokens(f.read()))
     return h.hexdigest()
 
 

@@ -96,8 +96,11 @@ int device_simds() {
 // reduction pass costs less than idle SIMDs.  With more blocks than that but
 // fewer than one per CU, some CUs would idle: the sequence is cut so that the
 // grid holds about three workgroups per CU (the kernel's occupancy), with
-// chunks of at least 512 steps.  (The Mamba-130M-like layer, 192 blocks: 4
-// chunks, 203 us against 218 us in one chunk; 2, 3 or 5 chunks were slower.)
+// chunks of at least 512 steps.  Chunk lengths are rounded up to the 32-step
+// tile.  (The Mamba-130M-like layer, 192 blocks: 4 chunks of 512 steps, 179 us
+// against 196 us in one chunk and 189-230 us for chunks of 192 to 1024 steps;
+// the long single row: 96 chunks of 2752 steps, 3.26 ms, with chunks of 1024
+// to 8192 steps within 3 %.)
 void choose_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_plan* p) {
   const int64_t blocks = batch * ((d_inner + 63) / 64);
   const int64_t waves = std::max<int64_t>(1, blocks * 4);
@@ -111,6 +114,9 @@ void choose_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_
     chunks = std::min(chunks, std::max<int64_t>(1, seqlen / 512));
   }
   int64_t chunk_len = seqlen > 0 ? (seqlen + chunks - 1) / chunks : 1;
+  // a cut sequence is cut at multiples of the kernel's 32-step tile, so that
+  // only the last chunk can have a ragged tile
+  if (chunks > 1) chunk_len = (chunk_len + 31) / 32 * 32;
   if (chunk_len < 1) chunk_len = 1;
   p->states_per_wave = 4;
   p->reserved0 = 0;

@@ -137,8 +137,8 @@ __global__ void __launch_bounds__(64) affine_exclusive_scan_kernel(const float* 
 // D skip and the gate and stores out.  The state and the per-step x, delta,
 // z and out stream (non-temporal loads and stores): one step touches them
 // once, and the 128 MiB state of a batch-256 step does not survive in the
-// caches until the next step anyway.  Streaming the state too took that step
-// from 62.7 to 53.3 us on MI355X (4.6 -> 5.4 TB/s).  A, B, C, D and the bias,
+// caches until the next step anyway.  Streaming the state too takes that step
+// from 63.9 to 57.7 us on MI355X (4.5 -> 5.0 TB/s).  A, B, C, D and the bias,
 // which many rows share, are ordinary cached loads.
 template <typename Tin>
 __device__ __forceinline__ float nt_load(const void* p, int64_t i) {

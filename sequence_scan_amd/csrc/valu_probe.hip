@@ -21,6 +21,10 @@
 //   6  the state update of kind 3 without the exponential (a = w * A_n):
 //      four VALU instructions per update, no transcendental in the stream
 //   7  v_mul_f32 with a wave-uniform operand read from an SGPR, 8 chains
+//   9  the scan's state update with transitions as powers of one number e
+//      (per step and 4 states: e^2, e^4, two selects, the base, three chain
+//      multiplies, then per state u * B, fma(a, h, .), fma(C, h, y)): 21 fp32
+//      VALU instructions per 4 updates, no transcendental
 //   8  even wavefronts run v_exp_f32 only (2 chains), odd wavefronts
 //      v_fma_f32 only (8 chains): the count is of instructions issued per
 //      pair of wavefronts, 2 exps + 8 FMAs per step
@@ -83,7 +87,18 @@ __global__ void __launch_bounds__(256) probe_kernel(int iters, float seed, float
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      if constexpr (KIND == 3 || KIND == 6) {
+      if constexpr (KIND == 9) {
+        PROBE_OPAQUE(w);
+        PROBE_OPAQUE(u);
+        const float e = w, e2 = e * e, e4 = e2 * e2;
+        float ap = (e * __builtin_fmaf(q[0], e, q[1])) * __builtin_fmaf(q[2], e2, q[3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i > 0) ap = ap * e4;
+          r[i] = __builtin_fmaf(ap, r[i], u * Bv[i]);
+          ys[s] = __builtin_fmaf(Cv[i], r[i], ys[s]);
+        }
+      } else if constexpr (KIND == 3 || KIND == 6) {
         PROBE_OPAQUE(w);
         PROBE_OPAQUE(u);
 #pragma unroll
@@ -123,10 +138,10 @@ __global__ void __launch_bounds__(256) probe_kernel(int iters, float seed, float
 
 extern "C" {
 
-// Instructions of the measured kind per wavefront and iteration (kinds 3 and
-// 6 count state updates: five and four instructions each; kind 8 counts the
-// average over its two kinds of wavefront).
-int ssm_probe_ops_per_iter(int kind) { return (kind == 3 || kind == 6) ? 32 : (kind == 8 ? 40 : 64); }
+// Instructions of the measured kind per wavefront and iteration (kinds 3, 6
+// and 9 count state updates: five, four and 5.25 instructions each; kind 8
+// counts the average over its two kinds of wavefront).
+int ssm_probe_ops_per_iter(int kind) { return (kind == 3 || kind == 6 || kind == 9) ? 32 : (kind == 8 ? 40 : 64); }
 
 // Launch `blocks` workgroups of 256 threads (4 wavefronts) running `iters`
 // iterations of kind `kind`.  sink: blocks * 256 floats; stamps: blocks * 4 * 4
@@ -147,6 +162,7 @@ int ssm_probe_launch(int kind, int blocks, int iters, float seed, float* sink, i
     case 6: hipLaunchKernelGGL(probe_kernel<6>, grid, block, 0, s, iters, seed, u, sink, stamps); break;
     case 7: hipLaunchKernelGGL(probe_kernel<7>, grid, block, 0, s, iters, seed, u, sink, stamps); break;
     case 8: hipLaunchKernelGGL(probe_kernel<8>, grid, block, 0, s, iters, seed, u, sink, stamps); break;
+    case 9: hipLaunchKernelGGL(probe_kernel<9>, grid, block, 0, s, iters, seed, u, sink, stamps); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

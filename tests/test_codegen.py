@@ -62,3 +62,14 @@ def test_no_outlined_calls(asm):
     # through the calling convention's stack
     for name, body in kernels(asm):
         assert "s_swappc" not in body and "s_setpc" not in body, f"{name} makes a call"
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The profile records are keyed to the kernels' code: a comment or layout
+    edit keeps the hash, any change of code or of a string literal moves it."""
+    tok = lib_build._code_tokens
+    base = 'float f(float x) { return x * 2.0f; }  // twice\nconst char* s = "a // b";\n'
+    assert tok(base) == tok('/* doc */ float f(float x)\n{ return x * 2.0f; }\nconst char* s = "a // b";')
+    assert tok(base) != tok(base.replace("2.0f", "3.0f"))
+    assert tok(base) != tok(base.replace('"a // b"', '"a // c"'))
+    assert tok("char c = '\"'; int y; // z") == tok("char c = '\"';  int y;")
