@@ -328,8 +328,8 @@ ssm_status ssm_conv1d_update(void* conv_state, const void* x, const float* weigh
  *   initial/last_state    : [batch, nheads, headdim, d_state] fp32
  * Supported: in_dtype bf16 (x, dt, z, B, C; the chunk products run on bf16
  * matrix cores with fp32 accumulation), out fp32 or bf16; headdim 64;
- * d_state 64 or 128; nheads a multiple of ngroups.  softplus: 0 or
- * SSM_SOFTPLUS.  Optional (NULL): D, z, dt_bias, initial_state (zero),
+ * d_state 64 or 128; nheads a multiple of ngroups and at most 65535.
+ * softplus: 0 or SSM_SOFTPLUS.  Optional (NULL): D, z, dt_bias, initial_state (zero),
  * last_state.  last_state may be the same buffer as initial_state; no other
  * overlap of an output with anything is allowed.  Every pointer 16-byte
  * aligned, except dt (element alignment).  The chunk form sums in a

@@ -391,8 +391,10 @@ ssm_status ssd_check(int64_t batch, int64_t seqlen, int64_t nheads, int64_t head
       !mul_ok(t2, headdim * d_state, &sz->state) || !mul_ok(sz->state, 8, &t3))
     return fail(SSM_ERR_BAD_SHAPE, "element count overflows int64");
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch=%lld exceeds 65535", (long long)batch);
-  if (!scan && nheads > 65535)  // the decode grid has one workgroup row per head
-    return fail(SSM_ERR_UNSUPPORTED, "nheads=%lld exceeds 65535 for the decode step", (long long)nheads);
+  // the decode grid and the carry of a chunked scan have one workgroup row per
+  // head, and the scan kernel addresses one 32-step chunk of a tensor with
+  // 32-bit byte offsets, which at most 65535 heads keep below 2^31
+  if (nheads > 65535) return fail(SSM_ERR_UNSUPPORTED, "nheads=%lld exceeds 65535", (long long)nheads);
   if (nheads > INT32_MAX || headdim > INT32_MAX || ngroups > INT32_MAX)
     return fail(SSM_ERR_UNSUPPORTED, "nheads, headdim and ngroups must fit in 32 bits");
   return SSM_OK;
@@ -823,9 +825,6 @@ static ssm_status ssd_impl(const void* x, const void* dt, const float* A, const 
     choose_ssd_plan(batch, seqlen, nheads, device_simds(), &plan);
   }
   const int64_t K = std::max<int64_t>(1, plan.n_chunks);
-  // the carry between time chunks has one workgroup row per head
-  if (K > 1 && nheads > 65535)
-    return fail(SSM_ERR_UNSUPPORTED, "nheads=%lld exceeds 65535 for a scan cut into time chunks", (long long)nheads);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch == 0) return ok();

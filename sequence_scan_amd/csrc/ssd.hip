@@ -154,28 +154,48 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
   const bool has_D = a.D != nullptr;
   const int p = 16 * w + lr;              // this lane's channel in the readout and the state
   const float Dp = has_D ? a.D[(int64_t)h * kP + p] : 0.0f;
+  const uint32_t off_o = ((uint32_t)(4 * q) * (uint32_t)xrow + (uint32_t)p) * (uint32_t)sizeof(Tout);
 
   // Global loads and LDS staging: row-major 16-byte vectors (thread v covers
   // row v / (width / 8), vector v % (width / 8)); rows past the chunk's last
-  // step re-read that step.
+  // step re-read that step.  Addresses are a chunk base, uniform across the
+  // workgroup and held in scalar registers, plus a per-lane 32-bit byte offset
+  // that is the same for every full chunk: one chunk of any tensor spans less
+  // than 2^31 bytes, since heads are at most 65535.
   const int xrow_i = tid >> 3, xc8 = tid & 7;
+  const uint32_t bc_rowb = (uint32_t)bcrow * 2u, x_rowb = (uint32_t)xrow * 2u, dt_rowb = (uint32_t)H * 2u;
+  auto bc_off = [&](int r, int nrow) SSM_INLINE {
+    const int v = tid + 256 * r;
+    return (uint32_t)min(v / (N / 8), nrow - 1) * bc_rowb + (uint32_t)(v % (N / 8)) * 16u;
+  };
+  uint32_t off_bc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) off_bc[r] = bc_off(r, kQ);
+  const uint32_t off_x = (uint32_t)xrow_i * x_rowb + (uint32_t)xc8 * 16u;
+  const uint32_t off_dt = (uint32_t)min(tid, kQ - 1) * dt_rowb;
   struct Bank {
     u32x4_t c[NR], bb[NR], x, z;
     uint32_t dt;
   };
   Bank bank;
   auto issue = [&](int64_t t0, int nt) SSM_INLINE {
+    const char* Bc = reinterpret_cast<const char*>(Bb + t0 * bcrow);
+    const char* Cc = reinterpret_cast<const char*>(Cb + t0 * bcrow);
+    const char* xc = reinterpret_cast<const char*>(xb + t0 * xrow);
+    const char* zc = has_z ? reinterpret_cast<const char*>(zb + t0 * xrow) : nullptr;
+    const char* dtc = reinterpret_cast<const char*>(dtb + t0 * H);
+    const bool full = nt == kQ;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const int v = tid + 256 * r;
-      const int64_t off = (t0 + min(v / (N / 8), nt - 1)) * bcrow + (v % (N / 8)) * 8;
-      if (!STATE_ONLY) bank.c[r] = *reinterpret_cast<const u32x4_t*>(Cb + off);
-      bank.bb[r] = *reinterpret_cast<const u32x4_t*>(Bb + off);
+      const uint32_t o = full ? off_bc[r] : bc_off(r, nt);
+      if (!STATE_ONLY) bank.c[r] = *reinterpret_cast<const u32x4_t*>(Cc + o);
+      bank.bb[r] = *reinterpret_cast<const u32x4_t*>(Bc + o);
     }
-    const int64_t xoff = (t0 + min(xrow_i, nt - 1)) * xrow + xc8 * 8;
-    bank.x = *reinterpret_cast<const u32x4_t*>(xb + xoff);
-    if (has_z) bank.z = *reinterpret_cast<const u32x4_t*>(zb + xoff);
-    if (tid < kQ) bank.dt = dtb[(t0 + min(tid, nt - 1)) * H];
+    const uint32_t ox = full ? off_x : (uint32_t)min(xrow_i, nt - 1) * x_rowb + (uint32_t)xc8 * 16u;
+    bank.x = *reinterpret_cast<const u32x4_t*>(xc + ox);
+    if (has_z) bank.z = *reinterpret_cast<const u32x4_t*>(zc + ox);
+    if (tid < kQ)
+      bank.dt = *reinterpret_cast<const uint16_t*>(dtc + (full ? off_dt : (uint32_t)min(tid, nt - 1) * dt_rowb));
   };
 
   // Stage the banked chunk (steps past nt carry x = 0 and dt = 0, so they
@@ -258,17 +278,21 @@ __global__ void __launch_bounds__(256, 3) ssd_chunk_kernel(SsdArgs a) {
         y[ib][r] = v;
       }
     }
+    // out: chunk base (scalar) + row base 16 ib + r (scalar) + this lane's 32-bit offset
+    Tout* oc = ob + t0 * xrow;
     if (nt == kQ) {
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Io<Tout>::store(ob, (t0 + 16 * ib + 4 * q + r) * xrow + p, y[ib][r]);
+        for (int r = 0; r < 4; ++r)
+          Io<Tout>::store(reinterpret_cast<char*>(oc + (16 * ib + r) * xrow) + off_o, 0, y[ib][r]);
     } else {
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (16 * ib + 4 * q + r < nt) Io<Tout>::store(ob, (t0 + 16 * ib + 4 * q + r) * xrow + p, y[ib][r]);
+          if (16 * ib + 4 * q + r < nt)
+            Io<Tout>::store(reinterpret_cast<char*>(oc + (16 * ib + r) * xrow) + off_o, 0, y[ib][r]);
     }
   };
 

@@ -377,8 +377,10 @@ def test_ssd_plan_choices_and_rejections():
         return lib.ssm_ssd_fwd_plan(P, P + 0x10000000000, P + 0x20000000000, P + 0x30000000000, P + 0x40000000000,
                                     None, None, None, 1, None, P + 0x50000000000, None, 1, seqlen, nheads, 64, 1, 128,
                                     BF16, F32, None, ctypes.byref(pl))
-    # the carry between time chunks puts the heads on a grid axis of at most 65535
+    # at most 65535 heads, chunked (the carry's grid axis) or not (the kernel's
+    # 32-bit offsets within a chunk)
     assert ssd_heads(65536, 32) == ssm.SSM_ERR_UNSUPPORTED and "65535" in ssm.ssm_last_error()
+    assert ssd_heads(65536, 64) == ssm.SSM_ERR_UNSUPPORTED and "65535" in ssm.ssm_last_error()
 
 
 def test_ssd_rejections():
