@@ -24,9 +24,9 @@ namespace {
 // incoming state, and with two-channel items each transition, in registers),
 // then runs the reverse recurrence on those values.  Sums over a
 // channel's 16 states go through LDS partials, summed in a fixed order; dB and
-// dC are reduced over the wavefront's 64 channels through a wave-local LDS
-// transpose and 3 DPP steps, and stored per channel block for a second,
-// fixed-order reduction kernel: the result does not depend on timing.
+// dC are reduced over the wavefront's 64 channels in registers (lane swaps and
+// DPP, lane_sum8), and stored per channel block for a second, fixed-order
+// reduction kernel: the result does not depend on timing.
 //
 // A long sequence with few channel blocks is cut into time chunks, one
 // workgroup per (chunk, batch row, block).  Chunk k then starts its forward
@@ -36,6 +36,45 @@ namespace {
 // and carry below; the caller's dlast for the last chunk).  The chunk length
 // is a multiple of the tile, so the chunk's tiles are tiles of the whole
 // sequence and share its checkpoint layout.
+
+// Totals over the 64 lanes of a wavefront of eight values per lane, in
+// registers: gfx950's lane-swap instructions pair lanes l and l ^ 32 (then
+// l ^ 16) while halving the values each lane carries, a rotation by 8 within
+// each 16-lane row pairs l and l ^ 8 for the last two, and three DPP steps sum
+// each 8-lane group.  Every lane of 8-lane group l >> 3 returns the total of
+// value sum8_index(l).
+__device__ __forceinline__ float2 swap_lanes32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));  // {a[0..31], b[0..31]}, {a[32..], b[32..]}
+}
+__device__ __forceinline__ float2 swap_rows16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));  // rows {a0, b0, a2, b2}, {a1, b1, a3, b3}
+}
+__device__ __forceinline__ int sum8_index(int lane) {
+  const int r = (lane >> 4) & 3;
+  return ((r & 1) << 1) + (r >> 1) + 4 * ((lane >> 3) & 1);
+}
+__device__ __forceinline__ float lane_sum8(const float (&v)[8], int lane) {
+  float S[4], T[2];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float2 r = swap_lanes32(v[2 * p], v[2 * p + 1]);
+    S[p] = r.x + r.y;   // lanes 0..31: value 2p over l, l + 32; lanes 32..63: value 2p + 1
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const float2 r = swap_rows16(S[2 * p], S[2 * p + 1]);
+    T[p] = r.x + r.y;   // row 0: value 4p, row 1: 4p + 2, row 2: 4p + 1, row 3: 4p + 3 (over 4 lanes)
+  }
+  const bool hi = (lane >> 3) & 1;
+  const float keep = hi ? T[1] : T[0], give = hi ? T[0] : T[1];
+  float u = keep + SSM_DPP(0.0f, give, 0x128, 0xf);   // row_ror:8 brings lane l ^ 8
+  u += SSM_DPP(0.0f, u, 0xb1, 0xf);                   // quad_perm [1,0,3,2]
+  u += SSM_DPP(0.0f, u, 0x4e, 0xf);                   // quad_perm [2,3,0,1]
+  u += SSM_DPP(0.0f, u, 0x141, 0xf);                  // row_half_mirror
+  return u;
+}
 
 template <typename Tin, typename Tg, bool HAS_Z, int CW>
 __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
@@ -57,7 +96,6 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
   __shared__ float sh_y[T][G * kWave + 1];     // forward readout partials
   __shared__ float sh_s1[T][G * kWave + 1];    // partial dh . B'
   __shared__ float sh_s2[T][G * kWave + 1];    // partial sum dh A a h_{t-1}
-  __shared__ float sh_red[G][kWave * 9];        // per-lane dB', dC contributions, stride 9
   __shared__ float sh_bc[T][2][kDState];       // the tile's dB', dC of this block
 
   const int tid = threadIdx.x;
@@ -285,34 +323,24 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
         }
         sh_s1[s][g * kWave + lane] = s1;
         sh_s2[s][g * kWave + lane] = s2;
-        // dB', dC of this step over the wavefront's 64 channels: every lane
-        // stages its 8 contributions; lane 8j + p sums contribution j of
-        // lanes 8p .. 8p + 7; three DPP steps (two within the quad, then
-        // row_half_mirror, which swaps the two quads of each 8-lane half)
-        // leave the total in all 8 lanes of group j.
-        // (a lane's 8 values sit at stride 9: 9 is odd, so both the writes
-        // and the column reads below touch 64 distinct banks)
-        float* red = &sh_red[g][0];
+        // dB', dC of this step over the wavefront's 64 channels (lanes),
+        // in registers; lanes past the last channel hold duplicates and
+        // contribute zero
+        float v8[8];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-          red[lane * 9 + i] = cb[i];
-          red[lane * 9 + NS + i] = cc[i];
+          v8[i] = cb[i];
+          v8[NS + i] = cc[i];
         }
-        __builtin_amdgcn_wave_barrier();
-        const int j = lane >> 3, p = lane & 7;
-        float acc = 0.0f;
-        if (nvalid == kWave) {
+        if (nvalid != kWave) {
 #pragma unroll
-          for (int m = 0; m < 8; ++m) acc += red[(p * 8 + m) * 9 + j];
-        } else {  // lanes past the last channel hold duplicates: leave them out
-#pragma unroll
-          for (int m = 0; m < 8; ++m) acc += (p * 8 + m < nvalid) ? red[(p * 8 + m) * 9 + j] : 0.0f;
+          for (int i = 0; i < 8; ++i) v8[i] = lane < nvalid ? v8[i] : 0.0f;
         }
-        acc += SSM_DPP(0.0f, acc, 0xb1, 0xf);   // quad_perm [1,0,3,2]
-        acc += SSM_DPP(0.0f, acc, 0x4e, 0xf);   // quad_perm [2,3,0,1]
-        acc += SSM_DPP(0.0f, acc, 0x141, 0xf);  // row_half_mirror
-        if (p == 0) sh_bc[s][j >> 2][g * NS + (j & 3)] = acc;
-        __builtin_amdgcn_wave_barrier();
+        const float tot = lane_sum8(v8, lane);
+        if ((lane & 7) == 0) {
+          const int j = sum8_index(lane);
+          sh_bc[s][j >> 2][g * NS + (j & 3)] = tot;
+        }
       }
     }
     block_sync();
