@@ -401,6 +401,9 @@ def backward_case(cfg, steps=5):
                                    softplus=True, dout=dout)
     settle(run, 0.1)
     ms, _ = time_steps(run, steps, 2)
+    # single calls with a synchronisation after each: the workspace (about 840 MB)
+    # is reused from the library's pool instead of being mapped again per call
+    iso_avg, iso_med, _ = per_launch_ms(run, 5)
     # VALU cycles per wavefront state update: the checkpoint forward (3 VALU +
     # exp = 20), the tile's forward again with the readout (4 + exp = 24), the
     # reverse step (11 VALU + exp = 52) and the lane reductions of dB, dC (~12)
@@ -410,7 +413,9 @@ def backward_case(cfg, steps=5):
     del t, dout
     return {"workload": f"ssm_scan_bwd {cfg.name}: batch {cfg.batch}, seqlen {cfg.seqlen}, d_inner {cfg.d_inner}, "
                         "bf16 inputs and gradients, softplus, D, z",
-            "us_per_call": round(ms * 1e3, 1), "alu_floor_us": round(floor_us, 1),
+            "us_per_call": round(ms * 1e3, 1), "isolated_call_us": {"avg": round(iso_avg * 1e3, 1),
+                                                                    "median": round(iso_med * 1e3, 1)},
+            "alu_floor_us": round(floor_us, 1),
             "alu_frac": round(floor_us / (ms * 1e3), 4), "long_sequence": backward_long_case()}
 
 

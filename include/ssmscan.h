@@ -29,10 +29,16 @@
  * state and every intermediate are fp32; out is fp32 or bf16 (out_dtype,
  * rounded to nearest even).
  *
- * Ownership: every pointer is a device pointer owned by the caller.  The
- * library keeps no device memory between calls.  A scan over more than one
- * time chunk takes a temporary workspace with hipMallocAsync on `stream` and
- * releases it with hipFreeAsync on the same stream.
+ * Ownership: every pointer is a device pointer owned by the caller.  A scan
+ * over more than one time chunk (and the backward, and a chunked Mamba-2
+ * scan) takes a temporary workspace, stream-ordered on `stream` and freed on
+ * it before the call returns.  Workspaces come from a memory pool that the
+ * library keeps per device: memory a call frees stays reserved for later
+ * calls (at most the largest set of workspaces in use at one time), so a call
+ * after a synchronisation does not map its workspace again;
+ * ssm_trim_workspace() returns it to the system.  Under stream capture the
+ * workspace comes from hipMallocAsync on the stream instead, and the graph
+ * owns it.  ssm_scan_fwd_noalloc uses a fixed array instead (below).
  *
  * Errors: every argument is checked on the host before anything is enqueued.
  * A non-OK status means nothing was enqueued and no output was written;
@@ -55,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 8
+#define SSM_ABI_VERSION 9
 
 /*
  * Bits of the step-flags argument (named `softplus` in the calls below):
@@ -176,7 +182,8 @@ ssm_status ssm_scan_fwd_from(const void* x, const void* delta, const float* A, c
  * ssm_scan_fwd_from for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, results and checks as ssm_scan_fwd_from, and
- * the same kernels; it calls no hipMalloc, hipMallocAsync or hipFree.  A plan
+ * the same kernels; it calls no hipMalloc, hipMallocAsync,
+ * hipMallocFromPoolAsync or hipFree.  A plan
  * with more than one time chunk keeps its carry workspace (about
  * batch * n_chunks * d_inner * 68 bytes, plus the state when initial_state
  * is last_state) in a fixed array of SSM_NOALLOC_SCRATCH_BYTES bytes that
@@ -219,7 +226,7 @@ ssm_status ssm_scan_fwd_noalloc(const void* x, const void* delta, const float* A
  * bitwise reproducible for a given plan (below).  A workspace of about
  * batch * seqlen * d_inner * 8 + batch * seqlen * ceil(d_inner / 64) * 128
  * bytes (the states entering every 8-step tile, and per-block dB, dC) is taken
- * with hipMallocAsync on `stream` and released with hipFreeAsync.  With few
+ * on `stream` as described under Ownership.  With few
  * channel blocks the sequence is cut into time chunks (ssm_scan_bwd_plan).
  * Outputs must not overlap any input or each other.  Sizes, dtypes, alignment
  * and errors as for ssm_scan_fwd (grad_dtype in place of out_dtype).
@@ -355,7 +362,7 @@ ssm_status ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void
  * multiple of 32 whenever it is below seqlen; at most 65535 chunks;
  * states_per_wave is ignored.  A chunked run takes
  * batch * n_chunks * nheads * (headdim * d_state + 1) * 4 bytes of workspace
- * (plus a copy of an in-place initial state) with hipMallocAsync on `stream`.
+ * (plus a copy of an in-place initial state), taken as described under Ownership.
  * Any valid plan computes the same function up to rounding order.  Otherwise
  * as for ssm_ssd_fwd.
  */
@@ -400,6 +407,14 @@ const char* ssm_status_string(ssm_status s);
 const char* ssm_last_error(void);
 /* SSM_ABI_VERSION of the loaded library. */
 int ssm_abi_version(void);
+
+/*
+ * Returns the workspace memory that the library's pool on the current device
+ * holds and no call is using to the system (hipMemPoolTrimTo).  Call it after
+ * synchronising the streams the library ran on; the next call that needs a
+ * workspace maps it again.  SSM_OK also when the pool was never created.
+ */
+ssm_status ssm_trim_workspace(void);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,7 @@ Functions carry the C names: ``ssm_scan_fwd``, ``ssm_state_update``,
 ``ssm_scan_bwd``, ``ssm_scan_bwd_plan``, ``ssm_scan_bwd_plan_query``, ``ssm_conv1d_fwd``,
 ``ssm_conv1d_update``, ``ssm_ssd_fwd``, ``ssm_ssd_fwd_plan``, ``ssm_ssd_plan_query``, ``ssm_ssd_state_update``,
 ``ssm_affine_exclusive_scan``,
-``ssm_status_string``, ``ssm_last_error``, ``ssm_abi_version``.
+``ssm_status_string``, ``ssm_last_error``, ``ssm_abi_version``, ``ssm_trim_workspace``.
 """
 from __future__ import annotations
 
@@ -106,6 +106,8 @@ def _load():
     lib.ssm_last_error.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
     lib.ssm_abi_version.restype = ctypes.c_int
+    lib.ssm_trim_workspace.argtypes = []
+    lib.ssm_trim_workspace.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -181,6 +183,12 @@ def ssm_last_error() -> str:
 
 def ssm_abi_version() -> int:
     return int(_load().ssm_abi_version())
+
+
+def ssm_trim_workspace() -> None:
+    """Return the workspace memory the library's pool on the current device holds
+    unused to the system (call after synchronising)."""
+    _check(_load().ssm_trim_workspace())
 
 
 def ssm_scan_plan(batch: int, seqlen: int, d_inner: int, d_state: int = D_STATE) -> dict:

@@ -16,6 +16,7 @@
 extern "C" void fake_fail_next_alloc(void);
 extern "C" long fake_launches(void);
 extern "C" long fake_live_allocs(void);
+extern "C" int fake_pools(void);
 
 namespace {
 int g_failures = 0;
@@ -275,6 +276,11 @@ int main() {
     std::fprintf(stderr, "%ld workspace allocations not freed\n", fake_live_allocs());
     ++g_failures;
   }
+  if (fake_pools() != 1) {
+    std::fprintf(stderr, "%d workspace pools created, expected one\n", fake_pools());
+    ++g_failures;
+  }
+  expect("trim_workspace", ssm_trim_workspace(), SSM_OK);
   for (void* p : g_bufs) std::free(p);
   if (g_failures) {
     std::fprintf(stderr, "%d expectation(s) failed\n", g_failures);

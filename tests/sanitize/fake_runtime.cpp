@@ -56,6 +56,27 @@ hipError_t hipMallocAsync(void** p, size_t bytes, hipStream_t) {
   ++g_allocs;
   return hipSuccess;
 }
+int g_pools = 0;
+hipError_t hipMemPoolCreate(hipMemPool_t* pool, const hipMemPoolProps* props) {
+  if (props->location.type != hipMemLocationTypeDevice || props->allocType != hipMemAllocationTypePinned)
+    std::abort();
+  static int dummy;
+  *pool = reinterpret_cast<hipMemPool_t>(&dummy);
+  ++g_pools;
+  return hipSuccess;
+}
+hipError_t hipMemPoolSetAttribute(hipMemPool_t, hipMemPoolAttr, void*) { return hipSuccess; }
+hipError_t hipMemPoolDestroy(hipMemPool_t) { return hipSuccess; }
+hipError_t hipMemPoolTrimTo(hipMemPool_t, size_t) { return hipSuccess; }
+hipError_t hipMallocFromPoolAsync(void** p, size_t bytes, hipMemPool_t, hipStream_t s) {
+  return hipMallocAsync(p, bytes, s);
+}
+int hipGetStreamDeviceId(hipStream_t) { return 0; }
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* st) {
+  *st = hipStreamCaptureStatusNone;
+  return hipSuccess;
+}
+int fake_pools(void) { return g_pools; }
 hipError_t hipFreeAsync(void* p, hipStream_t) {
   std::free(p);
   ++g_frees;

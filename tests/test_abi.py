@@ -24,13 +24,13 @@ def test_every_declared_function_is_exported():
             "ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_affine_exclusive_scan", "ssm_status_string",
             "ssm_last_error", "ssm_abi_version", "ssm_scan_bwd", "ssm_scan_bwd_plan", "ssm_scan_bwd_plan_query",
             "ssm_ssd_fwd", "ssm_ssd_fwd_plan", "ssm_ssd_plan_query", "ssm_ssd_state_update",
-            "ssm_scan_fwd_noalloc"} <= set(names)
+            "ssm_scan_fwd_noalloc", "ssm_trim_workspace"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssmscan.h but not exported"
 
 
 def test_version_and_strings():
-    assert ssm.ssm_abi_version() == 8
+    assert ssm.ssm_abi_version() == 9
     for code, name in ssm.STATUS_NAMES.items():
         assert ssm.ssm_status_string(code).startswith(name)
     assert "unknown" in ssm.ssm_status_string(99)
@@ -214,7 +214,7 @@ def test_noalloc_rejections():
 
 
 def test_failed_workspace_allocation_is_reported():
-    """Without a usable device a chunked plan's hipMallocAsync fails: the call returns
+    """Without a usable device a chunked plan's workspace allocation fails: the call returns
     SSM_ERR_HIP naming the allocation.  (That a later valid call is not handed the same
     error again is checked on the GPU, where the failure is forced by size.)"""
     lib = ssm.library()
@@ -225,7 +225,7 @@ def test_failed_workspace_allocation_is_reported():
     pl.states_per_wave, pl.chunk_len = 4, 4
     st = lib.ssm_scan_fwd_plan(P, P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, None, None, None, 1,
                                P + 0x5000000, None, 2, 8, 64, 16, F32, F32, None, ctypes.byref(pl))
-    assert st == ssm.SSM_ERR_HIP and "hipMallocAsync" in ssm.ssm_last_error()
+    assert st == ssm.SSM_ERR_HIP and "workspace allocation" in ssm.ssm_last_error()
 
 
 def test_conv1d_rejections():

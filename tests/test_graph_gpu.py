@@ -175,8 +175,9 @@ def test_ssd_graph(chunk_len):
 
 @pytest.mark.parametrize("chunk_len", [None, 32])
 def test_backward_graph(chunk_len):
-    """The backward, whose workspace comes from hipMallocAsync on the stream (a
-    graph allocation node), one chunk and time chunks (forward and reverse carries)."""
+    """The backward, whose workspace comes from hipMallocAsync on the capturing
+    stream (a graph allocation node; outside capture it comes from the library's
+    pool), one chunk and time chunks (forward and reverse carries)."""
     L = 150
     say(f"graph: backward batch 2 L {L} d_inner 96 bf16, chunk_len {chunk_len}")
     cfg = workloads.ScanConfig("g", 2, 96, 16, L, "bf16")

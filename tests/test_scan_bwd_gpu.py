@@ -242,3 +242,28 @@ def test_bwd_long_dna_sampled():
     head = oracle.scan_bwd(np_(x[:, :m]), np_(dl[:, :m]), np_(A), np_(B[:, :m]), np_(C[:, :m]), np_(D),
                            np_(z[:, :m]), np_(bias), softplus=True, dout=np_(dout[:, :m]))
     assert rowinf(np_(res["dC"][:, :m]), head["dC"], 1) <= TOL
+
+
+def test_workspace_pool_keeps_memory_until_trimmed():
+    """Workspaces come from the library's own pool, whose freed memory stays mapped
+    across synchronisations (so a call after a sync does not map it again) until
+    ssm_trim_workspace returns it; results are the same whichever memory a call gets."""
+    say("workspace pool: reuse after synchronisation, then trim")
+    batch, L, Dn = 2, 4096, 512
+    inp, g, gl, h0 = _case(batch, L, Dn, dtype="bf16", seed=21)
+    # the checkpoints alone: batch x blocks x tiles x 64 x 16 fp32
+    ckpt_bytes = batch * (Dn // 64) * (L // 8) * 64 * 16 * 4
+    first = _run(inp, g, gl, h0)
+    free1, _ = torch.cuda.mem_get_info()
+    second = _run(inp, g, gl, h0)
+    free2, _ = torch.cuda.mem_get_info()
+    ssm.ssm_trim_workspace()
+    torch.cuda.synchronize()
+    free3, _ = torch.cuda.mem_get_info()
+    third = _run(inp, g, gl, h0)
+    for k in first:
+        assert np.array_equal(first[k], second[k]) and np.array_equal(first[k], third[k]), k
+    say(f"free after call 1 {free1 / 2**20:.0f} MiB, after call 2 {free2 / 2**20:.0f}, after trim {free3 / 2**20:.0f}; "
+        f"checkpoints {ckpt_bytes / 2**20:.0f} MiB")
+    assert free2 >= free1 - ckpt_bytes // 4, "the second call mapped its workspace again"
+    assert free3 - free2 >= ckpt_bytes // 2, "trimming did not return the workspace"
