@@ -26,7 +26,8 @@
 //  * Long sequences are cut into chunks.  Pass A reduces every chunk but the
 //    last to its affine pair per state coordinate: the end state from zero and
 //    the step-size sum S (the chunk's decay is exp(A S)).  The carry kernel
-//    scans the pairs in time order with a wavefront DPP scan (lane = chunk).
+//    scans the pairs in time order with a wavefront DPP scan (lane = chunk);
+//    with at most 16 chunks one thread per coordinate applies them in order.
 //    Pass B re-runs each chunk from its incoming state with the full readout.
 #include <mutex>
 
@@ -102,6 +103,40 @@ __global__ void __launch_bounds__(256) carry_kernel(float* ws_state, const float
       if (r < np && col < ncol) ws_state[((int64_t)b * K + p0 + r) * ncol + col] = sb[r][lane];
     }
     block_sync();
+  }
+}
+
+// The carry for a sequence cut into few chunks (at most kFewPairs pairs): one
+// thread per (batch row, coordinate) applies its pairs in time order,
+// h <- exp2(A[d,n] S_p) h + end_p from h = 0, and stores each h in slot p.
+// The loads of every pair are independent of h, so they are all in flight at
+// once; the wavefront scan above would spend a whole DPP scan on each column
+// for a handful of lanes.
+constexpr int kFewPairs = 15;
+__global__ void __launch_bounds__(256) carry_few_kernel(float* ws_state, const float* ws_dtsum, const float* A,
+                                                        int64_t Dn, int K) {
+  const int64_t ncol = Dn * kDState;
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = blockIdx.y;
+  if (col >= ncol) return;
+  const float a2 = A[col];  // S is a sum of log2-unit step sizes
+  const int np = K - 1;
+  float e[kFewPairs], S[kFewPairs];
+#pragma unroll
+  for (int p = 0; p < kFewPairs; ++p) {
+    if (p < np) {
+      const int64_t slot = b * K + p;
+      e[p] = ws_state[slot * ncol + col];
+      S[p] = ws_dtsum[slot * Dn + (col >> 4)];
+    }
+  }
+  float h = 0.0f;
+#pragma unroll
+  for (int p = 0; p < kFewPairs; ++p) {
+    if (p < np) {
+      h = __builtin_fmaf(__builtin_amdgcn_exp2f(S[p] * a2), h, e[p]);
+      ws_state[(b * K + p) * ncol + col] = h;
+    }
   }
 }
 
@@ -218,6 +253,12 @@ hipError_t launch_scan(const ScanArgs& a, DT in, DT out, int ns, hipStream_t s) 
 }
 
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s) {
+  if (a.n_chunks - 1 <= kFewPairs) {
+    const unsigned nblk = (unsigned)((a.d_inner * kDState + 255) / 256);
+    hipLaunchKernelGGL(carry_few_kernel, dim3(nblk, (unsigned)a.batch), dim3(256), 0, s, a.ws_state,
+                       (const float*)a.ws_dtsum, a.A, a.d_inner, a.n_chunks);
+    return hipGetLastError();
+  }
   const unsigned ncolblk = (unsigned)((a.d_inner * kDState + 63) / 64);
   hipLaunchKernelGGL(carry_kernel, dim3(ncolblk, (unsigned)a.batch), dim3(256), 0, s, a.ws_state,
                      (const float*)a.ws_dtsum, a.A, a.d_inner, a.n_chunks);
