@@ -189,42 +189,17 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
     }
   };
 
-  // ---- phase 1: forward, storing the state entering each tile
+  // The state entering every tile comes from the forward scan kernel's
+  // checkpoint pass (ScanArgs::ckpt), run before this kernel: slot 4 j + i of
+  // a lane's 16 holds state j + 4 i, so this wave's states 4 g .. 4 g + 3 are
+  // slots g, g + 4, g + 8, g + 12.
+  auto ld_ckpt = [&](int64_t k) SSM_INLINE {
+    const float* p = ck + (k * kWave + lane) * kDState + g;
+    return make_float4(p[0], p[4], p[8], p[12]);
+  };
   float h[NS];
-  const float* hsrc = kc > 0 ? a.ws_hin + ((row - 1) * Dn + dl) * kDState
-                      : a.h0 != nullptr ? a.h0 + (b * Dn + dl) * kDState : nullptr;
-#pragma unroll
-  for (int i = 0; i < NS; ++i) h[i] = hsrc != nullptr ? hsrc[g * NS + i] : 0.0f;
-  // Progress weights for ProgressPriority: a phase-1 tile counts 2, a
-  // phase-2 tile (about 4.5 times the work) 9.
-  const ProgressPriority prio(11 * ntiles);
+  const ProgressPriority prio(ntiles);
   Bank cur, nxt;
-  load(cur, 0, false);
-  for (int64_t k = 0; k < ntiles; ++k) {
-    if (a.fair) prio.at(2 * k);
-    const int nt = tile_rows(k);
-    *reinterpret_cast<float4*>(ck + (k * kWave + lane) * kDState + g * NS) = make_float4(h[0], h[1], h[2], h[3]);
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-#pragma unroll
-      for (int q = 0; q < CW; ++q) {
-        const float u2 = (cur.rd[it].get(q) + ibias[it][q]) * kLog2e;
-        const float dt2 = softplus ? softplus2_f(u2) : u2;
-        sh_dtu[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * cur.rx[it].get(q));
-      }
-    }
-    stage_bc(cur, false);
-    if (k + 1 < ntiles) load(nxt, k + 1, false);
-    block_sync();
-    for (int s = 0; s < nt; ++s) {
-      const float2 v = sh_dtu[s][loff];
-#pragma unroll
-      for (int i = 0; i < NS; ++i)
-        h[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(v.x * Ad[i]), h[i], v.y * sh_B[s][g * NS + i]);
-    }
-    block_sync();
-    cur = nxt;
-  }
 
   // ---- phase 2: the tiles in reverse
   float carry[NS], dAacc[NS];
@@ -242,9 +217,9 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
     for (int q = 0; q < CW; ++q) dDacc[it][q] = dBacc[it][q] = 0.0f;
 
   load(cur, ntiles - 1, true);
-  float4 hc = *reinterpret_cast<const float4*>(ck + ((ntiles - 1) * kWave + lane) * kDState + g * NS);
+  float4 hc = ld_ckpt(ntiles - 1);
   for (int64_t k = ntiles - 1; k >= 0; --k) {
-    if (a.fair) prio.at(2 * ntiles + 9 * (ntiles - 1 - k));
+    if (a.fair) prio.at(ntiles - 1 - k);
     const int64_t t0 = k * T;
     const int nt = tile_rows(k);
     // the tile's per-element values, from the raw inputs (which stay live for
@@ -270,7 +245,7 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
     h[0] = hc.x; h[1] = hc.y; h[2] = hc.z; h[3] = hc.w;
     if (k > 0) {
       load(nxt, k - 1, true);
-      hc = *reinterpret_cast<const float4*>(ck + ((k - 1) * kWave + lane) * kDState + g * NS);
+      hc = ld_ckpt(k - 1);
     }
     block_sync();
 
@@ -641,11 +616,9 @@ void launch_bwd_pass(K kern, dim3 grid, const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, b);
 }
 
-// The chunked backward's carries: each chunk's entering state (the forward's
-// pass A and carry, run by the forward scan's own launcher), then each
-// chunk's arriving gradient (reverse pass A, reverse carry).
-template <typename Tin, typename Tg>
-hipError_t launch_bwd_carries(const BwdArgs& a, DT in, hipStream_t s) {
+// The forward scan's arguments for the backward's forward work: the chunk
+// carry (states_only) and the checkpoint pass (ckpt).
+ScanArgs forward_args(const BwdArgs& a) {
   ScanArgs f{};
   f.x = a.x;
   f.delta = a.delta;
@@ -663,6 +636,15 @@ hipError_t launch_bwd_carries(const BwdArgs& a, DT in, hipStream_t s) {
   f.softplus = a.softplus;
   f.batch = a.batch;
   f.cus = a.cus;
+  return f;
+}
+
+// The chunked backward's carries: each chunk's entering state (the forward's
+// pass A and carry, run by the forward scan's own launcher), then each
+// chunk's arriving gradient (reverse pass A, reverse carry).
+template <typename Tin, typename Tg>
+hipError_t launch_bwd_carries(const BwdArgs& a, DT in, hipStream_t s) {
+  ScanArgs f = forward_args(a);
   f.states_only = 1;
   hipError_t e = launch_scan(f, in, DT::F32, 4, s);
   if (e != hipSuccess) return e;
@@ -685,6 +667,15 @@ template <typename Tin, typename Tg>
 hipError_t launch_scan_bwd_t(const BwdArgs& a, DT in, float* dA, void* dB, void* dC, float* dD, float* dbias,
                              hipStream_t s) {
   const dim3 grid((unsigned)a.nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
+  // the state entering every 8-step tile, from the forward scan kernel's
+  // checkpoint pass (after the chunk carry, whose states it starts from)
+  auto checkpoints = [&]() {
+    ScanArgs f = forward_args(a);
+    f.ckpt = a.ws_ckpt;
+    f.ckpt_nblk = a.nblk;
+    f.ckpt_tiles = (a.seqlen + kBwdTile - 1) / kBwdTile;
+    return launch_scan(f, in, DT::F32, 4, s);
+  };
   if (a.seqlen > 0) {
     // channels per element item: 8-step tiles x 64 channels = 256 threads x 2
     if (a.d_inner % 2 == 0) {
@@ -692,6 +683,7 @@ hipError_t launch_scan_bwd_t(const BwdArgs& a, DT in, float* dA, void* dB, void*
         const hipError_t e = launch_bwd_carries<Tin, Tg>(a, in, s);
         if (e != hipSuccess) return e;
       }
+      if (const hipError_t e = checkpoints(); e != hipSuccess) return e;
       if (a.z != nullptr) launch_bwd_pass(scan_bwd_kernel<Tin, Tg, true, 2>, grid, a, s);
       else launch_bwd_pass(scan_bwd_kernel<Tin, Tg, false, 2>, grid, a, s);
     } else {
@@ -699,6 +691,7 @@ hipError_t launch_scan_bwd_t(const BwdArgs& a, DT in, float* dA, void* dB, void*
         const hipError_t e = launch_bwd_carries<Tin, Tg>(a, in, s);
         if (e != hipSuccess) return e;
       }
+      if (const hipError_t e = checkpoints(); e != hipSuccess) return e;
       if (a.z != nullptr) launch_bwd_pass(scan_bwd_kernel<Tin, Tg, true, 1>, grid, a, s);
       else launch_bwd_pass(scan_bwd_kernel<Tin, Tg, false, 1>, grid, a, s);
     }

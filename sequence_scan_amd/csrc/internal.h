@@ -38,6 +38,16 @@ struct ScanArgs {
   int32_t fair;           // set by the launcher: the whole grid is co-resident
   int32_t states_only;    // chunked runs: stop after the carry pass (ws_state then holds
                           // the state entering chunk k + 1 in slot k); no out is written
+  // Checkpoint pass (ckpt != nullptr; 4 states per wavefront): instead of a scan,
+  // run every chunk from its entering state (chunk 0: h0; chunk k > 0: slot k - 1
+  // of ws_state, left by a states_only run) without readout or output, and store
+  // the state entering every global step t with t % 8 == 0 at
+  // ckpt[((b * ckpt_nblk + block) * ckpt_tiles + t / 8) * 1024 + lane * 16 + 4 g + i],
+  // which holds state g + 4 i of channel d0 + lane (lanes past d_inner repeat the
+  // last channel).  Chunk lengths must be multiples of 8.
+  float* ckpt;
+  int64_t ckpt_tiles;
+  int32_t ckpt_nblk;
 };
 
 struct DecodeArgs {

@@ -140,8 +140,11 @@ scan_chunk_kernel(ScanArgs a) {
     }
   }
 
+  // checkpoint pass (see ScanArgs::ckpt): pass A's instance, run from each
+  // chunk's entering state, storing the state every 8 steps
+  const bool ckpt_mode = PASS_A && NS == 4 && a.ckpt != nullptr;
   float h[NS];
-  if (!PASS_A && k > 0) {
+  if ((!PASS_A || ckpt_mode) && k > 0) {
     const float* src = a.ws_state + (((int64_t)b * K + (k - 1)) * Dn + dl) * kDState;
 #pragma unroll
     for (int i = 0; i < NS; ++i) h[i] = src[st_of(i)];
@@ -154,6 +157,14 @@ scan_chunk_kernel(ScanArgs a) {
     for (int i = 0; i < NS; ++i) h[i] = 0.0f;
   }
   float dtsum = 0.0f;
+  float* const ckb = ckpt_mode ? a.ckpt + (((int64_t)b * a.ckpt_nblk + blockIdx.x) * a.ckpt_tiles) * (kWave * kDState) +
+                                     lane * kDState + g * 4
+                               : nullptr;
+  // the state entering chunk-relative step tt (t_begin + tt a multiple of 8)
+  auto store_ckpt = [&](int64_t tt) SSM_INLINE {
+    if constexpr (PASS_A && NS == 4)
+      *reinterpret_cast<float4*>(ckb + ((t_begin + tt) >> 3) * (kWave * kDState)) = make_float4(h[0], h[1], h[2], h[3]);
+  };
 
   // Row pointers of this chunk: element (t_begin + tt, d0) of batch row b.
   const int64_t base_e = ((int64_t)b * L + t_begin) * Dn + d0;
@@ -268,8 +279,10 @@ scan_chunk_kernel(ScanArgs a) {
   // is selected by per-wave 0/1 constants (fma(f, v, 1 - f) is v or exactly 1).
   // No transcendental: eight multiplies, two selects and the update's three
   // instructions per state.
-  auto run_steps_pow_plain = [&](int n) SSM_INLINE {  // the peeled ragged tile
+  auto run_steps_pow_plain = [&](int n, int64_t tt0) SSM_INLINE {  // the peeled ragged tile
+    const int ph = (int)((t_begin + tt0) & 7);
     for (int s = 0; s < n; ++s) {
+      if (ckpt_mode && ((ph + s) & 7) == 0) store_ckpt(tt0 + s);
       const float2 v = sh_dtv[s][loff];
       const float e = v.x;
       const float e2 = e * e;
@@ -289,8 +302,9 @@ scan_chunk_kernel(ScanArgs a) {
       }
     }
   };
-  auto run_steps_pow_piped = [&](auto n_c) SSM_INLINE {  // full tiles (n is a constant)
+  auto run_steps_pow_piped = [&](auto n_c, int64_t tt0) SSM_INLINE {  // full tiles (n is a constant)
     constexpr int n = decltype(n_c)::value;
+    const int ph = (int)((t_begin + tt0) & 7);
     // Software-pipelined by two steps: a step's LDS operands -- (e, dt2 x) of the
     // lane's channel and the wave's four B and C values -- are read two steps
     // before they are used.  Without the exponentials a step is only about
@@ -309,6 +323,7 @@ scan_chunk_kernel(ScanArgs a) {
 #pragma unroll
     for (int s = 0; s < n; ++s) {
       if (s + PD < n) fetch(s + PD, (s + PD) % (PD + 1));
+      if (ckpt_mode && ((ph + s) & 7) == 0) store_ckpt(tt0 + s);
       const int cur = s % (PD + 1);
       const float2 v = rv[cur];
       const float bv[4] = {rb[cur].x, rb[cur].y, rb[cur].z, rb[cur].w};
@@ -334,18 +349,19 @@ scan_chunk_kernel(ScanArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto run_steps_pow = [&](auto n_c) SSM_INLINE {
-    if constexpr (std::is_same_v<decltype(n_c), int>) run_steps_pow_plain(n_c);
-    else run_steps_pow_piped(n_c);
+  auto run_steps_pow = [&](auto n_c, int64_t tt0) SSM_INLINE {
+    if constexpr (std::is_same_v<decltype(n_c), int>) run_steps_pow_plain(n_c, tt0);
+    else run_steps_pow_piped(n_c, tt0);
   };
-  auto run_steps = [&](auto n_c) SSM_INLINE {
+  auto run_steps = [&](auto n_c, int64_t tt0) SSM_INLINE {
     if constexpr (kPow) {
       if (pow_mode) {
-        run_steps_pow(n_c);
+        run_steps_pow(n_c, tt0);
         return;
       }
     }
     const int n = n_c;
+    const int ph = (int)((t_begin + tt0) & 7);
     float2 v = sh_dtv[0][loff];
     float ar[NS], rr[NR];
 #pragma unroll
@@ -367,6 +383,7 @@ scan_chunk_kernel(ScanArgs a) {
           if constexpr (ZOH) rn[i] = zoh_ratio(an[i], u2);
         }
       }
+      if (ckpt_mode && ((ph + s) & 7) == 0) store_ckpt(tt0 + s);
       float y = 0.0f;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -432,7 +449,7 @@ scan_chunk_kernel(ScanArgs a) {
     if (!PASS_A && decltype(has_prev_c)::value) store(prev0, T, true);
     issue(bk, pf0, T);
     block_sync();
-    run_steps(std::integral_constant<int, T>());
+    run_steps(std::integral_constant<int, T>(), tt0);
     block_sync();
     if (!PASS_A) finish();
   };
@@ -447,7 +464,7 @@ scan_chunk_kernel(ScanArgs a) {
     commit(bk0);
     if (nfull > 1) issue(bk0, tail + T, T);
     block_sync();
-    run_steps(tail);
+    run_steps(tail, 0);
     block_sync();
     if (!PASS_A) {
       finish();
@@ -474,12 +491,12 @@ scan_chunk_kernel(ScanArgs a) {
     if (!PASS_A) store(last_full, T, true);
   }
 
-  if (PASS_A) {
+  if (PASS_A && !ckpt_mode) {
     float* dst = a.ws_state + (((int64_t)b * K + k) * Dn + dl) * kDState;
 #pragma unroll
     for (int i = 0; i < NS; ++i) dst[st_of(i)] = h[i];
     if (g == 0) a.ws_dtsum[((int64_t)b * K + k) * Dn + dl] = dtsum;
-  } else if (k == K - 1 && a.last_state != nullptr) {
+  } else if (!PASS_A && k == K - 1 && a.last_state != nullptr) {
     float* dst = a.last_state + ((int64_t)b * Dn + dl) * kDState;
 #pragma unroll
     for (int i = 0; i < NS; ++i) dst[st_of(i)] = h[i];
@@ -507,6 +524,11 @@ hipError_t launch_scan_w(const ScanArgs& a, hipStream_t s) {
   static const int occBz = resident_per_cu(kBz, NTHR);
   static const int occB = resident_per_cu(kB, NTHR);
   const unsigned nblk = (unsigned)((a.d_inner + kWave - 1) / kWave);
+  if (a.ckpt != nullptr) {  // the checkpoint pass over every chunk
+    if constexpr (NS != 4) return hipErrorInvalidValue;
+    launch_pass(kA, occA, dim3(nblk, (unsigned)a.n_chunks, (unsigned)a.batch), NTHR, a, s);
+    return hipGetLastError();
+  }
   if (a.n_chunks > 1) {
     launch_pass(kA, occA, dim3(nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch), NTHR, a, s);
     const hipError_t e = launch_carry(a, s);
