@@ -267,3 +267,17 @@ def test_workspace_pool_keeps_memory_until_trimmed():
         f"checkpoints {ckpt_bytes / 2**20:.0f} MiB")
     assert free2 >= free1 - ckpt_bytes // 4, "the second call mapped its workspace again"
     assert free3 - free2 >= ckpt_bytes // 2, "trimming did not return the workspace"
+
+
+@pytest.mark.parametrize("Dn", [70, 128])
+@pytest.mark.parametrize("L,chunk_len", [(203, None), (256, None), (203, 24), (300, 64)])
+def test_bwd_structured_A(Dn, L, chunk_len):
+    """A with rows (n + 1) A[d, 0]: the forward's checkpoint pass then forms the
+    transitions as powers of one exponential; ragged lengths put checkpoints inside
+    the forward's peeled first tile, and time chunks start it from carried states."""
+    say(f"backward, A rows (n + 1) A[d, 0]: batch 2, L {L}, d_inner {Dn}, chunk_len {chunk_len}")
+    inp, g, gl, h0 = _case(2, L, Dn, seed=17)
+    a0 = -np.exp(np.random.default_rng(170).uniform(-1.0, 1.5, Dn)).astype(np.float32)
+    inp["A"] = (np.arange(1, 17, dtype=np.float32)[None, :] * a0[:, None]).astype(np.float32)
+    got = _run(inp, g, gl, h0, chunk_len=chunk_len)
+    _compare(got, _ref(inp, g, gl, h0))
