@@ -105,6 +105,27 @@ def mix_ceiling(powers=False):
             "issue model (no valu-record in profiles/)")
 
 
+def backward_cycles():
+    """SIMD-cycles per wavefront state update of the backward on the workload's A,
+    from the VALU probe's issue rates: the forward kernel's checkpoint pass (the
+    powers update without its readout FMA: 17 of the 21 instructions per 4 updates),
+    the tile's recompute with readout (one exponential per update: the probe's
+    exponential mix), the reverse step (9 VALU per update) and the dB/dC lane sums
+    (18 VALU per step for 4 updates), the last two at the VALU rate of a stream that
+    carries exponentials (the exponential mix less its v_exp_f32, over its 4 VALU)."""
+    powers, src = mix_ceiling(True)
+    mix, _ = mix_ceiling(False)
+    rec = read_record("valu-record")
+    try:
+        exp_c = float(rec["cycles"]["v_exp_f32"]["8"])
+    except (TypeError, KeyError, ValueError):
+        exp_c = 8.3
+    valu_in_exp_stream = (mix - exp_c) / 4
+    parts = {"checkpoint_pass": powers * 17 / 21, "recompute": mix, "reverse": 9 * valu_in_exp_stream,
+             "lane_sums": 18 / 4 * valu_in_exp_stream}
+    return sum(parts.values()), {k: round(v, 2) for k, v in parts.items()}, src
+
+
 def alu_floor_us(updates, cycles):
     """Time of `updates` state updates at `cycles` SIMD-cycles per wavefront of 64,
     on every SIMD at the 2.4 GHz peak clock."""
@@ -404,18 +425,16 @@ def backward_case(cfg, steps=5):
     # single calls with a synchronisation after each: the workspace (about 840 MB)
     # is reused from the library's pool instead of being mapped again per call
     iso_avg, iso_med, _ = per_launch_ms(run, 5)
-    # VALU cycles per wavefront state update: the checkpoint forward (3 VALU +
-    # exp = 20), the tile's forward again with the readout (4 + exp = 24), the
-    # reverse step (11 VALU + exp = 52) and the lane reductions of dB, dC (~12)
-    cyc = 20 + 24 + 52 + 12
+    cyc, parts, src = backward_cycles()
     updates = cfg.batch * cfg.seqlen * cfg.d_inner * cfg.d_state
-    floor_us = updates / 64 * cyc / (SIMDS * CLOCK_HZ) * 1e6
+    floor_us = alu_floor_us(updates, cyc)
     del t, dout
     return {"workload": f"ssm_scan_bwd {cfg.name}: batch {cfg.batch}, seqlen {cfg.seqlen}, d_inner {cfg.d_inner}, "
                         "bf16 inputs and gradients, softplus, D, z",
             "us_per_call": round(ms * 1e3, 1), "isolated_call_us": {"avg": round(iso_avg * 1e3, 1),
                                                                     "median": round(iso_med * 1e3, 1)},
-            "alu_floor_us": round(floor_us, 1),
+            "alu_floor_us": round(floor_us, 1), "alu_cycles_per_wave_update": round(cyc, 2),
+            "alu_cycles_parts": parts, "alu_cycles_source": src,
             "alu_frac": round(floor_us / (ms * 1e3), 4), "long_sequence": backward_long_case()}
 
 
