@@ -428,14 +428,32 @@ def backward_case(cfg, steps=5):
     cyc, parts, src = backward_cycles()
     updates = cfg.batch * cfg.seqlen * cfg.d_inner * cfg.d_state
     floor_us = alu_floor_us(updates, cyc)
-    del t, dout
+    # a training step's scan: forward then backward, with the backward computing its
+    # checkpoints again, against the forward keeping them (ssm_scan_fwd_ckpt) and the
+    # backward reading them (ssm_scan_bwd_ckpt)
+    args = (t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"])
+    out = torch.empty(t["x"].shape, device="cuda")
+    ck = torch.empty((ssm.ssm_scan_ckpt_bytes(cfg.batch, cfg.seqlen, cfg.d_inner),), dtype=torch.uint8, device="cuda")
+    step = lambda: (ssm.ssm_scan_fwd_from(*args, out=out), ssm.ssm_scan_bwd(*args, softplus=True, dout=dout))
+    step_ck = lambda: (ssm.ssm_scan_fwd_ckpt(*args, out=out, ckpt=ck),
+                       ssm.ssm_scan_bwd(*args, softplus=True, dout=dout, ckpt=ck))
+    fwd_ck = lambda: ssm.ssm_scan_fwd_ckpt(*args, out=out, ckpt=ck)
+    bwd_ck = lambda: ssm.ssm_scan_bwd(*args, softplus=True, dout=dout, ckpt=ck)
+    tr = {}
+    for name, fn in (("forward_then_backward", step), ("forward_with_checkpoints_then_backward", step_ck),
+                     ("forward_with_checkpoints", fwd_ck), ("backward_from_checkpoints", bwd_ck)):
+        settle(fn, 0.05)
+        tr[name + "_us"] = round(time_steps(fn, steps, 1)[0] * 1e3, 1)
+    del t, dout, out, ck
     return {"workload": f"ssm_scan_bwd {cfg.name}: batch {cfg.batch}, seqlen {cfg.seqlen}, d_inner {cfg.d_inner}, "
                         "bf16 inputs and gradients, softplus, D, z",
             "us_per_call": round(ms * 1e3, 1), "isolated_call_us": {"avg": round(iso_avg * 1e3, 1),
                                                                     "median": round(iso_med * 1e3, 1)},
             "alu_floor_us": round(floor_us, 1), "alu_cycles_per_wave_update": round(cyc, 2),
             "alu_cycles_parts": parts, "alu_cycles_source": src,
-            "alu_frac": round(floor_us / (ms * 1e3), 4), "long_sequence": backward_long_case()}
+            "alu_frac": round(floor_us / (ms * 1e3), 4),
+            "training_step": dict(tr, checkpoint_bytes=ssm.ssm_scan_ckpt_bytes(cfg.batch, cfg.seqlen, cfg.d_inner)),
+            "long_sequence": backward_long_case()}
 
 
 def backward_long_case():

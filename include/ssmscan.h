@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 9
+#define SSM_ABI_VERSION 10
 
 /*
  * Bits of the step-flags argument (named `softplus` in the calls below):
@@ -267,6 +267,48 @@ ssm_status ssm_scan_bwd_plan(const void* x, const void* delta, const float* A, c
                              float* ddelta_bias, float* dinitial_state, int64_t batch,
                              int64_t seqlen, int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
                              ssm_dtype grad_dtype, void* stream, const ssm_plan* plan);
+
+/*
+ * The backward's checkpoints from the forward.  ssm_scan_bwd first runs the
+ * forward again to store the state entering every 8-step tile; a training
+ * step that has just run the forward can keep those states instead
+ * (vladkulikov.com, "Модуль 8. Альтернативы Transformer", section 7: the
+ * forward's recurrence gives the state at every step; the backward is the
+ * chain rule over the same recurrence).
+ *   ssm_scan_ckpt_bytes : size of the checkpoint buffer for these sizes:
+ *                         batch * ceil(d_inner / 64) * ceil(seqlen / 8) *
+ *                         1024 * 4 bytes (the Mamba-2.8B-like layer: 671 MB).
+ *   ssm_scan_fwd_ckpt   : ssm_scan_fwd_from (the planner's plan) that also
+ *                         stores the checkpoints in ckpt (device memory, 16-byte
+ *                         aligned, overlapping nothing else).  SSM_ZOH is
+ *                         rejected (so is it by the backward).  out and
+ *                         last_state are bitwise those of ssm_scan_fwd_from.
+ *   ssm_scan_bwd_ckpt   : ssm_scan_bwd reading those checkpoints instead of
+ *                         computing them; ckpt must come from
+ *                         ssm_scan_fwd_ckpt over the same inputs, initial state
+ *                         and step flags.  The gradients equal ssm_scan_bwd's
+ *                         to rounding, and bitwise where neither call's plan
+ *                         cuts the sequence into time chunks (chunked plans
+ *                         join chunks at different steps, so their states
+ *                         differ in rounding).
+ * The buffer's layout is the library's own; it is read and written only by
+ * these calls.  Otherwise as for ssm_scan_fwd_from and ssm_scan_bwd.
+ */
+ssm_status ssm_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int64_t* bytes);
+
+ssm_status ssm_scan_fwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int softplus,
+                             const float* initial_state, void* out, float* last_state, float* ckpt, int64_t batch,
+                             int64_t seqlen, int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
+                             ssm_dtype out_dtype, void* stream);
+
+ssm_status ssm_scan_bwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int softplus,
+                             const float* initial_state, const void* dout, const float* dlast_state,
+                             const float* ckpt, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                             void* dz, float* ddelta_bias, float* dinitial_state, int64_t batch, int64_t seqlen,
+                             int64_t d_inner, int64_t d_state, ssm_dtype in_dtype, ssm_dtype grad_dtype,
+                             void* stream);
 
 /*
  * The block's short causal depthwise convolution that feeds the scan (page

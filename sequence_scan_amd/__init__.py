@@ -11,6 +11,7 @@ Functions carry the C names: ``ssm_scan_fwd``, ``ssm_state_update``,
 ``ssm_scan_bwd``, ``ssm_scan_bwd_plan``, ``ssm_scan_bwd_plan_query``, ``ssm_conv1d_fwd``,
 ``ssm_conv1d_update``, ``ssm_ssd_fwd``, ``ssm_ssd_fwd_plan``, ``ssm_ssd_plan_query``, ``ssm_ssd_state_update``,
 ``ssm_affine_exclusive_scan``,
+``ssm_scan_ckpt_bytes``, ``ssm_scan_fwd_ckpt``, ``ssm_scan_bwd_ckpt`` (``ssm_scan_bwd(..., ckpt=)``),
 ``ssm_status_string``, ``ssm_last_error``, ``ssm_abi_version``, ``ssm_trim_workspace``.
 """
 from __future__ import annotations
@@ -75,6 +76,14 @@ def _load():
     lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_scan_bwd_plan.argtypes = lib.ssm_scan_bwd.argtypes + [ctypes.POINTER(ssm_plan)]
     lib.ssm_scan_bwd_plan.restype = ctypes.c_int
+    lib.ssm_scan_ckpt_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.ssm_scan_ckpt_bytes.restype = ctypes.c_int
+    lib.ssm_scan_fwd_ckpt.argtypes = [_vp] * 8 + [ctypes.c_int] + [_vp] * 4 + [_i64] * 4 + [ctypes.c_int,
+                                                                                       ctypes.c_int, _vp]
+    lib.ssm_scan_fwd_ckpt.restype = ctypes.c_int
+    lib.ssm_scan_bwd_ckpt.argtypes = [_vp] * 8 + [ctypes.c_int] + [_vp] * 13 + [_i64] * 4 + [ctypes.c_int,
+                                                                                        ctypes.c_int, _vp]
+    lib.ssm_scan_bwd_ckpt.restype = ctypes.c_int
     lib.ssm_scan_bwd_plan_query.argtypes = [_i64, _i64, _i64, _i64, ctypes.POINTER(ssm_plan)]
     lib.ssm_scan_bwd_plan_query.restype = ctypes.c_int
     lib.ssm_conv1d_fwd.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
@@ -260,6 +269,42 @@ def ssm_scan_fwd_from(x, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
                       last_state, out_dtype, stream, plan, zoh)
 
 
+def ssm_scan_ckpt_bytes(batch: int, seqlen: int, d_inner: int, d_state: int = D_STATE) -> int:
+    """Bytes of the backward's checkpoints for these sizes (``ssm_scan_fwd_ckpt``)."""
+    n = ctypes.c_int64(0)
+    _check(_load().ssm_scan_ckpt_bytes(batch, seqlen, d_inner, d_state, ctypes.byref(n)))
+    return int(n.value)
+
+
+def ssm_scan_fwd_ckpt(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                      initial_state=None, out=None, last_state=None, ckpt=None, out_dtype=None, stream=None):
+    """``ssm_scan_fwd_from`` that also keeps the backward's checkpoints.  Returns
+    (out, ckpt); ``ckpt`` (a uint8 device tensor of ``ssm_scan_ckpt_bytes`` bytes) is
+    allocated if None.  Pass it to ``ssm_scan_bwd(..., ckpt=ckpt)`` with the same inputs."""
+    import torch
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be [batch, seqlen, d_inner] and A [d_inner, d_state]")
+    batch, seqlen, d_inner = x.shape
+    d_state = A.shape[1]
+    f32, xs, bcs, st = torch.float32, (batch, seqlen, d_inner), (batch, seqlen, d_state), (batch, d_inner, d_state)
+    _expect(x, x=(x, xs, None), delta=(delta, xs, x.dtype), z=(z, xs, x.dtype), B=(B, bcs, x.dtype),
+            C=(C, bcs, x.dtype), A=(A, (d_inner, d_state), f32), D=(D, (d_inner,), f32),
+            delta_bias=(delta_bias, (d_inner,), f32), out=(out, xs, None), last_state=(last_state, st, f32),
+            initial_state=(initial_state, st, f32))
+    nbytes = ssm_scan_ckpt_bytes(batch, seqlen, d_inner, d_state)
+    if ckpt is None:
+        ckpt = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
+    elif ckpt.numel() * ckpt.element_size() < nbytes or not ckpt.is_contiguous() or ckpt.device != x.device:
+        raise ValueError(f"ckpt must be a contiguous tensor of at least {nbytes} bytes on {x.device}")
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(_load().ssm_scan_fwd_ckpt(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                     _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(out),
+                                     _ptr(last_state), _ptr(ckpt), batch, seqlen, d_inner, d_state,
+                                     _dtype_code(x), _dtype_code(out), _stream(stream)))
+    return out, ckpt
+
+
 def ssm_scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
                          initial_state=None, out=None, last_state=None, out_dtype=None, stream=None,
                          plan: Optional[dict] = None, zoh: bool = False):
@@ -306,13 +351,15 @@ def ssm_scan_bwd_plan_query(batch: int, seqlen: int, d_inner: int, d_state: int 
 
 def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, initial_state=None,
                  dout=None, dlast_state=None, want_dinitial_state: bool = False, grad_dtype=None, stream=None,
-                 plan: Optional[dict] = None):
+                 plan: Optional[dict] = None, ckpt=None):
     """Gradients of the scan (see include/ssmscan.h).  Forward inputs as for
     ``ssm_scan_fwd_from``; ``dout`` [batch, seqlen, d_inner] (its dtype is the gradient
     dtype unless ``grad_dtype`` is given); ``dlast_state`` optional.  Returns a dict with
     dx, ddelta, dA, dB, dC and, for the inputs given, dD, dz, ddelta_bias, and
     dinitial_state when ``want_dinitial_state``.  ``plan`` = {"states_per_wave": 4,
-    "chunk_len": ..} forces the time chunks (``ssm_scan_bwd_plan``)."""
+    "chunk_len": ..} forces the time chunks (``ssm_scan_bwd_plan``).  ``ckpt``: the
+    checkpoints of ``ssm_scan_fwd_ckpt`` over the same inputs (``ssm_scan_bwd_ckpt``:
+    the forward is not run again)."""
     import torch
     if x.dim() != 3 or dout is None:
         raise ValueError("x must be [batch, seqlen, d_inner] and dout given")
@@ -346,7 +393,14 @@ def ssm_scan_bwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: b
             _ptr(g.get("ddelta_bias")), _ptr(g.get("dinitial_state")), batch, seqlen, d_inner, d_state,
             _dtype_code(x), _dtype_code(g["dx"]), _stream(stream))
     lib = _load()
-    if plan is None:
+    if ckpt is not None:
+        if plan is not None:
+            raise ValueError("ssm_scan_bwd_ckpt runs the default plan")
+        nbytes = ssm_scan_ckpt_bytes(batch, seqlen, d_inner, d_state)
+        if ckpt.numel() * ckpt.element_size() < nbytes or not ckpt.is_contiguous() or ckpt.device != x.device:
+            raise ValueError(f"ckpt must be a contiguous tensor of at least {nbytes} bytes on {x.device}")
+        _check(lib.ssm_scan_bwd_ckpt(*args[:12], _ptr(ckpt), *args[12:]))
+    elif plan is None:
         _check(lib.ssm_scan_bwd(*args))
     else:
         _check(lib.ssm_scan_bwd_plan(*args, _plan_struct(plan)))

@@ -201,6 +201,16 @@ void choose_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_
 // 1.51 ms, the long single-row sequence (32 blocks, 262144 steps) 13.5 ms in
 // chunks of 1024 steps against 14.6 ms in chunks of 10928 and 184 ms in one.
 // At 512 blocks two chunks were slower (2.00 against 1.77 ms).
+// Bytes of the backward's checkpoints: the state entering every 8-step tile,
+// [batch, ceil(d_inner / 64), ceil(seqlen / 8), 64, 16] fp32.
+ssm_status ckpt_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t* bytes) {
+  const int64_t nblk = (d_inner + 63) / 64, ntiles = (seqlen + ssm::kBwdTile - 1) / ssm::kBwdTile;
+  int64_t n;
+  if (!mul_ok(batch * nblk, ntiles * 64 * ssm::kDState, &n) || !mul_ok(n, 4, bytes))
+    return fail(SSM_ERR_BAD_SHAPE, "checkpoint size overflows int64");
+  return SSM_OK;
+}
+
 void choose_bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int simds, ssm_plan* p) {
   const int64_t blocks = std::max<int64_t>(1, batch * ((d_inner + 63) / 64));
   const int64_t cus = std::max(1, simds / 4);
@@ -297,11 +307,16 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
                      const float* D, const void* z, const float* delta_bias, int softplus, const float* h0,
                      void* out, float* last_state, int64_t batch, int64_t seqlen, int64_t d_inner,
                      int64_t d_state, ssm_dtype in_dtype, ssm_dtype out_dtype, void* stream,
-                     const ssm_plan* plan_in, bool fixed_scratch = false) {
+                     const ssm_plan* plan_in, bool fixed_scratch = false, float* ckpt = nullptr) {
   Sizes sz;
   ssm_status st = check_common(batch, seqlen, d_inner, d_state, in_dtype, out_dtype, &sz);
   if (st != SSM_OK) return st;
   if ((st = check_flags(softplus, true)) != SSM_OK) return st;
+  int64_t ckpt_bytes = 0;
+  if (ckpt != nullptr) {
+    if (softplus & SSM_ZOH) return fail(SSM_ERR_UNSUPPORTED, "checkpoints are for the backward, which rejects SSM_ZOH");
+    if ((st = ckpt_size(batch, seqlen, d_inner, &ckpt_bytes)) != SSM_OK) return st;
+  }
   // a required pointer may be NULL only when its tensor is empty
   const bool need_e = sz.elems > 0, need_bc = sz.bc > 0, need_a = d_inner > 0;
   if ((need_e && (!x || !delta || !out)) || (need_a && !A) || (need_bc && (!B || !C))) {
@@ -309,10 +324,10 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
                       : (need_bc && !B) ? "B" : (need_bc && !C) ? "C" : "out";
     return fail(SSM_ERR_NULL_ARG, "required pointer %s is NULL", which);
   }
-  const void* ptrs[] = {x, delta, A, B, C, D, z, delta_bias, out, last_state, h0};
+  const void* ptrs[] = {x, delta, A, B, C, D, z, delta_bias, out, last_state, h0, ckpt};
   const char* names[] = {"x", "delta", "A", "B", "C", "D", "z", "delta_bias", "out", "last_state",
-                         "initial_state"};
-  for (int i = 0; i < 11; ++i)
+                         "initial_state", "ckpt"};
+  for (int i = 0; i < 12; ++i)
     if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
   const int64_t si = esize(in_dtype), so = esize(out_dtype);
   const Range ins[] = {
@@ -333,6 +348,11 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   // the final state may replace the initial one in place, but not overlap it otherwise
   const bool h0_in_place = h0 != nullptr && static_cast<const void*>(h0) == static_cast<const void*>(last_state);
   if (!h0_in_place && overlaps(rl, rh)) return fail(SSM_ERR_UNSUPPORTED, "last_state partly overlaps initial_state");
+  const Range rc = range("ckpt", ckpt, ckpt_bytes);
+  for (const Range& r : ins)
+    if (overlaps(rc, r)) return fail(SSM_ERR_UNSUPPORTED, "ckpt overlaps input %s", r.name);
+  if (overlaps(rc, ro) || overlaps(rc, rl) || overlaps(rc, rh))
+    return fail(SSM_ERR_UNSUPPORTED, "ckpt overlaps out, last_state or initial_state");
 
   ssm_plan plan;
   if (plan_in) {
@@ -378,6 +398,11 @@ ssm_status scan_impl(const void* x, const void* delta, const float* A, const voi
   a.zoh = (softplus & SSM_ZOH) ? 1 : 0;
   a.batch = (int32_t)batch;
   a.cus = device_simds() / 4;
+  if (ckpt != nullptr) {  // the default plan: 4 states per wavefront, chunks of a multiple of 32 steps
+    a.ckpt = ckpt;
+    a.ckpt_nblk = (int32_t)((d_inner + 63) / 64);
+    a.ckpt_tiles = (seqlen + ssm::kBwdTile - 1) / ssm::kBwdTile;
+  }
 
   void* ws = nullptr;       // a stream-ordered allocation, freed below
   hipError_t e = hipSuccess;
@@ -573,7 +598,8 @@ static ssm_status bwd_impl(const void* x, const void* delta, const float* A, con
                            const float* initial_state, const void* dout, const float* dlast_state, void* dx,
                            void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
                            float* dinitial_state, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                           ssm_dtype in_dtype, ssm_dtype grad_dtype, void* stream, const ssm_plan* plan_in) {
+                           ssm_dtype in_dtype, ssm_dtype grad_dtype, void* stream, const ssm_plan* plan_in,
+                           const float* ckpt_in = nullptr) {
   Sizes sz;
   ssm_status st = check_common(batch, seqlen, d_inner, d_state, in_dtype, grad_dtype, &sz);
   if (st != SSM_OK) return st;
@@ -597,6 +623,10 @@ static ssm_status bwd_impl(const void* x, const void* delta, const float* A, con
                          "dinitial_state"};
   for (int i = 0; i < 20; ++i)
     if ((st = check_align(names[i], ptrs[i])) != SSM_OK) return st;
+  if ((st = check_align("ckpt", ckpt_in)) != SSM_OK) return st;
+  int64_t ckpt_bytes = 0;
+  if (ckpt_in != nullptr && (st = ckpt_size(batch, seqlen, d_inner, &ckpt_bytes)) != SSM_OK) return st;
+  const Range rck = range("ckpt", ckpt_in, ckpt_bytes);
   const int64_t si = esize(in_dtype), sg = esize(grad_dtype);
   const Range ins[] = {
       range("x", x, sz.elems * si),          range("delta", delta, sz.elems * si),
@@ -614,6 +644,7 @@ static ssm_status bwd_impl(const void* x, const void* delta, const float* A, con
       range("dinitial_state", dinitial_state, sz.state * 4),
   };
   for (int i = 0; i < 9; ++i) {
+    if (overlaps(outs[i], rck)) return fail(SSM_ERR_UNSUPPORTED, "%s overlaps input ckpt", outs[i].name);
     for (const Range& r : ins)
       if (overlaps(outs[i], r)) return fail(SSM_ERR_UNSUPPORTED, "%s overlaps input %s", outs[i].name, r.name);
     for (int j = 0; j < i; ++j)
@@ -657,7 +688,9 @@ static ssm_status bwd_impl(const void* x, const void* delta, const float* A, con
   // per (row, chunk): dA partials, dD / dbias partials; chunked runs also
   // keep each chunk's entering state, arriving gradient and reverse pair
   int64_t n_ck, n_bc, n_a, n_dd, n_cs, n_cd, bytes;
-  if (!mul_ok(batch * nblk, ntiles * 64 * d_state, &n_ck) || !mul_ok(sz.bc / d_state, nblk * 2 * d_state, &n_bc) ||
+  // (the checkpoints live in the workspace unless the caller hands them in)
+  if (!mul_ok(batch * nblk, ckpt_in ? 0 : ntiles * 64 * d_state, &n_ck) ||
+      !mul_ok(sz.bc / d_state, nblk * 2 * d_state, &n_bc) ||
       !mul_ok(sz.state, K, &n_a) || !mul_ok(batch * d_inner, 2 * K, &n_dd) ||
       !mul_ok(sz.state, K > 1 ? K : 0, &n_cs) || !mul_ok(batch * d_inner, K > 1 ? K : 0, &n_cd) ||
       !mul_ok(n_ck + n_bc + n_a + n_dd + 3 * n_cs + 2 * n_cd, 4, &bytes))
@@ -681,8 +714,9 @@ static ssm_status bwd_impl(const void* x, const void* delta, const float* A, con
   a.dx = dx;
   a.ddelta = ddelta;
   a.dz = dz;
-  a.ws_ckpt = static_cast<float*>(ws);
-  a.ws_bc = a.ws_ckpt + n_ck;
+  a.ws_ckpt = ckpt_in ? const_cast<float*>(ckpt_in) : static_cast<float*>(ws);  // read only when given
+  a.ckpt_given = ckpt_in ? 1 : 0;
+  a.ws_bc = static_cast<float*>(ws) + n_ck;
   a.ws_a = a.ws_bc + n_bc;
   a.ws_dd = a.ws_a + n_a;
   if (K > 1) {
@@ -717,6 +751,39 @@ ssm_status ssm_scan_bwd(const void* x, const void* delta, const float* A, const 
   return bwd_impl(x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, dout, dlast_state, dx, ddelta, dA,
                   dB, dC, dD, dz, ddelta_bias, dinitial_state, batch, seqlen, d_inner, d_state, in_dtype, grad_dtype,
                   stream, nullptr);
+}
+
+ssm_status ssm_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int64_t* bytes) {
+  if (!bytes) return fail(SSM_ERR_NULL_ARG, "bytes is NULL");
+  if (batch < 0 || seqlen < 0 || d_inner < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "negative size (batch=%lld seqlen=%lld d_inner=%lld)", (long long)batch,
+                (long long)seqlen, (long long)d_inner);
+  if (d_state != ssm::kDState)
+    return fail(SSM_ERR_UNSUPPORTED, "d_state=%lld is not supported (16)", (long long)d_state);
+  return ckpt_size(batch, seqlen, d_inner, bytes);
+}
+
+ssm_status ssm_scan_fwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int softplus,
+                             const float* initial_state, void* out, float* last_state, float* ckpt, int64_t batch,
+                             int64_t seqlen, int64_t d_inner, int64_t d_state, ssm_dtype in_dtype,
+                             ssm_dtype out_dtype, void* stream) {
+  if (!ckpt && batch > 0 && seqlen > 0 && d_inner > 0) return fail(SSM_ERR_NULL_ARG, "required pointer ckpt is NULL");
+  return scan_impl(x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, out, last_state, batch, seqlen,
+                   d_inner, d_state, in_dtype, out_dtype, stream, nullptr, false, ckpt);
+}
+
+ssm_status ssm_scan_bwd_ckpt(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int softplus,
+                             const float* initial_state, const void* dout, const float* dlast_state,
+                             const float* ckpt, void* dx, void* ddelta, float* dA, void* dB, void* dC, float* dD,
+                             void* dz, float* ddelta_bias, float* dinitial_state, int64_t batch, int64_t seqlen,
+                             int64_t d_inner, int64_t d_state, ssm_dtype in_dtype, ssm_dtype grad_dtype,
+                             void* stream) {
+  if (!ckpt && batch > 0 && seqlen > 0 && d_inner > 0) return fail(SSM_ERR_NULL_ARG, "required pointer ckpt is NULL");
+  return bwd_impl(x, delta, A, B, C, D, z, delta_bias, softplus, initial_state, dout, dlast_state, dx, ddelta, dA,
+                  dB, dC, dD, dz, ddelta_bias, dinitial_state, batch, seqlen, d_inner, d_state, in_dtype, grad_dtype,
+                  stream, nullptr, ckpt);
 }
 
 ssm_status ssm_scan_bwd_plan(const void* x, const void* delta, const float* A, const void* B, const void* C,

@@ -640,14 +640,17 @@ ScanArgs forward_args(const BwdArgs& a) {
 }
 
 // The chunked backward's carries: each chunk's entering state (the forward's
-// pass A and carry, run by the forward scan's own launcher), then each
-// chunk's arriving gradient (reverse pass A, reverse carry).
+// pass A and carry, run by the forward scan's own launcher; only to start the
+// checkpoint pass, so not when the checkpoints are given), then each chunk's
+// arriving gradient (reverse pass A, reverse carry).
 template <typename Tin, typename Tg>
 hipError_t launch_bwd_carries(const BwdArgs& a, DT in, hipStream_t s) {
-  ScanArgs f = forward_args(a);
-  f.states_only = 1;
-  hipError_t e = launch_scan(f, in, DT::F32, 4, s);
-  if (e != hipSuccess) return e;
+  if (!a.ckpt_given) {
+    ScanArgs f = forward_args(a);
+    f.states_only = 1;
+    const hipError_t e = launch_scan(f, in, DT::F32, 4, s);
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)a.nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch);
   // the wide items need rows that split into aligned groups of 8
   const bool wide = a.d_inner % 8 == 0;
@@ -670,8 +673,10 @@ hipError_t launch_scan_bwd_t(const BwdArgs& a, DT in, float* dA, void* dB, void*
   // the state entering every 8-step tile, from the forward scan kernel's
   // checkpoint pass (after the chunk carry, whose states it starts from)
   auto checkpoints = [&]() {
+    if (a.ckpt_given) return hipSuccess;
     ScanArgs f = forward_args(a);
     f.ckpt = a.ws_ckpt;
+    f.ckpt_only = 1;
     f.ckpt_nblk = a.nblk;
     f.ckpt_tiles = (a.seqlen + kBwdTile - 1) / kBwdTile;
     return launch_scan(f, in, DT::F32, 4, s);

@@ -38,16 +38,18 @@ struct ScanArgs {
   int32_t fair;           // set by the launcher: the whole grid is co-resident
   int32_t states_only;    // chunked runs: stop after the carry pass (ws_state then holds
                           // the state entering chunk k + 1 in slot k); no out is written
-  // Checkpoint pass (ckpt != nullptr; 4 states per wavefront): instead of a scan,
-  // run every chunk from its entering state (chunk 0: h0; chunk k > 0: slot k - 1
-  // of ws_state, left by a states_only run) without readout or output, and store
-  // the state entering every global step t with t % 8 == 0 at
-  // ckpt[((b * ckpt_nblk + block) * ckpt_tiles + t / 8) * 1024 + lane * 16 + 4 g + i],
-  // which holds state g + 4 i of channel d0 + lane (lanes past d_inner repeat the
-  // last channel).  Chunk lengths must be multiples of 8.
+  // Checkpoints (ckpt != nullptr; 4 states per wavefront; chunk lengths
+  // multiples of 8): the state entering every global step t with t % 8 == 0 is
+  // stored at ckpt[((b * ckpt_nblk + block) * ckpt_tiles + t / 8) * 1024 +
+  // lane * 16 + 4 g + i], which holds state g + 4 i of channel d0 + lane (lanes
+  // past d_inner repeat the last channel).  With ckpt_only the launch is only
+  // that: every chunk runs from its entering state (chunk 0: h0; chunk k > 0:
+  // slot k - 1 of ws_state, left by a states_only run) without readout or
+  // output.  Without it the scan runs as usual and its pass B stores them.
   float* ckpt;
   int64_t ckpt_tiles;
   int32_t ckpt_nblk;
+  int32_t ckpt_only;
 };
 
 struct DecodeArgs {
@@ -141,6 +143,7 @@ struct BwdArgs {
   float* ws_rev;          // [.., 16] slot k: dL/d(state entering chunk k) when none arrives at its end
   float* ws_rsum;         // [..] slot k: chunk k's step-size sum (log2 units)
   float* ws_dl;           // [.., 16] slot k: dL/d(state after chunk k), k < n_chunks - 1
+  int32_t ckpt_given;     // ws_ckpt holds the forward's checkpoints already (ssm_scan_fwd_ckpt)
   int64_t seqlen;
   int64_t d_inner;
   int64_t chunk_len;      // steps per chunk: a multiple of kBwdTile unless n_chunks == 1

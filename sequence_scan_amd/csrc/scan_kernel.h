@@ -47,7 +47,7 @@ namespace {
 // exactly, once, and otherwise runs the exponentials.  With NS == 4, wave g
 // carries the states n = g + 4 i (i < 4), so its transitions are
 // e^(g+1) * (e^4)^i; B and C rows are staged in that order.
-template <typename Tin, typename Tout, int NS, bool PASS_A, bool HAS_Z, bool WIDE, bool ZOH>
+template <typename Tin, typename Tout, int NS, bool PASS_A, bool HAS_Z, bool WIDE, bool ZOH, bool CKPT = false>
 __global__ void __launch_bounds__(kWave * (kDState / NS))
 scan_chunk_kernel(ScanArgs a) {
   constexpr int G = kDState / NS;         // wavefronts per workgroup (state groups)
@@ -140,9 +140,10 @@ scan_chunk_kernel(ScanArgs a) {
     }
   }
 
-  // checkpoint pass (see ScanArgs::ckpt): pass A's instance, run from each
-  // chunk's entering state, storing the state every 8 steps
-  const bool ckpt_mode = PASS_A && NS == 4 && a.ckpt != nullptr;
+  // checkpoints (see ScanArgs::ckpt), a separate instance: stored by pass B,
+  // or by pass A's instance run from each chunk's entering state (ckpt_only).
+  // (A runtime switch in the ordinary instances cost 10 % on the layer.)
+  constexpr bool ckpt_mode = CKPT && NS == 4;
   float h[NS];
   if ((!PASS_A || ckpt_mode) && k > 0) {
     const float* src = a.ws_state + (((int64_t)b * K + (k - 1)) * Dn + dl) * kDState;
@@ -162,7 +163,7 @@ scan_chunk_kernel(ScanArgs a) {
                                : nullptr;
   // the state entering chunk-relative step tt (t_begin + tt a multiple of 8)
   auto store_ckpt = [&](int64_t tt) SSM_INLINE {
-    if constexpr (PASS_A && NS == 4)
+    if constexpr (NS == 4)
       *reinterpret_cast<float4*>(ckb + ((t_begin + tt) >> 3) * (kWave * kDState)) = make_float4(h[0], h[1], h[2], h[3]);
   };
 
@@ -524,10 +525,17 @@ hipError_t launch_scan_w(const ScanArgs& a, hipStream_t s) {
   static const int occBz = resident_per_cu(kBz, NTHR);
   static const int occB = resident_per_cu(kB, NTHR);
   const unsigned nblk = (unsigned)((a.d_inner + kWave - 1) / kWave);
-  if (a.ckpt != nullptr) {  // the checkpoint pass over every chunk
-    if constexpr (NS != 4) return hipErrorInvalidValue;
-    launch_pass(kA, occA, dim3(nblk, (unsigned)a.n_chunks, (unsigned)a.batch), NTHR, a, s);
-    return hipGetLastError();
+  if (a.ckpt != nullptr) {
+    if constexpr (NS == 4 && !ZOH) {
+      if (a.ckpt_only) {  // the checkpoint pass over every chunk
+        const auto kC = scan_chunk_kernel<Tin, Tout, NS, true, false, WIDE, ZOH, true>;
+        static const int occC = resident_per_cu(kC, NTHR);
+        launch_pass(kC, occC, dim3(nblk, (unsigned)a.n_chunks, (unsigned)a.batch), NTHR, a, s);
+        return hipGetLastError();
+      }
+    } else {
+      return hipErrorInvalidValue;
+    }
   }
   if (a.n_chunks > 1) {
     launch_pass(kA, occA, dim3(nblk, (unsigned)(a.n_chunks - 1), (unsigned)a.batch), NTHR, a, s);
@@ -536,6 +544,17 @@ hipError_t launch_scan_w(const ScanArgs& a, hipStream_t s) {
   }
   if (a.states_only) return hipGetLastError();
   const dim3 gridB(nblk, (unsigned)a.n_chunks, (unsigned)a.batch);
+  if constexpr (NS == 4 && !ZOH) {
+    if (a.ckpt != nullptr) {  // pass B that also stores the checkpoints
+      const auto kBzC = scan_chunk_kernel<Tin, Tout, NS, false, true, WIDE, ZOH, true>;
+      const auto kBC = scan_chunk_kernel<Tin, Tout, NS, false, false, WIDE, ZOH, true>;
+      static const int occBzC = resident_per_cu(kBzC, NTHR);
+      static const int occBC = resident_per_cu(kBC, NTHR);
+      if (a.z != nullptr) launch_pass(kBzC, occBzC, gridB, NTHR, a, s);
+      else launch_pass(kBC, occBC, gridB, NTHR, a, s);
+      return hipGetLastError();
+    }
+  }
   if (a.z != nullptr) launch_pass(kBz, occBz, gridB, NTHR, a, s);
   else launch_pass(kB, occB, gridB, NTHR, a, s);
   return hipGetLastError();

@@ -158,6 +158,26 @@ void scan_rejections() {
   expect("a valid call after the failure", s.from(s.h0, s.last, &p, false), SSM_OK);
 }
 
+void checkpoint_calls() {
+  for (ssm_dtype in : {SSM_F32, SSM_BF16})
+    for (int64_t L : {37, 3000}) {   // one chunk; chunks (3000 steps, 2 x 70 channels: the planner cuts it)
+      Scan s(2, L, 70, in, SSM_F32);
+      int64_t bytes = 0;
+      expect("scan_ckpt_bytes", ssm_scan_ckpt_bytes(2, L, 70, 16, &bytes), SSM_OK);
+      float* ck = static_cast<float*>(buf(bytes / 4, 4));
+      expect("scan_fwd_ckpt", ssm_scan_fwd_ckpt(s.x, s.dl, s.A, s.B, s.C, s.D, s.z, s.bias, SSM_SOFTPLUS, s.h0, s.y,
+                                                s.last, ck, 2, L, 70, 16, in, SSM_F32, nullptr), SSM_OK);
+      const int64_t n = 2 * L * 70, r = 2 * L;
+      void *dout = buf(n, es(in)), *dx = buf(n, es(in)), *ddl = buf(n, es(in)), *dz = buf(n, es(in));
+      void *dB = buf(r * 16, es(in)), *dC = buf(r * 16, es(in));
+      float *dA = static_cast<float*>(buf(70 * 16, 4)), *dD = static_cast<float*>(buf(70, 4));
+      float* dbias = static_cast<float*>(buf(70, 4));
+      expect("scan_bwd_ckpt", ssm_scan_bwd_ckpt(s.x, s.dl, s.A, s.B, s.C, s.D, s.z, s.bias, SSM_SOFTPLUS, s.h0, dout,
+                                                nullptr, ck, dx, ddl, dA, dB, dC, dD, dz, dbias, nullptr, 2, L, 70, 16,
+                                                in, in, nullptr), SSM_OK);
+    }
+}
+
 void decode_calls() {
   for (ssm_dtype in : {SSM_F32, SSM_BF16}) {
     const int64_t b = 3, d = 70;
@@ -270,6 +290,7 @@ int main() {
   scan_rejections();
   decode_calls();
   bwd_calls();
+  checkpoint_calls();
   conv_calls();
   ssd_calls();
   if (fake_live_allocs() != 0) {

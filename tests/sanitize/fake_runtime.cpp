@@ -119,6 +119,12 @@ hipError_t launch_scan(const ScanArgs& a, DT in, DT out, int states_per_wave, hi
     touch("ws_state", a.ws_state, states * a.n_chunks, 4);
     touch("ws_dtsum", a.ws_dtsum, (int64_t)a.batch * a.n_chunks * a.d_inner, 4);
   }
+  if (a.ckpt) {
+    if (states_per_wave != 4 || a.ckpt_nblk != (a.d_inner + 63) / 64 || a.ckpt_tiles != (a.seqlen + 7) / 8 ||
+        (a.n_chunks > 1 && a.chunk_len % 8 != 0))
+      std::abort();
+    touch("ckpt", a.ckpt, (int64_t)a.batch * a.ckpt_nblk * a.ckpt_tiles * 1024, 4);
+  }
   ++g_launches;
   return hipSuccess;
 }

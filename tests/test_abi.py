@@ -24,13 +24,14 @@ def test_every_declared_function_is_exported():
             "ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_affine_exclusive_scan", "ssm_status_string",
             "ssm_last_error", "ssm_abi_version", "ssm_scan_bwd", "ssm_scan_bwd_plan", "ssm_scan_bwd_plan_query",
             "ssm_ssd_fwd", "ssm_ssd_fwd_plan", "ssm_ssd_plan_query", "ssm_ssd_state_update",
-            "ssm_scan_fwd_noalloc", "ssm_trim_workspace"} <= set(names)
+            "ssm_scan_fwd_noalloc", "ssm_trim_workspace", "ssm_scan_ckpt_bytes", "ssm_scan_fwd_ckpt",
+            "ssm_scan_bwd_ckpt"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssmscan.h but not exported"
 
 
 def test_version_and_strings():
-    assert ssm.ssm_abi_version() == 9
+    assert ssm.ssm_abi_version() == 10
     for code, name in ssm.STATUS_NAMES.items():
         assert ssm.ssm_status_string(code).startswith(name)
     assert "unknown" in ssm.ssm_status_string(99)
@@ -211,6 +212,36 @@ def test_noalloc_rejections():
     assert run(0, 2048, 5120, 128) == ssm.SSM_OK          # empty: nothing to do, nothing looked up
     assert lib.ssm_scan_fwd_noalloc(P, P + G, P + 2 * G, P + 3 * G, P + 4 * G, None, None, None, 4, None,
                                     P + 5 * G, None, 1, 8, 64, 16, F32, F32, None, None) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_checkpoint_calls_rejections():
+    """The calls that hand the backward's checkpoints from the forward: their size, and
+    the host checks of ssm_scan_fwd_ckpt / ssm_scan_bwd_ckpt (nothing is enqueued)."""
+    lib = ssm.library()
+    G = 0x10000000000  # 1 TiB apart: the fake tensors never overlap
+    assert ssm.ssm_scan_ckpt_bytes(8, 2048, 5120) == 8 * 80 * 256 * 1024 * 4
+    assert ssm.ssm_scan_ckpt_bytes(2, 37, 70) == 2 * 2 * 5 * 1024 * 4       # ragged tiles and channel blocks
+    n = ctypes.c_int64(0)
+    assert lib.ssm_scan_ckpt_bytes(8, 2048, 5120, 8, ctypes.byref(n)) == ssm.SSM_ERR_UNSUPPORTED
+    assert lib.ssm_scan_ckpt_bytes(8, -1, 5120, 16, ctypes.byref(n)) == ssm.SSM_ERR_BAD_SHAPE
+    assert lib.ssm_scan_ckpt_bytes(8, 2048, 5120, 16, None) == ssm.SSM_ERR_NULL_ARG
+
+    def fwd(ckpt, flags=1, out=P + 5 * G):
+        return lib.ssm_scan_fwd_ckpt(P, P + G, P + 2 * G, P + 3 * G, P + 4 * G, None, None, None, flags, None, out,
+                                     None, ckpt, 8, 2048, 5120, 16, BF16, F32, None)
+    assert fwd(None) == ssm.SSM_ERR_NULL_ARG and "ckpt" in ssm.ssm_last_error()
+    assert fwd(P + 6 * G, flags=3) == ssm.SSM_ERR_UNSUPPORTED and "ZOH" in ssm.ssm_last_error()
+    assert fwd(P + 6 * G + 4) == ssm.SSM_ERR_UNSUPPORTED and "aligned" in ssm.ssm_last_error()
+    assert fwd(P + 5 * G + 1024) == ssm.SSM_ERR_UNSUPPORTED and "ckpt" in ssm.ssm_last_error()  # inside out
+    assert fwd(P + G) == ssm.SSM_ERR_UNSUPPORTED and "ckpt" in ssm.ssm_last_error()             # on delta
+
+    def bwd(ckpt, dx=P + 7 * G):
+        return lib.ssm_scan_bwd_ckpt(P, P + G, P + 2 * G, P + 3 * G, P + 4 * G, None, None, None, 1, None, P + 5 * G,
+                                     None, ckpt, dx, P + 8 * G, P + 9 * G, P + 10 * G, P + 11 * G, None, None, None,
+                                     None, 8, 2048, 5120, 16, BF16, BF16, None)
+    assert bwd(None) == ssm.SSM_ERR_NULL_ARG and "ckpt" in ssm.ssm_last_error()
+    assert bwd(P + 6 * G + 8) == ssm.SSM_ERR_UNSUPPORTED and "aligned" in ssm.ssm_last_error()
+    assert bwd(P + 6 * G, dx=P + 6 * G + 4096) == ssm.SSM_ERR_UNSUPPORTED and "ckpt" in ssm.ssm_last_error()
 
 
 def test_failed_workspace_allocation_is_reported():

@@ -281,3 +281,43 @@ def test_bwd_structured_A(Dn, L, chunk_len):
     inp["A"] = (np.arange(1, 17, dtype=np.float32)[None, :] * a0[:, None]).astype(np.float32)
     got = _run(inp, g, gl, h0, chunk_len=chunk_len)
     _compare(got, _ref(inp, g, gl, h0))
+
+
+@pytest.mark.parametrize("batch,L,Dn,dtype,a_kind", [(2, 37, 70, "f32", "random"), (2, 300, 128, "bf16", "random"),
+                                                     (1, 3000, 64, "bf16", "structured"),
+                                                     (2, 203, 65, "f32", "structured")])
+def test_checkpoints_from_the_forward(batch, L, Dn, dtype, a_kind):
+    """ssm_scan_fwd_ckpt keeps the backward's checkpoints while it scans: its out and
+    last_state equal ssm_scan_fwd_from's bit for bit.  ssm_scan_bwd_ckpt from them equals
+    ssm_scan_bwd bit for bit where neither planner cuts the sequence (the checkpoints are
+    then the same states); the 3000-step case is cut, at different points by the two
+    planners, so its checkpoints differ by rounding and its gradients are held to the
+    oracle instead."""
+    say(f"checkpoints from the forward: batch {batch}, L {L}, d_inner {Dn}, {dtype}, A {a_kind}")
+    inp, g, gl, h0 = _case(batch, L, Dn, dtype=dtype, seed=31)
+    if a_kind == "structured":
+        a0 = -np.exp(np.random.default_rng(310).uniform(-1.0, 1.5, Dn)).astype(np.float32)
+        inp["A"] = (np.arange(1, 17, dtype=np.float32)[None, :] * a0[:, None]).astype(np.float32)
+    t = to_dev(inp)
+    h0t = torch.from_numpy(h0).cuda()
+    last1 = torch.empty((batch, Dn, 16), device="cuda")
+    last2 = torch.empty((batch, Dn, 16), device="cuda")
+    out1 = ssm.ssm_scan_fwd_from(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                                 initial_state=h0t, last_state=last1, out_dtype=torch.float32)
+    out2, ck = ssm.ssm_scan_fwd_ckpt(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                                     initial_state=h0t, last_state=last2, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(last1, last2)
+    dout = torch.from_numpy(g).cuda()   # fp32 gradients, held to the oracle's bar where compared with it
+    dlast = torch.from_numpy(gl).cuda()
+    kw = dict(softplus=True, initial_state=h0t, dout=dout, dlast_state=dlast, want_dinitial_state=True)
+    ref = ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], **kw)
+    got = ssm.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], ckpt=ck,
+                           **kw)
+    torch.cuda.synchronize()
+    cut = (ssm.ssm_scan_plan(batch, L, Dn)["n_chunks"] > 1 or ssm.ssm_scan_bwd_plan_query(batch, L, Dn)["n_chunks"] > 1)
+    if not cut:
+        for k in ref:
+            assert torch.equal(ref[k], got[k]), k
+    else:
+        _compare({k: v.float().cpu().numpy() for k, v in got.items()}, _ref(inp, g, gl, h0))
