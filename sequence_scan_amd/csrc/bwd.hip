@@ -564,21 +564,46 @@ __global__ void __launch_bounds__(256) bwd_rev_carry_kernel(BwdArgs a) {
   }
 }
 
-// dB, dC: sum the per-block partials in block order (dB also takes the ln 2).
+// dB, dC: sum the per-block partials (dB also takes the ln 2).  One wavefront
+// per (batch row, step): that row's nblk x 32 partials are contiguous, so the
+// wavefront reads them with 16-byte loads, lane l taking float4s l, l + 64, ...
+// Every such float4 holds values 4(l % 8) .. 4(l % 8) + 3 of one block, so
+// each lane sums its blocks in order and the 8 lanes with equal l % 8 then
+// combine theirs (xor 8, 16, 32): a fixed order, the same on every call.
 template <typename Tg>
 __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(const float* ws_bc, Tg* dB, Tg* dC, int64_t rows,
                                                             int nblk) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * 2 * kDState) return;
-  const int64_t row = i / (2 * kDState);
-  const int w = (int)(i % (2 * kDState));
-  float acc = 0.0f;
-  for (int k = 0; k < nblk; ++k) acc += ws_bc[(row * nblk + k) * (2 * kDState) + w];
-  Tg* dst = w < kDState ? dB : dC;
-  const float v = w < kDState ? acc * kLn2 : acc;
-  const int64_t o = row * kDState + (w % kDState);
-  if constexpr (sizeof(Tg) == 4) dst[o] = v;
-  else dst[o] = f32_to_bf16_rne(v);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float4* src = reinterpret_cast<const float4*>(ws_bc + row * nblk * (2 * kDState));
+  const int n4 = nblk * (2 * kDState / 4);
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+  for (int q = lane; q < n4; q += kWave) {
+    const float4 v = src[q];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+#pragma unroll
+  for (int m = 8; m < kWave; m <<= 1) {
+    acc.x += __shfl_xor(acc.x, m);
+    acc.y += __shfl_xor(acc.y, m);
+    acc.z += __shfl_xor(acc.z, m);
+    acc.w += __shfl_xor(acc.w, m);
+  }
+  if (lane >= 8) return;
+  const bool isB = lane < 4;
+  Tg* dst = (isB ? dB : dC) + row * kDState + 4 * (lane & 3);
+  const float f = isB ? kLn2 : 1.0f;
+  const float v[4] = {acc.x * f, acc.y * f, acc.z * f, acc.w * f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (sizeof(Tg) == 4) dst[j] = v[j];
+    else dst[j] = f32_to_bf16_rne(v[j]);
+  }
 }
 
 // dA, dD, dbias: sum the per-(row, chunk) partials in order (`batch` counts
@@ -701,8 +726,7 @@ hipError_t launch_scan_bwd_t(const BwdArgs& a, DT in, float* dA, void* dB, void*
       else launch_bwd_pass(scan_bwd_kernel<Tin, Tg, false, 1>, grid, a, s);
     }
     const int64_t rows = (int64_t)a.batch * a.seqlen;
-    const int64_t n = rows * 2 * kDState;
-    hipLaunchKernelGGL((bwd_reduce_bc_kernel<Tg>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.ws_bc,
+    hipLaunchKernelGGL((bwd_reduce_bc_kernel<Tg>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a.ws_bc,
                        static_cast<Tg*>(dB), static_cast<Tg*>(dC), rows, a.nblk);
   }
   const int64_t np = a.d_inner * kDState;
