@@ -277,9 +277,10 @@ scan_chunk_kernel(ScanArgs a) {
   constexpr int NR = ZOH ? NS : 1;
   // The recurrence with transitions from powers: slot i holds state g + 4 i,
   // whose transition is e^(g+1) * (e^4)^i; e^(g+1) = e * e^(g&1) * (e^2)^(g>>1)
-  // is selected by per-wave 0/1 constants (fma(f, v, 1 - f) is v or exactly 1).
-  // No transcendental: eight multiplies, two selects and the update's three
-  // instructions per state.
+  // is selected by per-wave 0/1 constants (fma(f, v, 1 - f) is v or exactly 1)
+  // in the peeled ragged tile; full tiles run a copy of the loop per wave with
+  // the base formed directly.  No transcendental: at most eight multiplies,
+  // two selects and the update's three instructions per state.
   auto run_steps_pow_plain = [&](int n, int64_t tt0) SSM_INLINE {  // the peeled ragged tile
     const int ph = (int)((t_begin + tt0) & 7);
     for (int s = 0; s < n; ++s) {
@@ -303,8 +304,15 @@ scan_chunk_kernel(ScanArgs a) {
       }
     }
   };
-  auto run_steps_pow_piped = [&](auto n_c, int64_t tt0) SSM_INLINE {  // full tiles (n is a constant)
+  // Full tiles (n is a constant), instantiated once per wave: GB is the wave
+  // index g, so the base e^(g+1) is e, e^2, e * e^2 or e^4, the same products
+  // the selects form, with no select.
+  auto run_steps_pow_piped = [&](auto n_c, auto gb_c, int64_t tt0) SSM_INLINE {
     constexpr int n = decltype(n_c)::value;
+    constexpr int GB = decltype(gb_c)::value;
+    // Keeps the compiler from hoisting the four copies' common LDS reads above
+    // the switch on g, which held them live across it (187 VGPRs against 149).
+    __asm__ volatile("" ::: "memory");
     const int ph = (int)((t_begin + tt0) & 7);
     // Software-pipelined by two steps: a step's LDS operands -- (e, dt2 x) of the
     // lane's channel and the wave's four B and C values -- are read two steps
@@ -332,7 +340,11 @@ scan_chunk_kernel(ScanArgs a) {
       const float e = v.x;
       const float e2 = e * e;
       const float e4 = e2 * e2;
-      float ap = (e * __builtin_fmaf(pf1, e, pn1)) * __builtin_fmaf(pf2, e2, pn2);
+      float ap;
+      if constexpr (GB == 0) ap = e;
+      else if constexpr (GB == 1) ap = e2;
+      else if constexpr (GB == 2) ap = e * e2;
+      else ap = e4;
       float y = 0.0f;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -351,8 +363,16 @@ scan_chunk_kernel(ScanArgs a) {
     }
   };
   auto run_steps_pow = [&](auto n_c, int64_t tt0) SSM_INLINE {
-    if constexpr (std::is_same_v<decltype(n_c), int>) run_steps_pow_plain(n_c, tt0);
-    else run_steps_pow_piped(n_c, tt0);
+    if constexpr (std::is_same_v<decltype(n_c), int>) {
+      run_steps_pow_plain(n_c, tt0);
+    } else {
+      switch (g) {   // wave-uniform
+        case 0: run_steps_pow_piped(n_c, std::integral_constant<int, 0>(), tt0); break;
+        case 1: run_steps_pow_piped(n_c, std::integral_constant<int, 1>(), tt0); break;
+        case 2: run_steps_pow_piped(n_c, std::integral_constant<int, 2>(), tt0); break;
+        default: run_steps_pow_piped(n_c, std::integral_constant<int, 3>(), tt0); break;
+      }
+    }
   };
   auto run_steps = [&](auto n_c, int64_t tt0) SSM_INLINE {
     if constexpr (kPow) {

@@ -59,9 +59,17 @@ def test_no_scratch_spills(asm):
 
 def test_no_outlined_calls(asm):
     # every helper of a kernel body is inlined: a call would move live state
-    # through the calling convention's stack
+    # through the calling convention's stack.  A kernel larger than a branch's
+    # reach (+-128 KiB) jumps by s_getpc / s_add / s_setpc to a label of its
+    # own: that is a branch, not a call.
     for name, body in kernels(asm):
-        assert "s_swappc" not in body and "s_setpc" not in body, f"{name} makes a call"
+        assert "s_swappc" not in body and "s_call" not in body, f"{name} makes a call"
+        lines = body.split("\n")
+        for i, ln in enumerate(lines):
+            if "s_setpc" in ln:
+                window = "\n".join(lines[max(0, i - 5):i])
+                assert "s_getpc_b64" in window and re.search(r"s_add_u32 s\d+, s\d+, \(\.LBB", window), \
+                    f"{name}: s_setpc that is not a long branch"
 
 
 def test_kernel_hash_ignores_comments_only():
