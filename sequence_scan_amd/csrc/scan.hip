@@ -167,14 +167,20 @@ __global__ void __launch_bounds__(64) affine_exclusive_scan_kernel(const float* 
 // ----------------------------------------------------------- decode kernel
 //
 // One (b, d) pair per quad of lanes; lane q of the quad owns states 4q..4q+3
-// (one 16-byte load and store of the fp32 state).  The readout is reduced
-// over the quad with two DPP quad permutes; lane 0 of the quad applies the
-// D skip and the gate and stores out.  The state and the per-step x, delta,
-// z and out stream (non-temporal loads and stores): one step touches them
-// once, and the 128 MiB state of a batch-256 step does not survive in the
-// caches until the next step anyway.  Streaming the state too takes that step
-// from 63.9 to 57.7 us on MI355X (4.5 -> 5.0 TB/s).  A, B, C, D and the bias,
-// which many rows share, are ordinary cached loads.
+// (one 16-byte load and store of the fp32 state).  Each thread takes the same
+// channel in kDecodeRows consecutive batch rows: it issues every row's loads
+// before the first row's arithmetic, and the rows share the channel's A, D
+// and bias.  The readout is reduced over the quad with two DPP quad permutes;
+// lane 0 of the quad applies the D skip and the gate and stores out.  The
+// state and the per-step x, delta, z and out stream (non-temporal loads and
+// stores): one step touches them once, and the 128 MiB state of a batch-256
+// step does not survive in the caches until the next step anyway.  Streaming
+// the state too took that step from 63.9 to 57.7 us on MI355X (4.5 -> 5.0
+// TB/s), and two rows per thread from 58.3 to 50.7 us (5.7 TB/s; four rows:
+// 52.2 us; two lanes of eight states per channel: 60.8 us).  A, B, C, D and
+// the bias, which many rows share, are ordinary cached loads.
+constexpr int kDecodeRows = 2;
+
 template <typename Tin>
 __device__ __forceinline__ float nt_load(const void* p, int64_t i) {
   if constexpr (sizeof(Tin) == 4) {
@@ -187,46 +193,62 @@ __device__ __forceinline__ float nt_load(const void* p, int64_t i) {
 
 template <typename Tin, typename Tout, bool ZOH>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
-  // grid: x = blocks of 64 channels, y = batch row (no division by runtime sizes)
+  // grid: x = blocks of 64 channels, y = groups of kDecodeRows batch rows
   const int64_t d = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
   const int q = threadIdx.x & 3;
   if (d >= a.d_inner) return;  // whole quads leave together
-  const int64_t b = blockIdx.y;
-  const int64_t e = b * a.d_inner + d;
-
-  float4 hs = load_stream4(a.state + e * kDState + 4 * q);
+  const int64_t nb = a.pairs / a.d_inner;
   const float4 av = *reinterpret_cast<const float4*>(a.A + d * kDState + 4 * q);
-  float Bv[4], Cv[4];
-  load4<Tin>(a.B, b * kDState + 4 * q, Bv);
-  load4<Tin>(a.C, b * kDState + 4 * q, Cv);
-  const float x = nt_load<Tin>(a.x, e);
-  const float dl = nt_load<Tin>(a.delta, e);
-  const float u = dl + (a.bias != nullptr ? a.bias[d] : 0.0f);
-  const float dt = a.softplus ? softplus_f(u) : u;
-  const float dtx = dt * x;
-  float h[4] = {hs.x, hs.y, hs.z, hs.w};
   const float A2[4] = {av.x * kLog2e, av.y * kLog2e, av.z * kLog2e, av.w * kLog2e};
-  float y = 0.0f;
+  const float bias = a.bias != nullptr ? a.bias[d] : 0.0f;
+  const float Dd = a.D != nullptr ? a.D[d] : 0.0f;
+  // every row's loads first; a row past the batch (odd batch) re-reads the
+  // last row and stores nothing
+  float4 hs[kDecodeRows];
+  float Bv[kDecodeRows][4], Cv[kDecodeRows][4], x[kDecodeRows], dl[kDecodeRows], zv[kDecodeRows];
+  int64_t e[kDecodeRows];
+  bool live[kDecodeRows];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float u2 = dt * A2[i];
-    const float ar = __builtin_amdgcn_exp2f(u2);
-    // ZOH: (e^{dt A} - 1) / A = zoh_ratio(ar) * dt * log2(e)
-    if constexpr (ZOH) h[i] = __builtin_fmaf(ar, h[i], (zoh_ratio(ar, u2) * kLog2e) * (dtx * Bv[i]));
-    else h[i] = __builtin_fmaf(ar, h[i], dtx * Bv[i]);
-    y = __builtin_fmaf(Cv[i], h[i], y);
+  for (int r = 0; r < kDecodeRows; ++r) {
+    const int64_t br = (int64_t)blockIdx.y * kDecodeRows + r;
+    live[r] = br < nb;
+    const int64_t b = live[r] ? br : nb - 1;
+    e[r] = b * a.d_inner + d;
+    hs[r] = load_stream4(a.state + e[r] * kDState + 4 * q);
+    load4<Tin>(a.B, b * kDState + 4 * q, Bv[r]);
+    load4<Tin>(a.C, b * kDState + 4 * q, Cv[r]);
+    x[r] = nt_load<Tin>(a.x, e[r]);
+    dl[r] = nt_load<Tin>(a.delta, e[r]);
+    zv[r] = a.z != nullptr ? nt_load<Tin>(a.z, e[r]) : 0.0f;
   }
-  store_stream4(a.state + e * kDState + 4 * q, make_float4(h[0], h[1], h[2], h[3]));
-  // quad sum in a fixed order: (q0 + q1) + (q2 + q3) on every lane
-  y = y + SSM_DPP(0.0f, y, 0xB1, 0xf);  // quad_perm [1,0,3,2]
-  y = y + SSM_DPP(0.0f, y, 0x4E, 0xf);  // quad_perm [2,3,0,1]
-  if (q == 0) {
-    if (a.D != nullptr) y = __builtin_fmaf(a.D[d], x, y);
-    if (a.z != nullptr) y = y * silu_f(nt_load<Tin>(a.z, e));
-    if constexpr (sizeof(Tout) == 4) {
-      __builtin_nontemporal_store(y, static_cast<float*>(a.out) + e);
-    } else {
-      __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<uint16_t*>(a.out) + e);
+#pragma unroll
+  for (int r = 0; r < kDecodeRows; ++r) {
+    const float u = dl[r] + bias;
+    const float dt = a.softplus ? softplus_f(u) : u;
+    const float dtx = dt * x[r];
+    float h[4] = {hs[r].x, hs[r].y, hs[r].z, hs[r].w};
+    float y = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float u2 = dt * A2[i];
+      const float ar = __builtin_amdgcn_exp2f(u2);
+      // ZOH: (e^{dt A} - 1) / A = zoh_ratio(ar) * dt * log2(e)
+      if constexpr (ZOH) h[i] = __builtin_fmaf(ar, h[i], (zoh_ratio(ar, u2) * kLog2e) * (dtx * Bv[r][i]));
+      else h[i] = __builtin_fmaf(ar, h[i], dtx * Bv[r][i]);
+      y = __builtin_fmaf(Cv[r][i], h[i], y);
+    }
+    if (live[r]) store_stream4(a.state + e[r] * kDState + 4 * q, make_float4(h[0], h[1], h[2], h[3]));
+    // quad sum in a fixed order: (q0 + q1) + (q2 + q3) on every lane
+    y = y + SSM_DPP(0.0f, y, 0xB1, 0xf);  // quad_perm [1,0,3,2]
+    y = y + SSM_DPP(0.0f, y, 0x4E, 0xf);  // quad_perm [2,3,0,1]
+    if (q == 0 && live[r]) {
+      if (a.D != nullptr) y = __builtin_fmaf(Dd, x[r], y);
+      if (a.z != nullptr) y = y * silu_f(zv[r]);
+      if constexpr (sizeof(Tout) == 4) {
+        __builtin_nontemporal_store(y, static_cast<float*>(a.out) + e[r]);
+      } else {
+        __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<uint16_t*>(a.out) + e[r]);
+      }
     }
   }
 }
@@ -269,7 +291,8 @@ namespace {
 
 template <bool ZOH>
 void launch_decode_z(const DecodeArgs& a, DT in, DT out, hipStream_t s) {
-  const dim3 grid((unsigned)((a.d_inner + 63) / 64), (unsigned)(a.pairs / a.d_inner));
+  const dim3 grid((unsigned)((a.d_inner + 63) / 64),
+                  (unsigned)((a.pairs / a.d_inner + kDecodeRows - 1) / kDecodeRows));
   if (in == DT::F32 && out == DT::F32)
     hipLaunchKernelGGL((decode_kernel<float, float, ZOH>), dim3(grid), dim3(256), 0, s, a);
   else if (in == DT::F32 && out == DT::BF16)

@@ -455,54 +455,73 @@ __global__ void __launch_bounds__(256) ssd_carry_kernel(SsdArgs a) {
 // One step for every (b, h, p): the state row [N] is read and written once
 // (16 bytes per lane, N / 4 lanes per row), the readout is reduced across
 // those lanes with butterfly shuffles, and the row's first lane finishes y.
+// Each thread takes two rows of one head, channels p and p + kSsdRowStride
+// (kSsdRowStride = rows per 256 threads), which share the head's step, decay
+// and B/C values: both rows' loads are issued before either row's arithmetic.
+// (One row per thread took the batch-64 step of a 2.7B-like layer 69.6 us.)
 template <typename Tin, typename Tout, int N>
 __global__ void __launch_bounds__(256) ssd_update_kernel(SsdArgs a) {
   constexpr int LPR = N / 4;   // lanes per state row
-  // grid: x = blocks of 256 / LPR channels of one head, y = head, z = batch row
+  constexpr int RPB = 256 / LPR;  // rows per 256 threads: the stride between a thread's two rows
+  // grid: x = blocks of 2 * RPB channels of one head, y = head, z = batch row
   // (the indices come from the grid, with no division by runtime sizes)
-  const int p = (int)(blockIdx.x * (256 / LPR) + threadIdx.x / LPR);
+  const int p0 = (int)(blockIdx.x * (2 * RPB) + threadIdx.x / LPR);
   const int q = (int)(threadIdx.x % LPR);
   const int P = a.headdim, H = a.nheads, G = a.ngroups;
-  if (p >= P) return;                     // whole rows leave together
+  if (p0 >= P) return;                    // whole rows leave together
   const int h = (int)blockIdx.y;
   const int64_t b = blockIdx.z;
   const int64_t bh = b * H + h;
-  const int64_t row = bh * P + p;         // (b * H + h) * P + p
   const int g = h / (H / G);              // uniform in the workgroup
-  const float u = ld_in(static_cast<const Tin*>(a.dt) + bh) + (a.bias ? a.bias[h] : 0.0f);
-  const float dt = a.softplus ? softplus_f(u) : u;
-  const float ar = __builtin_amdgcn_exp2f(dt * a.A[h] * kLog2e);
-  const float x = ld_in(static_cast<const Tin*>(a.x) + row);
-  const float dtx = dt * x;
-  float* st = a.state + row * N + 4 * q;
-  float4 s4 = load_stream4(st);  // the state streams, as in the Mamba-1 decode
-  float hs[4] = {s4.x, s4.y, s4.z, s4.w};
   const int64_t bc = (b * G + g) * N + 4 * q;
   float Bv[4], Cv[4];
   load4<Tin>(a.B, bc, Bv);
   load4<Tin>(a.C, bc, Cv);
-  float y = 0.0f;
+  // the second row may lie past the head (headdim not a multiple of 2 RPB):
+  // it then re-reads the first row and stores nothing
+  const bool live1 = p0 + RPB < P;
+  int64_t row[2];
+  row[0] = bh * P + p0;                   // (b * H + h) * P + p
+  row[1] = live1 ? row[0] + RPB : row[0];
+  float4 s4[2];
+  float x[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hs[i] = __builtin_fmaf(ar, hs[i], dtx * Bv[i]);
-    y = __builtin_fmaf(Cv[i], hs[i], y);
+  for (int r = 0; r < 2; ++r) {
+    s4[r] = load_stream4(a.state + row[r] * N + 4 * q);  // the state streams, as in the Mamba-1 decode
+    x[r] = ld_in(static_cast<const Tin*>(a.x) + row[r]);
   }
-  store_stream4(st, make_float4(hs[0], hs[1], hs[2], hs[3]));
-  // The row's readout over its LPR lanes (16 or 32, aligned to the 16-lane
-  // DPP rows): quad permutes, then the 8- and 16-lane mirrors leave each
-  // 16-lane row's sum in all its lanes; with 32 lanes, row_bcast:15 adds the
-  // first half's sum into the second, whose first lane then holds the total.
-  y += SSM_DPP(0.0f, y, 0xB1, 0xf);   // quad_perm [1,0,3,2]
-  y += SSM_DPP(0.0f, y, 0x4E, 0xf);   // quad_perm [2,3,0,1]
-  y += SSM_DPP(0.0f, y, 0x141, 0xf);  // row_half_mirror
-  y += SSM_DPP(0.0f, y, 0x140, 0xf);  // row_mirror
-  if constexpr (LPR == 32) y += SSM_DPP(0.0f, y, 0x142, 0xa);  // row_bcast:15 into rows 1 and 3
-  static_assert(LPR == 16 || LPR == 32, "the readout sum assumes 16 or 32 lanes per row");
-  constexpr int kOut = LPR == 32 ? 16 : 0;  // the lane that holds the row's total
-  if (q == kOut) {
-    if (a.D) y = __builtin_fmaf(a.D[(int64_t)h * P + p], x, y);
-    if (a.z) y = y * silu_f(ld_in(static_cast<const Tin*>(a.z) + row));
-    Io<Tout>::store(a.out, row, y);
+  const float u = ld_in(static_cast<const Tin*>(a.dt) + bh) + (a.bias ? a.bias[h] : 0.0f);
+  const float dt = a.softplus ? softplus_f(u) : u;
+  const float ar = __builtin_amdgcn_exp2f(dt * a.A[h] * kLog2e);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (r == 1 && !live1) break;
+    const float dtx = dt * x[r];
+    float hs[4] = {s4[r].x, s4[r].y, s4[r].z, s4[r].w};
+    float y = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hs[i] = __builtin_fmaf(ar, hs[i], dtx * Bv[i]);
+      y = __builtin_fmaf(Cv[i], hs[i], y);
+    }
+    store_stream4(a.state + row[r] * N + 4 * q, make_float4(hs[0], hs[1], hs[2], hs[3]));
+    // The row's readout over its LPR lanes (16 or 32, aligned to the 16-lane
+    // DPP rows): quad permutes, then the 8- and 16-lane mirrors leave each
+    // 16-lane row's sum in all its lanes; with 32 lanes, row_bcast:15 adds the
+    // first half's sum into the second, whose first lane then holds the total.
+    y += SSM_DPP(0.0f, y, 0xB1, 0xf);   // quad_perm [1,0,3,2]
+    y += SSM_DPP(0.0f, y, 0x4E, 0xf);   // quad_perm [2,3,0,1]
+    y += SSM_DPP(0.0f, y, 0x141, 0xf);  // row_half_mirror
+    y += SSM_DPP(0.0f, y, 0x140, 0xf);  // row_mirror
+    if constexpr (LPR == 32) y += SSM_DPP(0.0f, y, 0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+    static_assert(LPR == 16 || LPR == 32, "the readout sum assumes 16 or 32 lanes per row");
+    constexpr int kOut = LPR == 32 ? 16 : 0;  // the lane that holds the row's total
+    if (q == kOut) {
+      const int p = r == 0 ? p0 : p0 + RPB;
+      if (a.D) y = __builtin_fmaf(a.D[(int64_t)h * P + p], x[r], y);
+      if (a.z) y = y * silu_f(ld_in(static_cast<const Tin*>(a.z) + row[r]));
+      Io<Tout>::store(a.out, row[r], y);
+    }
   }
 }
 
@@ -537,7 +556,7 @@ void launch_ssd_n(const SsdArgs& a, DT out, hipStream_t s) {
 
 template <typename Tin, typename Tout>
 void launch_ssd_update_t(const SsdArgs& a, hipStream_t s) {
-  const int rows_per_block = 256 / (a.d_state / 4);
+  const int rows_per_block = 2 * (256 / (a.d_state / 4));  // two rows per thread
   const dim3 grid((unsigned)((a.headdim + rows_per_block - 1) / rows_per_block), (unsigned)a.nheads,
                   (unsigned)a.batch);
   if (a.d_state == 64) hipLaunchKernelGGL((ssd_update_kernel<Tin, Tout, 64>), grid, dim3(256), 0, s, a);
