@@ -26,7 +26,8 @@ the whole batch with inputs resident in HBM.  Prints ONE JSON line:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--out-dtype f32|bf16] [--no-cpu-baseline] [--no-decode] [--no-legs]
   --workload valu   only the VALU issue-rate probe
-  --workload copy   only a 1 GiB device copy (the byte counters' reference)
+  --workload copy   only the 1 GiB streaming legs: torch's copy (the byte counters'
+                    reference) and the streaming probe's copy and read
 """
 from __future__ import annotations
 
@@ -345,12 +346,15 @@ def decode_case(steps):
     ms = e0.elapsed_time(e1)
     per_step_bytes = workloads.decode_algorithmic_bytes(cfg.batch, cfg.d_inner, cfg.d_state, "bf16", "f32")
     step_ms = ms / steps
+    copy_rec = read_record("copy-record")
     return {
         "workload": f"decode batch {cfg.batch}, d_inner {cfg.d_inner}, d_state 16, {steps} steps, bf16 in, fp32 state/out",
         "tokens_per_s": cfg.batch * steps / (ms / 1e3),
         "us_per_step": step_ms * 1e3,
         "GBps_incl_state": per_step_bytes / (step_ms / 1e3) / 1e9,
         "hbm_frac_incl_state": per_step_bytes / (step_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "frac_of_measured_copy": (round(per_step_bytes / (step_ms / 1e3) / 1e9 / copy_rec["GBps"], 4)
+                                  if copy_rec else None),
     }
 
 
@@ -615,6 +619,43 @@ def ssd_long_case():
     return res
 
 
+def stream_case(steps, warmup):
+    """1 GiB of fp32 copied by torch (the byte counters' reference), and copied and
+    read by the streaming probe (csrc/stream_probe.hip): the achievable HBM rates
+    for a read + write stream and a read-only stream."""
+    import ctypes
+
+    import torch
+
+    from sequence_scan_amd import build as lib_build
+    lib = ctypes.CDLL(lib_build.PROBE_LIB)
+    lib.ssm_stream_probe_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_void_p]
+    lib.ssm_stream_probe_launch.restype = ctypes.c_int
+    n = 1 << 28
+    nbytes = n * 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def probe(kind, out):
+        rc = lib.ssm_stream_probe_launch(kind, src.data_ptr(), out.data_ptr(), n // 4, stream)
+        if rc != 0:
+            raise RuntimeError(f"stream probe launch failed: hip error {rc}")
+
+    res = {"metric": "device streaming bandwidth", "unit": "GB/s", "buffer_bytes": nbytes, "n_gpus": 1,
+           "steps": steps, "warmup": warmup}
+    for name, fn, traffic in (("torch_copy", lambda: dst.copy_(src), 2 * nbytes),
+                              ("probe_copy", lambda: probe(0, dst), 2 * nbytes),
+                              ("probe_read", lambda: probe(1, sink), nbytes)):
+        settle(fn)
+        ms, _ = time_steps(fn, steps, warmup)
+        res[name] = {"GBps": round(traffic / (ms / 1e3) / 1e9, 1), "ms": round(ms, 4), "bytes": traffic}
+    res["value"] = res["probe_copy"]["GBps"]
+    return res
+
+
 def valu_probe_case(total_iters=16384):
     """SIMD-cycles per wave64 instruction of v_mul_f32, v_fma_f32, v_exp_f32, v_log_f32
     and v_rcp_f32, and per state update of the scan's instruction mix (two v_mul, two
@@ -811,18 +852,10 @@ def main():
     ssm.library()
 
     if args.workload == "copy":
-        # a plain device-to-device copy of known size: the reference point for
-        # the hardware byte counters and the achievable streaming bandwidth
-        n = 1 << 28
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        copy = lambda: dst.copy_(src)
-        settle(copy)
-        ms, _ = time_steps(copy, args.steps, args.warmup)
-        nbytes = 2 * n * 4
-        print(json.dumps({"metric": "device copy bandwidth (read + write)", "value": round(nbytes / (ms / 1e3) / 1e9, 1),
-                          "unit": "GB/s", "bytes_per_copy": nbytes, "ms_per_copy": round(ms, 4), "n_gpus": 1,
-                          "steps": args.steps, "warmup": args.warmup}), flush=True)
+        # a plain device-to-device copy of known size (torch's copy kernel): the
+        # reference point for the hardware byte counters; beside it the streaming
+        # probe's copy and read of the same buffer, the achievable HBM rates
+        print(json.dumps(stream_case(args.steps, args.warmup)), flush=True)
         return
 
     if args.workload == "valu":
@@ -888,6 +921,7 @@ def main():
         "launch_timing": "timed region (back-to-back launches)" if single_launch else "single calls",
         "isolated_call_us": round(i_avg * 1e3, 2),
         "frac_of_measured_copy": (round(k_gbs / copy_rec["GBps"], 4) if copy_rec else None),
+        "measured_copy_GBps": copy_rec["GBps"] if copy_rec else None,
         "cold_cache_us": {k: round(v * 1e3, 2) for k, v in cw.items()},
         "cold_cache_timing": "single synchronised calls, cold (after a 1 GiB read) and warm interleaved",
         # The ceiling beside HBM is the VALU issue rate of the state update's

@@ -43,9 +43,9 @@ SOURCES = sorted({u[0] for u in DEVICE_UNITS + HOST_UNITS})
 HEADERS = [os.path.join(CSRC, f) for f in ("internal.h", "device.h", "scan_kernel.h")] + [
     os.path.join(os.path.dirname(HERE), "include", "ssmscan.h")]
 LIB = os.path.join(HERE, "libssmscan.so")
-# The benchmark's VALU issue-rate probe: a separate small library, not part of
-# the scan library's ABI.
-PROBE_SRC = os.path.join(CSRC, "valu_probe.hip")
+# The benchmark's probes (VALU issue rates, streaming bandwidth): a separate
+# small library, not part of the scan library's ABI.
+PROBE_SRCS = [os.path.join(CSRC, "valu_probe.hip"), os.path.join(CSRC, "stream_probe.hip")]
 PROBE_LIB = os.path.join(HERE, "libssmprobe.so")
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
@@ -126,7 +126,7 @@ def build(verbose: bool = False) -> str:
         # -z defs: a launcher declared but built in no unit fails here, not at load time
         ptmp = PROBE_LIB + f".tmp{os.getpid()}"
         _run_all([["hipcc", *FLAGS, "-Wl,-z,defs", *objs, "-o", tmp],
-                  ["hipcc", *FLAGS, "-Wl,-z,defs", PROBE_SRC, "-o", ptmp]], verbose)
+                  ["hipcc", *FLAGS, "-Wl,-z,defs", *PROBE_SRCS, "-o", ptmp]], verbose)
     os.replace(tmp, LIB)
     os.replace(ptmp, PROBE_LIB)
     return LIB

@@ -30,6 +30,17 @@ def test_every_declared_function_is_exported():
         assert hasattr(lib, n), f"{n} declared in ssmscan.h but not exported"
 
 
+def test_probe_library_exports():
+    """The benchmark's probe library (VALU issue rates, streaming bandwidth) is
+    separate from the scan library and exports its launchers."""
+    from sequence_scan_amd import build as lib_build
+    probe = ctypes.CDLL(lib_build.PROBE_LIB)
+    for n in ("ssm_probe_launch", "ssm_probe_ops_per_iter", "ssm_stream_probe_launch"):
+        assert hasattr(probe, n)
+    lib = ssm.library()
+    assert not hasattr(lib, "ssm_stream_probe_launch") and not hasattr(lib, "ssm_probe_launch")
+
+
 def test_version_and_strings():
     assert ssm.ssm_abi_version() == 10
     for code, name in ssm.STATUS_NAMES.items():
