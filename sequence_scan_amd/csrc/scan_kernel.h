@@ -74,7 +74,6 @@ scan_chunk_kernel(ScanArgs a) {
   __shared__ float sh_B[T][kDState];
   __shared__ float sh_C[PASS_A ? 1 : T][kDState];
   __shared__ float sh_y[PASS_A ? 1 : T][G * kWave + 1];  // partial readouts, [row][wave][channel]
-  __shared__ float sh_dt2[PASS_A && kPow ? T : 1][kWave + 1];  // pass A with powers: dt2 for the step-size sum
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -158,6 +157,14 @@ scan_chunk_kernel(ScanArgs a) {
     for (int i = 0; i < NS; ++i) h[i] = 0.0f;
   }
   float dtsum = 0.0f;
+  // pass A with powers: the step sizes of this thread's items, summed over the
+  // chunk's steps in the staging phase (reduced over threads at the end)
+  constexpr bool kItemSum = PASS_A && kPow;
+  float isum[kItemSum ? IPT : 1][kItemSum ? CW : 1];
+#pragma unroll
+  for (int it = 0; it < (kItemSum ? IPT : 1); ++it)
+#pragma unroll
+    for (int q = 0; q < (kItemSum ? CW : 1); ++q) isum[it][q] = 0.0f;
   float* const ckb = ckpt_mode ? a.ckpt + (((int64_t)b * a.ckpt_nblk + blockIdx.x) * a.ckpt_tiles) * (kWave * kDState) +
                                      lane * kDState + g * 4
                                : nullptr;
@@ -212,7 +219,7 @@ scan_chunk_kernel(ScanArgs a) {
   // fp32.  The softplus switch is taken once per tile (a uniform branch
   // around the whole item loop), never per element.
   // With transitions from powers, (e, dt2 * x) is staged, e = exp2(dt2 A[d, 0]).
-  auto discretise = [&](Bank& bk, auto sp_c, auto pow_c) SSM_INLINE {
+  auto discretise = [&](Bank& bk, int nt, auto sp_c, auto pow_c) SSM_INLINE {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
 #pragma unroll
@@ -222,7 +229,8 @@ scan_chunk_kernel(ScanArgs a) {
         const float dt2 = decltype(sp_c)::value ? softplus2_f(u2) : u2;
         if constexpr (decltype(pow_c)::value) {
           sh_dtv[irow[it]][icol[it] + q] = make_float2(__builtin_amdgcn_exp2f(dt2 * iA0[it][q]), dt2 * x);
-          if constexpr (PASS_A) sh_dt2[irow[it]][icol[it] + q] = dt2;
+          // rows past a ragged tile's end repeat its last row: not summed
+          if constexpr (kItemSum) isum[it][q] += irow[it] < nt ? dt2 : 0.0f;
         } else {
           sh_dtv[irow[it]][icol[it] + q] = make_float2(dt2, dt2 * x);
         }
@@ -230,18 +238,18 @@ scan_chunk_kernel(ScanArgs a) {
       }
     }
   };
-  auto commit = [&](Bank& bk) SSM_INLINE {
+  auto commit = [&](Bank& bk, int nt) SSM_INLINE {
     if constexpr (kPow) {
       if (pow_mode) {
-        if (softplus) discretise(bk, std::true_type(), std::true_type());
-        else discretise(bk, std::false_type(), std::true_type());
+        if (softplus) discretise(bk, nt, std::true_type(), std::true_type());
+        else discretise(bk, nt, std::false_type(), std::true_type());
       } else {
-        if (softplus) discretise(bk, std::true_type(), std::false_type());
-        else discretise(bk, std::false_type(), std::false_type());
+        if (softplus) discretise(bk, nt, std::true_type(), std::false_type());
+        else discretise(bk, nt, std::false_type(), std::false_type());
       }
     } else {
-      if (softplus) discretise(bk, std::true_type(), std::false_type());
-      else discretise(bk, std::false_type(), std::false_type());
+      if (softplus) discretise(bk, nt, std::true_type(), std::false_type());
+      else discretise(bk, nt, std::false_type(), std::false_type());
     }
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
@@ -297,11 +305,7 @@ scan_chunk_kernel(ScanArgs a) {
         h[i] = __builtin_fmaf(ap, h[i], v.y * sh_B[s][g * NS + i]);
         if (!PASS_A) y = __builtin_fmaf(sh_C[PASS_A ? 0 : s][g * NS + i], h[i], y);
       }
-      if (PASS_A) {
-        dtsum += sh_dt2[PASS_A ? s : 0][loff];
-      } else {
-        sh_y[PASS_A ? 0 : s][(PASS_A ? 0 : g) * kWave + lane] = y;
-      }
+      if (!PASS_A) sh_y[PASS_A ? 0 : s][(PASS_A ? 0 : g) * kWave + lane] = y;
     }
   };
   // Full tiles (n is a constant), instantiated once per wave: GB is the wave
@@ -352,11 +356,7 @@ scan_chunk_kernel(ScanArgs a) {
         h[i] = __builtin_fmaf(ap, h[i], v.y * bv[i]);
         if (!PASS_A) y = __builtin_fmaf(cv[i], h[i], y);
       }
-      if (PASS_A) {
-        dtsum += sh_dt2[PASS_A ? s : 0][loff];
-      } else {
-        sh_y[PASS_A ? 0 : s][(PASS_A ? 0 : g) * kWave + lane] = y;
-      }
+      if (!PASS_A) sh_y[PASS_A ? 0 : s][(PASS_A ? 0 : g) * kWave + lane] = y;
       // keep the prefetch distance: the scheduler would otherwise sink the
       // reads of step s + PD next to their use
       __builtin_amdgcn_sched_barrier(0);
@@ -466,7 +466,7 @@ scan_chunk_kernel(ScanArgs a) {
   // have been committed: the wait for those inputs then never includes the
   // acknowledgement of stores issued just before it.
   auto full_tile = [&](Bank& bk, int64_t tt0, int64_t pf0, auto has_prev_c, int64_t prev0) SSM_INLINE {
-    commit(bk);
+    commit(bk, T);
     if (!PASS_A && decltype(has_prev_c)::value) store(prev0, T, true);
     issue(bk, pf0, T);
     block_sync();
@@ -482,7 +482,7 @@ scan_chunk_kernel(ScanArgs a) {
   if (tail > 0) {
     issue(bk0, 0, tail);
     if (nfull > 0) issue(bk1, tail, T);
-    commit(bk0);
+    commit(bk0, tail);
     if (nfull > 1) issue(bk0, tail + T, T);
     block_sync();
     run_steps(tail, 0);
@@ -516,6 +516,22 @@ scan_chunk_kernel(ScanArgs a) {
     float* dst = a.ws_state + (((int64_t)b * K + k) * Dn + dl) * kDState;
 #pragma unroll
     for (int i = 0; i < NS; ++i) dst[st_of(i)] = h[i];
+    if (kItemSum && pow_mode) {
+      // the items' sums, one row of the tile's channels per thread row, in the
+      // LDS of the last tile's (e, dt2 x), which the barrier after that tile's
+      // recurrence has freed; each channel then sums its T rows in order
+      float* red = reinterpret_cast<float*>(&sh_dtv[0][0]);  // [T][kWave]
+#pragma unroll
+      for (int it = 0; it < (kItemSum ? IPT : 1); ++it)
+#pragma unroll
+        for (int q = 0; q < (kItemSum ? CW : 1); ++q) red[irow[it] * kWave + icol[it] + q] = isum[it][q];
+      block_sync();
+      if (g == 0) {
+        float sum = 0.0f;
+        for (int r = 0; r < T; ++r) sum += red[r * kWave + loff];
+        dtsum = sum;
+      }
+    }
     if (g == 0) a.ws_dtsum[((int64_t)b * K + k) * Dn + dl] = dtsum;
   } else if (!PASS_A && k == K - 1 && a.last_state != nullptr) {
     float* dst = a.last_state + ((int64_t)b * Dn + dl) * kDState;
