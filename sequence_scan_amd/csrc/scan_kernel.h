@@ -159,7 +159,7 @@ scan_chunk_kernel(ScanArgs a) {
   float dtsum = 0.0f;
   // pass A with powers: the step sizes of this thread's items, summed over the
   // chunk's steps in the staging phase (reduced over threads at the end)
-  constexpr bool kItemSum = PASS_A && kPow;
+  constexpr bool kItemSum = PASS_A && kPow && !CKPT;  // the checkpoint pass writes no sums
   float isum[kItemSum ? IPT : 1][kItemSum ? CW : 1];
 #pragma unroll
   for (int it = 0; it < (kItemSum ? IPT : 1); ++it)
