@@ -275,18 +275,36 @@ __global__ void __launch_bounds__(256, 3) scan_bwd_kernel(BwdArgs a) {
       }
     }
 
-    // reverse within the tile
+    // reverse within the tile.  With bf16 inputs each step's LDS operands are
+    // read one step ahead, before the later step's guard (rows past a ragged
+    // tile's end are in bounds and unused), so their latency hides behind that
+    // step's arithmetic; fp32 inputs' wider register banks leave no room for
+    // the prefetch (it would spill), so they read each step's operands there.
+    constexpr bool kPrefetch = sizeof(Tin) == 2;
+    float2 fv;
+    float fdy;
+    float4 fb, fc;
+    auto fetch = [&](int r) SSM_INLINE {
+      fv = sh_dtu[r][loff];
+      fdy = sh_dy[r][loff];
+      fb = *reinterpret_cast<const float4*>(&sh_B[r][g * NS]);
+      fc = *reinterpret_cast<const float4*>(&sh_C[r][g * NS]);
+    };
+    if (kPrefetch) fetch(T - 1);
 #pragma unroll
     for (int s = T - 1; s >= 0; --s) {
+      if (!kPrefetch) fetch(s);
+      const float2 v = fv;
+      const float dy = fdy;
+      const float bq[4] = {fb.x, fb.y, fb.z, fb.w}, cq[4] = {fc.x, fc.y, fc.z, fc.w};
+      if (kPrefetch && s > 0) fetch(s - 1);
       if (s < nt) {
-        const float2 v = sh_dtu[s][loff];
-        const float dy = sh_dy[s][loff];
         float s1 = 0.0f, s2 = 0.0f, cb[NS], cc[NS];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
           const float aa = kKeepA ? ap[s][i] : __builtin_amdgcn_exp2f(v.x * Ad[i]);
-          const float Bs = sh_B[s][g * NS + i];
-          const float dh = __builtin_fmaf(dy, sh_C[s][g * NS + i], carry[i]);
+          const float Bs = bq[i];
+          const float dh = __builtin_fmaf(dy, cq[i], carry[i]);
           const float hs = s + 1 < T ? hp[s + 1][i] : h[i];  // the state after step s
           cc[i] = dy * hs;
           cb[i] = dh * v.y;
