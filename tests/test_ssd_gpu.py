@@ -129,7 +129,10 @@ def test_ssd_chunked_prefill_and_empty():
     assert torch.equal(last, state)
 
 
-@pytest.mark.parametrize("dtype,P,N,G", [("f32", 64, 128, 1), ("bf16", 64, 64, 2), ("f32", 48, 64, 1)])
+# headdim 48 at d_state 64 and 20, 40 at d_state 128 leave the second row of some
+# threads (channels p and p + 256 * 4 / d_state) past the head
+@pytest.mark.parametrize("dtype,P,N,G", [("f32", 64, 128, 1), ("bf16", 64, 64, 2), ("f32", 48, 64, 1),
+                                         ("bf16", 20, 128, 1), ("f32", 40, 128, 2)])
 def test_ssd_decode_vs_oracle(dtype, P, N, G):
     say(f"SSD decode {dtype} headdim {P} d_state {N} ngroups {G}: 5 steps from a stored state")
     batch, H, steps = 3, 4, 5
